@@ -1,0 +1,213 @@
+"""Throughput of the layer-wise, height-sharded VAE decode on one MI355X.
+
+One step = one band decode (vaep_decode_bands) of the 1024x1024 bf16 preset:
+latent 1x16x128x128 split into 4 uneven latent row bands (31/33/32/32), every
+layer of the decoder on every band, output 1x3x1024x1024.  Latent, weights and
+workspace are resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is decoded Mpixel/s from a plain timed region
+(W warmup + K timed decodes between stream synchronisations).  A second region
+of K decodes brackets every kernel launch with HIP events on the decode stream
+(vaep_profile_begin/_end) to give each kernel's average duration, from which
+the roofline fractions are computed with algorithmic flops / bytes per launch.
+The CPU baseline times the oracle on a bounded sample of the same decoder.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decoded Mpixel/s, 1024² bf16 VAE decode; conv MFMA util; GroupNorm GB/s"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=3, help="preset id (3 = the 1024^2 headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-latent", type=int, default=48,
+                    help="latent side of the oracle's bounded sample")
+    return ap.parse_args()
+
+
+def summarise(recs, steps):
+    """Group per-launch records into the classes the roofline reports."""
+    import spatially_sharded_conv_amd._lib as L
+    out = {}
+
+    def add(key, r):
+        d = out.setdefault(key, {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
+        d["launches"] += 1
+        d["ms"] += r["ms"]
+        d["flops"] += r["flops"]
+        d["bytes"] += r["bytes"]
+
+    for r in recs:
+        if r["step"] == L.STEP_CONV:
+            k = r["kt"] * r["ks"] * r["ks"] * r["cin"]
+            # MFMA-bound convolutions: spatial 3x3 (x3) with K >= 1152 and >= 96 outputs;
+            # conv_in, conv_out, 1x1 projections and time convs are reported apart
+            dense = r["ks"] == 3 and k >= 1152 and r["cout"] >= 96 and r["mode"] == 0
+            add("conv_mfma" if dense else "conv_other", r)
+        elif r["step"] == L.STEP_GROUPNORM:
+            add("groupnorm", r)
+        elif r["step"] == L.STEP_RMSNORM:
+            add("rmsnorm", r)
+        elif r["step"] == L.STEP_ATTENTION:
+            add("attention", r)
+        else:
+            add("other", r)
+    total = sum(d["ms"] for d in out.values())
+    for d in out.values():
+        d["ms_per_step"] = d["ms"] / steps
+        d["share"] = d["ms"] / total if total else 0.0
+        d["tflops"] = d["flops"] / (d["ms"] * 1e-3) / 1e12 if d["ms"] else 0.0
+        d["gbs"] = d["bytes"] / (d["ms"] * 1e-3) / 1e9 if d["ms"] else 0.0
+        d["avg_launch_ms"] = d["ms"] / d["launches"]
+    return out
+
+
+def cpu_baseline(cfg_id, side):
+    """The oracle as it stands, on a bounded sample: the same decoder on a side x side latent."""
+    import torch
+    from oracle import Precision, decode_full
+    from synth import make_latent, make_params, preset
+    cfg = preset(cfg_id).with_size(latent_h=side, latent_w=side, band_starts=(0, side))
+    params = make_params(cfg)
+    z = make_latent(cfg)
+    t0 = time.perf_counter()
+    y = decode_full(cfg, params, z, Precision("f32"))
+    dt = time.perf_counter() - t0
+    px = y.shape[0] * y.shape[-1] * y.shape[-2] * (y.shape[2] if y.dim() == 5 else 1)
+    return {"value": px / dt / 1e6, "unit": "Mpixel/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"one full decode of the same decoder and weights on a seeded {side}x{side} latent "
+                      f"({y.shape[-2]}x{y.shape[-1]} output, {px} px) in {dt:.1f} s, fp64 arithmetic"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: every band of the decode runs on this device and there "
+              f"is no multi-GPU path in this build (asked for --gpus {args.gpus}, WORLD_SIZE {world}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import spatially_sharded_conv_amd as vaep
+    from synth import make_latent, make_params, preset
+
+    torch.cuda.set_device(0)
+    cfg = preset(args.config)
+    params = make_params(cfg)
+    lc = vaep.make_config(cfg.family, cfg.dtype, cfg.z_channels, cfg.stage_channels,
+                          cfg.resnets_per_stage, cfg.norm_groups, cfg.temporal_up_stages, cfg.eps)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dev = [params[n].to(tdt).cuda() for n, _ in vaep.param_info(lc)]
+    dec = vaep.Decoder(lc, dev)
+    del dev
+    latent = make_latent(cfg).to(tdt).cuda()
+    starts = cfg.band_starts
+    nb = len(starts) - 1
+    out = torch.empty(cfg.output_shape(), dtype=torch.float32, device="cuda")
+    ws = dec.workspace(cfg.batch, cfg.frames, cfg.latent_h, cfg.latent_w, nb)
+    stream = torch.cuda.current_stream()
+    pixels = out.numel() // 3
+
+    for _ in range(args.warmup):
+        dec.decode_bands(latent, starts, out, ws, stream)
+    torch.cuda.synchronize()
+
+    # plain timed region
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        rc, info = dec.decode_bands(latent, starts, out, ws, stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+    value = pixels / (ms * 1e-3) / 1e6
+
+    # event-bracketed region: per-launch kernel durations on the decode stream
+    vaep.profile_begin(dec, max_launches=args.steps * (info.n_launches + 8))
+    torch.cuda.synchronize()
+    p_start = torch.cuda.Event(enable_timing=True)
+    p_end = torch.cuda.Event(enable_timing=True)
+    p_start.record(stream)
+    for _ in range(args.steps):
+        dec.decode_bands(latent, starts, out, ws, stream)
+    p_end.record(stream)
+    torch.cuda.synchronize()
+    recs = vaep.profile_end(dec)
+    ms_prof = p_start.elapsed_time(p_end) / args.steps
+    cls = summarise(recs, args.steps)
+    conv = cls.get("conv_mfma", {"tflops": 0.0, "flops": 0.0, "launches": 1, "avg_launch_ms": 0.0})
+    gn = cls.get("groupnorm") or cls.get("rmsnorm") or {"gbs": 0.0}
+
+    roofline = {
+        "kernel": "conv_mfma_bf16 (implicit-GEMM 3x3 / 3x3x3 halo conv, v_mfma_f32_32x32x16_bf16)",
+        "bound": "mfma",
+        "achieved": round(conv["tflops"], 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(conv["tflops"] / PEAK_BF16_TFLOPS, 4),
+        "traffic": None,
+        "launches_per_step": conv["launches"] // args.steps,
+        "avg_launch_ms": round(conv["avg_launch_ms"], 4),
+        "flops_per_launch": conv["flops"] / max(1, conv["launches"]),
+    }
+    norm_key = "groupnorm" if "groupnorm" in cls else "rmsnorm"
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "Mpixel/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: band decode of a seeded {cfg.z_channels}x{cfg.latent_h}x{cfg.latent_w} "
+                        f"latent (batch {cfg.batch}{', frames ' + str(cfg.frames) if cfg.is_video else ''}) "
+                        f"on {nb} latent row bands {[b - a for a, b in zip(starts, starts[1:])]}, "
+                        f"output {list(out.shape)}",
+            "batch": cfg.batch, "bands": list(starts), "random_init": True,
+            "storage": "bf16 weights/latent/matrix operands, fp32 conv outputs and statistics",
+        },
+        "roofline": roofline,
+        "norm": {
+            "kernel": f"{norm_key} (stats -> merge -> apply + SiLU)" if norm_key == "groupnorm" else "rmsnorm + SiLU",
+            "bound": "hbm", "achieved": round(gn.get("gbs", 0.0), 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gn.get("gbs", 0.0) / PEAK_HBM_GBS, 4),
+        },
+        "breakdown": {k: {"ms_per_step": round(v["ms_per_step"], 4), "share": round(v["share"], 4),
+                          "launches_per_step": v["launches"] // args.steps,
+                          "tflops": round(v["tflops"], 2), "gbs": round(v["gbs"], 1)}
+                      for k, v in sorted(cls.items())},
+        "profiled_ms_per_step": round(ms_prof, 4),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample_latent if not cfg.is_video else 8)
+    dec.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+/*
+ * vaep.h -- C ABI of the layer-wise, height-sharded VAE decoder for MI355X (gfx950).
+ *
+ * The method (ChituDiffusion, "VAEP: VAE 并行解码", sections on height sharding,
+ * conv halos, the GroupNorm merge and AGKV; and "Static Layer-Wise VAE Decode",
+ * "Semantics and Communication" operator table):
+ *   - the latent is split along its height into disjoint row bands, which may be
+ *     uneven; every band keeps all channels, the full width and the whole time axis,
+ *     and its rows double with every 2x upsample;
+ *   - a convolution reads kernel-radius halo rows from the neighbouring bands, with
+ *     zero padding only at the global image edges, and keeps only its own output rows;
+ *   - GroupNorm computes local FP32 central moments per (sample, group) and merges them
+ *     with actual-element-count weights;
+ *   - attention computes Q, K, V locally and runs each band's Q against the global K/V;
+ *   - activations, pointwise ops, channel RMSNorm and nearest upsampling stay local;
+ *   - the decoded rows of every band land in one output (the leader's).
+ * On one GPU every band is a share of this device: halo rows, statistics and K/V pass
+ * through device memory; there are no collectives.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named "device" are HIP device pointers owned by the caller, unless a
+ *     function says otherwise.  Host pointers are read before the call returns.
+ *   - All GPU work is enqueued on the caller's stream (a hipStream_t passed as void*;
+ *     NULL = the default stream); the caller keeps device buffers alive until the
+ *     stream has finished.  No entry point synchronises the stream, except
+ *     vaep_model_create (see there).
+ *   - Return value: VAEP_OK (0) on success, a positive warning code on success with a
+ *     warning, or a negative error code.  On error nothing has been enqueued and
+ *     output buffers are untouched; vaep_last_error() describes the failure.
+ *   - No C++ exception crosses this boundary.
+ */
+#ifndef VAEP_H
+#define VAEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status codes */
+enum {
+  VAEP_OK = 0,
+  VAEP_WARN_FELL_BACK = 1,      /* decoded, but as one dense band (see vaep_decode_bands) */
+  VAEP_ERR_INVALID_ARG = -1,    /* bad pointer, shape, band table or size */
+  VAEP_ERR_UNSUPPORTED = -2,    /* configuration outside what the library implements */
+  VAEP_ERR_WORKSPACE = -3,      /* workspace missing or smaller than vaep_workspace_bytes */
+  VAEP_ERR_HIP = -4,            /* a HIP runtime call failed */
+  VAEP_ERR_NOT_READY = -5       /* no usable gfx950 device */
+};
+
+enum { VAEP_FAMILY_KL2D = 1,    /* AutoencoderKL-style 2-D decoder (GroupNorm) */
+       VAEP_FAMILY_WAN3D = 2 }; /* Wan-style causal 3-D video decoder (channel RMSNorm) */
+/* Storage policy.  Convolution / projection outputs -- the residual stream, conv1
+ * outputs, shortcuts and the decoded image -- are fp32 in every configuration (the
+ * fp32 accumulator is stored as is).  The compute dtype is that of the weights, the
+ * latent, and the operands of the matrix products: normalised (norm + SiLU)
+ * activations and the attention Q, K, V and attention output.  Statistics are fp32
+ * (band moments are accumulated and merged in fp64, then rounded once). */
+enum { VAEP_DTYPE_F32 = 1,      /* fp32 everywhere */
+       VAEP_DTYPE_BF16 = 2 };   /* bf16 weights, latent and matrix-product operands */
+
+#define VAEP_MAX_STAGES 6
+#define VAEP_MAX_BANDS 64
+
+/* Decoder description.  Stage i (decode order) ends with `resnets_per_stage` resnets
+ * whose first maps the previous width to stage_channels[i]; every stage but the last
+ * is followed by nearest-2x + 3x3 conv; for WAN3D the first `temporal_up_stages`
+ * of those also run the causal temporal upsample (T -> 2T-1) before it. */
+typedef struct vaep_config {
+  int32_t family;                           /* VAEP_FAMILY_* */
+  int32_t dtype;                            /* VAEP_DTYPE_* */
+  int32_t z_channels;                       /* latent channels */
+  int32_t n_stages;                         /* 1 .. VAEP_MAX_STAGES */
+  int32_t stage_channels[VAEP_MAX_STAGES];  /* output width of each up stage (<= 1024) */
+  int32_t resnets_per_stage;
+  int32_t norm_groups;                      /* GroupNorm groups (KL2D); 0 for WAN3D */
+  int32_t temporal_up_stages;               /* WAN3D only */
+  float eps;                                /* norm epsilon */
+} vaep_config;
+
+/* Optional report filled by vaep_decode_bands. */
+typedef struct vaep_decode_info {
+  int32_t bands_used;        /* number of bands actually decoded */
+  int32_t fell_back;         /* 1 if the dense one-band path was taken */
+  int32_t n_launches;        /* kernels enqueued by the call */
+  int32_t reserved;
+  uint64_t workspace_bytes;  /* bytes of the workspace the call used */
+} vaep_decode_info;
+
+typedef struct vaep_model vaep_model;  /* opaque; owned by the library */
+
+/* Thread-local text of the last error on this thread ("" if none).  Never NULL. */
+const char* vaep_last_error(void);
+
+/* Library version string, e.g. "vaep 0.1 gfx950". */
+const char* vaep_version(void);
+
+/* Fill *out with preset `id`: 1 tiny KL2D fp32 (4ch 8x8 latent, widths 64/32, GN 8);
+ * 2-4 FLUX.1-style KL2D bf16 (16ch latent, widths 512/512/256/128, 3 resnets, GN 32);
+ * 5 Wan-style WAN3D bf16 (16ch latent, widths 384/384/192/96, 2 resnets, RMSNorm,
+ * 2 temporal upsample stages).  Presets 2-4 share the decoder and differ only in the
+ * latent the caller decodes.  Returns VAEP_ERR_INVALID_ARG for other ids. */
+int vaep_config_preset(int id, vaep_config* out);
+
+/* Canonical parameter list of a decoder.  vaep_param_count returns the number of
+ * parameter tensors (or a negative error).  vaep_param_info writes the name of
+ * parameter j (NUL-terminated, truncated to name_cap), its PyTorch-style shape
+ * (conv weight [Co, Ci, (kt,) kh, kw], linear weight [Co, Ci], bias/norm [C]) into
+ * shape[0..*ndim-1] (at most 5 dims) and returns VAEP_OK. */
+int vaep_param_count(const vaep_config* cfg);
+int vaep_param_info(const vaep_config* cfg, int j, char* name, int name_cap,
+                    int64_t shape[5], int* ndim);
+
+/* Build a decoder.  params[j] is a device pointer to parameter j in canonical order,
+ * contiguous, in the config's dtype.  The library copies and repacks every parameter
+ * into memory it owns (one hipMalloc), so the caller may free params once this
+ * returns; this call synchronises `stream` before returning.  *out receives the model.
+ * Errors: INVALID_ARG (NULL pointers, n_params mismatch, channel counts that are not
+ * multiples of 32 where the kernels need it), UNSUPPORTED, HIP, NOT_READY. */
+int vaep_model_create(const vaep_config* cfg, const void* const* params, int n_params,
+                      void* stream, vaep_model** out);
+
+/* Release a model and its device memory.  The caller must have finished every
+ * stream that uses it.  NULL is accepted (no-op). */
+int vaep_model_destroy(vaep_model* model);
+
+/* Workspace needed to decode a latent of `batch` x [frames x] latent_h x latent_w
+ * with up to `n_bands` bands (frames = 1 for KL2D).  The same size serves
+ * vaep_decode_full and every band table with at most n_bands bands. */
+int vaep_workspace_bytes(const vaep_model* model, int batch, int frames, int latent_h,
+                         int latent_w, int n_bands, size_t* bytes_out);
+
+/* Full-image decode: identical to vaep_decode_bands with the single band {0, latent_h}.
+ * latent: device, contiguous (batch, z_channels, [frames,] latent_h, latent_w), in the
+ *         config's dtype.
+ * out:    device, contiguous fp32 (batch, 3, [frames_out,] 2^(n_stages-1)*latent_h,
+ *         2^(n_stages-1)*latent_w), frames_out = frames doubled-minus-one per
+ *         temporal upsample stage.
+ * ws:     device workspace of ws_bytes >= vaep_workspace_bytes(model, ..., 1). */
+int vaep_decode_full(vaep_model* model, const void* latent, int batch, int frames,
+                     int latent_h, int latent_w, void* out, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Band decode.  row_starts: host array of n_bands+1 latent row indices with
+ * row_starts[0] = 0 < row_starts[1] < ... < row_starts[n_bands] = latent_h; band i owns
+ * latent rows [row_starts[i], row_starts[i+1]) and the matching output rows scaled by
+ * 2^(n_stages-1).  Every layer runs on all bands; convs read one halo row from each
+ * neighbour band (the 3x3 kernels' radius), so every band must own at least one row.
+ * A table with more than VAEP_MAX_BANDS bands is decoded as one dense band and
+ * VAEP_WARN_FELL_BACK is returned (the dense fallback of the pages).  Other arguments
+ * as for vaep_decode_full; info (nullable) receives a report.
+ * Errors: INVALID_ARG (non-monotonic, zero-length or uncovered bands, NULL pointers),
+ * WORKSPACE, HIP. */
+int vaep_decode_bands(vaep_model* model, const void* latent, int batch, int frames,
+                      int latent_h, int latent_w, const int32_t* row_starts, int n_bands,
+                      void* out, void* ws, size_t ws_bytes, void* stream,
+                      vaep_decode_info* info);
+
+/* Launch timing.  While profiling is on for a model, every kernel launch of its decodes
+ * is bracketed by two HIP events on the caller's stream and the library records the
+ * step's kind, shape and algorithmic work (each tensor counted once; convolution flops
+ * 2*M*N*K with true channel counts; attention 4*Nq*Nk*C).  vaep_profile_begin creates
+ * 2*max_launches events (host-side HIP objects, no device memory) and clears earlier
+ * records; launches beyond max_launches are not recorded.  vaep_profile_end waits for
+ * the recorded events, writes up to `cap` entries in launch order, sets *n_out to the
+ * number recorded, turns profiling off and releases the events.  The events serialise
+ * nothing beyond the caller's own stream order. */
+enum { VAEP_STEP_CONV = 1, VAEP_STEP_GROUPNORM = 2, VAEP_STEP_RMSNORM = 3,
+       VAEP_STEP_ATTENTION = 4, VAEP_STEP_MOVE = 5 };
+typedef struct vaep_profile_entry {
+  int32_t step;        /* VAEP_STEP_* */
+  int32_t n_kernels;   /* kernels inside the bracket */
+  int32_t kt, ks;      /* conv: temporal taps and spatial kernel size */
+  int32_t cin, cout;   /* conv: true input / output channels; norm and attention: channels */
+  int32_t ups, mode;   /* conv: fused nearest-2x; epilogue mode (internal) */
+  int64_t pixels;      /* conv: output pixels; norm: positions; attention: queries */
+  double flops;        /* algorithmic flops */
+  double bytes;        /* algorithmic HBM bytes */
+  float ms;            /* time between the bracketing events */
+  int32_t reserved;
+} vaep_profile_entry;
+int vaep_profile_begin(vaep_model* model, int max_launches);
+int vaep_profile_end(vaep_model* model, vaep_profile_entry* out, int cap, int* n_out);
+
+/* GroupNorm statistics merge (feature page, GroupNorm section; validation page,
+ * formula under the operator table): for each of n_stats (sample, group) entries,
+ *   w_i  = counts[i][s] / sum_j counts[j][s]
+ *   mean = sum_i w_i * local_mean[i][s]
+ *   var  = sum_i w_i * (local_var[i][s] + (local_mean[i][s] - mean)^2)
+ * All arrays are device, row-major [n_shards][n_stats]; local_var is the population
+ * (divide-by-count) variance.  A shard whose count is 0 has weight 0.  Computed in fp32
+ * with the shards in index order.  Errors: INVALID_ARG (NULL, n_shards < 1, n_stats < 0,
+ * n_shards > 4096); an entry whose counts all are 0 yields mean = var = 0. */
+int vaep_groupnorm_merge(int n_shards, int n_stats, const float* local_mean,
+                         const float* local_var, const int64_t* counts, float* mean_out,
+                         float* var_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VAEP_H */

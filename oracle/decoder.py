@@ -38,14 +38,27 @@ F64 = torch.float64
 
 @dataclass(frozen=True)
 class Precision:
-    """Storage precision of materialised tensors: 'f32' or 'bf16' (RNE)."""
+    """Rounding of materialised tensors.
+
+    ``storage='f32'``: every tensor is float32.  ``storage='bf16'``: the
+    operands of the matrix products -- normalised activations (norm and SiLU
+    outputs) and the attention Q, K, V and attention output -- are rounded to
+    bfloat16 (round to nearest even); every convolution / projection output
+    (the residual stream, conv1 outputs, shortcuts, the decoded image) stays
+    float32, i.e. it is the float32 accumulation itself.  Weights and the latent
+    arrive bf16-rounded from the generator.
+    """
     storage: str = "f32"
 
-    def finish(self, x: torch.Tensor) -> torch.Tensor:
+    def finish(self, x: torch.Tensor, kind: str = "operand") -> torch.Tensor:
+        """Round a float64 result: kind 'operand' (bf16 when storage is bf16) or 'acc' (float32)."""
         y = x.to(torch.float32)
-        if self.storage == "bf16":
+        if self.storage == "bf16" and kind == "operand":
             y = y.to(torch.bfloat16).to(torch.float32)
         return y
+
+    def acc(self, x: torch.Tensor) -> torch.Tensor:
+        return self.finish(x, "acc")
 
 
 def _as5d(w: torch.Tensor) -> torch.Tensor:
@@ -63,7 +76,8 @@ class _Ops:
         self.cfg = cfg
         self.prec = prec
         self.video = cfg.is_video
-        self.fin = prec.finish
+        self.fin = prec.finish       # operands of matrix products
+        self.acc = prec.acc          # conv / projection outputs
 
 
 class FullOps(_Ops):
@@ -71,7 +85,7 @@ class FullOps(_Ops):
 
     def conv(self, x, w, b, causal=None, residual=None):
         causal = self.video and w.dim() == 5 if causal is None else causal
-        return ops.conv_full(x, _as5d(w), b, causal, self.fin, residual)
+        return ops.conv_full(x, _as5d(w), b, causal, self.acc, residual)
 
     def norm(self, x, p, prefix, act):
         if self.video:
@@ -92,14 +106,14 @@ class FullOps(_Ops):
                 o = self.fin(ops.attention_rows(q, k, v, 1.0 / math.sqrt(c)))
                 proj = o.to(F64) @ p["mid.attn.out.weight"].to(F64).T + p["mid.attn.out.bias"].to(F64)
                 res = _tokens(x, n, t).to(F64) + proj
-                y[n, :, t] = self.fin(res).T.reshape(c, x.shape[3], x.shape[4])
+                y[n, :, t] = self.acc(res).T.reshape(c, x.shape[3], x.shape[4])
         return y
 
     def upsample(self, x):
         return ops.upsample_nearest2x(x)
 
     def temporal_upsample(self, x, w, b):
-        z = ops.conv_full(x, w, b, True, self.fin)
+        z = ops.conv_full(x, w, b, True, self.acc)
         return ops.temporal_upsample_interleave(x, z)
 
     def enter(self, z):
@@ -119,7 +133,7 @@ class BandOps(_Ops):
     def conv(self, xb, w, b, causal=None, residual=None):
         causal = self.video and w.dim() == 5 if causal is None else causal
         w5 = _as5d(w)
-        return [ops.conv_band(xb, i, w5, b, causal, self.fin,
+        return [ops.conv_band(xb, i, w5, b, causal, self.acc,
                               None if residual is None else residual[i]) for i in range(len(xb))]
 
     def norm(self, xb, p, prefix, act):
@@ -152,7 +166,7 @@ class BandOps(_Ops):
                     proj = (o.to(F64) @ p["mid.attn.out.weight"].to(F64).T
                             + p["mid.attn.out.bias"].to(F64))
                     res = _tokens(x, n, t).to(F64) + proj
-                    outs[i][n, :, t] = self.fin(res).T.reshape(c, x.shape[3], x.shape[4])
+                    outs[i][n, :, t] = self.acc(res).T.reshape(c, x.shape[3], x.shape[4])
         return outs
 
     def upsample(self, xb):
@@ -161,7 +175,7 @@ class BandOps(_Ops):
     def temporal_upsample(self, xb, w, b):
         out = []
         for x in xb:    # the whole time axis lives on every band and the kernel is 1x1 in space
-            z = ops.conv_band([x], 0, w, b, True, self.fin)
+            z = ops.conv_band([x], 0, w, b, True, self.acc)
             out.append(ops.temporal_upsample_interleave(x, z))
         return out
 

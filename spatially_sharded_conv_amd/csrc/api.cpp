@@ -1,0 +1,1205 @@
+// C ABI of the layer-wise, height-sharded VAE decoder: configuration, model creation
+// (weight repacking), workspace planning and the band-wise decode walker.
+//
+// The walker runs every layer of the decoder on all bands with one kernel launch per
+// layer step, on the caller's stream and without host synchronisation.  Halo rows,
+// GroupNorm statistics and the global K/V pass between bands through device memory
+// (the one-device form of the exchange steps in ChituDiffusion "VAEP" feature page
+// and the "Static Layer-Wise VAE Decode" operator table).  The same walker runs in a
+// dry mode that only sizes the workspace.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "vaep_internal.h"
+#include "../../include/vaep_steps.h"
+
+namespace vaep {
+
+BandLayout make_layout(int nb, const int* rows, int n_img, int frames, int W, int C) {
+  BandLayout L;
+  std::memset(&L, 0, sizeof(L));
+  L.nb = nb;
+  L.n_img = n_img;
+  L.frames = frames;
+  L.W = W;
+  L.C = C;
+  long long off = 0;
+  int r0 = 0;
+  for (int i = 0; i < nb; ++i) {
+    L.rows[i] = rows[i];
+    L.row0[i] = r0;
+    L.off[i] = off;
+    r0 += rows[i];
+    off += (long long)n_img * (rows[i] + 2) * W * C;
+  }
+  L.H = r0;
+  return L;
+}
+
+BandLayout upsampled(const BandLayout& L, int C) {
+  int rows[kMaxBands];
+  for (int i = 0; i < L.nb; ++i) rows[i] = 2 * L.rows[i];
+  return make_layout(L.nb, rows, L.n_img, L.frames, 2 * L.W, C);
+}
+
+BandLayout reshaped(const BandLayout& L, int C, int n_img, int frames) {
+  return make_layout(L.nb, L.rows, n_img, frames, L.W, C);
+}
+
+}  // namespace vaep
+
+using namespace vaep;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(VAEP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct ParamDesc {
+  std::string name;
+  std::vector<int64_t> shape;
+};
+
+bool is_video(const vaep_config& c) { return c.family == VAEP_FAMILY_WAN3D; }
+
+bool stage_ups(const vaep_config& c, int i) { return i < c.n_stages - 1; }
+bool stage_time_ups(const vaep_config& c, int i) {
+  return is_video(c) && stage_ups(c, i) && i < c.temporal_up_stages;
+}
+
+// Canonical parameter list (names follow the decoder structure).
+std::vector<ParamDesc> param_list(const vaep_config& c) {
+  std::vector<ParamDesc> P;
+  const bool v = is_video(c);
+  auto conv = [&](const std::string& n, int co, int ci, std::vector<int64_t> k) {
+    std::vector<int64_t> s = {co, ci};
+    s.insert(s.end(), k.begin(), k.end());
+    P.push_back({n + ".weight", s});
+    P.push_back({n + ".bias", {co}});
+  };
+  auto lin = [&](const std::string& n, int co, int ci) {
+    P.push_back({n + ".weight", {co, ci}});
+    P.push_back({n + ".bias", {co}});
+  };
+  auto norm = [&](const std::string& n, int ch) {
+    P.push_back({n + ".weight", {ch}});
+    if (!v) P.push_back({n + ".bias", {ch}});
+  };
+  const std::vector<int64_t> k3 = v ? std::vector<int64_t>{3, 3, 3} : std::vector<int64_t>{3, 3};
+  const std::vector<int64_t> k1 = v ? std::vector<int64_t>{1, 1, 1} : std::vector<int64_t>{1, 1};
+  auto resnet = [&](const std::string& p, int ci, int co) {
+    norm(p + ".norm1", ci);
+    conv(p + ".conv1", co, ci, k3);
+    norm(p + ".norm2", co);
+    conv(p + ".conv2", co, co, k3);
+    if (ci != co) conv(p + ".shortcut", co, ci, k1);
+  };
+  const int top = c.stage_channels[0];
+  conv("conv_in", top, c.z_channels, k3);
+  resnet("mid.res0", top, top);
+  norm("mid.attn.norm", top);
+  for (const char* s : {"q", "k", "v", "out"}) lin(std::string("mid.attn.") + s, top, top);
+  resnet("mid.res1", top, top);
+  int prev = top;
+  for (int i = 0; i < c.n_stages; ++i) {
+    const int co = c.stage_channels[i];
+    for (int j = 0; j < c.resnets_per_stage; ++j) {
+      resnet("up" + std::to_string(i) + ".res" + std::to_string(j), prev, co);
+      prev = co;
+    }
+    if (stage_time_ups(c, i)) conv("up" + std::to_string(i) + ".time_conv", 2 * co, co, {3, 1, 1});
+    if (stage_ups(c, i)) conv("up" + std::to_string(i) + ".upsample", co, co, {3, 3});
+  }
+  norm("norm_out", prev);
+  conv("conv_out", 3, prev, k3);
+  return P;
+}
+
+int check_config(const vaep_config* c) {
+  if (!c) return fail(VAEP_ERR_INVALID_ARG, "config is NULL");
+  if (c->family != VAEP_FAMILY_KL2D && c->family != VAEP_FAMILY_WAN3D)
+    return fail(VAEP_ERR_UNSUPPORTED, "unknown family %d", c->family);
+  if (c->dtype != VAEP_DTYPE_F32 && c->dtype != VAEP_DTYPE_BF16)
+    return fail(VAEP_ERR_UNSUPPORTED, "unknown dtype %d", c->dtype);
+  if (c->n_stages < 1 || c->n_stages > VAEP_MAX_STAGES)
+    return fail(VAEP_ERR_INVALID_ARG, "n_stages %d outside 1..%d", c->n_stages, VAEP_MAX_STAGES);
+  if (c->z_channels < 1 || c->resnets_per_stage < 1)
+    return fail(VAEP_ERR_INVALID_ARG, "z_channels and resnets_per_stage must be >= 1");
+  if (!(c->eps > 0.f)) return fail(VAEP_ERR_INVALID_ARG, "eps must be > 0");
+  const bool bf = c->dtype == VAEP_DTYPE_BF16;
+  for (int i = 0; i < c->n_stages; ++i) {
+    const int ch = c->stage_channels[i];
+    if (ch < 1 || ch > 1024) return fail(VAEP_ERR_INVALID_ARG, "stage_channels[%d] = %d outside 1..1024", i, ch);
+    if (bf && ch % 32 != 0)
+      return fail(VAEP_ERR_UNSUPPORTED, "bf16 kernels need channel counts that are multiples of 32 (stage %d: %d)", i, ch);
+    if (!bf && ch % 4 != 0)
+      return fail(VAEP_ERR_UNSUPPORTED, "fp32 kernels need channel counts that are multiples of 4 (stage %d: %d)", i, ch);
+    if (c->family == VAEP_FAMILY_KL2D && (c->norm_groups < 1 || ch % c->norm_groups != 0))
+      return fail(VAEP_ERR_INVALID_ARG, "norm_groups %d does not divide %d", c->norm_groups, ch);
+  }
+  if (c->family == VAEP_FAMILY_WAN3D && (c->temporal_up_stages < 0 || c->temporal_up_stages > c->n_stages - 1))
+    return fail(VAEP_ERR_INVALID_ARG, "temporal_up_stages %d outside 0..%d", c->temporal_up_stages, c->n_stages - 1);
+  const int top = c->stage_channels[0];
+  if (bf && top != 128 && top != 256 && top != 384 && top != 512)
+    return fail(VAEP_ERR_UNSUPPORTED, "bf16 attention supports 128/256/384/512 channels, got %d", top);
+  return VAEP_OK;
+}
+
+// ------------------------------------------------------------------ model layout
+struct ConvW {
+  void* w = nullptr;
+  float* b = nullptr;
+  int co = 0, ci = 0, co_pad = 0, ci_pad = 0, kt = 1, ks = 3;
+};
+struct NormW {
+  float* g = nullptr;
+  float* b = nullptr;
+  int c = 0;
+};
+struct ResW {
+  NormW n1, n2;
+  ConvW c1, c2, sc;
+  bool has_sc = false;
+};
+struct AttnW {
+  NormW norm;
+  ConvW qkv, out;
+};
+struct StageW {
+  std::vector<ResW> res;
+  bool time_up = false, up = false;
+  ConvW time_conv, up_conv;
+};
+
+}  // namespace
+
+namespace {
+// Event-bracketed launch records of one model (see vaep_profile_begin).
+struct Profiler {
+  bool on = false;
+  int cap = 0;
+  std::vector<hipEvent_t> ev;
+  std::vector<vaep_profile_entry> rec;
+};
+}  // namespace
+
+struct vaep_model {
+  vaep_config cfg;
+  void* mem = nullptr;
+  size_t mem_bytes = 0;
+  Profiler prof;
+  ConvW conv_in;
+  ResW mid0, mid1;
+  AttnW attn;
+  std::vector<StageW> stages;
+  NormW norm_out;
+  ConvW conv_out;
+};
+
+namespace {
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+int round_up(int v, int a) { return (v + a - 1) / a * a; }
+
+// Carves the model's single allocation; first pass sizes, second pass assigns.
+struct Carver {
+  char* base = nullptr;
+  size_t used = 0;
+  void* take(size_t bytes) {
+    void* p = base ? base + used : nullptr;
+    used = align_up(used + bytes, 256);
+    return p;
+  }
+};
+
+struct Builder {
+  const vaep_config& c;
+  const void* const* params;
+  std::map<std::string, int> index;
+  Carver carve;
+  hipStream_t st;
+  bool dry;
+  int dtype;
+  hipError_t err = hipSuccess;
+
+  const void* P(const std::string& n) const { return params ? params[index.at(n)] : nullptr; }
+  void ok(hipError_t e) {
+    if (err == hipSuccess && e != hipSuccess) err = e;
+  }
+
+  ConvW conv(const std::string& n, int co, int ci, int kt, int ks, int co_pad_to = 0) {
+    ConvW w;
+    const bool bf = dtype == VAEP_DTYPE_BF16;
+    w.co = co;
+    w.ci = ci;
+    w.kt = kt;
+    w.ks = ks;
+    w.co_pad = bf ? round_up(co, kConvTileN) : co;
+    if (co_pad_to) w.co_pad = co_pad_to;
+    w.ci_pad = bf ? round_up(ci, 32) : ci;
+    const int taps = kt * ks * ks;
+    w.w = carve.take((size_t)w.co_pad * taps * w.ci_pad * dtype_bytes(dtype));
+    w.b = (float*)carve.take((size_t)w.co_pad * sizeof(float));
+    if (!dry) {
+      ok(launch_pack_weight(P(n + ".weight"), co, ci, taps, w.w, w.co_pad, w.ci_pad, dtype, st));
+      ok(launch_to_f32(P(n + ".bias"), co, w.b, w.co_pad, dtype, st));
+    }
+    return w;
+  }
+  NormW norm(const std::string& n, int ch) {
+    NormW w;
+    w.c = ch;
+    w.g = (float*)carve.take(ch * sizeof(float));
+    w.b = (float*)carve.take(ch * sizeof(float));
+    if (!dry) {
+      ok(launch_to_f32(P(n + ".weight"), ch, w.g, ch, dtype, st));
+      ok(launch_to_f32(is_video(c) ? nullptr : P(n + ".bias"), ch, w.b, ch, dtype, st));
+    }
+    return w;
+  }
+  ResW resnet(const std::string& p, int ci, int co) {
+    ResW r;
+    const int kt = is_video(c) ? 3 : 1;
+    r.n1 = norm(p + ".norm1", ci);
+    r.c1 = conv(p + ".conv1", co, ci, kt, 3);
+    r.n2 = norm(p + ".norm2", co);
+    r.c2 = conv(p + ".conv2", co, co, kt, 3);
+    r.has_sc = ci != co;
+    if (r.has_sc) r.sc = conv(p + ".shortcut", co, ci, 1, 1);
+    return r;
+  }
+  AttnW attention(int ch) {
+    AttnW a;
+    a.norm = norm("mid.attn.norm", ch);
+    const bool bf = dtype == VAEP_DTYPE_BF16;
+    ConvW q;
+    q.co = 3 * ch;
+    q.ci = ch;
+    q.kt = 1;
+    q.ks = 1;
+    q.co_pad = bf ? round_up(3 * ch, kConvTileN) : 3 * ch;
+    q.ci_pad = ch;
+    const size_t eb = dtype_bytes(dtype);
+    q.w = carve.take((size_t)q.co_pad * ch * eb);
+    q.b = (float*)carve.take((size_t)q.co_pad * sizeof(float));
+    if (!dry) {
+      const char* names[3] = {"mid.attn.q", "mid.attn.k", "mid.attn.v"};
+      for (int i = 0; i < 3; ++i) {
+        ok(launch_pack_weight(P(std::string(names[i]) + ".weight"), ch, ch, 1,
+                              (char*)q.w + (size_t)i * ch * ch * eb, ch, ch, dtype, st));
+        ok(launch_to_f32(P(std::string(names[i]) + ".bias"), ch, q.b + (size_t)i * ch, ch, dtype, st));
+      }
+    }
+    a.qkv = q;
+    a.out = conv("mid.attn.out", ch, ch, 1, 1);
+    return a;
+  }
+  void build(vaep_model& m) {
+    const int kt = is_video(c) ? 3 : 1;
+    const int top = c.stage_channels[0];
+    m.conv_in = conv("conv_in", top, c.z_channels, kt, 3);
+    m.mid0 = resnet("mid.res0", top, top);
+    m.attn = attention(top);
+    m.mid1 = resnet("mid.res1", top, top);
+    m.stages.clear();
+    int prev = top;
+    for (int i = 0; i < c.n_stages; ++i) {
+      StageW s;
+      const int co = c.stage_channels[i];
+      for (int j = 0; j < c.resnets_per_stage; ++j) {
+        s.res.push_back(resnet("up" + std::to_string(i) + ".res" + std::to_string(j), prev, co));
+        prev = co;
+      }
+      s.time_up = stage_time_ups(c, i);
+      if (s.time_up) s.time_conv = conv("up" + std::to_string(i) + ".time_conv", 2 * co, co, 3, 1);
+      s.up = stage_ups(c, i);
+      if (s.up) s.up_conv = conv("up" + std::to_string(i) + ".upsample", co, co, 1, 3);
+      m.stages.push_back(s);
+    }
+    m.norm_out = norm("norm_out", prev);
+    m.conv_out = conv("conv_out", 3, prev, kt, 3);
+  }
+};
+
+// ------------------------------------------------------------------ executor
+struct Exec {
+  const vaep_model* m = nullptr;
+  int dtype = VAEP_DTYPE_BF16;
+  hipStream_t st = nullptr;
+  bool dry = true;
+  // workspace regions
+  char* ws = nullptr;
+  void* act[4] = {nullptr, nullptr, nullptr, nullptr};
+  void* qb = nullptr;
+  void* kb = nullptr;
+  void* vb = nullptr;
+  float* scratch = nullptr;
+  // sizes (dry pass)
+  size_t act_bytes = 0, qkv_bytes = 0, scratch_bytes = 0;
+  int launches = 0;
+  Profiler* prof = nullptr;
+  bool recording = false;
+  vaep_profile_entry pending;
+
+  // Bracket the next launch(es) with events when profiling is on.
+  void rec_begin(const vaep_profile_entry& e) {
+    recording = false;
+    if (dry || !prof || !prof->on || (int)prof->rec.size() >= prof->cap) return;
+    const size_t i = prof->rec.size();
+    if (hipEventRecord(prof->ev[2 * i], st) != hipSuccess) return;
+    pending = e;
+    recording = true;
+  }
+  void rec_end() {
+    if (!recording) return;
+    const size_t i = prof->rec.size();
+    if (hipEventRecord(prof->ev[2 * i + 1], st) == hipSuccess) prof->rec.push_back(pending);
+    recording = false;
+  }
+  static vaep_profile_entry entry(int step, int n_kernels) {
+    vaep_profile_entry e;
+    std::memset(&e, 0, sizeof(e));
+    e.step = step;
+    e.n_kernels = n_kernels;
+    return e;
+  }
+  int groups = 0;      // GroupNorm groups; 0 selects channel RMSNorm
+  float eps = 1e-6f;
+
+  size_t eb() const { return dtype_bytes(dtype); }   // operand (normalised activation) element
+  void need_act(const BandLayout& L, size_t elem) { act_bytes = std::max(act_bytes, (size_t)layout_elems(L) * elem); }
+
+  size_t total() const {
+    return 4 * align_up(act_bytes, 256) + 3 * align_up(qkv_bytes, 256) + align_up(scratch_bytes, 256);
+  }
+  void assign(char* base) {
+    ws = base;
+    size_t o = 0;
+    for (int i = 0; i < 4; ++i) {
+      act[i] = base + o;
+      o += align_up(act_bytes, 256);
+    }
+    qb = base + o;
+    o += align_up(qkv_bytes, 256);
+    kb = base + o;
+    o += align_up(qkv_bytes, 256);
+    vb = base + o;
+    o += align_up(qkv_bytes, 256);
+    scratch = (float*)(base + o);
+  }
+
+  // x_f32: the input is an fp32 conv output (else a normalised activation in the operand dtype).
+  int conv(const ConvW& w, const void* x, const BandLayout& Lin, bool x_f32, void* y,
+           const BandLayout& Lout, int mode, const void* res, int ups, int final_frames = 1) {
+    if (mode == kModeBand || mode == kModeTimeInterleave) need_act(Lout, 4);
+    need_act(Lin, x_f32 ? 4 : eb());
+    if (dry) return VAEP_OK;
+    ConvArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.x = x;
+    a.w = w.w;
+    a.bias = w.b;
+    a.res = res;
+    a.y = y;
+    a.q = qb;
+    a.k = kb;
+    a.vt = vb;
+    a.in = Lin;
+    a.out = Lout;
+    a.cin = Lin.C;
+    a.cout = w.co;
+    a.cout_pad = w.co_pad;
+    a.kt = w.kt;
+    a.ks = w.ks;
+    a.ups = ups;
+    a.mode = mode;
+    a.x_f32 = x_f32 ? 1 : 0;
+    a.final_frames = final_frames;
+    if (Lin.C != w.ci_pad) return fail(VAEP_ERR_INVALID_ARG, "internal: conv input has %d channels, weight %d", Lin.C, w.ci_pad);
+    {
+      vaep_profile_entry pe = entry(VAEP_STEP_CONV, 1);
+      const long long m = (long long)Lin.n_img * Lin.H * Lin.W * (ups ? 4 : 1);
+      const long long k = (long long)w.kt * w.ks * w.ks * w.ci;
+      pe.kt = w.kt;
+      pe.ks = w.ks;
+      pe.cin = w.ci;
+      pe.cout = w.co;
+      pe.ups = ups;
+      pe.mode = mode;
+      pe.pixels = m;
+      pe.flops = 2.0 * (double)m * w.co * (double)k;
+      const double in_b = (double)Lin.n_img * Lin.H * Lin.W * w.ci * (x_f32 ? 4 : eb());
+      const double out_elem = mode == kModeQKV ? (double)eb() : 4.0;
+      pe.bytes = in_b + (double)w.co * k * eb() + (double)m * w.co * out_elem + (res ? (double)m * w.co * 4 : 0.0);
+      rec_begin(pe);
+    }
+    hipError_t e = launch_conv(a, dtype, st);
+    rec_end();
+    if (e != hipSuccess) return hip_fail(e, "conv launch");
+    ++launches;
+    return VAEP_OK;
+  }
+
+  int norm(const NormW& w, const void* x, const BandLayout& L, void* y, int act, float* merged_out = nullptr) {
+    need_act(L, 4);
+    if (groups > 0)
+      scratch_bytes = std::max(scratch_bytes, gn_partials_floats(L, groups, dtype) * sizeof(float));
+    if (dry) return VAEP_OK;
+    NormArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.x = x;
+    a.y = y;
+    a.L = L;
+    a.groups = groups;
+    a.eps = eps;
+    a.gamma = w.g;
+    a.beta = w.b;
+    a.act = act;
+    a.partials = reinterpret_cast<double*>(scratch);
+    a.merged_out = merged_out;
+    {
+      vaep_profile_entry pe = entry(groups > 0 ? VAEP_STEP_GROUPNORM : VAEP_STEP_RMSNORM, groups > 0 ? 3 : 1);
+      const double elems = (double)L.n_img * L.H * L.W * L.C;
+      pe.cin = pe.cout = L.C;
+      pe.pixels = (long long)L.n_img * L.H * L.W;
+      // GroupNorm: statistics read + apply read (fp32) + apply write; RMSNorm: one read + write
+      pe.bytes = elems * ((groups > 0 ? 8.0 : 4.0) + (double)eb());
+      rec_begin(pe);
+    }
+    hipError_t e = groups > 0 ? launch_groupnorm(a, dtype, st) : launch_rmsnorm(a, dtype, st);
+    rec_end();
+    if (e != hipSuccess) return hip_fail(e, "norm launch");
+    launches += groups > 0 ? 3 : 1;
+    return VAEP_OK;
+  }
+
+  int attention(const AttnW& w, const void* x, const BandLayout& L, void* a_buf, void* o_buf, void* y) {
+    const int c = L.C;
+    qkv_bytes = std::max(qkv_bytes, (size_t)L.n_img * L.H * L.W * c * eb());
+    int rc = norm(w.norm, x, L, a_buf, 0);
+    if (rc) return rc;
+    rc = conv(w.qkv, a_buf, L, false, nullptr, L, kModeQKV, nullptr, 0);
+    if (rc) return rc;
+    need_act(L, eb());
+    if (!dry) {
+      AttnArgs aa;
+      std::memset(&aa, 0, sizeof(aa));
+      aa.q = qb;
+      aa.k = kb;
+      aa.vt = vb;
+      aa.o = o_buf;
+      aa.L = L;
+      aa.c = c;
+      aa.tokens = L.H * L.W;
+      aa.scale = 1.0f / std::sqrt((float)c);
+      vaep_profile_entry pe = entry(VAEP_STEP_ATTENTION, 1);
+      const double nq = (double)L.n_img * L.H * L.W, nk = (double)L.H * L.W;
+      pe.cin = pe.cout = c;
+      pe.pixels = (long long)nq;
+      pe.flops = 4.0 * nq * nk * c;
+      pe.bytes = 4.0 * nq * c * (double)eb();   // Q, K, V read once, O written once
+      rec_begin(pe);
+      hipError_t e = launch_attention(aa, dtype, st);
+      rec_end();
+      if (e != hipSuccess) return hip_fail(e, "attention launch");
+      ++launches;
+    }
+    return conv(w.out, o_buf, L, false, y, L, kModeBand, x, 0);
+  }
+};
+
+// Buffers other than `cur`, in a fixed order.
+void others(int cur, int* o) {
+  int k = 0;
+  for (int i = 0; i < 4; ++i)
+    if (i != cur) o[k++] = i;
+}
+
+int resnet(Exec& E, const ResW& r, int& cur, BandLayout& L) {
+  int o[3];
+  others(cur, o);
+  const BandLayout Lx = L;
+  const BandLayout Lh = reshaped(L, r.c1.co, L.n_img, L.frames);
+  int rc;
+  if ((rc = E.norm(r.n1, E.act[cur], Lx, E.act[o[0]], 1))) return rc;
+  if ((rc = E.conv(r.c1, E.act[o[0]], Lx, false, E.act[o[1]], Lh, kModeBand, nullptr, 0))) return rc;
+  if ((rc = E.norm(r.n2, E.act[o[1]], Lh, E.act[o[0]], 1))) return rc;
+  const void* res = E.act[cur];
+  if (r.has_sc) {
+    if ((rc = E.conv(r.sc, E.act[cur], Lx, true, E.act[o[2]], Lh, kModeBand, nullptr, 0))) return rc;
+    res = E.act[o[2]];
+  }
+  if ((rc = E.conv(r.c2, E.act[o[0]], Lh, false, E.act[o[1]], Lh, kModeBand, res, 0))) return rc;
+  cur = o[1];
+  L = Lh;
+  return VAEP_OK;
+}
+
+// Decode a latent on the given bands (rows per band at latent resolution).
+int walk(Exec& E, const void* latent, int B, int T, int W, const int* rows, int nb, void* out) {
+  const vaep_model& m = *E.m;
+  const vaep_config& c = m.cfg;
+  const bool video = is_video(c);
+  E.groups = video ? 0 : c.norm_groups;
+  E.eps = c.eps;
+  BandLayout L = make_layout(nb, rows, B * T, T, W, m.conv_in.ci_pad);
+  int rc;
+  int cur = 0;
+  E.need_act(L, E.eb());
+  if (!E.dry) {
+    hipError_t e = launch_pack(latent, c.z_channels, E.act[0], L, E.dtype, E.st);
+    if (e != hipSuccess) return hip_fail(e, "latent pack");
+    ++E.launches;
+  }
+  BandLayout L1 = reshaped(L, m.conv_in.co, L.n_img, T);
+  if ((rc = E.conv(m.conv_in, E.act[0], L, false, E.act[1], L1, kModeBand, nullptr, 0))) return rc;
+  cur = 1;
+  L = L1;
+  if ((rc = resnet(E, m.mid0, cur, L))) return rc;
+  {
+    int o[3];
+    others(cur, o);
+    if ((rc = E.attention(m.attn, E.act[cur], L, E.act[o[0]], E.act[o[1]], E.act[o[2]]))) return rc;
+    cur = o[2];
+  }
+  if ((rc = resnet(E, m.mid1, cur, L))) return rc;
+  for (const StageW& s : m.stages) {
+    for (const ResW& r : s.res)
+      if ((rc = resnet(E, r, cur, L))) return rc;
+    if (s.time_up) {
+      int o[3];
+      others(cur, o);
+      const int Tn = 2 * L.frames - 1;
+      const BandLayout Lt = reshaped(L, L.C, (L.n_img / L.frames) * Tn, Tn);
+      if ((rc = E.conv(s.time_conv, E.act[cur], L, true, E.act[o[0]], Lt, kModeTimeInterleave, nullptr, 0))) return rc;
+      if (!E.dry) {
+        hipError_t e = launch_copy_frame0(E.act[cur], L, E.act[o[0]], Lt, VAEP_DTYPE_F32, E.st);
+        if (e != hipSuccess) return hip_fail(e, "frame copy");
+        ++E.launches;
+      }
+      cur = o[0];
+      L = Lt;
+    }
+    if (s.up) {
+      int o[3];
+      others(cur, o);
+      const BandLayout Lu = upsampled(L, s.up_conv.co);
+      if ((rc = E.conv(s.up_conv, E.act[cur], L, true, E.act[o[0]], Lu, kModeBand, nullptr, 1))) return rc;
+      cur = o[0];
+      L = Lu;
+    }
+  }
+  int o[3];
+  others(cur, o);
+  if ((rc = E.norm(m.norm_out, E.act[cur], L, E.act[o[0]], 1))) return rc;
+  (void)video;
+  return E.conv(m.conv_out, E.act[o[0]], L, false, out, L, kModeFinal, nullptr, 0, L.frames);
+}
+
+// Rows of nb bands that split H as evenly as possible (used to size workspaces).
+std::vector<int> even_rows(int H, int nb) {
+  std::vector<int> r(nb, H / nb);
+  for (int i = 0; i < H % nb; ++i) r[i] += 1;
+  return r;
+}
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(VAEP_ERR_NOT_READY, "no HIP device: %s", hipGetErrorString(e));
+  hipDeviceProp_t p;
+  e = hipGetDeviceProperties(&p, dev);
+  if (e != hipSuccess) return fail(VAEP_ERR_NOT_READY, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (std::strncmp(p.gcnArchName, "gfx950", 6) != 0)
+    return fail(VAEP_ERR_NOT_READY, "device %d is %s; this library is built for gfx950", dev, p.gcnArchName);
+  return VAEP_OK;
+}
+
+int check_latent_dims(const vaep_model* m, int batch, int frames, int h, int w) {
+  if (!m) return fail(VAEP_ERR_INVALID_ARG, "model is NULL");
+  if (batch < 1 || h < 1 || w < 1 || frames < 1)
+    return fail(VAEP_ERR_INVALID_ARG, "latent dims must be >= 1 (batch %d frames %d h %d w %d)", batch, frames, h, w);
+  if (!is_video(m->cfg) && frames != 1) return fail(VAEP_ERR_INVALID_ARG, "2-D decoder needs frames = 1");
+  const long long up = 1LL << (m->cfg.n_stages - 1);
+  if ((long long)h * up > (1 << 20) || (long long)w * up > (1 << 20))
+    return fail(VAEP_ERR_INVALID_ARG, "latent %dx%d too large", h, w);
+  return VAEP_OK;
+}
+
+int plan_bytes(const vaep_model* m, int batch, int frames, int h, int w, int nb, size_t* bytes) {
+  Exec E;
+  E.m = m;
+  E.dtype = m->cfg.dtype;
+  E.dry = true;
+  std::vector<int> rows = even_rows(h, nb);
+  int rc = walk(E, nullptr, batch, frames, w, rows.data(), nb, nullptr);
+  if (rc) return rc;
+  *bytes = E.total();
+  return VAEP_OK;
+}
+
+
+// ------------------------------------------------------------------ step helpers
+int step_bands(const int32_t* rs, int nb, int h, std::vector<int>& rows) {
+  if (!rs) return fail(VAEP_ERR_INVALID_ARG, "row_starts is NULL");
+  if (nb < 1 || nb > kMaxBands) return fail(VAEP_ERR_INVALID_ARG, "n_bands %d outside 1..%d", nb, kMaxBands);
+  if (rs[0] != 0 || rs[nb] != h) return fail(VAEP_ERR_INVALID_ARG, "bands must cover rows 0..%d", h);
+  rows.clear();
+  for (int i = 0; i < nb; ++i) {
+    if (rs[i + 1] <= rs[i]) return fail(VAEP_ERR_INVALID_ARG, "band %d is empty or reversed", i);
+    rows.push_back(rs[i + 1] - rs[i]);
+  }
+  return VAEP_OK;
+}
+
+int step_dims(int dtype, int batch, int frames, int c, int h, int w) {
+  if (dtype != VAEP_DTYPE_F32 && dtype != VAEP_DTYPE_BF16) return fail(VAEP_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (batch < 1 || frames < 1 || c < 1 || h < 1 || w < 1)
+    return fail(VAEP_ERR_INVALID_ARG, "dims must be >= 1 (batch %d frames %d c %d h %d w %d)", batch, frames, c, h, w);
+  return VAEP_OK;
+}
+
+// Sizes the step workspace on the first pass (base == NULL) and hands out pointers on the second.
+int step_finish_sizing(const Carver& cv, void* ws, size_t ws_bytes, size_t* bytes_out, bool* sized) {
+  *sized = false;
+  if (!ws) {
+    if (!bytes_out) return fail(VAEP_ERR_INVALID_ARG, "ws and bytes_out are both NULL");
+    *bytes_out = cv.used;
+    *sized = true;
+    return VAEP_OK;
+  }
+  if (ws_bytes < cv.used) return fail(VAEP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", cv.used, ws_bytes);
+  return VAEP_OK;
+}
+
+int norm_channels_ok(int dtype, int c) {
+  (void)dtype;   // norm inputs are fp32 conv outputs: 4 channels per 16-byte load, 256 threads
+  if (c % 4 != 0 || c > 1024) return fail(VAEP_ERR_UNSUPPORTED, "norm kernels need channels %% 4 == 0 and <= 1024");
+  return VAEP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vaep_last_error(void) { return g_err.c_str(); }
+
+const char* vaep_version(void) { return "vaep 0.1 gfx950"; }
+
+int vaep_config_preset(int id, vaep_config* out) {
+  if (!out) return fail(VAEP_ERR_INVALID_ARG, "out is NULL");
+  vaep_config c;
+  std::memset(&c, 0, sizeof(c));
+  c.eps = 1e-6f;
+  if (id == 1) {
+    c.family = VAEP_FAMILY_KL2D;
+    c.dtype = VAEP_DTYPE_F32;
+    c.z_channels = 4;
+    c.n_stages = 2;
+    c.stage_channels[0] = 64;
+    c.stage_channels[1] = 32;
+    c.resnets_per_stage = 2;
+    c.norm_groups = 8;
+  } else if (id >= 2 && id <= 4) {
+    c.family = VAEP_FAMILY_KL2D;
+    c.dtype = VAEP_DTYPE_BF16;
+    c.z_channels = 16;
+    c.n_stages = 4;
+    const int ch[4] = {512, 512, 256, 128};
+    for (int i = 0; i < 4; ++i) c.stage_channels[i] = ch[i];
+    c.resnets_per_stage = 3;
+    c.norm_groups = 32;
+  } else if (id == 5) {
+    c.family = VAEP_FAMILY_WAN3D;
+    c.dtype = VAEP_DTYPE_BF16;
+    c.z_channels = 16;
+    c.n_stages = 4;
+    const int ch[4] = {384, 384, 192, 96};
+    for (int i = 0; i < 4; ++i) c.stage_channels[i] = ch[i];
+    c.resnets_per_stage = 2;
+    c.norm_groups = 0;
+    c.temporal_up_stages = 2;
+  } else {
+    return fail(VAEP_ERR_INVALID_ARG, "unknown preset %d (1..5)", id);
+  }
+  *out = c;
+  return VAEP_OK;
+}
+
+int vaep_param_count(const vaep_config* cfg) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  return (int)param_list(*cfg).size();
+}
+
+int vaep_param_info(const vaep_config* cfg, int j, char* name, int name_cap, int64_t shape[5], int* ndim) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  const auto P = param_list(*cfg);
+  if (j < 0 || j >= (int)P.size()) return fail(VAEP_ERR_INVALID_ARG, "parameter index %d outside 0..%d", j, (int)P.size() - 1);
+  if (name && name_cap > 0) {
+    std::strncpy(name, P[j].name.c_str(), name_cap - 1);
+    name[name_cap - 1] = 0;
+  }
+  if (shape)
+    for (size_t i = 0; i < P[j].shape.size() && i < 5; ++i) shape[i] = P[j].shape[i];
+  if (ndim) *ndim = (int)P[j].shape.size();
+  return VAEP_OK;
+}
+
+int vaep_model_create(const vaep_config* cfg, const void* const* params, int n_params, void* stream,
+                      vaep_model** out) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!out) return fail(VAEP_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  const auto P = param_list(*cfg);
+  if (!params) return fail(VAEP_ERR_INVALID_ARG, "params is NULL");
+  if (n_params != (int)P.size()) return fail(VAEP_ERR_INVALID_ARG, "expected %d parameters, got %d", (int)P.size(), n_params);
+  for (int j = 0; j < n_params; ++j)
+    if (!params[j]) return fail(VAEP_ERR_INVALID_ARG, "parameter %d (%s) is NULL", j, P[j].name.c_str());
+  if ((rc = check_device())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  vaep_model* m = new (std::nothrow) vaep_model();
+  if (!m) return fail(VAEP_ERR_INVALID_ARG, "out of host memory");
+  m->cfg = *cfg;
+  Builder sz{*cfg, params, {}, {}, st, true, cfg->dtype};
+  for (size_t j = 0; j < P.size(); ++j) sz.index[P[j].name] = (int)j;
+  sz.build(*m);
+  m->mem_bytes = sz.carve.used;
+  hipError_t e = hipMalloc(&m->mem, m->mem_bytes);
+  if (e != hipSuccess) {
+    delete m;
+    return hip_fail(e, "hipMalloc(model)");
+  }
+  e = hipMemsetAsync(m->mem, 0, m->mem_bytes, st);
+  Builder b{*cfg, params, sz.index, {}, st, false, cfg->dtype};
+  b.carve.base = (char*)m->mem;
+  b.build(*m);
+  if (e == hipSuccess) e = b.err;
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) {
+    (void)hipFree(m->mem);
+    delete m;
+    return hip_fail(e, "model build");
+  }
+  *out = m;
+  return VAEP_OK;
+}
+
+int vaep_model_destroy(vaep_model* model) {
+  if (!model) return VAEP_OK;
+  for (hipEvent_t ev : model->prof.ev) (void)hipEventDestroy(ev);
+  hipError_t e = hipSuccess;
+  if (model->mem) e = hipFree(model->mem);
+  delete model;
+  if (e != hipSuccess) return hip_fail(e, "hipFree(model)");
+  return VAEP_OK;
+}
+
+int vaep_workspace_bytes(const vaep_model* model, int batch, int frames, int latent_h, int latent_w,
+                         int n_bands, size_t* bytes_out) {
+  int rc = check_latent_dims(model, batch, frames, latent_h, latent_w);
+  if (rc) return rc;
+  if (!bytes_out) return fail(VAEP_ERR_INVALID_ARG, "bytes_out is NULL");
+  if (n_bands < 1) return fail(VAEP_ERR_INVALID_ARG, "n_bands must be >= 1");
+  const int nb = std::min(std::min(n_bands, kMaxBands), latent_h);
+  return plan_bytes(model, batch, frames, latent_h, latent_w, nb, bytes_out);
+}
+
+int vaep_decode_bands(vaep_model* model, const void* latent, int batch, int frames, int latent_h,
+                      int latent_w, const int32_t* row_starts, int n_bands, void* out, void* ws,
+                      size_t ws_bytes, void* stream, vaep_decode_info* info) {
+  int rc = check_latent_dims(model, batch, frames, latent_h, latent_w);
+  if (rc) return rc;
+  if (!latent || !out) return fail(VAEP_ERR_INVALID_ARG, "latent and out must be device pointers");
+  if (!row_starts) return fail(VAEP_ERR_INVALID_ARG, "row_starts is NULL");
+  if (n_bands < 1) return fail(VAEP_ERR_INVALID_ARG, "n_bands must be >= 1");
+  if (row_starts[0] != 0 || row_starts[n_bands] != latent_h)
+    return fail(VAEP_ERR_INVALID_ARG, "bands must cover rows 0..%d (got %d..%d)", latent_h, row_starts[0], row_starts[n_bands]);
+  for (int i = 0; i < n_bands; ++i)
+    if (row_starts[i + 1] <= row_starts[i])
+      return fail(VAEP_ERR_INVALID_ARG, "band %d is empty or reversed (%d..%d)", i, row_starts[i], row_starts[i + 1]);
+  int status = VAEP_OK;
+  std::vector<int> rows;
+  if (n_bands > kMaxBands) {
+    rows.assign(1, latent_h);      // dense fallback: one band
+    status = VAEP_WARN_FELL_BACK;
+  } else {
+    for (int i = 0; i < n_bands; ++i) rows.push_back(row_starts[i + 1] - row_starts[i]);
+  }
+  const int nb = (int)rows.size();
+  Exec E;
+  E.m = model;
+  E.dtype = model->cfg.dtype;
+  E.st = (hipStream_t)stream;
+  E.dry = true;
+  E.prof = &model->prof;
+  if ((rc = walk(E, latent, batch, frames, latent_w, rows.data(), nb, out))) return rc;
+  const size_t need = E.total();
+  if (!ws || ws_bytes < need)
+    return fail(VAEP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  E.assign((char*)ws);
+  E.dry = false;
+  if ((rc = walk(E, latent, batch, frames, latent_w, rows.data(), nb, out))) return rc;
+  if (info) {
+    info->bands_used = nb;
+    info->fell_back = status == VAEP_WARN_FELL_BACK;
+    info->n_launches = E.launches;
+    info->reserved = 0;
+    info->workspace_bytes = need;
+  }
+  if (status == VAEP_WARN_FELL_BACK)
+    fail(VAEP_WARN_FELL_BACK, "%d bands exceed the %d-band limit: decoded as one dense band", n_bands, kMaxBands);
+  return status;
+}
+
+int vaep_decode_full(vaep_model* model, const void* latent, int batch, int frames, int latent_h,
+                     int latent_w, void* out, void* ws, size_t ws_bytes, void* stream) {
+  const int32_t starts[2] = {0, latent_h};
+  return vaep_decode_bands(model, latent, batch, frames, latent_h, latent_w, starts, 1, out, ws,
+                           ws_bytes, stream, nullptr);
+}
+
+int vaep_profile_begin(vaep_model* model, int max_launches) {
+  if (!model) return fail(VAEP_ERR_INVALID_ARG, "model is NULL");
+  if (max_launches < 1 || max_launches > (1 << 20)) return fail(VAEP_ERR_INVALID_ARG, "max_launches %d outside 1..2^20", max_launches);
+  Profiler& p = model->prof;
+  for (hipEvent_t e : p.ev) (void)hipEventDestroy(e);
+  p.ev.clear();
+  p.rec.clear();
+  p.on = false;
+  for (int i = 0; i < 2 * max_launches; ++i) {
+    hipEvent_t e;
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      for (hipEvent_t x : p.ev) (void)hipEventDestroy(x);
+      p.ev.clear();
+      return hip_fail(r, "hipEventCreate");
+    }
+    p.ev.push_back(e);
+  }
+  p.cap = max_launches;
+  p.on = true;
+  return VAEP_OK;
+}
+
+int vaep_profile_end(vaep_model* model, vaep_profile_entry* out, int cap, int* n_out) {
+  if (!model) return fail(VAEP_ERR_INVALID_ARG, "model is NULL");
+  Profiler& p = model->prof;
+  int rc = VAEP_OK;
+  const int n = (int)p.rec.size();
+  for (int i = 0; i < n; ++i) {
+    float ms = 0.f;
+    hipError_t r = hipEventSynchronize(p.ev[2 * i + 1]);
+    if (r == hipSuccess) r = hipEventElapsedTime(&ms, p.ev[2 * i], p.ev[2 * i + 1]);
+    if (r != hipSuccess && rc == VAEP_OK) rc = hip_fail(r, "profile events");
+    p.rec[i].ms = ms;
+    if (out && i < cap) out[i] = p.rec[i];
+  }
+  if (n_out) *n_out = n;
+  for (hipEvent_t e : p.ev) (void)hipEventDestroy(e);
+  p.ev.clear();
+  p.rec.clear();
+  p.on = false;
+  p.cap = 0;
+  return rc;
+}
+
+int vaep_groupnorm_merge(int n_shards, int n_stats, const float* local_mean, const float* local_var,
+                         const int64_t* counts, float* mean_out, float* var_out, void* stream) {
+  if (n_shards < 1 || n_shards > 4096) return fail(VAEP_ERR_INVALID_ARG, "n_shards %d outside 1..4096", n_shards);
+  if (n_stats < 0) return fail(VAEP_ERR_INVALID_ARG, "n_stats must be >= 0");
+  if (n_stats > 0 && (!local_mean || !local_var || !counts || !mean_out || !var_out))
+    return fail(VAEP_ERR_INVALID_ARG, "NULL device pointer");
+  hipError_t e = launch_moment_merge(n_shards, n_stats, local_mean, local_var, counts, mean_out, var_out,
+                                     (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "groupnorm merge launch");
+  return VAEP_OK;
+}
+
+int vaep_step_conv(int dtype, int x_dtype, const void* x, int batch, int frames, int cin, int h,
+                   int w, const void* weight, const void* bias, int cout, int kt, int kh, int kw,
+                   int causal, int upsample, const void* residual, const int32_t* row_starts,
+                   int n_bands, void* y, void* ws, size_t ws_bytes, size_t* bytes_out, void* stream) {
+  int rc = step_dims(dtype, batch, frames, cin, h, w);
+  if (rc) return rc;
+  if (x_dtype != VAEP_DTYPE_F32 && x_dtype != dtype)
+    return fail(VAEP_ERR_UNSUPPORTED, "x_dtype must be fp32 or the compute dtype");
+  if (cout < 1) return fail(VAEP_ERR_INVALID_ARG, "cout must be >= 1");
+  if (kh != kw || (kh != 1 && kh != 3)) return fail(VAEP_ERR_UNSUPPORTED, "spatial kernel %dx%d (1x1 or 3x3 only)", kh, kw);
+  if (kt != 1 && kt != 3) return fail(VAEP_ERR_UNSUPPORTED, "temporal kernel %d (1 or 3 only)", kt);
+  if (kt == 3 && !causal) return fail(VAEP_ERR_UNSUPPORTED, "a temporal kernel of 3 must be causal");
+  if (kt == 3 && kh == 1) return fail(VAEP_ERR_UNSUPPORTED, "(3,1,1) convs run through vaep_step_temporal_upsample");
+  if (upsample && (kt != 1 || kh != 3)) return fail(VAEP_ERR_UNSUPPORTED, "upsample fuses into 2-D 3x3 convs only");
+  const bool bf = dtype == VAEP_DTYPE_BF16;
+  if (bf && cout % 4 != 0) return fail(VAEP_ERR_UNSUPPORTED, "bf16 conv outputs need cout %% 4 == 0");
+  std::vector<int> rows;
+  if ((rc = step_bands(row_starts, n_bands, h, rows))) return rc;
+  const int nb = (int)rows.size();
+  const int cin_pad = bf ? round_up(cin, 32) : cin;
+  const int co_pad = bf ? round_up(cout, kConvTileN) : cout;
+  const int taps = kt * kh * kw;
+  const BandLayout Lin = make_layout(nb, rows.data(), batch * frames, frames, w, cin_pad);
+  const BandLayout Lout = upsample ? upsampled(Lin, cout) : reshaped(Lin, cout, Lin.n_img, frames);
+  const size_t eb = dtype_bytes(dtype);
+  const bool x_f32 = x_dtype == VAEP_DTYPE_F32;
+  Carver cv;
+  cv.base = (char*)ws;
+  void* xin = cv.take(layout_elems(Lin) * dtype_bytes(x_dtype));
+  void* yo = cv.take(layout_elems(Lout) * 4);
+  void* rb = residual ? cv.take(layout_elems(Lout) * 4) : nullptr;
+  ConvW cw;
+  cw.co = cout;
+  cw.ci = cin;
+  cw.co_pad = co_pad;
+  cw.ci_pad = cin_pad;
+  cw.kt = kt;
+  cw.ks = kh;
+  cw.w = cv.take((size_t)co_pad * taps * cin_pad * eb);
+  cw.b = (float*)cv.take((size_t)co_pad * sizeof(float));
+  bool sized;
+  if ((rc = step_finish_sizing(cv, ws, ws_bytes, bytes_out, &sized)) || sized) return rc;
+  if (!x || !weight || !y) return fail(VAEP_ERR_INVALID_ARG, "x, weight and y must be device pointers");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_pack(x, cin, xin, Lin, x_dtype, st);
+  if (e == hipSuccess && residual) e = launch_pack(residual, cout, rb, Lout, VAEP_DTYPE_F32, st);
+  if (e == hipSuccess) e = launch_pack_weight(weight, cout, cin, taps, cw.w, co_pad, cin_pad, dtype, st);
+  if (e == hipSuccess) e = launch_to_f32(bias, cout, cw.b, co_pad, dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "step conv staging");
+  Exec E;
+  E.dtype = dtype;
+  E.st = st;
+  E.dry = false;
+  if ((rc = E.conv(cw, xin, Lin, x_f32, yo, Lout, kModeBand, rb, upsample))) return rc;
+  e = launch_unpack(yo, Lout, y, cout, VAEP_DTYPE_F32, st);
+  if (e != hipSuccess) return hip_fail(e, "step conv gather");
+  return VAEP_OK;
+}
+
+int vaep_step_groupnorm(int dtype, const void* x, int batch, int frames, int c, int h, int w, int groups,
+                        float eps, const float* gamma, const float* beta, int act,
+                        const int32_t* row_starts, int n_bands, void* y, float* band_moments,
+                        float* merged, void* ws, size_t ws_bytes, size_t* bytes_out, void* stream) {
+  int rc = step_dims(dtype, batch, frames, c, h, w);
+  if (rc) return rc;
+  if ((rc = norm_channels_ok(dtype, c))) return rc;
+  if (groups < 1 || groups > 1024 || c % groups != 0) return fail(VAEP_ERR_INVALID_ARG, "groups %d must divide %d (<= 1024)", groups, c);
+  if (!(eps > 0.f)) return fail(VAEP_ERR_INVALID_ARG, "eps must be > 0");
+  std::vector<int> rows;
+  if ((rc = step_bands(row_starts, n_bands, h, rows))) return rc;
+  const int nb = (int)rows.size();
+  const BandLayout L = make_layout(nb, rows.data(), batch * frames, frames, w, c);
+  const size_t eb = dtype_bytes(dtype);
+  Carver cv;
+  cv.base = (char*)ws;
+  void* xin = cv.take(layout_elems(L) * 4);
+  void* yo = cv.take(layout_elems(L) * eb);
+  float* scratch = (float*)cv.take(gn_partials_floats(L, groups, dtype) * sizeof(float));
+  bool sized;
+  if ((rc = step_finish_sizing(cv, ws, ws_bytes, bytes_out, &sized)) || sized) return rc;
+  if (!x || !y || !gamma || !beta) return fail(VAEP_ERR_INVALID_ARG, "x, y, gamma and beta must be device pointers");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_pack(x, c, xin, L, VAEP_DTYPE_F32, st);
+  if (e != hipSuccess) return hip_fail(e, "step groupnorm staging");
+  NormArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.x = xin;
+  a.y = yo;
+  a.L = L;
+  a.groups = groups;
+  a.eps = eps;
+  a.gamma = gamma;
+  a.beta = beta;
+  a.act = act;
+  a.partials = reinterpret_cast<double*>(scratch);
+  a.merged_out = merged;
+  e = launch_groupnorm(a, dtype, st);
+  if (e == hipSuccess && band_moments)
+    e = hipMemcpyAsync(band_moments, a.band_moments, sizeof(float) * 3 * nb * L.n_img * groups,
+                       hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess) e = launch_unpack(yo, L, y, c, dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "step groupnorm");
+  return VAEP_OK;
+}
+
+int vaep_step_rmsnorm(int dtype, const void* x, int batch, int frames, int c, int h, int w, float eps,
+                      const float* gamma, int act, const int32_t* row_starts, int n_bands, void* y,
+                      void* ws, size_t ws_bytes, size_t* bytes_out, void* stream) {
+  int rc = step_dims(dtype, batch, frames, c, h, w);
+  if (rc) return rc;
+  if ((rc = norm_channels_ok(dtype, c))) return rc;
+  if (!(eps > 0.f)) return fail(VAEP_ERR_INVALID_ARG, "eps must be > 0");
+  std::vector<int> rows;
+  if ((rc = step_bands(row_starts, n_bands, h, rows))) return rc;
+  const int nb = (int)rows.size();
+  const BandLayout L = make_layout(nb, rows.data(), batch * frames, frames, w, c);
+  const size_t eb = dtype_bytes(dtype);
+  Carver cv;
+  cv.base = (char*)ws;
+  void* xin = cv.take(layout_elems(L) * 4);
+  void* yo = cv.take(layout_elems(L) * eb);
+  bool sized;
+  if ((rc = step_finish_sizing(cv, ws, ws_bytes, bytes_out, &sized)) || sized) return rc;
+  if (!x || !y || !gamma) return fail(VAEP_ERR_INVALID_ARG, "x, y and gamma must be device pointers");
+  hipStream_t st = (hipStream_t)stream;
+  NormArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.x = xin;
+  a.y = yo;
+  a.L = L;
+  a.eps = eps;
+  a.gamma = gamma;
+  a.act = act;
+  hipError_t e = launch_pack(x, c, xin, L, VAEP_DTYPE_F32, st);
+  if (e == hipSuccess) e = launch_rmsnorm(a, dtype, st);
+  if (e == hipSuccess) e = launch_unpack(yo, L, y, c, dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "step rmsnorm");
+  return VAEP_OK;
+}
+
+int vaep_step_attention(int dtype, const void* x, int batch, int frames, int c, int h, int w, int groups,
+                        float eps, const float* norm_gamma, const float* norm_beta, const void* wq,
+                        const void* bq, const void* wk, const void* bk, const void* wv, const void* bv,
+                        const void* wo, const void* bo, const int32_t* row_starts, int n_bands, void* y,
+                        void* ws, size_t ws_bytes, size_t* bytes_out, void* stream) {
+  int rc = step_dims(dtype, batch, frames, c, h, w);
+  if (rc) return rc;
+  if ((rc = norm_channels_ok(dtype, c))) return rc;
+  const bool bf = dtype == VAEP_DTYPE_BF16;
+  if (bf && c != 128 && c != 256 && c != 384 && c != 512)
+    return fail(VAEP_ERR_UNSUPPORTED, "bf16 attention supports 128/256/384/512 channels, got %d", c);
+  if (groups < 0 || (groups > 0 && (groups > 1024 || c % groups != 0)))
+    return fail(VAEP_ERR_INVALID_ARG, "groups %d must divide %d", groups, c);
+  if (!(eps > 0.f)) return fail(VAEP_ERR_INVALID_ARG, "eps must be > 0");
+  std::vector<int> rows;
+  if ((rc = step_bands(row_starts, n_bands, h, rows))) return rc;
+  const int nb = (int)rows.size();
+  const BandLayout L = make_layout(nb, rows.data(), batch * frames, frames, w, c);
+  const size_t eb = dtype_bytes(dtype);
+  Carver cv;
+  cv.base = (char*)ws;
+  void* bufs[4];  // x (fp32), normalised x, attention output (operand dtype), y (fp32)
+  for (int i = 0; i < 4; ++i) bufs[i] = cv.take(layout_elems(L) * ((i == 0 || i == 3) ? 4 : eb));
+  const size_t qkv = (size_t)L.n_img * h * w * c * eb;
+  void* qb = cv.take(qkv);
+  void* kb = cv.take(qkv);
+  void* vb = cv.take(qkv);
+  float* scratch = groups > 0 ? (float*)cv.take(gn_partials_floats(L, groups, dtype) * sizeof(float)) : nullptr;
+  AttnW aw;
+  aw.norm.g = const_cast<float*>(norm_gamma);
+  aw.norm.b = const_cast<float*>(norm_beta);
+  aw.norm.c = c;
+  aw.qkv.co = 3 * c;
+  aw.qkv.ci = c;
+  aw.qkv.co_pad = bf ? round_up(3 * c, kConvTileN) : 3 * c;
+  aw.qkv.ci_pad = c;
+  aw.qkv.kt = 1;
+  aw.qkv.ks = 1;
+  aw.qkv.w = cv.take((size_t)aw.qkv.co_pad * c * eb);
+  aw.qkv.b = (float*)cv.take((size_t)aw.qkv.co_pad * sizeof(float));
+  aw.out = aw.qkv;
+  aw.out.co = c;
+  aw.out.co_pad = bf ? round_up(c, kConvTileN) : c;
+  aw.out.w = cv.take((size_t)aw.out.co_pad * c * eb);
+  aw.out.b = (float*)cv.take((size_t)aw.out.co_pad * sizeof(float));
+  bool sized;
+  if ((rc = step_finish_sizing(cv, ws, ws_bytes, bytes_out, &sized)) || sized) return rc;
+  if (!x || !y || !norm_gamma || (groups > 0 && !norm_beta) || !wq || !wk || !wv || !wo)
+    return fail(VAEP_ERR_INVALID_ARG, "NULL device pointer");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipMemsetAsync(aw.qkv.w, 0, (size_t)aw.qkv.co_pad * c * eb, st);
+  const void* ws_[3] = {wq, wk, wv};
+  const void* bs_[3] = {bq, bk, bv};
+  for (int i = 0; i < 3 && e == hipSuccess; ++i) {
+    e = launch_pack_weight(ws_[i], c, c, 1, (char*)aw.qkv.w + (size_t)i * c * c * eb, c, c, dtype, st);
+    if (e == hipSuccess) e = launch_to_f32(bs_[i], c, aw.qkv.b + (size_t)i * c, c, dtype, st);
+  }
+  if (e == hipSuccess) e = launch_to_f32(nullptr, 0, aw.qkv.b + 3 * c, aw.qkv.co_pad - 3 * c, dtype, st);
+  if (e == hipSuccess) e = launch_pack_weight(wo, c, c, 1, aw.out.w, aw.out.co_pad, c, dtype, st);
+  if (e == hipSuccess) e = launch_to_f32(bo, c, aw.out.b, aw.out.co_pad, dtype, st);
+  if (e == hipSuccess) e = launch_pack(x, c, bufs[0], L, VAEP_DTYPE_F32, st);
+  if (e != hipSuccess) return hip_fail(e, "step attention staging");
+  Exec E;
+  E.dtype = dtype;
+  E.st = st;
+  E.dry = false;
+  E.groups = groups;
+  E.eps = eps;
+  E.qb = qb;
+  E.kb = kb;
+  E.vb = vb;
+  E.scratch = scratch;
+  if ((rc = E.attention(aw, bufs[0], L, bufs[1], bufs[2], bufs[3]))) return rc;
+  e = launch_unpack(bufs[3], L, y, c, VAEP_DTYPE_F32, st);
+  if (e != hipSuccess) return hip_fail(e, "step attention gather");
+  return VAEP_OK;
+}
+
+int vaep_step_temporal_upsample(int dtype, const void* x, int batch, int frames, int c, int h, int w,
+                                const void* weight, const void* bias, const int32_t* row_starts,
+                                int n_bands, void* y, void* ws, size_t ws_bytes, size_t* bytes_out,
+                                void* stream) {
+  int rc = step_dims(dtype, batch, frames, c, h, w);
+  if (rc) return rc;
+  const bool bf = dtype == VAEP_DTYPE_BF16;
+  if (bf && c % 32 != 0) return fail(VAEP_ERR_UNSUPPORTED, "bf16 temporal upsample needs c %% 32 == 0");
+  std::vector<int> rows;
+  if ((rc = step_bands(row_starts, n_bands, h, rows))) return rc;
+  const int nb = (int)rows.size();
+  const int T2 = 2 * frames - 1;
+  const BandLayout Lx = make_layout(nb, rows.data(), batch * frames, frames, w, c);
+  const BandLayout Lt = reshaped(Lx, c, batch * T2, T2);
+  const size_t eb = dtype_bytes(dtype);
+  Carver cv;
+  cv.base = (char*)ws;
+  void* xin = cv.take(layout_elems(Lx) * 4);
+  void* yo = cv.take(layout_elems(Lt) * 4);
+  ConvW cw;
+  cw.co = 2 * c;
+  cw.ci = c;
+  cw.co_pad = bf ? round_up(2 * c, kConvTileN) : 2 * c;
+  cw.ci_pad = c;
+  cw.kt = 3;
+  cw.ks = 1;
+  cw.w = cv.take((size_t)cw.co_pad * 3 * c * eb);
+  cw.b = (float*)cv.take((size_t)cw.co_pad * sizeof(float));
+  bool sized;
+  if ((rc = step_finish_sizing(cv, ws, ws_bytes, bytes_out, &sized)) || sized) return rc;
+  if (!x || !y || !weight) return fail(VAEP_ERR_INVALID_ARG, "x, weight and y must be device pointers");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_pack(x, c, xin, Lx, VAEP_DTYPE_F32, st);
+  if (e == hipSuccess) e = launch_pack_weight(weight, 2 * c, c, 3, cw.w, cw.co_pad, c, dtype, st);
+  if (e == hipSuccess) e = launch_to_f32(bias, 2 * c, cw.b, cw.co_pad, dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "step temporal upsample staging");
+  Exec E;
+  E.dtype = dtype;
+  E.st = st;
+  E.dry = false;
+  if ((rc = E.conv(cw, xin, Lx, true, yo, Lt, kModeTimeInterleave, nullptr, 0))) return rc;
+  e = launch_copy_frame0(xin, Lx, yo, Lt, VAEP_DTYPE_F32, st);
+  if (e == hipSuccess) e = launch_unpack(yo, Lt, y, c, VAEP_DTYPE_F32, st);
+  if (e != hipSuccess) return hip_fail(e, "step temporal upsample");
+  return VAEP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,266 @@
+// AGKV attention: each band's queries against the global K/V.
+//
+// ChituDiffusion "VAEP" feature page, attention section, and "Static Layer-Wise VAE
+// Decode", attention row: Q, K and V are computed per band; K and V of all bands are
+// gathered once; each band runs softmax attention of its local Q against the global
+// K/V and keeps its own output rows.  On one device the gather is the QKV projection
+// writing K and V straight into global token-major buffers at the band's token offset;
+// this kernel then reads them.  Single head, d = channels, scale 1/sqrt(d).
+//
+// bf16 path (flash style): a workgroup owns 64 queries of one band and image (16 per
+// wave).  Per 64-key tile, K (64 x d) and V^T (d x 64) are staged in LDS; each wave
+// computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (Q held in registers), runs the
+// online softmax in fp32 (exp2 domain) on its 16 query columns, casts P to bf16 and
+// accumulates O^T += V^T P^T in registers.  The P^T operand comes straight from the
+// S^T accumulators: the 32-key K index of the PV product is permuted identically in
+// both operands, which leaves the sum unchanged.
+#include "vaep_internal.h"
+
+namespace vaep {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+namespace {
+
+__device__ __forceinline__ long long band_offset(const BandLayout& L, int b, int n, int r, int c) {
+  return L.off[b] + (((long long)n * (L.rows[b] + 2) + r + 1) * L.W + c) * (long long)L.C;
+}
+
+__device__ __forceinline__ unsigned short f2bf(float v) {
+  __hip_bfloat16 h = __float2bfloat16(v);
+  return *reinterpret_cast<unsigned short*>(&h);
+}
+
+__device__ __forceinline__ int band_of(const AttnArgs& a, int blk) {
+  int b = 0;
+  while (b + 1 < a.L.nb && blk >= a.tile_start[b + 1]) ++b;
+  return b;
+}
+
+constexpr int kQ = 64;    // queries per workgroup
+constexpr int kKeys = 64; // keys per tile
+
+template <int D>
+__global__ void __launch_bounds__(256) flash_bf16(const AttnArgs a) {
+  constexpr int LDK = D + 8;
+  constexpr int LDV = kKeys + 8;
+  constexpr int NKK = D / 32;
+  constexpr int NDB = D / 16;
+  __shared__ __attribute__((aligned(16))) unsigned short sK[kKeys * LDK];
+  __shared__ __attribute__((aligned(16))) unsigned short sV[D * LDV];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = band_of(a, blockIdx.x);
+  const int local = blockIdx.x - a.tile_start[b];
+  const int W = a.L.W;
+  const int nq = a.L.rows[b] * W;
+  const int qt_img = (nq + kQ - 1) / kQ;
+  const int n = local / qt_img;
+  const int qt = local - n * qt_img;
+  const int tokens = a.tokens;
+  const long long tok0 = (long long)a.L.row0[b] * W;
+  const int ql = qt * kQ + wave * 16 + (lane & 15);
+  const bool qvalid = ql < nq;
+  const long long qtok = tok0 + (qvalid ? ql : nq - 1);
+
+  const unsigned short* Q = reinterpret_cast<const unsigned short*>(a.q) + ((long long)n * tokens + qtok) * D;
+  bf16x8_t qf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk)
+    qf[kk] = *reinterpret_cast<const bf16x8_t*>(Q + kk * 32 + (lane >> 4) * 8);
+
+  f32x4_t o[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -1e30f, l_run = 0.f;
+  const float sl2 = a.scale * 1.4426950408889634f;
+  const unsigned short* Kg = reinterpret_cast<const unsigned short*>(a.k) + (long long)n * tokens * D;
+  const unsigned short* Vg = reinterpret_cast<const unsigned short*>(a.vt) + (long long)n * D * tokens;
+  const bool vec_ok = (tokens & 7) == 0;
+
+  for (int k0 = 0; k0 < tokens; k0 += kKeys) {
+    __syncthreads();
+    for (int idx = tid; idx < kKeys * D / 8; idx += 256) {
+      const int row = idx / (D / 8), col = (idx - row * (D / 8)) * 8;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (k0 + row < tokens) v = *reinterpret_cast<const uint4*>(Kg + (long long)(k0 + row) * D + col);
+      *reinterpret_cast<uint4*>(&sK[row * LDK + col]) = v;
+    }
+    for (int idx = tid; idx < D * kKeys / 8; idx += 256) {
+      const int row = idx / (kKeys / 8), col = (idx - row * (kKeys / 8)) * 8;
+      const unsigned short* src = Vg + (long long)row * tokens + k0 + col;
+      uint4 v;
+      if (vec_ok && k0 + col + 8 <= tokens) {
+        v = *reinterpret_cast<const uint4*>(src);
+      } else {
+        unsigned short t[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = (k0 + col + e < tokens) ? src[e] : 0;
+        v.x = t[0] | ((unsigned)t[1] << 16);
+        v.y = t[2] | ((unsigned)t[3] << 16);
+        v.z = t[4] | ((unsigned)t[5] << 16);
+        v.w = t[6] | ((unsigned)t[7] << 16);
+      }
+      *reinterpret_cast<uint4*>(&sV[row * LDV + col]) = v;
+    }
+    __syncthreads();
+
+    // S^T[key][query] for the 4 key blocks of the tile
+    f32x4_t s[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+            &sK[(kb * 16 + (lane & 15)) * LDK + kk * 32 + (lane >> 4) * 8]);
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], s[kb], 0, 0, 0);
+      }
+    }
+    // online softmax over the tile (column = this lane's query)
+    float mt = -1e30f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = k0 + kb * 16 + (lane >> 4) * 4 + j;
+        const float v = key < tokens ? s[kb][j] * sl2 : -1e30f;
+        s[kb][j] = v;
+        mt = fmaxf(mt, v);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = exp2f(m_run - m_new);
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p = exp2f(s[kb][j] - m_new);
+        s[kb][j] = p;
+        ls += p;
+      }
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) o[i] *= alpha;
+
+    bf16x8_t pf[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pf[h][j] = (__bf16)s[2 * h][j];
+        pf[h][4 + j] = (__bf16)s[2 * h + 1][j];
+      }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const unsigned short* vr = &sV[(db * 16 + (lane & 15)) * LDV + h * 32 + (lane >> 4) * 4];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
+        uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(&u);
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[h], o[db], 0, 0, 0);
+      }
+    }
+  }
+
+  if (!qvalid) return;
+  const float inv = 1.f / l_run;
+  const int r = ql / W, c = ql - (ql / W) * W;
+  unsigned short* out = reinterpret_cast<unsigned short*>(a.o) + band_offset(a.L, b, n, r, c);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int d = db * 16 + (lane >> 4) * 4;
+    uint2 p;
+    p.x = (unsigned)f2bf(o[db][0] * inv) | ((unsigned)f2bf(o[db][1] * inv) << 16);
+    p.y = (unsigned)f2bf(o[db][2] * inv) | ((unsigned)f2bf(o[db][3] * inv) << 16);
+    *reinterpret_cast<uint2*>(out + d) = p;
+  }
+}
+
+// fp32 path: one wave per query, keys in sequence with an online softmax; lanes split d.
+__global__ void __launch_bounds__(256) attn_f32(const AttnArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = band_of(a, blockIdx.x);
+  const int local = blockIdx.x - a.tile_start[b];
+  const int W = a.L.W;
+  const int nq = a.L.rows[b] * W;
+  const int qt_img = (nq + 3) / 4;
+  const int n = local / qt_img;
+  const int ql = (local - n * qt_img) * 4 + wave;
+  if (ql >= nq) return;
+  const int D = a.c, tokens = a.tokens;
+  const long long qtok = (long long)a.L.row0[b] * W + ql;
+  const float* Q = reinterpret_cast<const float*>(a.q) + ((long long)n * tokens + qtok) * D;
+  const float* K = reinterpret_cast<const float*>(a.k) + (long long)n * tokens * D;
+  const float* Vt = reinterpret_cast<const float*>(a.vt) + (long long)n * D * tokens;
+  constexpr int kMaxPer = 16;   // d <= 1024
+  float q[kMaxPer], o[kMaxPer];
+  const int per = (D + 63) / 64;
+  for (int i = 0; i < kMaxPer; ++i) {
+    const int d = lane + 64 * i;
+    q[i] = (i < per && d < D) ? Q[d] : 0.f;
+    o[i] = 0.f;
+  }
+  float m = -1e30f, l = 0.f;
+  for (int key = 0; key < tokens; ++key) {
+    float part = 0.f;
+    for (int i = 0; i < per; ++i) {
+      const int d = lane + 64 * i;
+      if (d < D) part += q[i] * K[(long long)key * D + d];
+    }
+    for (int w = 32; w > 0; w >>= 1) part += __shfl_xor(part, w);
+    const float sc = part * a.scale;
+    const float mn = fmaxf(m, sc);
+    const float al = __expf(m - mn);
+    const float p = __expf(sc - mn);
+    l = l * al + p;
+    for (int i = 0; i < per; ++i) {
+      const int d = lane + 64 * i;
+      if (d < D) o[i] = o[i] * al + p * Vt[(long long)d * tokens + key];
+    }
+    m = mn;
+  }
+  const int r = ql / W, c = ql - (ql / W) * W;
+  float* out = reinterpret_cast<float*>(a.o) + band_offset(a.L, b, n, r, c);
+  for (int i = 0; i < per; ++i) {
+    const int d = lane + 64 * i;
+    if (d < D) out[d] = o[i] / l;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention(AttnArgs& a, int dtype, hipStream_t s) {
+  const int per = dtype == VAEP_DTYPE_F32 ? 4 : kQ;
+  int t = 0;
+  for (int b = 0; b < a.L.nb; ++b) {
+    a.tile_start[b] = t;
+    t += a.L.n_img * ((a.L.rows[b] * a.L.W + per - 1) / per);
+  }
+  a.tile_start[a.L.nb] = t;
+  a.tiles_total = t;
+  if (t == 0) return hipSuccess;
+  if (dtype == VAEP_DTYPE_F32) {
+    if (a.c > 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_f32, dim3(t), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  switch (a.c) {
+    case 128: hipLaunchKernelGGL(flash_bf16<128>, dim3(t), dim3(256), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(flash_bf16<256>, dim3(t), dim3(256), 0, s, a); break;
+    case 384: hipLaunchKernelGGL(flash_bf16<384>, dim3(t), dim3(256), 0, s, a); break;
+    case 512: hipLaunchKernelGGL(flash_bf16<512>, dim3(t), dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace vaep

@@ -1,0 +1,155 @@
+// Data movement around the band buffers: scatter a whole tensor into bands (with the
+// neighbours' boundary rows in the halo slots), gather bands back, the first frame of
+// the causal temporal upsample, and weight repacking.
+#include "vaep_internal.h"
+
+namespace vaep {
+namespace {
+
+template <typename T>
+__global__ void pack_kernel(const T* src, int c_src, T* dst, const BandLayout L) {
+  const int b = blockIdx.y;
+  const long long total = (long long)L.n_img * (L.rows[b] + 2) * L.W * L.C;
+  const long long HW = (long long)L.H * L.W;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int ch = (int)(i % L.C);
+    const long long pix = i / L.C;
+    const int c = (int)(pix % L.W);
+    const long long rr = pix / L.W;
+    const int rp = (int)(rr % (L.rows[b] + 2));
+    const int n = (int)(rr / (L.rows[b] + 2));
+    const int g = L.row0[b] + rp - 1;   // global row of this slot
+    T v = T(0.f);
+    if (ch < c_src && g >= 0 && g < L.H) {
+      const int bs = n / L.frames, t = n - bs * L.frames;
+      v = src[(((long long)bs * c_src + ch) * L.frames + t) * HW + (long long)g * L.W + c];
+    }
+    dst[L.off[b] + i] = v;
+  }
+}
+
+template <typename T>
+__global__ void unpack_kernel(const T* src, const BandLayout L, T* dst, int c_dst) {
+  const long long HW = (long long)L.H * L.W;
+  const long long total = (long long)L.n_img * c_dst * HW;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int c = (int)(i % L.W);
+    const int g = (int)((i / L.W) % L.H);
+    const long long rest = i / HW;               // (bs, ch, t)
+    const int t = (int)(rest % L.frames);
+    const int ch = (int)((rest / L.frames) % c_dst);
+    const int bs = (int)(rest / ((long long)L.frames * c_dst));
+    const int n = bs * L.frames + t;
+    int b = 0;
+    while (b + 1 < L.nb && g >= L.row0[b + 1]) ++b;
+    const int r = g - L.row0[b];
+    dst[i] = src[L.off[b] + (((long long)n * (L.rows[b] + 2) + r + 1) * L.W + c) * L.C + ch];
+  }
+}
+
+template <typename T>
+__global__ void copy_frame0_kernel(const T* src, const BandLayout Ls, T* dst, const BandLayout Ld) {
+  const int b = blockIdx.y;
+  const int bs = blockIdx.z;
+  const long long per = (long long)(Ls.rows[b] + 2) * Ls.W * Ls.C;   // one frame, halos included
+  const T* s = src + Ls.off[b] + (long long)(bs * Ls.frames) * per;
+  T* d = dst + Ld.off[b] + (long long)(bs * Ld.frames) * per;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < per;
+       i += (long long)gridDim.x * blockDim.x)
+    d[i] = s[i];
+}
+
+template <typename T>
+__global__ void pack_weight_kernel(const T* src, int co, int ci, int taps, T* dst, int co_pad,
+                                   int ci_pad) {
+  const long long total = (long long)co_pad * taps * ci_pad;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int c = (int)(i % ci_pad);
+    const int t = (int)((i / ci_pad) % taps);
+    const int o = (int)(i / ((long long)ci_pad * taps));
+    T v = T(0.f);
+    if (o < co && c < ci) v = src[((long long)o * ci + c) * taps + t];
+    dst[i] = v;
+  }
+}
+
+template <typename T>
+__global__ void to_f32_kernel(const T* src, int n, float* dst, int n_pad) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n_pad) dst[i] = (src != nullptr && i < n) ? (float)src[i] : 0.f;
+}
+
+int grid_for(long long n) {
+  long long g = (n + 255) / 256;
+  if (g > 16384) g = 16384;
+  return g < 1 ? 1 : (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_pack(const void* src, int c_src, void* dst, const BandLayout& L, int dtype,
+                       hipStream_t s) {
+  long long mx = 0;
+  for (int b = 0; b < L.nb; ++b) {
+    const long long e = (long long)L.n_img * (L.rows[b] + 2) * L.W * L.C;
+    if (e > mx) mx = e;
+  }
+  dim3 grid(grid_for(mx), L.nb);
+  if (dtype == VAEP_DTYPE_F32)
+    hipLaunchKernelGGL(pack_kernel<float>, grid, dim3(256), 0, s, (const float*)src, c_src, (float*)dst, L);
+  else
+    hipLaunchKernelGGL(pack_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)src, c_src, (bf16*)dst, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(const void* src, const BandLayout& L, void* dst, int c_dst, int dtype,
+                         hipStream_t s) {
+  const long long total = (long long)L.n_img * c_dst * L.H * L.W;
+  if (dtype == VAEP_DTYPE_F32)
+    hipLaunchKernelGGL(unpack_kernel<float>, dim3(grid_for(total)), dim3(256), 0, s, (const float*)src, L, (float*)dst, c_dst);
+  else
+    hipLaunchKernelGGL(unpack_kernel<bf16>, dim3(grid_for(total)), dim3(256), 0, s, (const bf16*)src, L, (bf16*)dst, c_dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_frame0(const void* src, const BandLayout& Ls, void* dst, const BandLayout& Ld,
+                              int dtype, hipStream_t s) {
+  long long mx = 0;
+  for (int b = 0; b < Ls.nb; ++b) {
+    const long long e = (long long)(Ls.rows[b] + 2) * Ls.W * Ls.C;
+    if (e > mx) mx = e;
+  }
+  const int batch = Ls.n_img / Ls.frames;
+  dim3 grid(grid_for(mx), Ls.nb, batch);
+  if (dtype == VAEP_DTYPE_F32)
+    hipLaunchKernelGGL(copy_frame0_kernel<float>, grid, dim3(256), 0, s, (const float*)src, Ls, (float*)dst, Ld);
+  else
+    hipLaunchKernelGGL(copy_frame0_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)src, Ls, (bf16*)dst, Ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_weight(const void* src, int co, int ci, int taps, void* dst, int co_pad,
+                              int ci_pad, int dtype, hipStream_t s) {
+  const long long total = (long long)co_pad * taps * ci_pad;
+  if (dtype == VAEP_DTYPE_F32)
+    hipLaunchKernelGGL(pack_weight_kernel<float>, dim3(grid_for(total)), dim3(256), 0, s,
+                       (const float*)src, co, ci, taps, (float*)dst, co_pad, ci_pad);
+  else
+    hipLaunchKernelGGL(pack_weight_kernel<bf16>, dim3(grid_for(total)), dim3(256), 0, s,
+                       (const bf16*)src, co, ci, taps, (bf16*)dst, co_pad, ci_pad);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_f32(const void* src, int n, float* dst, int n_pad, int dtype, hipStream_t s) {
+  if (n_pad <= 0) return hipSuccess;
+  if (dtype == VAEP_DTYPE_F32)
+    hipLaunchKernelGGL(to_f32_kernel<float>, dim3((n_pad + 255) / 256), dim3(256), 0, s, (const float*)src, n, dst, n_pad);
+  else
+    hipLaunchKernelGGL(to_f32_kernel<bf16>, dim3((n_pad + 255) / 256), dim3(256), 0, s, (const bf16*)src, n, dst, n_pad);
+  return hipGetLastError();
+}
+
+}  // namespace vaep

@@ -1,0 +1,150 @@
+// Internal declarations shared by the host executor and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/vaep.h"
+
+namespace vaep {
+
+constexpr int kMaxBands = VAEP_MAX_BANDS;
+
+using bf16 = __hip_bfloat16;
+
+// Per-band activation buffers.  Band i holds `rows[i]` owned rows plus one halo row
+// above and one below, for every image (batch x frames), channels innermost:
+//   element (band i, image n, row r in [-1, rows[i]], col c, channel ch) lives at
+//   off[i] + ((n * (rows[i] + 2) + r + 1) * W + c) * C + ch.
+// The halo rows of band i hold copies of the neighbours' boundary rows, written by
+// the producer of the tensor (the "halo push"); rows outside the image are never read.
+struct BandLayout {
+  int nb;          // number of bands
+  int n_img;       // images = batch * frames
+  int frames;      // frames per sample (1 for images)
+  int H, W, C;     // global height, width, channel stride
+  int rows[kMaxBands];
+  int row0[kMaxBands];      // global index of the band's first row
+  long long off[kMaxBands]; // element offset of band i's buffer
+};
+
+// Total elements of a layout (all bands, halo rows included).
+inline long long layout_elems(const BandLayout& L) {
+  long long e = 0;
+  for (int i = 0; i < L.nb; ++i) e += (long long)L.n_img * (L.rows[i] + 2) * L.W * L.C;
+  return e;
+}
+
+// Fill a layout from band row counts; bands are stored back to back from element 0.
+BandLayout make_layout(int nb, const int* rows, int n_img, int frames, int W, int C);
+// The same bands after a nearest-2x upsample: rows and width double.
+BandLayout upsampled(const BandLayout& L, int C);
+// Same rows/width, a different channel count and image count.
+BandLayout reshaped(const BandLayout& L, int C, int n_img, int frames);
+
+// ------------------------------------------------------------------ conv
+enum ConvMode : int {
+  kModeBand = 0,            // band-layout output (+bias, +residual), halo push
+  kModeQKV = 1,             // global token-major Q, K and transposed V
+  kModeFinal = 2,           // NC[T]HW output, first `cout` channels
+  kModeTimeInterleave = 3,  // causal temporal upsample frame layout, halo push
+};
+
+struct ConvArgs {
+  const void* x;        // input band buffer
+  const void* w;        // packed weights [cout_pad][taps][cin]
+  const float* bias;    // [cout_pad] fp32
+  const void* res;      // fp32 residual, output layout (nullable)
+  void* y;              // fp32 output (band buffer, or final tensor for kModeFinal)
+  void* q;              // kModeQKV: Q [n_img][tokens][c]
+  void* k;              //           K [n_img][tokens][c]
+  void* vt;             //           V^T [n_img][c][tokens]
+  BandLayout in;
+  BandLayout out;       // output layout (kModeBand / kModeTimeInterleave)
+  int cin;              // == in.C
+  int cout;             // true output channels
+  int cout_pad;         // rows of the packed weight
+  int kt, ks;           // temporal taps (1 or 3, causal), spatial kernel (1 or 3)
+  int ups;              // nearest-2x fused into the load
+  int mode;
+  int x_f32;            // bf16 path: operand source stored as fp32 (rounded on load)
+  int final_frames;     // kModeFinal: frames per sample of the output tensor
+  int tiles_total;      // M tiles over all bands
+  int tile_start[kMaxBands + 1];  // prefix of M tiles per band
+};
+
+// Launch the convolution described by `a` (fills tile fields).  dtype: VAEP_DTYPE_*.
+hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s);
+// Pixel tile of the MFMA kernel along M and output-channel tile along N.
+constexpr int kConvTileM = 128;
+constexpr int kConvTileN = 128;
+
+// ------------------------------------------------------------------ norms
+// Local moments per (band, image, group): partial records of tiles, merged per band and
+// then across bands with the element-count-weighted merge.
+struct NormArgs {
+  const void* x;         // fp32 input (conv outputs are fp32 in every configuration)
+  void* y;               // output in the operand dtype
+  BandLayout L;
+  int groups;
+  float eps;
+  const float* gamma;
+  const float* beta;
+  int act;               // SiLU after the affine
+  double* partials;      // [blocks][groups][2] fp64 (mean, M2) of each stats block, then scratch
+  float* band_moments;   // [3][nb][n_img*groups] count, mean, var (device scratch)
+  float* stats;          // [2][n_img*groups] merged mean, rstd
+  float* merged_out;     // optional [2][n_img*groups] merged mean, var
+  int blk_start[kMaxBands + 1];   // stats blocks of band i start here
+  int blk_per_img[kMaxBands];     // stats blocks per image in band i
+  int pix_per_blk[kMaxBands];     // pixels covered by one stats block in band i
+  long long item_start[kMaxBands + 1];  // apply pass: first vector (GN) / pixel (RMS) of band i
+};
+
+// Scratch of a GroupNorm launch in floats (bounded over every band table of L.nb bands).
+size_t gn_partials_floats(const BandLayout& L, int groups, int dtype);
+hipError_t launch_groupnorm(NormArgs& a, int dtype, hipStream_t s);
+hipError_t launch_rmsnorm(NormArgs& a, int dtype, hipStream_t s);
+hipError_t launch_moment_merge(int n_shards, int n_stats, const float* mean, const float* var,
+                               const int64_t* counts, float* mean_out, float* var_out,
+                               hipStream_t s);
+
+// ------------------------------------------------------------------ attention
+struct AttnArgs {
+  const void* q;    // [n_img][tokens][c]
+  const void* k;    // [n_img][tokens][c]
+  const void* vt;   // [n_img][c][tokens]
+  void* o;          // band layout output, c channels
+  BandLayout L;     // layout of o (band rows, image = attention span)
+  int c;
+  int tokens;       // H * W of one span
+  float scale;
+  int tiles_total;
+  int tile_start[kMaxBands + 1];  // query tiles per band (per image)
+};
+hipError_t launch_attention(AttnArgs& a, int dtype, hipStream_t s);
+
+// ------------------------------------------------------------------ data movement
+// NC[T]HW tensor -> band layout (halo rows filled from neighbours, zeros at image
+// edges, channels >= c_src zero).  n_img = B*T.
+hipError_t launch_pack(const void* src, int c_src, void* dst, const BandLayout& L, int dtype,
+                       hipStream_t s);
+// band layout -> NC[T]HW tensor with c_dst channels.
+hipError_t launch_unpack(const void* src, const BandLayout& L, void* dst, int c_dst, int dtype,
+                         hipStream_t s);
+// Copy frame 0 of every sample of `src` (frames T) to frame 0 of `dst` (frames 2T-1),
+// halo rows included.
+hipError_t launch_copy_frame0(const void* src, const BandLayout& Ls, void* dst,
+                              const BandLayout& Ld, int dtype, hipStream_t s);
+// Conv weight [co][ci][taps] (dtype) -> [co_pad][taps][ci_pad] (dtype), zero padded.
+hipError_t launch_pack_weight(const void* src, int co, int ci, int taps, void* dst, int co_pad,
+                              int ci_pad, int dtype, hipStream_t s);
+// Any-dtype vector -> fp32 vector of n_pad entries (zero padded); src may be NULL (zeros).
+hipError_t launch_to_f32(const void* src, int n, float* dst, int n_pad, int dtype, hipStream_t s);
+
+inline size_t dtype_bytes(int dtype) { return dtype == VAEP_DTYPE_F32 ? 4 : 2; }
+
+}  // namespace vaep

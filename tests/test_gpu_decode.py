@@ -1,0 +1,178 @@
+"""Whole-decode parity of the HIP path against the oracle, through the C ABI.
+
+* tiny fp32 preset and the 512^2 preset against the oracle's full decode, as
+  full and band decodes;
+* reduced-size variants of the 1024^2 presets and of the video preset (same
+  graphs, latents small enough for the oracle) with uneven and one-row bands;
+* full-size 1024^2, batch-4 and video presets against oracle samples stored by
+  tests/golden/make_full_size_golden.py, in the configuration bench.py times;
+* band decode against full decode on the GPU; error paths; repeated and
+  alternating calls on one model.
+"""
+import importlib.util
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import spatially_sharded_conv_amd as vaep
+from spatially_sharded_conv_amd import _lib as L
+from oracle import Precision, decode_full as oracle_full
+from synth import make_latent, make_params, preset
+from tests._util import BAND_VS_FULL_REL, REFERENCE_PRECISION, TOL, assert_close, errors, to_dev
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def make_decoder(cfg, affine="default"):
+    params = make_params(cfg, affine=affine)
+    lc = vaep.make_config(cfg.family, cfg.dtype, cfg.z_channels, cfg.stage_channels,
+                          cfg.resnets_per_stage, cfg.norm_groups, cfg.temporal_up_stages, cfg.eps)
+    dev = [to_dev(params[n], cfg.dtype) for n, _ in vaep.param_info(lc)]
+    dec = vaep.Decoder(lc, dev)
+    del dev
+    return dec, params
+
+
+def gpu_decode(dec, cfg, latent, starts, ws=None):
+    lat = to_dev(latent, cfg.dtype)
+    b = latent.shape[0]
+    t = latent.shape[2] if latent.dim() == 5 else 1
+    h, w = latent.shape[-2:]
+    out = torch.empty(cfg.output_shape(b, t, h, w), dtype=torch.float32, device="cuda")
+    if ws is None:
+        ws = dec.workspace(b, t, h, w, len(starts) - 1)
+    rc, info = dec.decode_bands(lat, starts, out, ws)
+    torch.cuda.synchronize()
+    return out, rc, info
+
+
+def _check_against_oracle(cfg, starts_list, affine="default"):
+    dec, params = make_decoder(cfg, affine)
+    z = make_latent(cfg)
+    # the exact decode (fp32 storage, fp64 arithmetic); see REFERENCE_PRECISION in _util
+    ref = oracle_full(cfg, params, z, Precision(REFERENCE_PRECISION))
+    outs = []
+    for starts in starts_list:
+        y, rc, info = gpu_decode(dec, cfg, z, starts)
+        assert rc == 0 and info.bands_used == len(starts) - 1
+        assert_close(y, ref, *TOL[cfg.dtype], what=f"{cfg.name} bands {starts}")
+        outs.append(y)
+    full = outs[0]
+    for y in outs[1:]:
+        assert errors(y, full)[1] <= BAND_VS_FULL_REL
+    dec.close()
+
+
+def test_cfg1_tiny_fp32_full_and_bands(gpu_lib):
+    cfg = preset(1)
+    _check_against_oracle(cfg, [(0, 8), cfg.band_starts, tuple(range(9))], affine="random")
+
+
+def test_cfg1_default_init(gpu_lib):
+    cfg = preset(1)
+    _check_against_oracle(cfg, [(0, 8), cfg.band_starts])
+
+
+def test_cfg2_512_bf16_full_and_bands(gpu_lib):
+    cfg = preset(2)
+    _check_against_oracle(cfg, [(0, 64), cfg.band_starts])
+
+
+def test_kl_reduced_uneven_bands(gpu_lib):
+    cfg = preset(3).with_size(latent_h=12, latent_w=20, band_starts=(0, 3, 7, 8, 12))
+    _check_against_oracle(cfg, [(0, 12), cfg.band_starts], affine="random")
+
+
+def test_kl_reduced_batch(gpu_lib):
+    cfg = preset(4).with_size(batch=2, latent_h=10, latent_w=8, band_starts=(0, 3, 6, 10))
+    _check_against_oracle(cfg, [(0, 10), cfg.band_starts, (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10)],
+                          affine="random")
+
+
+def test_wan_reduced_video(gpu_lib):
+    cfg = preset(5).with_size(frames=3, latent_h=6, latent_w=10, band_starts=(0, 2, 3, 6))
+    _check_against_oracle(cfg, [(0, 6), cfg.band_starts], affine="random")
+
+
+def _golden(i):
+    path = os.path.join(GOLDEN, f"cfg{i}_oracle_samples.npy")
+    meta = os.path.join(GOLDEN, f"cfg{i}_oracle_summary.json")
+    if not (os.path.exists(path) and os.path.exists(meta)):
+        pytest.skip(f"stored oracle samples for config {i} not generated")
+    spec = importlib.util.spec_from_file_location("mk", os.path.join(GOLDEN, "make_full_size_golden.py"))
+    mk = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mk)
+    return np.load(path), json.load(open(meta)), mk
+
+
+@pytest.mark.parametrize("i", [3, 4, 5])
+def test_full_size_against_oracle_samples(gpu_lib, i):
+    vals, meta, mk = _golden(i)
+    cfg = preset(i)
+    dec, _ = make_decoder(cfg)
+    z = make_latent(cfg)
+    y_full, rc, _ = gpu_decode(dec, cfg, z, (0, cfg.latent_h))
+    assert rc == 0
+    y_band, rc, info = gpu_decode(dec, cfg, z, cfg.band_starts)
+    assert rc == 0 and info.bands_used == len(cfg.band_starts) - 1
+    assert list(y_full.shape) == meta["shape"]
+    pos = torch.from_numpy(mk.sample_positions(i, y_full.numel()))
+    ref = torch.from_numpy(vals).double()
+    for y in (y_full, y_band):
+        got = y.reshape(-1)[pos.cuda()].double().cpu()
+        assert_close(got, ref, *TOL[cfg.dtype], what=f"config {i} sampled outputs")
+    # whole-tensor summary statistics of the oracle output
+    yf = y_band.double()
+    assert abs(yf.mean().item() - meta["mean"]) < 1e-3
+    assert abs(yf.std().item() - meta["std"]) / meta["std"] < 1e-3
+    assert errors(y_band, y_full)[1] <= BAND_VS_FULL_REL
+    dec.close()
+
+
+def test_error_paths_leave_output_untouched(gpu_lib):
+    cfg = preset(3).with_size(latent_h=8, latent_w=8, band_starts=(0, 4, 8))
+    dec, _ = make_decoder(cfg)
+    z = to_dev(make_latent(cfg), "bf16")
+    out = torch.full(cfg.output_shape(), 7.0, dtype=torch.float32, device="cuda")
+    ws = dec.workspace(1, 1, 8, 8, 2)
+    small = ws[: ws.numel() // 2]
+    with pytest.raises(L.VaepError) as e:
+        dec.decode_bands(z, (0, 4, 8), out, small)
+    assert e.value.code == L.VAEP_ERR_WORKSPACE
+    for bad in [(0, 4, 4, 8), (0, 5, 3, 8), (0, 4, 7), (1, 4, 8)]:
+        with pytest.raises(L.VaepError) as e:
+            dec.decode_bands(z, bad, out, ws)
+        assert e.value.code == L.VAEP_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+    dec.close()
+
+
+def test_too_many_bands_fall_back_to_dense(gpu_lib):
+    cfg = preset(3).with_size(latent_h=70, latent_w=4, band_starts=(0, 70))
+    dec, _ = make_decoder(cfg)
+    z = make_latent(cfg)
+    full, rc, _ = gpu_decode(dec, cfg, z, (0, 70))
+    starts = tuple(range(71))
+    y, rc, info = gpu_decode(dec, cfg, z, starts)
+    assert rc == L.VAEP_WARN_FELL_BACK and info.fell_back == 1 and info.bands_used == 1
+    assert torch.equal(y, full)
+    dec.close()
+
+
+def test_repeat_and_alternating_calls(gpu_lib):
+    cfg = preset(3).with_size(latent_h=10, latent_w=12, band_starts=(0, 3, 10))
+    dec, _ = make_decoder(cfg, affine="random")
+    z = make_latent(cfg)
+    ws = dec.workspace(1, 1, 10, 12, 4)
+    a, _, _ = gpu_decode(dec, cfg, z, (0, 3, 10), ws)
+    b, _, _ = gpu_decode(dec, cfg, z, (0, 10), ws)
+    c, _, _ = gpu_decode(dec, cfg, z, (0, 1, 5, 9, 10), ws)
+    d, _, _ = gpu_decode(dec, cfg, z, (0, 3, 10), ws)
+    assert torch.equal(a, d)
+    assert errors(b, a)[1] <= BAND_VS_FULL_REL and errors(c, a)[1] <= BAND_VS_FULL_REL
+    dec.close()

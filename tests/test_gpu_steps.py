@@ -1,0 +1,222 @@
+"""Per-step parity of the HIP kernels against the oracle, through the C ABI.
+
+Shapes span several workgroup tiles with ragged tails, uneven and one-row
+bands, and channel counts that are not multiples of the output tile.  Inputs are
+seeded; the oracle evaluates each step's definition in float64 on the same
+values and rounds to the storage type once.
+"""
+import math
+
+import pytest
+import torch
+
+import spatially_sharded_conv_amd as vaep
+from oracle import ops
+from oracle.decoder import Precision
+from tests._util import assert_close, seeded, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# A step whose output is a normalised operand: the GPU and the oracle both round it to
+# the compute dtype once.  Conv outputs are fp32 accumulations of exact products.
+STEP_TOL = {"bf16": (2e-2, 4e-3), "f32": (1e-4, 1e-5)}
+ACC_TOL = (1e-4, 1e-5)
+
+
+def _op(x, dtype):
+    """The matrix-core operand the GPU forms from a stored tensor."""
+    return Precision(dtype).finish(x.double(), "operand")
+
+
+def _x5(x):
+    return x if x.dim() == 5 else x.unsqueeze(2)
+
+
+def _conv_ref(x, w, b, causal, res, dtype, upsample=False):
+    x5 = _x5(_op(x, dtype))
+    if upsample:
+        x5 = ops.upsample_nearest2x(x5)
+    w5 = w if w.dim() == 5 else w.unsqueeze(2)
+    r5 = None if res is None else _x5(res)
+    y = ops.conv_full(x5, w5, b, causal, Precision(dtype).acc, r5)
+    return y if x.dim() == 5 else y[:, :, 0]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", [
+    # (B, cin, cout, H, W, starts, with_residual)
+    (2, 64, 96, 13, 37, (0, 1, 6, 13), True),
+    (1, 32, 128, 16, 16, (0, 16), False),
+    (1, 128, 256, 9, 70, (0, 4, 5, 9), True),
+])
+def test_conv3x3_step(gpu_lib, dtype, case):
+    B, cin, cout, H, W, starts, with_res = case
+    x = seeded((B, cin, H, W), 11, dtype=dtype)
+    w = seeded((cout, cin, 3, 3), 12, 1 / math.sqrt(cin * 9), dtype=dtype)
+    b = seeded((cout,), 13, 0.1, dtype=dtype)
+    r = seeded((B, cout, H, W), 14, dtype="f32") if with_res else None
+    ref = _conv_ref(x, w, b, False, r, dtype)
+    got = vaep.step_conv(to_dev(x, dtype), to_dev(w, dtype), to_dev(b, dtype), starts,
+                         residual=None if r is None else r.cuda())
+    assert got.dtype == torch.float32
+    assert_close(got, ref, *ACC_TOL, what=f"conv3x3 {case}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_conv1x1_step(gpu_lib, dtype):
+    x = seeded((2, 192, 7, 45), 21, dtype=dtype)
+    w = seeded((96, 192, 1, 1), 22, 1 / math.sqrt(192), dtype=dtype)
+    b = seeded((96,), 23, 0.1, dtype=dtype)
+    ref = _conv_ref(x, w, b, False, None, dtype)
+    got = vaep.step_conv(to_dev(x, dtype), to_dev(w, dtype), to_dev(b, dtype), (0, 3, 7))
+    assert_close(got, ref, *ACC_TOL, what="conv1x1")
+
+
+def test_conv_from_fp32_source(gpu_lib):
+    # shortcut / upsample convs read the fp32 residual stream and round it to bf16 on load
+    x = seeded((1, 64, 9, 21), 24, dtype="f32")
+    w = seeded((128, 64, 3, 3), 25, 1 / math.sqrt(64 * 9), dtype="bf16")
+    b = seeded((128,), 26, 0.1, dtype="bf16")
+    ref = _conv_ref(x, w, b, False, None, "bf16")
+    got = vaep.step_conv(x.cuda(), to_dev(w, "bf16"), to_dev(b, "bf16"), (0, 2, 9))
+    assert_close(got, ref, *ACC_TOL, what="conv from fp32 source")
+    ref_up = _conv_ref(x, w, b, False, None, "bf16", upsample=True)
+    got_up = vaep.step_conv(x.cuda(), to_dev(w, "bf16"), to_dev(b, "bf16"), (0, 2, 9), upsample=True)
+    assert_close(got_up, ref_up, *ACC_TOL, what="upsample conv from fp32 source")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_upsample_conv_step(gpu_lib, dtype):
+    x = seeded((1, 64, 6, 11), 31, dtype=dtype)
+    w = seeded((64, 64, 3, 3), 32, 1 / math.sqrt(64 * 9), dtype=dtype)
+    b = seeded((64,), 33, 0.1, dtype=dtype)
+    starts = (0, 1, 2, 6)
+    ref = _conv_ref(x, w, b, False, None, dtype, upsample=True)
+    got = vaep.step_conv(to_dev(x, dtype), to_dev(w, dtype), to_dev(b, dtype), starts, upsample=True)
+    assert got.shape == (1, 64, 12, 22)
+    assert_close(got, ref, *ACC_TOL, what="upsample conv")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_causal_conv3d_step(gpu_lib, dtype):
+    x = seeded((1, 32, 4, 9, 11), 41, dtype=dtype)
+    w = seeded((64, 32, 3, 3, 3), 42, 1 / math.sqrt(32 * 27), dtype=dtype)
+    b = seeded((64,), 43, 0.1, dtype=dtype)
+    r = seeded((1, 64, 4, 9, 11), 44, dtype="f32")
+    ref = _conv_ref(x, w, b, True, r, dtype)
+    got = vaep.step_conv(to_dev(x, dtype), to_dev(w, dtype), to_dev(b, dtype), (0, 4, 9), causal=True,
+                         residual=r.cuda())
+    assert_close(got, ref, *ACC_TOL, what="causal conv3d")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_groupnorm_step(gpu_lib, dtype):
+    B, C, H, W, G = 2, 128, 11, 19, 32
+    starts = (0, 2, 5, 11)
+    x = seeded((B, C, H, W), 51, 2.0, offset=3.0, dtype="f32")
+    g = seeded((C,), 52, 0.25, offset=1.0, dtype="f32")
+    be = seeded((C,), 53, 0.1, dtype="f32")
+    x5 = _x5(x)
+    _, m, v = ops.groupnorm_moments(x5, G)
+    ref = Precision(dtype).finish(ops.groupnorm_apply(x5, m, v, g, be, 1e-6, act=True))[:, :, 0]
+    odt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    y, moments, merged = vaep.step_groupnorm(x.cuda(), G, 1e-6, g.cuda(), be.cuda(), starts, out_dtype=odt)
+    assert_close(y, ref, *STEP_TOL[dtype], what="groupnorm")
+    # merged statistics and every band's local moments against the two-pass definition
+    assert_close(merged[0].view(B, G), m, 1e-4, 1e-5, "merged mean")
+    assert_close(merged[1].view(B, G), v, 1e-3, 1e-5, "merged var")
+    for i, (s, e) in enumerate(zip(starts, starts[1:])):
+        cnt, mi, vi = ops.groupnorm_moments(x5[:, :, :, s:e], G)
+        assert torch.all(moments[0, i].cpu() == cnt)
+        assert_close(moments[1, i].view(B, G), mi, 1e-4, 1e-5, f"band {i} mean")
+        assert_close(moments[2, i].view(B, G), vi, 1e-3, 1e-5, f"band {i} var")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rmsnorm_step(gpu_lib, dtype):
+    x = seeded((1, 96, 3, 7, 10), 61, 1.5, dtype="f32")
+    g = seeded((96,), 62, 0.25, offset=1.0, dtype="f32")
+    ref = Precision(dtype).finish(ops.rmsnorm(x, g, 1e-6, act=True))
+    odt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    got = vaep.step_rmsnorm(x.cuda(), 1e-6, g.cuda(), (0, 1, 7), out_dtype=odt)
+    assert_close(got, ref, *STEP_TOL[dtype], what="rmsnorm")
+
+
+def _attn_ref(x, groups, g, be, wq, bq, wk, bk, wv, bv, wo, bo, dtype):
+    fin = Precision(dtype).finish
+    x5 = _x5(x)
+    if groups:
+        _, m, v = ops.groupnorm_moments(x5, groups)
+        h = fin(ops.groupnorm_apply(x5, m, v, g, be, 1e-6, act=False))
+    else:
+        h = fin(ops.rmsnorm(x5, g, 1e-6, act=False))
+    c = x5.shape[1]
+    y = torch.empty_like(x5)
+    for n in range(x5.shape[0]):
+        for t in range(x5.shape[2]):
+            tok = h[n, :, t].reshape(c, -1).T.double()
+            q = fin(tok @ wq.double().T + bq.double())
+            k = fin(tok @ wk.double().T + bk.double())
+            v_ = fin(tok @ wv.double().T + bv.double())
+            o = fin(ops.attention_rows(q, k, v_, 1 / math.sqrt(c)))
+            out = x5[n, :, t].reshape(c, -1).T.double() + o.double() @ wo.double().T + bo.double()
+            y[n, :, t] = Precision(dtype).acc(out).T.reshape(c, x5.shape[3], x5.shape[4])
+    return y if x.dim() == 5 else y[:, :, 0]
+
+
+@pytest.mark.parametrize("case", [
+    ("bf16", 512, 32, (1, 8, 25), (0, 3, 8)),          # 200 tokens: ragged key and query tiles
+    ("bf16", 384, 0, (2, 6, 10), (0, 1, 6)),           # per-frame span, RMSNorm pre-norm
+    ("f32", 64, 8, (1, 8, 8), (0, 3, 8)),
+])
+def test_attention_step(gpu_lib, case):
+    dtype, C, G, (T, H, W), starts = case
+    video = G == 0
+    shape = (1, C, T, H, W) if video else (1, C, H, W)
+    x = seeded(shape, 71, dtype="f32")
+    g = seeded((C,), 72, 0.25, offset=1.0, dtype="f32")
+    be = seeded((C,), 73, 0.1, dtype="f32")
+    ws = [seeded((C, C), 74 + i, 1 / math.sqrt(C), dtype=dtype) for i in range(4)]
+    bs = [seeded((C,), 80 + i, 0.1, dtype=dtype) for i in range(4)]
+    ref = _attn_ref(x, G, g, be, ws[0], bs[0], ws[1], bs[1], ws[2], bs[2], ws[3], bs[3], dtype)
+    dev = [to_dev(t, dtype) for t in ws + bs]
+    got = vaep.step_attention(x.cuda(), G, 1e-6, g.cuda(), be.cuda(), dev[0], dev[4], dev[1],
+                              dev[5], dev[2], dev[6], dev[3], dev[7], starts)
+    assert_close(got, ref, *STEP_TOL[dtype], what=f"attention {case}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_temporal_upsample_step(gpu_lib, dtype):
+    C = 64
+    x = seeded((1, C, 3, 5, 6), 91, dtype="f32")
+    w = seeded((2 * C, C, 3, 1, 1), 92, 1 / math.sqrt(3 * C), dtype=dtype)
+    b = seeded((2 * C,), 93, 0.1, dtype=dtype)
+    z = ops.conv_full(_op(x, dtype).float(), w, b, True, Precision(dtype).acc)
+    ref = ops.temporal_upsample_interleave(x, z)
+    got = vaep.step_temporal_upsample(x.cuda(), to_dev(w, dtype), to_dev(b, dtype), (0, 2, 5))
+    assert got.shape == (1, C, 5, 5, 6)
+    assert_close(got, ref, *ACC_TOL, what="temporal upsample")
+
+
+def test_groupnorm_merge_entry_point(gpu_lib):
+    from synth.gen import uniform_draws
+    n_shards, n_stats = 5, 37
+    mean = seeded((n_shards, n_stats), 101, 3.0, dtype="f32")
+    var = seeded((n_shards, n_stats), 102, 1.0, dtype="f32").abs()
+    counts = torch.from_numpy((uniform_draws(103, n_shards * n_stats) * 1000).astype("int64")).view(n_shards, n_stats)
+    counts[2, 5] = 0
+    counts[:, 7] = 0
+    # reference per statistic (column): counts differ per column
+    m_ref = torch.zeros(n_stats, dtype=torch.float64)
+    v_ref = torch.zeros(n_stats, dtype=torch.float64)
+    for s in range(n_stats):
+        cs = [int(counts[i, s]) for i in range(n_shards)]
+        if sum(cs) == 0:
+            continue
+        m, v = ops.merge_moments(cs, [mean[i, s:s + 1] for i in range(n_shards)],
+                                 [var[i, s:s + 1] for i in range(n_shards)])
+        m_ref[s], v_ref[s] = m.item(), v.item()
+    gm, gv = vaep.groupnorm_merge(mean.cuda(), var.cuda(), counts.cuda())
+    assert_close(gm, m_ref, 1e-5, 1e-6, "merged mean")
+    assert_close(gv, v_ref, 1e-5, 1e-6, "merged var")
+    assert gm[7].item() == 0.0 and gv[7].item() == 0.0
