@@ -384,6 +384,7 @@ struct Exec {
   }
   int groups = 0;      // GroupNorm groups; 0 selects channel RMSNorm
   float eps = 1e-6f;
+  int base_rows = 0;   // rows of the band table's own resolution (latent rows of a decode)
 
   size_t eb() const { return dtype_bytes(dtype); }   // operand (normalised activation) element
   void need_act(const BandLayout& L, size_t elem) { act_bytes = std::max(act_bytes, (size_t)layout_elems(L) * elem); }
@@ -461,8 +462,10 @@ struct Exec {
 
   int norm(const NormW& w, const void* x, const BandLayout& L, void* y, int act, float* merged_out = nullptr) {
     need_act(L, 4);
+    // statistics tiles never straddle a row any band table of this decode can cut at
+    const int slab_rows = base_rows > 0 ? L.H / base_rows : 1;
     if (groups > 0)
-      scratch_bytes = std::max(scratch_bytes, gn_partials_floats(L, groups, dtype) * sizeof(float));
+      scratch_bytes = std::max(scratch_bytes, gn_partials_floats(L, groups, slab_rows) * sizeof(float));
     if (dry) return VAEP_OK;
     NormArgs a;
     std::memset(&a, 0, sizeof(a));
@@ -476,6 +479,7 @@ struct Exec {
     a.act = act;
     a.partials = reinterpret_cast<double*>(scratch);
     a.merged_out = merged_out;
+    a.slab_rows = slab_rows;
     {
       vaep_profile_entry pe = entry(groups > 0 ? VAEP_STEP_GROUPNORM : VAEP_STEP_RMSNORM, groups > 0 ? 3 : 1);
       const double elems = (double)L.n_img * L.H * L.W * L.C;
@@ -561,6 +565,9 @@ int walk(Exec& E, const void* latent, int B, int T, int W, const int* rows, int 
   const bool video = is_video(c);
   E.groups = video ? 0 : c.norm_groups;
   E.eps = c.eps;
+  int H = 0;
+  for (int i = 0; i < nb; ++i) H += rows[i];
+  E.base_rows = H;
   BandLayout L = make_layout(nb, rows, B * T, T, W, m.conv_in.ci_pad);
   int rc;
   int cur = 0;
@@ -1014,7 +1021,7 @@ int vaep_step_groupnorm(int dtype, const void* x, int batch, int frames, int c, 
   cv.base = (char*)ws;
   void* xin = cv.take(layout_elems(L) * 4);
   void* yo = cv.take(layout_elems(L) * eb);
-  float* scratch = (float*)cv.take(gn_partials_floats(L, groups, dtype) * sizeof(float));
+  float* scratch = (float*)cv.take(gn_partials_floats(L, groups, 1) * sizeof(float));
   bool sized;
   if ((rc = step_finish_sizing(cv, ws, ws_bytes, bytes_out, &sized)) || sized) return rc;
   if (!x || !y || !gamma || !beta) return fail(VAEP_ERR_INVALID_ARG, "x, y, gamma and beta must be device pointers");
@@ -1033,6 +1040,7 @@ int vaep_step_groupnorm(int dtype, const void* x, int batch, int frames, int c, 
   a.act = act;
   a.partials = reinterpret_cast<double*>(scratch);
   a.merged_out = merged;
+  a.slab_rows = 1;
   e = launch_groupnorm(a, dtype, st);
   if (e == hipSuccess && band_moments)
     e = hipMemcpyAsync(band_moments, a.band_moments, sizeof(float) * 3 * nb * L.n_img * groups,
@@ -1104,7 +1112,7 @@ int vaep_step_attention(int dtype, const void* x, int batch, int frames, int c, 
   void* qb = cv.take(qkv);
   void* kb = cv.take(qkv);
   void* vb = cv.take(qkv);
-  float* scratch = groups > 0 ? (float*)cv.take(gn_partials_floats(L, groups, dtype) * sizeof(float)) : nullptr;
+  float* scratch = groups > 0 ? (float*)cv.take(gn_partials_floats(L, groups, 1) * sizeof(float)) : nullptr;
   AttnW aw;
   aw.norm.g = const_cast<float*>(norm_gamma);
   aw.norm.b = const_cast<float*>(norm_beta);

@@ -10,7 +10,9 @@
 //
 // bf16 path: implicit GEMM on the gfx950 matrix cores, D[co][pixel] = W[co][k] *
 // X[k][pixel] with k = (tap, input channel), v_mfma_f32_32x32x16_bf16, fp32
-// accumulation.  One 256-thread workgroup computes 128 output channels x 128 pixels of
+// accumulation.  Operands read from the fp32 residual stream (shortcut, upsample and
+// time convs) are split into bf16 hi and lo parts and both are multiplied, so these
+// convs see their input to about 16 significand bits.  One 256-thread workgroup computes 128 output channels x 128 pixels of
 // one band; 4 waves each own 64 x 64 (2 x 2 MFMA blocks).  K advances 32 channels of one
 // tap per step through a double-buffered LDS tile (global -> registers -> LDS while the
 // previous tile feeds the MFMAs).
@@ -92,17 +94,26 @@ __device__ __forceinline__ void store_band4(const BandLayout& L, void* y, int b,
   if (r == L.rows[b] - 1 && b + 1 < L.nb) st4f(y, band_offset(L, b + 1, n, -1, c) + ch, v);
 }
 
-// 8 channels of the operand source as packed bf16 (fp32 sources are rounded to nearest even).
+// bf16 part of an fp32 value: hi = bf16(v); lo = bf16(v - hi).  hi + lo carries 16
+// significand bits, so a product pass over each part recovers the fp32 operand to
+// about 2^-17 relative.
+__device__ __forceinline__ unsigned short split_part(float v, bool lo) {
+  const unsigned short h = f2bf(v);
+  return lo ? f2bf(v - bf2f(h)) : h;
+}
+
+// 8 channels of the operand source as packed bf16.  bf16 sources load as they are; fp32
+// sources (the residual stream) give their hi part, or their lo part when `lo` is set.
 template <bool XF32>
-__device__ __forceinline__ uint4 load8(const void* base, long long off) {
+__device__ __forceinline__ uint4 load8(const void* base, long long off, bool lo) {
   if (XF32) {
     const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
     const float4 a = p[0], b = p[1];
     uint4 u;
-    u.x = (unsigned)f2bf(a.x) | ((unsigned)f2bf(a.y) << 16);
-    u.y = (unsigned)f2bf(a.z) | ((unsigned)f2bf(a.w) << 16);
-    u.z = (unsigned)f2bf(b.x) | ((unsigned)f2bf(b.y) << 16);
-    u.w = (unsigned)f2bf(b.z) | ((unsigned)f2bf(b.w) << 16);
+    u.x = (unsigned)split_part(a.x, lo) | ((unsigned)split_part(a.y, lo) << 16);
+    u.y = (unsigned)split_part(a.z, lo) | ((unsigned)split_part(a.w, lo) << 16);
+    u.z = (unsigned)split_part(b.x, lo) | ((unsigned)split_part(b.y, lo) << 16);
+    u.w = (unsigned)split_part(b.z, lo) | ((unsigned)split_part(b.w, lo) << 16);
     return u;
   }
   return *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned short*>(base) + off);
@@ -133,7 +144,8 @@ __global__ void __launch_bounds__(256) conv_mfma_bf16(const ConvArgs a) {
   const int cin = a.cin;
   const int csteps = cin / BK;
   constexpr int TAPS = KT * KS * KS;
-  const int nsteps = TAPS * csteps;
+  // fp32 sources run the K loop twice: the hi parts, then the lo parts (same weights)
+  const int nsteps = TAPS * csteps * (XF32 ? 2 : 1);
   const long long ktot = (long long)TAPS * cin;
   const unsigned short* wg = reinterpret_cast<const unsigned short*>(a.w);
 
@@ -176,6 +188,7 @@ __global__ void __launch_bounds__(256) conv_mfma_bf16(const ConvArgs a) {
   long long xo0 = 0, xo1 = 0;
   bool xk0 = false, xk1 = false;
   int tap = 0, c0 = 0;
+  bool lo = false;
 
 #define VAEP_CONV_LOAD()                                                                        \
   {                                                                                             \
@@ -189,12 +202,15 @@ __global__ void __launch_bounds__(256) conv_mfma_bf16(const ConvArgs a) {
     }                                                                                           \
     w0 = *reinterpret_cast<const uint4*>(wrow0 + (long long)tap * cin + c0);                    \
     w1 = *reinterpret_cast<const uint4*>(wrow1 + (long long)tap * cin + c0);                    \
-    x0 = xk0 ? load8<XF32>(a.x, xo0 + c0) : make_uint4(0, 0, 0, 0);                             \
-    x1 = xk1 ? load8<XF32>(a.x, xo1 + c0) : make_uint4(0, 0, 0, 0);                             \
+    x0 = xk0 ? load8<XF32>(a.x, xo0 + c0, lo) : make_uint4(0, 0, 0, 0);                         \
+    x1 = xk1 ? load8<XF32>(a.x, xo1 + c0, lo) : make_uint4(0, 0, 0, 0);                         \
     c0 += BK;                                                                                   \
     if (c0 == cin) {                                                                            \
       c0 = 0;                                                                                   \
-      ++tap;                                                                                    \
+      if (++tap == TAPS) {                                                                      \
+        tap = 0;                                                                                \
+        lo = true;                                                                              \
+      }                                                                                         \
     }                                                                                           \
   }
 #define VAEP_CONV_STASH(buf)                                                                    \

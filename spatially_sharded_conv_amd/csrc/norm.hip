@@ -6,8 +6,13 @@
 // merged with actual-element-count weights,
 //     mean = sum_i w_i mean_i,  var = sum_i w_i (var_i + (mean_i - mean)^2),
 // and every band normalises with the merged statistics, then the channel affine and
-// (in the decoder's norm -> SiLU pairs) SiLU.  The same weighted merge combines the
-// per-workgroup tiles of a band into the band's moments.
+// (in the decoder's norm -> SiLU pairs) SiLU.
+//
+// Local moments are formed per tile of a fixed tiling of the image (slabs of rows that
+// no band boundary can split, cut into pixel chunks), in fp64 and two-pass.  The merged
+// statistics are the count-weighted merge of all tiles in global row order, and each
+// band's moments are the same merge over the tiles it owns.  Any band table therefore
+// yields bit-identical statistics: a decoded image does not depend on its partition.
 //
 // Data movement: the stats pass reads the band's rows once (16-byte loads, each
 // workgroup a contiguous slab of one band and image), two-pass in registers per tile;
@@ -59,10 +64,8 @@ __device__ __forceinline__ int band_of_block(const int* start, int nb, int blk) 
 
 __device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
 
-// Pass 1: central moments of one tile (kThreads/S pixel lanes x kPixPerThread pixels) of
-// one (band, image): partials[blk][g] = (mean, M2) of group g over the tile, two-pass
-// from registers, accumulated in fp64 so that the merged statistics do not depend on
-// where the band boundaries cut the image.
+// Pass 1: central moments of one tile (a pixel chunk of one slab of one image):
+// partials[tile][g] = (mean, M2) of group g, two-pass from registers, in fp64.
 __global__ void __launch_bounds__(kThreads) gn_stats(const NormArgs a) {
   __shared__ double red[kThreads * V];
   __shared__ double gmean[1024];
@@ -70,16 +73,20 @@ __global__ void __launch_bounds__(kThreads) gn_stats(const NormArgs a) {
   const int C = L.C, S = C / V, PL = kThreads / S;
   const int G = a.groups, cpg = C / G;
   const int blk = blockIdx.x;
-  const int b = band_of_block(a.blk_start, L.nb, blk);
-  const int local = blk - a.blk_start[b];
-  const int n = local / a.blk_per_img[b];
-  const int tile = local - n * a.blk_per_img[b];
-  const long long npix = (long long)L.rows[b] * L.W;
-  const long long p0 = (long long)tile * a.pix_per_blk[b];
+  const int per_img = a.slabs * a.chunks;
+  const int n = blk / per_img;
+  const int slab = (blk - n * per_img) / a.chunks;
+  const int chunk = blk - n * per_img - slab * a.chunks;
+  const int g0 = slab * a.slab_rows;                    // first global row of the slab
+  int b = 0;
+  while (b + 1 < L.nb && g0 >= L.row0[b + 1]) ++b;
+  const long long npix = (long long)a.slab_rows * L.W;  // pixels of the slab
+  const long long p0 = (long long)chunk * a.chunk_pix;
   const int tid = threadIdx.x;
   const int slot = tid % S, pl = tid / S;
   const bool active = pl < PL;
-  const float* base = reinterpret_cast<const float*>(a.x) + row_offset(L, b, n, 0) + (long long)slot * V;
+  const float* base = reinterpret_cast<const float*>(a.x) + row_offset(L, b, n, g0 - L.row0[b]) +
+                      (long long)slot * V;
 
   float x[kPixPerThread][V];
   int cnt = 0;
@@ -95,7 +102,7 @@ __global__ void __launch_bounds__(kThreads) gn_stats(const NormArgs a) {
     }
   }
   long long tp = npix - p0;
-  if (tp > (long long)PL * kPixPerThread) tp = (long long)PL * kPixPerThread;
+  if (tp > (long long)a.chunk_pix) tp = a.chunk_pix;
   const double n_el = (double)(tp * cpg);
 
   if (active) {
@@ -142,93 +149,97 @@ __global__ void __launch_bounds__(kThreads) gn_stats(const NormArgs a) {
   }
 }
 
-// Pass 2: one workgroup per (image n, group g).  The tiles of each band merge into the
-// band's (count, mean, var) with count weights; then the bands merge with the pages'
-// formula.  fp64 throughout; the merged mean and variance are rounded to fp32 once.
-// Writes the per-band moments, the merged mean / rstd and the per-channel scale/shift.
+// Count-weighted merge (feature page, GroupNorm section) of the tiles [t0, t1) of
+// image n, group g: mean = sum w_t mean_t, var = sum w_t (var_t + (mean_t - mean)^2),
+// w_t = n_t / sum n_t.  Fixed thread striding and a fixed tree: the result depends only
+// on the tiles.  Every thread returns (count, mean, var).
+__device__ void merge_tiles(const NormArgs& a, int n, int g, int t0, int t1, double* sh,
+                            double* cnt, double* mean, double* var) {
+  const int tid = threadIdx.x;
+  const int G = a.groups, cpg = a.L.C / G;
+  const long long slab_pix = (long long)a.slab_rows * a.L.W;
+  const double* P = a.partials + ((long long)n * a.slabs * a.chunks) * G * 2;
+  auto tile_n = [&](int t) {
+    const int chunk = t % a.chunks;
+    long long tp = slab_pix - (long long)chunk * a.chunk_pix;
+    if (tp > a.chunk_pix) tp = a.chunk_pix;
+    return (double)(tp * cpg);
+  };
+  // the tiles cover whole slabs: the element count is exact
+  const double total = (double)((t1 - t0) / a.chunks) * (double)slab_pix * cpg;
+  double s = 0.0;
+  for (int t = t0 + tid; t < t1; t += kThreads) s += (tile_n(t) / total) * P[((long long)t * G + g) * 2];
+  sh[tid] = s;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) sh[tid] += sh[tid + w];
+    __syncthreads();
+  }
+  const double m = sh[0];
+  __syncthreads();
+  s = 0.0;
+  for (int t = t0 + tid; t < t1; t += kThreads) {
+    const double nt = tile_n(t);
+    const double* pr = P + ((long long)t * G + g) * 2;
+    const double d = pr[0] - m;
+    s += (nt / total) * (pr[1] / nt + d * d);
+  }
+  sh[tid] = s;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) sh[tid] += sh[tid + w];
+    __syncthreads();
+  }
+  *cnt = total;
+  *mean = m;
+  *var = sh[0];
+  __syncthreads();
+}
+
+// Pass 2: one workgroup per (image n, group g).  Reports each band's moments (its own
+// tiles merged) and merges all tiles of the image into the statistics the apply uses;
+// the merged mean and variance are rounded to fp32 once.  Writes the per-channel
+// scale/shift of the apply.
 __global__ void __launch_bounds__(kThreads) gn_merge(const NormArgs a, float* coef) {
   __shared__ double sh[kThreads];
-  __shared__ double bmean[kMaxBands], bvar[kMaxBands], bcnt[kMaxBands];
   __shared__ float fin[2];
   const BandLayout& L = a.L;
   const int G = a.groups, C = L.C, cpg = C / G;
   const int n = blockIdx.x / G, g = blockIdx.x - (blockIdx.x / G) * G;
   const int tid = threadIdx.x;
+  const int s_idx = n * G + g, ns = L.n_img * G;
   for (int b = 0; b < L.nb; ++b) {
-    const int nt = a.blk_per_img[b];
-    const long long npix = (long long)L.rows[b] * L.W;
-    const double total = (double)(npix * cpg);
-    const int first = a.blk_start[b] + n * nt;
-    double s = 0.0;
-    for (int t = tid; t < nt; t += kThreads) {
-      long long tp = npix - (long long)t * a.pix_per_blk[b];
-      if (tp > a.pix_per_blk[b]) tp = a.pix_per_blk[b];
-      s += ((double)(tp * cpg) / total) * a.partials[((long long)(first + t) * G + g) * 2];
-    }
-    sh[tid] = s;
-    __syncthreads();
-    for (int w = kThreads / 2; w > 0; w >>= 1) {
-      if (tid < w) sh[tid] += sh[tid + w];
-      __syncthreads();
-    }
-    const double mb = sh[0];
-    __syncthreads();
-    s = 0.0;
-    for (int t = tid; t < nt; t += kThreads) {
-      long long tp = npix - (long long)t * a.pix_per_blk[b];
-      if (tp > a.pix_per_blk[b]) tp = a.pix_per_blk[b];
-      const double nt_el = (double)(tp * cpg);
-      const double* pr = a.partials + ((long long)(first + t) * G + g) * 2;
-      const double d = pr[0] - mb;
-      s += (nt_el / total) * (pr[1] / nt_el + d * d);
-    }
-    sh[tid] = s;
-    __syncthreads();
-    for (int w = kThreads / 2; w > 0; w >>= 1) {
-      if (tid < w) sh[tid] += sh[tid + w];
-      __syncthreads();
-    }
+    double cb, mb, vb;
+    const int t0 = (L.row0[b] / a.slab_rows) * a.chunks;
+    const int t1 = ((L.row0[b] + L.rows[b]) / a.slab_rows) * a.chunks;
+    merge_tiles(a, n, g, t0, t1, sh, &cb, &mb, &vb);
     if (tid == 0) {
-      bmean[b] = mb;
-      bvar[b] = sh[0];
-      bcnt[b] = total;
+      a.band_moments[(0 * L.nb + b) * (long long)ns + s_idx] = (float)cb;
+      a.band_moments[(1 * L.nb + b) * (long long)ns + s_idx] = (float)mb;
+      a.band_moments[(2 * L.nb + b) * (long long)ns + s_idx] = (float)vb;
     }
-    __syncthreads();
   }
+  double cnt, mean, var;
+  merge_tiles(a, n, g, 0, a.slabs * a.chunks, sh, &cnt, &mean, &var);
   if (tid == 0) {
-    double tot = 0.0;
-    for (int b = 0; b < L.nb; ++b) tot += bcnt[b];
-    double mean = 0.0;
-    for (int b = 0; b < L.nb; ++b) mean += (bcnt[b] / tot) * bmean[b];
-    double var = 0.0;
-    for (int b = 0; b < L.nb; ++b) {
-      const double d = bmean[b] - mean;
-      var += (bcnt[b] / tot) * (bvar[b] + d * d);
-    }
-    const int s = n * G + g, ns = L.n_img * G;
-    for (int b = 0; b < L.nb; ++b) {
-      a.band_moments[(0 * L.nb + b) * (long long)ns + s] = (float)bcnt[b];
-      a.band_moments[(1 * L.nb + b) * (long long)ns + s] = (float)bmean[b];
-      a.band_moments[(2 * L.nb + b) * (long long)ns + s] = (float)bvar[b];
-    }
     const float mean_f = (float)mean, var_f = (float)var;
     const float rstd = rsqrtf(var_f + a.eps);
-    a.stats[s] = mean_f;
-    a.stats[ns + s] = rstd;
+    a.stats[s_idx] = mean_f;
+    a.stats[ns + s_idx] = rstd;
     if (a.merged_out) {
-      a.merged_out[s] = mean_f;
-      a.merged_out[ns + s] = var_f;
+      a.merged_out[s_idx] = mean_f;
+      a.merged_out[ns + s_idx] = var_f;
     }
     fin[0] = mean_f;
     fin[1] = rstd;
   }
   __syncthreads();
-  const float mean = fin[0], rstd = fin[1];
+  const float mf = fin[0], rstd = fin[1];
   for (int j = tid; j < cpg; j += kThreads) {
     const int ch = g * cpg + j;
     const float sc = rstd * a.gamma[ch];
     coef[((long long)n * C + ch) * 2] = sc;
-    coef[((long long)n * C + ch) * 2 + 1] = a.beta[ch] - mean * sc;
+    coef[((long long)n * C + ch) * 2 + 1] = a.beta[ch] - mf * sc;
   }
 }
 
@@ -357,29 +368,28 @@ __global__ void moment_merge(int n_shards, int n_stats, const float* mean, const
 }  // namespace
 
 
-// Stats tiling of a layout: blocks per band and image, pixels per block.
-static void plan_stats(NormArgs& a, int dtype) {
-  const int S = a.L.C / V;
-  const int PL = kThreads / S;
-  const int pix = PL * kPixPerThread;
-  int t = 0;
-  for (int b = 0; b < a.L.nb; ++b) {
-    a.blk_start[b] = t;
-    const long long np = (long long)a.L.rows[b] * a.L.W;
-    a.blk_per_img[b] = (int)((np + pix - 1) / pix);
-    a.pix_per_blk[b] = pix;
-    t += a.blk_per_img[b] * a.L.n_img;
-  }
-  a.blk_start[a.L.nb] = t;
+// Stats tiling of a layout: slabs of a.slab_rows rows (set by the caller), chunks of
+// kThreads/S * kPixPerThread pixels.
+static int chunk_pixels(int C) { return (kThreads / (C / V)) * kPixPerThread; }
+
+static bool plan_stats(NormArgs& a) {
+  const BandLayout& L = a.L;
+  if (a.slab_rows < 1 || L.H % a.slab_rows != 0) return false;
+  for (int b = 0; b < L.nb; ++b)
+    if (L.row0[b] % a.slab_rows != 0 || L.rows[b] % a.slab_rows != 0) return false;
+  a.slabs = L.H / a.slab_rows;
+  a.chunk_pix = chunk_pixels(L.C);
+  const long long slab_pix = (long long)a.slab_rows * L.W;
+  a.chunks = (int)((slab_pix + a.chunk_pix - 1) / a.chunk_pix);
+  return true;
 }
 
-size_t gn_partials_floats(const BandLayout& L, int groups, int dtype) {
-  // Bound over every band table with L.nb bands: sum_i ceil(rows_i W / pix) <= ceil(H W / pix) + nb.
-  const int S = L.C / V;
-  const int pix = (kThreads / S) * kPixPerThread;
-  const long long blocks = (long long)L.n_img * (((long long)L.H * L.W + pix - 1) / pix + L.nb);
+size_t gn_partials_floats(const BandLayout& L, int groups, int slab_rows) {
   // (in floats) fp64 partials, per-channel coefficients, per-band moments, merged stats
-  return (size_t)(blocks * groups * 4 + 2LL * L.n_img * L.C + 3LL * L.nb * L.n_img * groups +
+  const int pix = chunk_pixels(L.C);
+  const long long slab_pix = (long long)slab_rows * L.W;
+  const long long tiles = (long long)L.n_img * (L.H / slab_rows) * ((slab_pix + pix - 1) / pix);
+  return (size_t)(tiles * groups * 4 + 2LL * L.n_img * L.C + 3LL * L.nb * L.n_img * groups +
                   2LL * L.n_img * groups);
 }
 
@@ -387,8 +397,10 @@ hipError_t launch_groupnorm(NormArgs& a, int dtype, hipStream_t s) {
   const BandLayout& L = a.L;
   if (L.C % V != 0 || L.C / V > kThreads || L.C % a.groups != 0 || a.groups > 1024)
     return hipErrorInvalidValue;
-  plan_stats(a, dtype);
-  const int blocks = a.blk_start[L.nb];
+  if (!plan_stats(a)) return hipErrorInvalidValue;
+  const long long blocks_ll = (long long)L.n_img * a.slabs * a.chunks;
+  if (blocks_ll > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int blocks = (int)blocks_ll;
   // Scratch carve-up inside a.partials (sized by gn_partials_floats).
   float* coef = reinterpret_cast<float*>(a.partials + (size_t)blocks * a.groups * 2);
   a.band_moments = coef + 2LL * L.n_img * L.C;

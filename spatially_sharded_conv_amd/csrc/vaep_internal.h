@@ -98,14 +98,19 @@ struct NormArgs {
   float* band_moments;   // [3][nb][n_img*groups] count, mean, var (device scratch)
   float* stats;          // [2][n_img*groups] merged mean, rstd
   float* merged_out;     // optional [2][n_img*groups] merged mean, var
-  int blk_start[kMaxBands + 1];   // stats blocks of band i start here
-  int blk_per_img[kMaxBands];     // stats blocks per image in band i
-  int pix_per_blk[kMaxBands];     // pixels covered by one stats block in band i
+  // GroupNorm statistics tiles.  The image is cut into slabs of `slab_rows` rows (the
+  // finest row unit any band table of this layer can own: 2^level rows of a decode, one
+  // row for a single step); a slab is split into chunks of `chunk_pix` pixels.  The tile
+  // set depends only on the image, never on where the bands cut it.
+  int slab_rows;
+  int slabs;             // slabs per image = H / slab_rows
+  int chunks;            // chunks per slab
+  int chunk_pix;         // pixels per chunk (last chunk of a slab may be shorter)
   long long item_start[kMaxBands + 1];  // apply pass: first vector (GN) / pixel (RMS) of band i
 };
 
-// Scratch of a GroupNorm launch in floats (bounded over every band table of L.nb bands).
-size_t gn_partials_floats(const BandLayout& L, int groups, int dtype);
+// Scratch of a GroupNorm launch in floats; slab_rows as in NormArgs.
+size_t gn_partials_floats(const BandLayout& L, int groups, int slab_rows);
 hipError_t launch_groupnorm(NormArgs& a, int dtype, hipStream_t s);
 hipError_t launch_rmsnorm(NormArgs& a, int dtype, hipStream_t s);
 hipError_t launch_moment_merge(int n_shards, int n_stats, const float* mean, const float* var,

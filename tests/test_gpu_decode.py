@@ -176,3 +176,20 @@ def test_repeat_and_alternating_calls(gpu_lib):
     assert torch.equal(a, d)
     assert errors(b, a)[1] <= BAND_VS_FULL_REL and errors(c, a)[1] <= BAND_VS_FULL_REL
     dec.close()
+
+
+@pytest.mark.parametrize("shape", [(10, 12), (12, 20), (9, 16)])
+def test_band_decode_is_bit_identical_to_full(gpu_lib, shape):
+    # convs and attention compute each element identically on any band table, and the
+    # GroupNorm statistics come from a tiling no band boundary can split: every band
+    # table decodes to exactly the full-image result
+    h, w = shape
+    cfg = preset(3).with_size(latent_h=h, latent_w=w, band_starts=(0, h))
+    dec, _ = make_decoder(cfg, affine="random")
+    z = make_latent(cfg)
+    ws = dec.workspace(1, 1, h, w, h)
+    full, _, _ = gpu_decode(dec, cfg, z, (0, h), ws)
+    for starts in [(0, 3, h), (0, 1, h), (0, h - 1, h), (0, 2, 5, 7, h), tuple(range(h + 1))]:
+        y, rc, _ = gpu_decode(dec, cfg, z, starts, ws)
+        assert rc == 0 and torch.equal(y, full), starts
+    dec.close()

@@ -32,8 +32,10 @@ def _x5(x):
     return x if x.dim() == 5 else x.unsqueeze(2)
 
 
-def _conv_ref(x, w, b, causal, res, dtype, upsample=False):
-    x5 = _x5(_op(x, dtype))
+def _conv_ref(x, w, b, causal, res, dtype, upsample=False, x_exact=False):
+    # bf16 operands load as they are; fp32 sources are split into hi + lo parts on the GPU,
+    # which carries them to ~2^-17 relative: the reference uses them unrounded
+    x5 = _x5(x if x_exact else _op(x, dtype))
     if upsample:
         x5 = ops.upsample_nearest2x(x5)
     w5 = w if w.dim() == 5 else w.unsqueeze(2)
@@ -73,14 +75,14 @@ def test_conv1x1_step(gpu_lib, dtype):
 
 
 def test_conv_from_fp32_source(gpu_lib):
-    # shortcut / upsample convs read the fp32 residual stream and round it to bf16 on load
+    # shortcut / upsample convs read the fp32 residual stream (hi + lo bf16 passes)
     x = seeded((1, 64, 9, 21), 24, dtype="f32")
     w = seeded((128, 64, 3, 3), 25, 1 / math.sqrt(64 * 9), dtype="bf16")
     b = seeded((128,), 26, 0.1, dtype="bf16")
-    ref = _conv_ref(x, w, b, False, None, "bf16")
+    ref = _conv_ref(x, w, b, False, None, "bf16", x_exact=True)
     got = vaep.step_conv(x.cuda(), to_dev(w, "bf16"), to_dev(b, "bf16"), (0, 2, 9))
     assert_close(got, ref, *ACC_TOL, what="conv from fp32 source")
-    ref_up = _conv_ref(x, w, b, False, None, "bf16", upsample=True)
+    ref_up = _conv_ref(x, w, b, False, None, "bf16", upsample=True, x_exact=True)
     got_up = vaep.step_conv(x.cuda(), to_dev(w, "bf16"), to_dev(b, "bf16"), (0, 2, 9), upsample=True)
     assert_close(got_up, ref_up, *ACC_TOL, what="upsample conv from fp32 source")
 
@@ -191,7 +193,7 @@ def test_temporal_upsample_step(gpu_lib, dtype):
     x = seeded((1, C, 3, 5, 6), 91, dtype="f32")
     w = seeded((2 * C, C, 3, 1, 1), 92, 1 / math.sqrt(3 * C), dtype=dtype)
     b = seeded((2 * C,), 93, 0.1, dtype=dtype)
-    z = ops.conv_full(_op(x, dtype).float(), w, b, True, Precision(dtype).acc)
+    z = ops.conv_full(x, w, b, True, Precision(dtype).acc)     # fp32 source: hi + lo passes
     ref = ops.temporal_upsample_interleave(x, z)
     got = vaep.step_temporal_upsample(x.cuda(), to_dev(w, dtype), to_dev(b, dtype), (0, 2, 5))
     assert got.shape == (1, C, 5, 5, 6)
@@ -220,3 +222,47 @@ def test_groupnorm_merge_entry_point(gpu_lib):
     assert_close(gm, m_ref, 1e-5, 1e-6, "merged mean")
     assert_close(gv, v_ref, 1e-5, 1e-6, "merged var")
     assert gm[7].item() == 0.0 and gv[7].item() == 0.0
+
+
+# ----------------------------------------------------------------------------- band invariance
+# Every step computes each output element with the same arithmetic whatever the band
+# table: convs and attention read the same operands in the same order, and GroupNorm
+# merges fp64 band moments rounded once to fp32.  Partitions must give bit-equal results.
+PARTITIONS = [(0, 10), (0, 3, 10), (0, 1, 5, 9, 10), (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10)]
+
+
+@pytest.mark.parametrize("kind", ["conv3", "conv3_f32src", "upconv_f32src", "conv1_f32src", "conv333"])
+def test_conv_band_invariance(gpu_lib, kind):
+    video = kind == "conv333"
+    shape = (1, 64, 3, 10, 12) if video else (1, 64, 10, 12)
+    src = "f32" if "f32src" in kind else "bf16"
+    x = to_dev(seeded(shape, 201, dtype=src), src)
+    k = (64, 64, 3, 3, 3) if video else ((64, 64, 1, 1) if kind == "conv1_f32src" else (64, 64, 3, 3))
+    w = to_dev(seeded(k, 202, 0.05), "bf16")
+    b = to_dev(seeded((64,), 203, 0.1), "bf16")
+    outs = [vaep.step_conv(x, w, b, p, causal=video, upsample=kind.startswith("up")) for p in PARTITIONS]
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_groupnorm_band_invariance(gpu_lib):
+    x = seeded((2, 512, 10, 12), 211, 3.0, offset=0.5, dtype="f32").cuda()
+    g = seeded((512,), 212, 0.25, offset=1.0, dtype="f32").cuda()
+    be = seeded((512,), 213, 0.1, dtype="f32").cuda()
+    outs = [vaep.step_groupnorm(x, 32, 1e-6, g, be, p)[0] for p in PARTITIONS]
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+@pytest.mark.parametrize("G", [32, 0])
+def test_attention_band_invariance(gpu_lib, G):
+    C = 512 if G else 384
+    x = seeded((1, C, 10, 12), 221, dtype="f32").cuda()
+    g = seeded((C,), 222, 0.25, offset=1.0, dtype="f32").cuda()
+    be = seeded((C,), 223, 0.1, dtype="f32").cuda()
+    ws = [to_dev(seeded((C, C), 224 + i, 1 / math.sqrt(C)), "bf16") for i in range(4)]
+    bs = [to_dev(seeded((C,), 230 + i, 0.1), "bf16") for i in range(4)]
+    outs = [vaep.step_attention(x, G, 1e-6, g, be, ws[0], bs[0], ws[1], bs[1], ws[2], bs[2], ws[3], bs[3], p)
+            for p in PARTITIONS]
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
