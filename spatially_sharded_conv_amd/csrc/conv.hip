@@ -22,6 +22,7 @@ namespace vaep {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;   // 16 bytes, native vector
 
 namespace {
 
@@ -102,39 +103,73 @@ __device__ __forceinline__ unsigned short split_part(float v, bool lo) {
   return lo ? f2bf(v - bf2f(h)) : h;
 }
 
-// 8 channels of the operand source as packed bf16.  bf16 sources load as they are; fp32
-// sources (the residual stream) give their hi part, or their lo part when `lo` is set.
+// Buffer resource over [base, base + bytes): loads outside the range return zeros, which
+// is how padding taps read (their offset is set past the end).  dword3 = raw buffer.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+constexpr unsigned kPadOffset = 0x80000000u;   // past every band buffer (< 2 GiB, host-checked)
+
+// 8 channels of the operand source as packed bf16 at byte offset voff + soff.  bf16
+// sources load as they are; fp32 sources (the residual stream) give their hi part, or
+// their lo part when `lo` is set.
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 template <bool XF32>
-__device__ __forceinline__ uint4 load8(const void* base, long long off, bool lo) {
+__device__ __forceinline__ u32x4_t load8(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff, bool lo) {
   if (XF32) {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
-    const float4 a = p[0], b = p[1];
-    uint4 u;
+    const f32x4_t a = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0));
+    const f32x4_t b = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff + 16, soff, 0));
+    u32x4_t u;
     u.x = (unsigned)split_part(a.x, lo) | ((unsigned)split_part(a.y, lo) << 16);
     u.y = (unsigned)split_part(a.z, lo) | ((unsigned)split_part(a.w, lo) << 16);
     u.z = (unsigned)split_part(b.x, lo) | ((unsigned)split_part(b.y, lo) << 16);
     u.w = (unsigned)split_part(b.z, lo) | ((unsigned)split_part(b.w, lo) << 16);
     return u;
   }
-  return *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned short*>(base) + off);
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0));
 }
 
-template <int KT, int KS, bool UPS, int MODE, bool XF32>
-__global__ void __launch_bounds__(256) conv_mfma_bf16(const ConvArgs a) {
+// Workgroup id -> tile id so that the 8 XCDs (which receive workgroups round-robin)
+// each work on a contiguous run of tiles: neighbouring pixel tiles share halo rows in
+// that XCD's L2.  A bijection on [0, total).
+__device__ __forceinline__ int xcd_remap(int lin, int total) {
+  const int q = total >> 3, r = total & 7;
+  const int x = lin & 7, i = lin >> 3;
+  return x * q + (x < r ? x : r) + i;
+}
+
+// Expand a statement for j = 0 .. NP-1 (NP = 2 or 4) with j a compile-time constant, so
+// that every array index below is static and the arrays live in registers.
+#define VAEP_FOR_J(...)                                                       \
+  {                                                                           \
+    { constexpr int j = 0; __VA_ARGS__ }                                      \
+    { constexpr int j = 1; __VA_ARGS__ }                                      \
+    if constexpr (NP > 2) {                                                   \
+      { constexpr int j = 2; __VA_ARGS__ }                                    \
+      { constexpr int j = 3; __VA_ARGS__ }                                    \
+    }                                                                         \
+  }
+
+template <int KT, int KS, bool UPS, int MODE, bool XF32, int BK>
+__global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
   constexpr int BM = kConvTileN;   // output channels per workgroup
   constexpr int BN = kConvTileM;   // pixels per workgroup
-  constexpr int BK = 32;
-  constexpr int LDK = BK + 8;      // padded LDS row (80 bytes)
+  // BK: K per pipeline step (64, or 32 when Cin is not a multiple of 64), one tap
+  constexpr int LDK = BK + 8;      // LDS row stride (144 bytes for BK 64): conflict-free reads
+  constexpr int CH = BK / 8;       // 16-byte chunks per tile row
+  constexpr int RP = 256 / CH;     // tile rows covered by one pass of the 256 threads
+  constexpr int NP = BN / RP;      // passes per tile
   __shared__ __attribute__((aligned(16))) unsigned short sW[2][BM * LDK];
   __shared__ __attribute__((aligned(16))) unsigned short sX[2][BN * LDK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int mt = blockIdx.x;
+  const int lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y);
+  const int mt = lin % gridDim.x;
   const int band = band_of_tile(a, mt);
   const int tile = mt - a.tile_start[band];
-  const int co0 = blockIdx.y * BM;
+  const int co0 = (lin / gridDim.x) * BM;
 
   const int rows_in = a.in.rows[band];
   const int rows_c = UPS ? 2 * rows_in : rows_in;
@@ -142,111 +177,148 @@ __global__ void __launch_bounds__(256) conv_mfma_bf16(const ConvArgs a) {
   const int plane = rows_c * wc;
   const long long m_band = (long long)a.in.n_img * plane;
   const int cin = a.cin;
-  const int csteps = cin / BK;
   constexpr int TAPS = KT * KS * KS;
   // fp32 sources run the K loop twice: the hi parts, then the lo parts (same weights)
-  const int nsteps = TAPS * csteps * (XF32 ? 2 : 1);
+  const int nsteps = TAPS * (cin / BK) * (XF32 ? 2 : 1);
   const long long ktot = (long long)TAPS * cin;
-  const unsigned short* wg = reinterpret_cast<const unsigned short*>(a.w);
 
-  // Operand-load roles: thread -> (row slots tid/4 and tid/4+64, 8-channel chunk tid%4).
-  const int q8 = (tid & 3) * 8;
-  int pn0, pr0, pc0, pn1, pr1, pc1;
-  bool pv0, pv1;
+  // Load roles: thread -> rows tid/CH + RP*j (j < NP) of both tiles, 8-channel chunk tid%CH.
+  const int rs = tid / CH;
+  const int q8 = (tid % CH) * 8;
+  int pn[NP], pr[NP], pc[NP];
+  bool pv[NP];
+  VAEP_FOR_J({
+    const long long p = (long long)tile * BN + rs + RP * j;
+    pv[j] = p < m_band;
+    const long long q = pv[j] ? p : 0;
+    pn[j] = (int)(q / plane);
+    const int rem = (int)(q - (long long)pn[j] * plane);
+    pr[j] = rem / wc;
+    pc[j] = rem - pr[j] * wc;
+  });
+  constexpr int XB = XF32 ? 4 : 2;   // bytes per input element
+  // weights: [cout_pad][taps][cin] bf16; thread rows co0 + rs + RP*j, chunk q8
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(a.w, (unsigned)((long long)a.cout_pad * ktot * 2));
+  unsigned wvo[NP];
+  VAEP_FOR_J({ wvo[j] = (unsigned)(((long long)(co0 + rs + RP * j) * ktot + q8) * 2); });
+  // input: the rows of this band's buffer the tile can read.  Row slot of (image n, row
+  // r in [-1, rows]) is n*(rows+2) + r + 1; the tile reads from the slot of its first
+  // pixel's top neighbour (KT-1 frames back for causal convs) to its last pixel's bottom
+  // neighbour.  The span stays far below 2 GiB, so the padding offset reads out of range.
+  long long first_slot, last_slot;
   {
-    const long long p0 = (long long)tile * BN + (tid >> 2);
-    const long long p1 = p0 + 64;
-    pv0 = p0 < m_band;
-    pv1 = p1 < m_band;
-    const long long q0 = pv0 ? p0 : 0, q1 = pv1 ? p1 : 0;
-    pn0 = (int)(q0 / plane);
-    int rem = (int)(q0 - (long long)pn0 * plane);
-    pr0 = rem / wc;
-    pc0 = rem - pr0 * wc;
-    pn1 = (int)(q1 / plane);
-    rem = (int)(q1 - (long long)pn1 * plane);
-    pr1 = rem / wc;
-    pc1 = rem - pr1 * wc;
+    const long long p0 = (long long)tile * BN;
+    long long p1 = p0 + BN - 1;
+    if (p1 >= m_band) p1 = m_band - 1;
+    const int n0 = (int)(p0 / plane), r0 = (int)((p0 - (long long)n0 * plane) / wc);
+    const int n1 = (int)(p1 / plane), r1 = (int)((p1 - (long long)n1 * plane) / wc);
+    const int top = UPS ? ((r0 - 1) >> 1) : r0 - 1;     // lowest source row (-1 = halo)
+    const int bot = UPS ? ((r1 + 1) >> 1) : r1 + 1;     // highest source row
+    first_slot = (long long)(n0 - (KT - 1)) * (rows_in + 2) + top + 1;
+    if (first_slot < 0) first_slot = 0;
+    last_slot = (long long)n1 * (rows_in + 2) + bot + 1;
   }
-  const unsigned short* wrow0 = wg + (long long)(co0 + (tid >> 2)) * ktot + q8;
-  const unsigned short* wrow1 = wrow0 + 64 * ktot;
-
-  f32x16_t acc[2][2];
+  const long long row_elems = (long long)a.in.W * a.in.C;
+  const long long x_base = a.in.off[band] + first_slot * row_elems;   // element offset
+  const __amdgpu_buffer_rsrc_t xrs =
+      make_rsrc(reinterpret_cast<const char*>(a.x) + x_base * XB,
+                (unsigned)((last_slot - first_slot + 1) * row_elems * XB));
+  f32x16_t acc00, acc01, acc10, acc11;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  for (int v = 0; v < 16; ++v) acc00[v] = acc01[v] = acc10[v] = acc11[v] = 0.f;
 
   const int wco = (wave >> 1) * 64;
   const int wpx = (wave & 1) * 64;
   const int frag = (lane & 31) * LDK + (lane >> 5) * 8;
-  const int srow = (tid >> 2) * LDK + q8;
+  const int srow = rs * LDK + q8;
 
-  uint4 w0, w1, x0, x1;
-  long long xo0 = 0, xo1 = 0;
-  bool xk0 = false, xk1 = false;
-  int tap = 0, c0 = 0;
+  u32x4_t wa[NP], xa[NP], wb[NP], xb[NP];
+  unsigned xo[NP];   // byte offset of this thread's chunk at the current tap, or kPadOffset
+  VAEP_FOR_J({ xo[j] = kPadOffset; });
+  int tap = 0, c0 = 0, loaded = 0;
   bool lo = false;
 
-#define VAEP_CONV_LOAD()                                                                        \
+// Loads: per step, weights at wvo[j] + (tap*cin + c0)*2 and inputs at xo[j] + c0*XB, both
+// with the step part as a scalar offset.  Padding taps read past the end of the band
+// buffer and get zeros; loads past the last step repeat the last step.
+#define VAEP_CONV_LOAD(W, X)                                                                    \
   {                                                                                             \
     if (c0 == 0) {                                                                              \
       const int dt = tap / (KS * KS), dy = (tap / KS) % KS, dx = tap % KS;                      \
-      bool ok;                                                                                  \
-      xo0 = tap_source(a.in, band, pn0, pr0, pc0, dt, dy, dx, KT, KS, UPS, &ok) + q8;           \
-      xk0 = ok && pv0;                                                                          \
-      xo1 = tap_source(a.in, band, pn1, pr1, pc1, dt, dy, dx, KT, KS, UPS, &ok) + q8;           \
-      xk1 = ok && pv1;                                                                          \
+      VAEP_FOR_J({                                                                              \
+        bool ok;                                                                                \
+        const long long o = tap_source(a.in, band, pn[j], pr[j], pc[j], dt, dy, dx, KT, KS, UPS, &ok); \
+        xo[j] = (ok && pv[j]) ? (unsigned)((o - x_base + q8) * XB) : kPadOffset;                \
+      });                                                                                       \
     }                                                                                           \
-    w0 = *reinterpret_cast<const uint4*>(wrow0 + (long long)tap * cin + c0);                    \
-    w1 = *reinterpret_cast<const uint4*>(wrow1 + (long long)tap * cin + c0);                    \
-    x0 = xk0 ? load8<XF32>(a.x, xo0 + c0, lo) : make_uint4(0, 0, 0, 0);                         \
-    x1 = xk1 ? load8<XF32>(a.x, xo1 + c0, lo) : make_uint4(0, 0, 0, 0);                         \
-    c0 += BK;                                                                                   \
-    if (c0 == cin) {                                                                            \
-      c0 = 0;                                                                                   \
-      if (++tap == TAPS) {                                                                      \
-        tap = 0;                                                                                \
-        lo = true;                                                                              \
+    const int ws = (tap * cin + c0) * 2;                                                        \
+    const int xs = c0 * XB;                                                                     \
+    VAEP_FOR_J({                                                                                \
+      W[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wvo[j], ws, 0)); \
+      X[j] = load8<XF32>(xrs, xo[j], xs, lo);                                                   \
+    });                                                                                         \
+    if (++loaded < nsteps) {                                                                    \
+      c0 += BK;                                                                                 \
+      if (c0 == cin) {                                                                          \
+        c0 = 0;                                                                                 \
+        if (++tap == TAPS) {                                                                    \
+          tap = 0;                                                                              \
+          lo = true;                                                                            \
+        }                                                                                       \
       }                                                                                         \
     }                                                                                           \
   }
-#define VAEP_CONV_STASH(buf)                                                                    \
+#define VAEP_CONV_STASH(W, X, buf)                                                              \
   {                                                                                             \
-    *reinterpret_cast<uint4*>(&sW[buf][srow]) = w0;                                             \
-    *reinterpret_cast<uint4*>(&sW[buf][srow + 64 * LDK]) = w1;                                  \
-    *reinterpret_cast<uint4*>(&sX[buf][srow]) = x0;                                             \
-    *reinterpret_cast<uint4*>(&sX[buf][srow + 64 * LDK]) = x1;                                  \
+    VAEP_FOR_J({                                                                                \
+      *reinterpret_cast<u32x4_t*>(&sW[buf][srow + RP * j * LDK]) = W[j];                        \
+      *reinterpret_cast<u32x4_t*>(&sX[buf][srow + RP * j * LDK]) = X[j];                        \
+    });                                                                                         \
+  }
+#define VAEP_MFMA_K(buf, kk)                                                                    \
+  {                                                                                             \
+    const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(&sW[buf][wco * LDK + frag + kk * 16]); \
+    const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(&sW[buf][(wco + 32) * LDK + frag + kk * 16]); \
+    const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(&sX[buf][wpx * LDK + frag + kk * 16]); \
+    const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(&sX[buf][(wpx + 32) * LDK + frag + kk * 16]); \
+    acc00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc00, 0, 0, 0);                    \
+    acc01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc01, 0, 0, 0);                    \
+    acc10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc10, 0, 0, 0);                    \
+    acc11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc11, 0, 0, 0);                    \
+  }
+#define VAEP_CONV_COMPUTE(buf)                                                                  \
+  {                                                                                             \
+    VAEP_MFMA_K(buf, 0);                                                                        \
+    VAEP_MFMA_K(buf, 1);                                                                        \
+    if constexpr (BK == 64) {                                                                   \
+      VAEP_MFMA_K(buf, 2);                                                                      \
+      VAEP_MFMA_K(buf, 3);                                                                      \
+    }                                                                                           \
   }
 
-  VAEP_CONV_LOAD();
-  VAEP_CONV_STASH(0);
+  // Two register stages (a, b) and two LDS buffers: the loads of step s+2 are issued
+  // before the MFMAs of step s and land in LDS at the end of step s+1.
+  // (stashes past the last step write a buffer no step reads)
+  VAEP_CONV_LOAD(wa, xa);
+  VAEP_CONV_LOAD(wb, xb);
+  VAEP_CONV_STASH(wa, xa, 0);
   __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nsteps) VAEP_CONV_LOAD();
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8_t af[2], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&sW[buf][(wco + 32 * i) * LDK + frag + kk * 16]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&sX[buf][(wpx + 32 * j) * LDK + frag + kk * 16]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (s + 1 < nsteps) VAEP_CONV_STASH(buf ^ 1);
+  for (int s = 0; s < nsteps; s += 2) {
+    VAEP_CONV_LOAD(wa, xa);
+    VAEP_CONV_COMPUTE(0);
+    VAEP_CONV_STASH(wb, xb, 1);
+    __syncthreads();
+    if (s + 1 == nsteps) break;
+    VAEP_CONV_LOAD(wb, xb);
+    VAEP_CONV_COMPUTE(1);
+    VAEP_CONV_STASH(wa, xa, 0);
     __syncthreads();
   }
 #undef VAEP_CONV_LOAD
 #undef VAEP_CONV_STASH
+#undef VAEP_CONV_COMPUTE
+#undef VAEP_MFMA_K
+  const f32x16_t acc[2][2] = {{acc00, acc01}, {acc10, acc11}};
 
   // Epilogue.  acc[i][j][v]: channel co0+wco+32i+8(v/4)+4(lane/32)+(v%4), pixel
   // tile*BN+wpx+32j+(lane%32).
@@ -386,11 +458,17 @@ __global__ void __launch_bounds__(128) conv_f32(const ConvArgs a) {
 
 template <int KT, int KS, bool UPS, int MODE>
 hipError_t go(const ConvArgs& a, hipStream_t s) {
-  dim3 grid(a.tiles_total, a.cout_pad / kConvTileN);
-  if (a.x_f32)
-    hipLaunchKernelGGL((conv_mfma_bf16<KT, KS, UPS, MODE, true>), grid, dim3(256), 0, s, a);
+  const int ny = a.cout_pad / kConvTileN;
+  dim3 grid(a.tiles_total, ny);
+  const bool k64 = a.cin % 64 == 0;
+  if (a.x_f32 && k64)
+    hipLaunchKernelGGL((conv_mfma_bf16<KT, KS, UPS, MODE, true, 64>), grid, dim3(256), 0, s, a);
+  else if (a.x_f32)
+    hipLaunchKernelGGL((conv_mfma_bf16<KT, KS, UPS, MODE, true, 32>), grid, dim3(256), 0, s, a);
+  else if (k64)
+    hipLaunchKernelGGL((conv_mfma_bf16<KT, KS, UPS, MODE, false, 64>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((conv_mfma_bf16<KT, KS, UPS, MODE, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((conv_mfma_bf16<KT, KS, UPS, MODE, false, 32>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -398,6 +476,16 @@ hipError_t go(const ConvArgs& a, hipStream_t s) {
 
 hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s) {
   const bool ups = a.ups != 0;
+  if (dtype != VAEP_DTYPE_F32) {
+    // buffer-resource addressing: the rows one tile can read (at most KT frames of a
+    // band) and the weights stay below 2 GiB, so the padding offset reads out of range
+    const long long xb = a.x_f32 ? 4 : 2;
+    for (int b = 0; b < a.in.nb; ++b)
+      if ((long long)a.kt * (a.in.rows[b] + 2) * a.in.W * a.in.C * xb + 2LL * kConvTileM * a.in.C * xb >=
+          (1LL << 31) - 4096)
+        return hipErrorInvalidValue;
+    if ((long long)a.cout_pad * a.kt * a.ks * a.ks * a.cin * 2 >= (1LL << 31)) return hipErrorInvalidValue;
+  }
   int t = 0;
   for (int b = 0; b < a.in.nb; ++b) {
     a.tile_start[b] = t;
