@@ -25,7 +25,6 @@ namespace vaep {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPixPerThread = 8;   // 16-byte vectors held in registers by one thread per stats tile
 constexpr int V = 4;               // channels per 16-byte load of the fp32 input
 
 __device__ __forceinline__ void load4(const float* p, float* v) {
@@ -65,10 +64,14 @@ __device__ __forceinline__ int band_of_block(const int* start, int nb, int blk) 
 __device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
 
 // Pass 1: central moments of one tile (a pixel chunk of one slab of one image):
-// partials[tile][g] = (mean, M2) of group g, two-pass from registers, in fp64.
+// partials[tile][g] = (mean, M2) of group g.  Each thread streams its channel slot over
+// the tile's pixels accumulating sums shifted by the tile's first pixel (fp32 over 4
+// pixels, then fp64); the block then reduces per group in fp64.  The tiling is fixed,
+// so the result does not depend on the band table.
 __global__ void __launch_bounds__(kThreads) gn_stats(const NormArgs a) {
-  __shared__ double red[kThreads * V];
-  __shared__ double gmean[1024];
+  __shared__ double r1[kThreads * V];
+  __shared__ double r2[kThreads * V];
+  __shared__ float shift[1024];
   const BandLayout& L = a.L;
   const int C = L.C, S = C / V, PL = kThreads / S;
   const int G = a.groups, cpg = C / G;
@@ -80,72 +83,83 @@ __global__ void __launch_bounds__(kThreads) gn_stats(const NormArgs a) {
   const int g0 = slab * a.slab_rows;                    // first global row of the slab
   int b = 0;
   while (b + 1 < L.nb && g0 >= L.row0[b + 1]) ++b;
-  const long long npix = (long long)a.slab_rows * L.W;  // pixels of the slab
+  const long long slab_pix = (long long)a.slab_rows * L.W;
   const long long p0 = (long long)chunk * a.chunk_pix;
+  long long tp = slab_pix - p0;
+  if (tp > a.chunk_pix) tp = a.chunk_pix;
   const int tid = threadIdx.x;
   const int slot = tid % S, pl = tid / S;
   const bool active = pl < PL;
-  const float* base = reinterpret_cast<const float*>(a.x) + row_offset(L, b, n, g0 - L.row0[b]) +
-                      (long long)slot * V;
-
-  float x[kPixPerThread][V];
-  int cnt = 0;
+  const float* tile_x = reinterpret_cast<const float*>(a.x) + row_offset(L, b, n, g0 - L.row0[b]) + p0 * C;
+  const float* base = tile_x + (long long)slot * V;
+  // per-channel shift: the tile's first pixel
+  for (int c = tid; c < C; c += kThreads) shift[c] = tile_x[c];
+  __syncthreads();
+  float k[V];
 #pragma unroll
-  for (int k = 0; k < kPixPerThread; ++k) {
-    const long long p = p0 + (long long)k * PL + pl;
-    if (active && p < npix) {
-      load4(base + p * C, x[k]);
-      ++cnt;
-    } else {
+  for (int e = 0; e < V; ++e) k[e] = shift[slot * V + e];
+  double s1[V], s2[V];
 #pragma unroll
-      for (int e = 0; e < V; ++e) x[k][e] = 0.f;
-    }
-  }
-  long long tp = npix - p0;
-  if (tp > (long long)a.chunk_pix) tp = a.chunk_pix;
-  const double n_el = (double)(tp * cpg);
-
+  for (int e = 0; e < V; ++e) s1[e] = s2[e] = 0.0;
   if (active) {
+    for (long long p = pl; p < tp; p += 4LL * PL) {
+      float f1[V], f2[V];
 #pragma unroll
-    for (int e = 0; e < V; ++e) {
-      double s = 0.0;
+      for (int e = 0; e < V; ++e) f1[e] = f2[e] = 0.f;
 #pragma unroll
-      for (int k = 0; k < kPixPerThread; ++k) s += (double)x[k][e];
-      red[pl * C + slot * V + e] = s;
+      for (int u = 0; u < 4; ++u) {
+        const long long q = p + (long long)u * PL;
+        if (q < tp) {
+          float x[V];
+          load4(base + q * C, x);
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            const float d = x[e] - k[e];
+            f1[e] += d;
+            f2[e] = fmaf(d, d, f2[e]);
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        s1[e] += (double)f1[e];
+        s2[e] += (double)f2[e];
+      }
     }
   }
-  __syncthreads();
-  if (tid < G) {
-    double s = 0.0;
-    for (int p = 0; p < PL; ++p)
-      for (int j = 0; j < cpg; ++j) s += red[p * C + tid * cpg + j];
-    gmean[tid] = s / n_el;
-  }
-  __syncthreads();
-  double s2[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) {
-    const double m = gmean[(slot * V + e) / cpg];
-    s2[e] = 0.0;
-#pragma unroll
-    for (int k = 0; k < kPixPerThread; ++k) {
-      const double d = (double)x[k][e] - m;
-      s2[e] += (k < cnt) ? d * d : 0.0;
-    }
+    r1[tid * V + e] = active ? s1[e] : 0.0;
+    r2[tid * V + e] = active ? s2[e] : 0.0;
   }
   __syncthreads();
-  if (active) {
-#pragma unroll
-    for (int e = 0; e < V; ++e) red[pl * C + slot * V + e] = s2[e];
-  }
-  __syncthreads();
+  // per channel c: sum over the PL pixel lanes (slot c / V, element c % V)
+  const double cnt = (double)tp;
   if (tid < G) {
-    double s = 0.0;
-    for (int p = 0; p < PL; ++p)
-      for (int j = 0; j < cpg; ++j) s += red[p * C + tid * cpg + j];
+    const int gc = tid * cpg;
+    double sum = 0.0;          // sum over the group of x
+    for (int j = 0; j < cpg; ++j) {
+      const int c = gc + j, sl = c / V, e = c % V;
+      double a1 = 0.0;
+      for (int q = 0; q < PL; ++q) a1 += r1[(q * S + sl) * V + e];
+      sum += cnt * (double)shift[c] + a1;
+    }
+    const double mean = sum / (cnt * cpg);
+    double m2 = 0.0;           // sum over the group of (x - mean)^2
+    for (int j = 0; j < cpg; ++j) {
+      const int c = gc + j, sl = c / V, e = c % V;
+      double a1 = 0.0, a2 = 0.0;
+      for (int q = 0; q < PL; ++q) {
+        a1 += r1[(q * S + sl) * V + e];
+        a2 += r2[(q * S + sl) * V + e];
+      }
+      // sum (x - mean)^2 = sum (d - dm)^2 with d = x - k_c, dm = mean - k_c
+      const double dm = mean - (double)shift[c];
+      m2 += a2 - 2.0 * dm * a1 + cnt * dm * dm;
+    }
     double* out = a.partials + ((long long)blk * G + tid) * 2;
-    out[0] = gmean[tid];
-    out[1] = s;
+    out[0] = mean;
+    out[1] = m2 > 0.0 ? m2 : 0.0;
   }
 }
 
@@ -244,40 +258,49 @@ __global__ void __launch_bounds__(kThreads) gn_merge(const NormArgs a, float* co
 }
 
 // Pass 3: y = act(x * scale_c + shift_c) over every owned row; boundary rows are also
-// written into the neighbours' halo slots.
+// written into the neighbours' halo slots.  Workgroup = a run of kApplyPix pixels of one
+// (band, image); thread = fixed channel slot, pixels strided by the pixel lanes.
+constexpr int kApplyPix = 128;
 template <typename TO>
 __global__ void __launch_bounds__(kThreads) gn_apply(const NormArgs a, const float* coef) {
   const BandLayout& L = a.L;
-  const int C = L.C, S = C / V;
-  const long long vtotal = a.item_start[L.nb];
-  const float* X = reinterpret_cast<const float*>(a.x);
+  const int C = L.C, S = C / V, PL = kThreads / S;
+  int b = 0;
+  while (b + 1 < L.nb && (long long)blockIdx.x >= a.item_start[b + 1]) ++b;
+  const long long local = blockIdx.x - a.item_start[b];
+  const long long runs = ((long long)L.rows[b] * L.W + kApplyPix - 1) / kApplyPix;
+  const int n = (int)(local / runs);
+  const long long p0 = (local - n * runs) * kApplyPix;
+  const long long npix = (long long)L.rows[b] * L.W;
+  const int tid = threadIdx.x;
+  const int slot = tid % S, pl = tid / S;
+  if (pl >= PL) return;
+  const float* X = reinterpret_cast<const float*>(a.x) + row_offset(L, b, n, 0) + slot * V;
   TO* Y = reinterpret_cast<TO*>(a.y);
-  for (long long gid = (long long)blockIdx.x * kThreads + threadIdx.x; gid < vtotal;
-       gid += (long long)gridDim.x * kThreads) {
-    int b = 0;
-    while (b + 1 < L.nb && gid >= a.item_start[b + 1]) ++b;
-    const long long v = gid - a.item_start[b];
-    const long long per_img = (long long)L.rows[b] * L.W * S;
-    const int n = (int)(v / per_img);
-    const long long rem = v - n * per_img;
-    const long long pix = rem / S;
-    const int slot = (int)(rem - pix * S);
-    const int r = (int)(pix / L.W);
-    const int c = (int)(pix - (long long)r * L.W);
-    const long long off = row_offset(L, b, n, r) + (long long)c * C + slot * V;
+  const long long ybase = row_offset(L, b, n, 0) + slot * V;
+  float sc[V], sh[V];
+  const float* cf = coef + ((long long)n * C + slot * V) * 2;
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    sc[e] = cf[2 * e];
+    sh[e] = cf[2 * e + 1];
+  }
+  const long long row_up = b > 0 ? row_offset(L, b - 1, n, L.rows[b - 1]) + slot * V : 0;
+  const long long row_dn = b + 1 < L.nb ? row_offset(L, b + 1, n, -1) + slot * V : 0;
+  const long long last_row_start = (long long)(L.rows[b] - 1) * L.W;
+  for (int k = 0; k < kApplyPix / PL + 1; ++k) {
+    const long long p = p0 + pl + (long long)k * PL;
+    if (p >= p0 + kApplyPix || p >= npix) break;
     float x[V];
-    load4(X + off, x);
-    const float* cf = coef + ((long long)n * C + slot * V) * 2;
+    load4(X + p * C, x);
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      const float y = x[e] * cf[2 * e] + cf[2 * e + 1];
+      const float y = x[e] * sc[e] + sh[e];
       x[e] = a.act ? silu(y) : y;
     }
-    Out<TO>::store4(Y + off, x);
-    if (r == 0 && b > 0)
-      Out<TO>::store4(Y + row_offset(L, b - 1, n, L.rows[b - 1]) + (long long)c * C + slot * V, x);
-    if (r == L.rows[b] - 1 && b + 1 < L.nb)
-      Out<TO>::store4(Y + row_offset(L, b + 1, n, -1) + (long long)c * C + slot * V, x);
+    Out<TO>::store4(Y + ybase + p * C, x);
+    if (p < L.W && b > 0) Out<TO>::store4(Y + row_up + p * C, x);
+    if (p >= last_row_start && b + 1 < L.nb) Out<TO>::store4(Y + row_dn + (p - last_row_start) * C, x);
   }
 }
 
@@ -368,9 +391,10 @@ __global__ void moment_merge(int n_shards, int n_stats, const float* mean, const
 }  // namespace
 
 
-// Stats tiling of a layout: slabs of a.slab_rows rows (set by the caller), chunks of
-// kThreads/S * kPixPerThread pixels.
-static int chunk_pixels(int C) { return (kThreads / (C / V)) * kPixPerThread; }
+// Stats tiling of a layout: slabs of a.slab_rows rows (set by the caller), cut into
+// chunks of chunk_pixels(C) pixels.
+// ~128 KiB of fp32 per statistics tile
+static int chunk_pixels(int C) { return (32768 + C - 1) / C; }
 
 static bool plan_stats(NormArgs& a) {
   const BandLayout& L = a.L;
@@ -408,14 +432,13 @@ hipError_t launch_groupnorm(NormArgs& a, int dtype, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(gn_stats, dim3(blocks), dim3(kThreads), 0, s, a);
   hipLaunchKernelGGL(gn_merge, dim3(L.n_img * a.groups), dim3(kThreads), 0, s, a, coef);
-  long long vt = 0;
+  long long nblk = 0;   // apply workgroups: runs of kApplyPix pixels per (band, image)
   for (int b = 0; b < L.nb; ++b) {
-    a.item_start[b] = vt;
-    vt += (long long)L.n_img * L.rows[b] * L.W * (L.C / V);
+    a.item_start[b] = nblk;
+    nblk += (long long)L.n_img * (((long long)L.rows[b] * L.W + kApplyPix - 1) / kApplyPix);
   }
-  a.item_start[L.nb] = vt;
-  long long nblk = (vt + kThreads - 1) / kThreads;
-  if (nblk > 65536) nblk = 65536;
+  a.item_start[L.nb] = nblk;
+  if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
   if (dtype == VAEP_DTYPE_F32)
     hipLaunchKernelGGL(gn_apply<float>, dim3((int)nblk), dim3(kThreads), 0, s, a, coef);
   else
