@@ -85,6 +85,12 @@ bool stage_ups(const vaep_config& c, int i) { return i < c.n_stages - 1; }
 bool stage_time_ups(const vaep_config& c, int i) {
   return is_video(c) && stage_ups(c, i) && i < c.temporal_up_stages;
 }
+// bf16 stages whose spatial upsample runs in sub-pixel form on the wide conv kernel: the
+// stage's last resnet stores its output as bf16 hi/lo parts (64-channel K steps).
+bool stage_sub(const vaep_config& c, int i) {
+  return c.dtype == VAEP_DTYPE_BF16 && stage_ups(c, i) && !stage_time_ups(c, i) &&
+         c.resnets_per_stage >= 1 && c.stage_channels[i] % 64 == 0;
+}
 
 // Canonical parameter list (names follow the decoder structure).
 std::vector<ParamDesc> param_list(const vaep_config& c) {
@@ -168,6 +174,7 @@ int check_config(const vaep_config* c) {
 struct ConvW {
   void* w = nullptr;
   float* b = nullptr;
+  void* wsub = nullptr;   // phase-folded weights of a sub-pixel upsample conv (else NULL)
   int co = 0, ci = 0, co_pad = 0, ci_pad = 0, kt = 1, ks = 3;
 };
 struct NormW {
@@ -187,6 +194,7 @@ struct AttnW {
 struct StageW {
   std::vector<ResW> res;
   bool time_up = false, up = false;
+  bool sub = false;   // the last resnet writes a split stream and the upsample runs sub-pixel
   ConvW time_conv, up_conv;
 };
 
@@ -333,6 +341,12 @@ struct Builder {
       if (s.time_up) s.time_conv = conv("up" + std::to_string(i) + ".time_conv", 2 * co, co, 3, 1);
       s.up = stage_ups(c, i);
       if (s.up) s.up_conv = conv("up" + std::to_string(i) + ".upsample", co, co, 1, 3);
+      s.sub = stage_sub(c, i);
+      if (s.sub) {
+        ConvW& u = s.up_conv;
+        u.wsub = carve.take((size_t)4 * u.co_pad * 4 * 2 * u.ci_pad * 2);
+        if (!dry) ok(launch_fold_subpixel_weight(P("up" + std::to_string(i) + ".upsample.weight"), co, co, u.wsub, u.co_pad, st));
+      }
       m.stages.push_back(s);
     }
     m.norm_out = norm("norm_out", prev);
@@ -341,6 +355,8 @@ struct Builder {
 };
 
 // ------------------------------------------------------------------ executor
+enum XIn : int { kXOp = 0, kXF32 = 1, kXSplit = 2 };
+
 struct Exec {
   const vaep_model* m = nullptr;
   int dtype = VAEP_DTYPE_BF16;
@@ -408,16 +424,21 @@ struct Exec {
     scratch = (float*)(base + o);
   }
 
-  // x_f32: the input is an fp32 conv output (else a normalised activation in the operand dtype).
-  int conv(const ConvW& w, const void* x, const BandLayout& Lin, bool x_f32, void* y,
+  // xk: what the input buffer holds (kXOp: a normalised activation in the operand dtype;
+  // kXF32: an fp32 conv output; kXSplit: bf16 hi/lo parts of an fp32 conv output, 2x the
+  // channels).  A split input with ups runs the sub-pixel form with w.wsub.
+  int conv(const ConvW& w, const void* x, const BandLayout& Lin, int xk, void* y,
            const BandLayout& Lout, int mode, const void* res, int ups, int final_frames = 1) {
     if (mode == kModeBand || mode == kModeTimeInterleave) need_act(Lout, 4);
-    need_act(Lin, x_f32 ? 4 : eb());
+    if (mode == kModeBandSplit) need_act(Lout, 2);
+    need_act(Lin, xk == kXOp ? eb() : (xk == kXF32 ? 4 : 2));
     if (dry) return VAEP_OK;
+    const bool sub = xk == kXSplit && ups;
+    if (sub && !w.wsub) return fail(VAEP_ERR_INVALID_ARG, "internal: sub-pixel conv without folded weights");
     ConvArgs a;
     std::memset(&a, 0, sizeof(a));
     a.x = x;
-    a.w = w.w;
+    a.w = sub ? w.wsub : w.w;
     a.bias = w.b;
     a.res = res;
     a.y = y;
@@ -426,16 +447,19 @@ struct Exec {
     a.vt = vb;
     a.in = Lin;
     a.out = Lout;
-    a.cin = Lin.C;
+    a.cin = w.ci_pad;
     a.cout = w.co;
     a.cout_pad = w.co_pad;
     a.kt = w.kt;
     a.ks = w.ks;
     a.ups = ups;
     a.mode = mode;
-    a.x_f32 = x_f32 ? 1 : 0;
+    a.x_f32 = xk == kXF32 ? 1 : 0;
+    a.x_split = xk == kXSplit ? 1 : 0;
+    a.sub = sub ? 1 : 0;
     a.final_frames = final_frames;
-    if (Lin.C != w.ci_pad) return fail(VAEP_ERR_INVALID_ARG, "internal: conv input has %d channels, weight %d", Lin.C, w.ci_pad);
+    if (Lin.C != (xk == kXSplit ? 2 : 1) * w.ci_pad)
+      return fail(VAEP_ERR_INVALID_ARG, "internal: conv input has %d channels, weight %d", Lin.C, w.ci_pad);
     {
       vaep_profile_entry pe = entry(VAEP_STEP_CONV, 1);
       const long long m = (long long)Lin.n_img * Lin.H * Lin.W * (ups ? 4 : 1);
@@ -448,7 +472,7 @@ struct Exec {
       pe.mode = mode;
       pe.pixels = m;
       pe.flops = 2.0 * (double)m * w.co * (double)k;
-      const double in_b = (double)Lin.n_img * Lin.H * Lin.W * w.ci * (x_f32 ? 4 : eb());
+      const double in_b = (double)Lin.n_img * Lin.H * Lin.W * w.ci * (xk == kXOp ? eb() : 4.0);
       const double out_elem = mode == kModeQKV ? (double)eb() : 4.0;
       pe.bytes = in_b + (double)w.co * k * eb() + (double)m * w.co * out_elem + (res ? (double)m * w.co * 4 : 0.0);
       rec_begin(pe);
@@ -501,7 +525,7 @@ struct Exec {
     qkv_bytes = std::max(qkv_bytes, (size_t)L.n_img * L.H * L.W * c * eb());
     int rc = norm(w.norm, x, L, a_buf, 0);
     if (rc) return rc;
-    rc = conv(w.qkv, a_buf, L, false, nullptr, L, kModeQKV, nullptr, 0);
+    rc = conv(w.qkv, a_buf, L, kXOp, nullptr, L, kModeQKV, nullptr, 0);
     if (rc) return rc;
     need_act(L, eb());
     if (!dry) {
@@ -527,7 +551,7 @@ struct Exec {
       if (e != hipSuccess) return hip_fail(e, "attention launch");
       ++launches;
     }
-    return conv(w.out, o_buf, L, false, y, L, kModeBand, x, 0);
+    return conv(w.out, o_buf, L, kXOp, y, L, kModeBand, x, 0);
   }
 };
 
@@ -538,23 +562,27 @@ void others(int cur, int* o) {
     if (i != cur) o[k++] = i;
 }
 
-int resnet(Exec& E, const ResW& r, int& cur, BandLayout& L) {
+// split_out: store the block output as bf16 hi/lo parts (layout with 2x the channels)
+// for a following split-input conv, instead of fp32.
+int resnet(Exec& E, const ResW& r, int& cur, BandLayout& L, bool split_out = false) {
   int o[3];
   others(cur, o);
   const BandLayout Lx = L;
   const BandLayout Lh = reshaped(L, r.c1.co, L.n_img, L.frames);
+  const BandLayout Ly = split_out ? reshaped(L, 2 * r.c1.co, L.n_img, L.frames) : Lh;
   int rc;
   if ((rc = E.norm(r.n1, E.act[cur], Lx, E.act[o[0]], 1))) return rc;
-  if ((rc = E.conv(r.c1, E.act[o[0]], Lx, false, E.act[o[1]], Lh, kModeBand, nullptr, 0))) return rc;
+  if ((rc = E.conv(r.c1, E.act[o[0]], Lx, kXOp, E.act[o[1]], Lh, kModeBand, nullptr, 0))) return rc;
   if ((rc = E.norm(r.n2, E.act[o[1]], Lh, E.act[o[0]], 1))) return rc;
   const void* res = E.act[cur];
   if (r.has_sc) {
-    if ((rc = E.conv(r.sc, E.act[cur], Lx, true, E.act[o[2]], Lh, kModeBand, nullptr, 0))) return rc;
+    if ((rc = E.conv(r.sc, E.act[cur], Lx, kXF32, E.act[o[2]], Lh, kModeBand, nullptr, 0))) return rc;
     res = E.act[o[2]];
   }
-  if ((rc = E.conv(r.c2, E.act[o[0]], Lh, false, E.act[o[1]], Lh, kModeBand, res, 0))) return rc;
+  if ((rc = E.conv(r.c2, E.act[o[0]], Lh, kXOp, E.act[o[1]], Ly, split_out ? kModeBandSplit : kModeBand, res, 0)))
+    return rc;
   cur = o[1];
-  L = Lh;
+  L = Ly;
   return VAEP_OK;
 }
 
@@ -578,7 +606,7 @@ int walk(Exec& E, const void* latent, int B, int T, int W, const int* rows, int 
     ++E.launches;
   }
   BandLayout L1 = reshaped(L, m.conv_in.co, L.n_img, T);
-  if ((rc = E.conv(m.conv_in, E.act[0], L, false, E.act[1], L1, kModeBand, nullptr, 0))) return rc;
+  if ((rc = E.conv(m.conv_in, E.act[0], L, kXOp, E.act[1], L1, kModeBand, nullptr, 0))) return rc;
   cur = 1;
   L = L1;
   if ((rc = resnet(E, m.mid0, cur, L))) return rc;
@@ -590,14 +618,14 @@ int walk(Exec& E, const void* latent, int B, int T, int W, const int* rows, int 
   }
   if ((rc = resnet(E, m.mid1, cur, L))) return rc;
   for (const StageW& s : m.stages) {
-    for (const ResW& r : s.res)
-      if ((rc = resnet(E, r, cur, L))) return rc;
+    for (size_t j = 0; j < s.res.size(); ++j)
+      if ((rc = resnet(E, s.res[j], cur, L, s.sub && j + 1 == s.res.size()))) return rc;
     if (s.time_up) {
       int o[3];
       others(cur, o);
       const int Tn = 2 * L.frames - 1;
       const BandLayout Lt = reshaped(L, L.C, (L.n_img / L.frames) * Tn, Tn);
-      if ((rc = E.conv(s.time_conv, E.act[cur], L, true, E.act[o[0]], Lt, kModeTimeInterleave, nullptr, 0))) return rc;
+      if ((rc = E.conv(s.time_conv, E.act[cur], L, kXF32, E.act[o[0]], Lt, kModeTimeInterleave, nullptr, 0))) return rc;
       if (!E.dry) {
         hipError_t e = launch_copy_frame0(E.act[cur], L, E.act[o[0]], Lt, VAEP_DTYPE_F32, E.st);
         if (e != hipSuccess) return hip_fail(e, "frame copy");
@@ -610,7 +638,8 @@ int walk(Exec& E, const void* latent, int B, int T, int W, const int* rows, int 
       int o[3];
       others(cur, o);
       const BandLayout Lu = upsampled(L, s.up_conv.co);
-      if ((rc = E.conv(s.up_conv, E.act[cur], L, true, E.act[o[0]], Lu, kModeBand, nullptr, 1))) return rc;
+      if ((rc = E.conv(s.up_conv, E.act[cur], L, s.sub ? kXSplit : kXF32, E.act[o[0]], Lu, kModeBand, nullptr, 1)))
+        return rc;
       cur = o[0];
       L = Lu;
     }
@@ -619,7 +648,7 @@ int walk(Exec& E, const void* latent, int B, int T, int W, const int* rows, int 
   others(cur, o);
   if ((rc = E.norm(m.norm_out, E.act[cur], L, E.act[o[0]], 1))) return rc;
   (void)video;
-  return E.conv(m.conv_out, E.act[o[0]], L, false, out, L, kModeFinal, nullptr, 0, L.frames);
+  return E.conv(m.conv_out, E.act[o[0]], L, kXOp, out, L, kModeFinal, nullptr, 0, L.frames);
 }
 
 // Rows of nb bands that split H as evenly as possible (used to size workspaces).
@@ -970,9 +999,14 @@ int vaep_step_conv(int dtype, int x_dtype, const void* x, int batch, int frames,
   const BandLayout Lout = upsample ? upsampled(Lin, cout) : reshaped(Lin, cout, Lin.n_img, frames);
   const size_t eb = dtype_bytes(dtype);
   const bool x_f32 = x_dtype == VAEP_DTYPE_F32;
+  // bf16 upsample conv of an fp32 input: split the input into bf16 hi/lo parts and run the
+  // sub-pixel form, as a decode does
+  const bool sub = bf && upsample && x_f32 && cin % 64 == 0;
+  const BandLayout Ls = reshaped(Lin, 2 * cin_pad, Lin.n_img, frames);
   Carver cv;
   cv.base = (char*)ws;
   void* xin = cv.take(layout_elems(Lin) * dtype_bytes(x_dtype));
+  void* xs = sub ? cv.take(layout_elems(Ls) * 2) : nullptr;
   void* yo = cv.take(layout_elems(Lout) * 4);
   void* rb = residual ? cv.take(layout_elems(Lout) * 4) : nullptr;
   ConvW cw;
@@ -984,6 +1018,7 @@ int vaep_step_conv(int dtype, int x_dtype, const void* x, int batch, int frames,
   cw.ks = kh;
   cw.w = cv.take((size_t)co_pad * taps * cin_pad * eb);
   cw.b = (float*)cv.take((size_t)co_pad * sizeof(float));
+  if (sub) cw.wsub = cv.take((size_t)4 * co_pad * 4 * 2 * cin_pad * 2);
   bool sized;
   if ((rc = step_finish_sizing(cv, ws, ws_bytes, bytes_out, &sized)) || sized) return rc;
   if (!x || !weight || !y) return fail(VAEP_ERR_INVALID_ARG, "x, weight and y must be device pointers");
@@ -992,12 +1027,16 @@ int vaep_step_conv(int dtype, int x_dtype, const void* x, int batch, int frames,
   if (e == hipSuccess && residual) e = launch_pack(residual, cout, rb, Lout, VAEP_DTYPE_F32, st);
   if (e == hipSuccess) e = launch_pack_weight(weight, cout, cin, taps, cw.w, co_pad, cin_pad, dtype, st);
   if (e == hipSuccess) e = launch_to_f32(bias, cout, cw.b, co_pad, dtype, st);
+  if (e == hipSuccess && sub) e = launch_split((const float*)xin, Lin, xs, st);
+  if (e == hipSuccess && sub) e = launch_fold_subpixel_weight(weight, cout, cin, cw.wsub, co_pad, st);
   if (e != hipSuccess) return hip_fail(e, "step conv staging");
   Exec E;
   E.dtype = dtype;
   E.st = st;
   E.dry = false;
-  if ((rc = E.conv(cw, xin, Lin, x_f32, yo, Lout, kModeBand, rb, upsample))) return rc;
+  if (sub) rc = E.conv(cw, xs, Ls, kXSplit, yo, Lout, kModeBand, rb, upsample);
+  else rc = E.conv(cw, xin, Lin, x_f32 ? kXF32 : kXOp, yo, Lout, kModeBand, rb, upsample);
+  if (rc) return rc;
   e = launch_unpack(yo, Lout, y, cout, VAEP_DTYPE_F32, st);
   if (e != hipSuccess) return hip_fail(e, "step conv gather");
   return VAEP_OK;
@@ -1203,7 +1242,7 @@ int vaep_step_temporal_upsample(int dtype, const void* x, int batch, int frames,
   E.dtype = dtype;
   E.st = st;
   E.dry = false;
-  if ((rc = E.conv(cw, xin, Lx, true, yo, Lt, kModeTimeInterleave, nullptr, 0))) return rc;
+  if ((rc = E.conv(cw, xin, Lx, kXF32, yo, Lt, kModeTimeInterleave, nullptr, 0))) return rc;
   e = launch_copy_frame0(xin, Lx, yo, Lt, VAEP_DTYPE_F32, st);
   if (e == hipSuccess) e = launch_unpack(yo, Lt, y, c, VAEP_DTYPE_F32, st);
   if (e != hipSuccess) return hip_fail(e, "step temporal upsample");

@@ -85,6 +85,18 @@ __device__ __forceinline__ void st4(void* base, long long off, const float* v) {
 __device__ __forceinline__ void st4f(void* base, long long off, const float* v) {
   *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + off) = make_float4(v[0], v[1], v[2], v[3]);
 }
+// 4 channels as bf16 hi parts at `off` and lo parts `half` channels later.
+__device__ __forceinline__ void st4split(void* base, long long off, int half, const float* v) {
+  unsigned short h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = f2bf(v[e]);
+    l[e] = f2bf(v[e] - bf2f(h[e]));
+  }
+  unsigned short* p = reinterpret_cast<unsigned short*>(base) + off;
+  *reinterpret_cast<uint2*>(p) = make_uint2((unsigned)h[0] | ((unsigned)h[1] << 16), (unsigned)h[2] | ((unsigned)h[3] << 16));
+  *reinterpret_cast<uint2*>(p + half) = make_uint2((unsigned)l[0] | ((unsigned)l[1] << 16), (unsigned)l[2] | ((unsigned)l[3] << 16));
+}
 
 // Band-layout fp32 store of 4 channels at (band b, image n, row r, col c) plus the halo
 // push into the neighbours' halo slots when r is a boundary row of the band.
@@ -93,6 +105,13 @@ __device__ __forceinline__ void store_band4(const BandLayout& L, void* y, int b,
   st4f(y, band_offset(L, b, n, r, c) + ch, v);
   if (r == 0 && b > 0) st4f(y, band_offset(L, b - 1, n, L.rows[b - 1], c) + ch, v);
   if (r == L.rows[b] - 1 && b + 1 < L.nb) st4f(y, band_offset(L, b + 1, n, -1, c) + ch, v);
+}
+// The same as bf16 hi / lo parts in a layout of 2 x `half` channels.
+__device__ __forceinline__ void store_split4(const BandLayout& L, void* y, int half, int b, int n, int r,
+                                             int c, int ch, const float* v) {
+  st4split(y, band_offset(L, b, n, r, c) + ch, half, v);
+  if (r == 0 && b > 0) st4split(y, band_offset(L, b - 1, n, L.rows[b - 1], c) + ch, half, v);
+  if (r == L.rows[b] - 1 && b + 1 < L.nb) st4split(y, band_offset(L, b + 1, n, -1, c) + ch, half, v);
 }
 
 // bf16 part of an fp32 value: hi = bf16(v); lo = bf16(v - hi).  hi + lo carries 16
@@ -342,16 +361,21 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
         v[1] = acc[i][j][4 * g + 1] + bb.y;
         v[2] = acc[i][j][4 * g + 2] + bb.z;
         v[3] = acc[i][j][4 * g + 3] + bb.w;
-        if (MODE == kModeBand) {
+        if (MODE == kModeBand || MODE == kModeBandSplit) {
           if (a.res) {
-            const float4 rr = *reinterpret_cast<const float4*>(
-                reinterpret_cast<const float*>(a.res) + band_offset(a.out, band, n, r, c) + co);
+            // residual: fp32 with `cout` channels in the output's band geometry
+            long long ro = band_offset(a.out, band, n, r, c);
+            if (MODE == kModeBandSplit) ro >>= 1;
+            const float4 rr = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.res) + ro + co);
             v[0] += rr.x;
             v[1] += rr.y;
             v[2] += rr.z;
             v[3] += rr.w;
           }
-          store_band4(a.out, a.y, band, n, r, c, co, v);
+          if (MODE == kModeBandSplit)
+            store_split4(a.out, a.y, a.cout, band, n, r, c, co, v);
+          else
+            store_band4(a.out, a.y, band, n, r, c, co, v);
         } else if (MODE == kModeTimeInterleave) {
           const int T = a.in.frames;
           const int t = n % T;
@@ -476,6 +500,9 @@ hipError_t go(const ConvArgs& a, hipStream_t s) {
 
 hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s) {
   const bool ups = a.ups != 0;
+  if (dtype != VAEP_DTYPE_F32 && conv_wide_fits(a)) return launch_conv_wide(a, s);
+  // split operands and sub-pixel weights exist only on the wide kernel
+  if (a.x_split || a.sub || (a.mode == kModeBandSplit && dtype == VAEP_DTYPE_F32)) return hipErrorInvalidValue;
   if (dtype != VAEP_DTYPE_F32) {
     // buffer-resource addressing: the rows one tile can read (at most KT frames of a
     // band) and the weights stay below 2 GiB, so the padding offset reads out of range
@@ -502,6 +529,8 @@ hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s) {
   }
   const int kt = a.kt, ks = a.ks, m = a.mode;
   if (kt == 1 && ks == 3 && !ups && m == kModeBand) return go<1, 3, false, kModeBand>(a, s);
+  if (kt == 1 && ks == 3 && !ups && m == kModeBandSplit) return go<1, 3, false, kModeBandSplit>(a, s);
+  if (kt == 3 && ks == 3 && !ups && m == kModeBandSplit) return go<3, 3, false, kModeBandSplit>(a, s);
   if (kt == 1 && ks == 3 && ups && m == kModeBand) return go<1, 3, true, kModeBand>(a, s);
   if (kt == 1 && ks == 1 && !ups && m == kModeBand) return go<1, 1, false, kModeBand>(a, s);
   if (kt == 1 && ks == 1 && !ups && m == kModeQKV) return go<1, 1, false, kModeQKV>(a, s);

@@ -1,0 +1,525 @@
+// Wide-tile halo convolution on the gfx950 matrix cores, for the large layers.
+//
+// The operation is the one of conv.hip: a band's conv reads its own rows plus the
+// kernel-radius halo rows its neighbours pushed into the band's halo slots, rows outside
+// the image and columns outside the width read as zero, and a band writes only its own
+// output rows (ChituDiffusion "VAEP" feature page, conv section; "Static Layer-Wise VAE
+// Decode", operator table, "Spatial convolution" row).
+//
+// Layout of the work: one 256-thread workgroup computes BM (128 or 256) output channels
+// x 256 pixels of one band as an implicit GEMM D[co][pixel] = W[co][k] X[k][pixel] with
+// v_mfma_f32_32x32x16_bf16; the four waves own (BM/2) x 128 each.  K advances one tap
+// and 64 channels per step, taps fastest.  Both operand tiles go global -> LDS directly (buffer loads
+// with the LDS destination), through S stages (2 for BM 256, 3 for BM 128), with one
+// barrier per step and no staging registers.  A lane's 16-byte chunk lands at a fixed
+// LDS slot, so the XOR swizzle that keeps the matrix-core reads free of bank conflicts is
+// applied on the global side: LDS slot (row, p) holds logical chunk p ^ f(row),
+// f(row) = (row & 7) ^ ((row >> 3) & 1).
+//
+// Nearest-2x upsample + 3x3 conv runs in sub-pixel form.  Output pixel (2i+py, 2j+px)
+// reads, through the upsample, only source pixels (i+a-1+py, j+b-1+px), a, b in {0, 1};
+// summing the 3x3 weights that fall on the same source pixel gives four 2x2 convs on the
+// source grid (one per phase), 2.25x fewer products.  A tap outside the upsampled image
+// is exactly a tap outside the source image, so zero padding carries over unchanged.  The
+// summed weights are no longer bf16 values and are applied as bf16 hi + lo parts.
+//
+// The operand of the sub-pixel form is the fp32 residual stream, pre-split into bf16
+// [hi | lo] channel halves (kModeBandSplit output or launch_split); K then runs over
+// three parts per tap: x_hi * w_hi, x_lo * w_hi, x_hi * w_lo (the dropped x_lo * w_lo is
+// below 2^-18 of the product).  Other convs have one part: x * w.
+#include "vaep_internal.h"
+
+namespace vaep {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+typedef __attribute__((address_space(3))) unsigned short lds_u16;
+
+namespace {
+
+constexpr int BN = kWideTileM;              // pixels per workgroup
+constexpr unsigned kPadOffset = 0x80000000u; // past every buffer resource (< 2 GiB, host-checked)
+
+// Raw buffer resource over [base, base + bytes): loads past the end return zeros, which is
+// how padding taps read (their offset is set past the end).
+__device__ __forceinline__ u32x4_t make_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long p = reinterpret_cast<unsigned long long>(base);
+  return u32x4_t{(unsigned)p, (unsigned)(p >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// 16 bytes per lane from the buffer at voff + soff into LDS at lds + 16 * lane (lds and
+// soff wave-uniform; lds goes through m0).  Written as inline assembly so that the
+// compiler does not track these LDS writes: it would otherwise wait for every outstanding
+// load before each LDS read, as it cannot tell the stages apart.  Completion is tracked
+// here with explicit vmcnt waits; the barrier asm carries a memory clobber so LDS reads
+// stay after it.  The compiler's hazard checks do not look inside the asm, so it carries
+// the wait states itself: 1 after the m0 write (LDS DMA reads m0), and 5 before the first
+// load of a batch, whose soffset may just have been written by a VALU readfirstlane.
+__device__ __forceinline__ void dma16(bool first, u32x4_t r, unsigned lds, unsigned voff, unsigned soff) {
+  if (first)
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                    "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
+  else
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                    "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
+}
+// L2 prefetch: 4 bytes per lane (one per 128-byte line) into a scratch LDS word per lane;
+// the data is never read.  soff may just have been written by a readfirstlane.
+__device__ __forceinline__ void prefetch4(u32x4_t r, unsigned lds, unsigned voff, unsigned soff) {
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                  "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+__device__ __forceinline__ unsigned lds_addr(const unsigned short* p) {
+  return (unsigned)reinterpret_cast<unsigned long long>((const lds_u16*)p);
+}
+
+__device__ __forceinline__ long long band_offset(const BandLayout& L, int b, int n, int r, int c) {
+  return L.off[b] + (((long long)n * (L.rows[b] + 2) + r + 1) * L.W + c) * (long long)L.C;
+}
+
+__device__ __forceinline__ int band_of_tile(const ConvArgs& a, int mt) {
+  int b = 0;
+  while (b + 1 < a.in.nb && mt >= a.tile_start[b + 1]) ++b;
+  return b;
+}
+
+// Workgroup id -> work id: each XCD (workgroups are dealt round-robin over 8) gets a
+// contiguous run of work ids, so neighbouring tiles share rows in that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int lin, int total) {
+  const int q = total >> 3, r = total & 7;
+  const int x = lin & 7, i = lin >> 3;
+  return x * q + (x < r ? x : r) + i;
+}
+
+__device__ __forceinline__ unsigned short f2bf(float v) {
+  __hip_bfloat16 h = __float2bfloat16(v);
+  return *reinterpret_cast<unsigned short*>(&h);
+}
+__device__ __forceinline__ float bf2f(unsigned short u) { return __uint_as_float(((unsigned)u) << 16); }
+
+__device__ __forceinline__ void st4f(void* base, long long off, const float* v) {
+  *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + off) = make_float4(v[0], v[1], v[2], v[3]);
+}
+// 4 channels as bf16 hi parts at `off` and lo parts at `off + half`.
+__device__ __forceinline__ void st4split(void* base, long long off, int half, const float* v) {
+  unsigned short h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = f2bf(v[e]);
+    l[e] = f2bf(v[e] - bf2f(h[e]));
+  }
+  unsigned short* p = reinterpret_cast<unsigned short*>(base) + off;
+  *reinterpret_cast<uint2*>(p) = make_uint2((unsigned)h[0] | ((unsigned)h[1] << 16), (unsigned)h[2] | ((unsigned)h[3] << 16));
+  *reinterpret_cast<uint2*>(p + half) = make_uint2((unsigned)l[0] | ((unsigned)l[1] << 16), (unsigned)l[2] | ((unsigned)l[3] << 16));
+}
+
+// Store 4 channels of pixel (b, n, r, c) and push boundary rows into the neighbours' halos.
+template <int MODE>
+__device__ __forceinline__ void store4(const BandLayout& L, void* y, int half, int b, int n, int r, int c,
+                                       int ch, const float* v) {
+  const long long o = band_offset(L, b, n, r, c) + ch;
+  const bool up = r == 0 && b > 0, dn = r == L.rows[b] - 1 && b + 1 < L.nb;
+  if (MODE == kModeBandSplit) {
+    st4split(y, o, half, v);
+    if (up) st4split(y, band_offset(L, b - 1, n, L.rows[b - 1], c) + ch, half, v);
+    if (dn) st4split(y, band_offset(L, b + 1, n, -1, c) + ch, half, v);
+  } else {
+    st4f(y, o, v);
+    if (up) st4f(y, band_offset(L, b - 1, n, L.rows[b - 1], c) + ch, v);
+    if (dn) st4f(y, band_offset(L, b + 1, n, -1, c) + ch, v);
+  }
+}
+
+// Part p of a tap: weight part (0 = w or w_hi, 1 = w_lo) and operand part (0 = x or x_hi, 1 = x_lo).
+__device__ __forceinline__ constexpr int wpart(int parts, int p) { return parts == 3 && p == 2 ? 1 : 0; }
+__device__ __forceinline__ constexpr int xpart(int p) { return p == 1 ? 1 : 0; }
+
+template <int KT, int KS, bool SUB, int PARTS, int MODE, int BM>
+__global__ void __launch_bounds__(256, 1) conv_wide(const ConvArgs a) {
+  constexpr int S = BM == 256 ? 2 : 3;        // LDS stages
+  constexpr int TAPS = SUB ? 4 : KT * KS * KS;
+  constexpr int WP = PARTS == 3 ? 2 : 1;      // weight parts per tap in the packed rows
+  constexpr int NA = BM / 32;                 // A (weight) chunk loads per thread per step
+  constexpr int NB = BN / 32;                 // B (pixel) chunk loads per thread per step
+  constexpr int MI = BM / 64;                 // 32-row channel blocks per wave
+  constexpr int NJ = 4;                       // 32-pixel blocks per wave
+  constexpr int PH = SUB ? 4 : 1;
+  // one array per stage: the compiler's wait-count tracking of LDS-destination loads
+  // tells distinct arrays apart, so a read of one stage does not wait for the loads that
+  // are filling another
+  __shared__ __attribute__((aligned(1024))) unsigned short sA0[BM * 64], sA1[BM * 64], sA2[S == 3 ? BM * 64 : 8];
+  __shared__ __attribute__((aligned(1024))) unsigned short sB0[BN * 64], sB1[BN * 64], sB2[S == 3 ? BN * 64 : 8];
+  __shared__ unsigned int sPF[64];             // prefetch landing words (never read)
+  constexpr int PFD = 2;                       // prefetch target: PFD steps past the step issued
+  constexpr int NG = NA + NB + 2;              // loads per thread per issued step
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const unsigned wrow = wave * 8 * 64 * 2;   // LDS byte offset of this wave's first row block
+  // work id -> (output-channel tile, pixel tile, phase); the phases of a pixel tile are adjacent
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int phase = lin % PH;
+  const int rest = lin / PH;
+  const int mt = rest % a.tiles_total;
+  const int co0 = (rest / a.tiles_total) * BM;
+  const int band = band_of_tile(a, mt);
+  const int tile = mt - a.tile_start[band];
+  const int py = phase >> 1, px = phase & 1;
+
+  const int rows_in = a.in.rows[band];
+  const int W = a.in.W;
+  const int plane = rows_in * W;                       // compute pixels per image (source grid)
+  const long long m_band = (long long)a.in.n_img * plane;
+  const int C = a.cin;                                 // input channels
+  const int XC = a.in.C;                               // channel stride of the input buffer
+  const int csteps = C >> 6;
+  const int nsteps = TAPS * PARTS * csteps;
+  const int kw = TAPS * WP * C;                        // packed weight row length (elements)
+
+  // Input rows the tile can read: from its first pixel's row - 1 (KT - 1 frames back) to
+  // its last pixel's row + 1; halo slots cover the rows beyond the band.
+  long long first_slot, last_slot;
+  {
+    const long long p0 = (long long)tile * BN;
+    long long p1 = p0 + BN - 1;
+    if (p1 >= m_band) p1 = m_band - 1;
+    const int n0 = (int)(p0 / plane), r0 = (int)((p0 - (long long)n0 * plane) / W);
+    const int n1 = (int)(p1 / plane), r1 = (int)((p1 - (long long)n1 * plane) / W);
+    first_slot = (long long)(n0 - (KT - 1)) * (rows_in + 2) + r0;
+    if (first_slot < 0) first_slot = 0;
+    last_slot = (long long)n1 * (rows_in + 2) + r1 + 2;
+  }
+  const long long row_elems = (long long)W * XC;
+  const u32x4_t xrs = make_rsrc(
+      reinterpret_cast<const unsigned short*>(a.x) + a.in.off[band] + first_slot * row_elems,
+      (unsigned)((last_slot - first_slot + 1) * row_elems * 2));
+  const u32x4_t wrs = make_rsrc(
+      reinterpret_cast<const unsigned short*>(a.w) + (long long)phase * a.cout_pad * kw,
+      (unsigned)((long long)a.cout_pad * kw * 2));
+
+  // This thread's chunk: LDS rows (j*4 + wave)*8 + lane/8, slot lane%8, logical chunk ck.
+  const int ck = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
+  unsigned avo[NA];
+#pragma unroll
+  for (int j = 0; j < NA; ++j)
+    avo[j] = (unsigned)(((long long)(co0 + (j * 4 + wave) * 8 + (lane >> 3)) * kw + ck * 8) * 2);
+  // Pixel rows: byte offset of the pixel's own position and validity bits
+  // (0..2: row shift -1..1 inside the image, 3..5: column shift -1..1, 6..8: frame shift
+  // -(KT-1)+dt not before frame 0).
+  unsigned pbase[NB];
+  int pmask[NB];
+  const int H = a.in.H;
+  const int g0 = a.in.row0[band];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const long long p = (long long)tile * BN + (j * 4 + wave) * 8 + (lane >> 3);
+    const bool ok = p < m_band;
+    const long long q = ok ? p : 0;
+    const int n = (int)(q / plane);
+    const int rem = (int)(q - (long long)n * plane);
+    const int r = rem / W;
+    const int c = rem - r * W;
+    const long long slot = (long long)n * (rows_in + 2) + r + 1;
+    pbase[j] = (unsigned)(((slot - first_slot) * W + c) * XC * 2 + ck * 16);
+    const int g = g0 + r;
+    int m = 0;
+    m |= (g - 1 >= 0) ? 1 : 0;
+    m |= 2;
+    m |= (g + 1 < H) ? 4 : 0;
+    m |= (c - 1 >= 0) ? 8 : 0;
+    m |= 16;
+    m |= (c + 1 < W) ? 32 : 0;
+    const int t = n % a.in.frames;
+#pragma unroll
+    for (int dt = 0; dt < KT; ++dt) m |= (t + dt - (KT - 1) >= 0) ? (64 << dt) : 0;
+    pmask[j] = ok ? m : 0;
+  }
+  unsigned bvo[NB];
+  // prefetch roles: weight row (wave*64 + lane) % BM, tile pixel wave*64 + lane
+  const unsigned pf_avo = (unsigned)((long long)(co0 + (wave * 64 + lane) % BM) * kw * 2);
+  unsigned pf_base;
+  int pf_mask;
+  {
+    const long long p = (long long)tile * BN + wave * 64 + lane;
+    const bool ok = p < m_band;
+    const long long q = ok ? p : 0;
+    const int n = (int)(q / plane);
+    const int rem = (int)(q - (long long)n * plane);
+    const int r = rem / W;
+    const int c = rem - r * W;
+    const long long slot = (long long)n * (rows_in + 2) + r + 1;
+    pf_base = (unsigned)(((slot - first_slot) * W + c) * XC * 2);
+    const int g = g0 + r;
+    int m = 2 | 16;
+    m |= (g - 1 >= 0) ? 1 : 0;
+    m |= (g + 1 < H) ? 4 : 0;
+    m |= (c - 1 >= 0) ? 8 : 0;
+    m |= (c + 1 < W) ? 32 : 0;
+    const int t = n % a.in.frames;
+#pragma unroll
+    for (int dt = 0; dt < KT; ++dt) m |= (t + dt - (KT - 1) >= 0) ? (64 << dt) : 0;
+    pf_mask = ok ? m : 0;
+  }
+
+  f32x16_t acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  // Issue the loads of step (c0, part, tap) into LDS stage st; taps vary fastest, so
+  // consecutive steps read shifted windows of the same rows and channels (L2 and the
+  // neighbouring tiles' reads then serve most of them).  bvo holds the tap's offsets.
+  int itap = 0, ipart = 0, ic = 0, issued = 0;
+  // validity bits a tap needs (see pmask) and its byte displacement in the input buffer
+#define VAEP_TAP_GEO(tp, need, delta)                                                          \
+  int need, delta;                                                                             \
+  {                                                                                            \
+    int dt, sy, sx;                                                                            \
+    if (SUB) {                                                                                 \
+      dt = KT - 1;                                                                             \
+      sy = ((tp) >> 1) - 1 + py;                                                               \
+      sx = ((tp) & 1) - 1 + px;                                                                \
+    } else {                                                                                   \
+      dt = (tp) / (KS * KS);                                                                   \
+      sy = ((tp) / KS) % KS - KS / 2;                                                          \
+      sx = (tp) % KS - KS / 2;                                                                 \
+    }                                                                                          \
+    need = (1 << (sy + 1)) | (8 << (sx + 1)) | (64 << dt);                                     \
+    delta = (int)((((long long)(dt - (KT - 1)) * (rows_in + 2) + sy) * W + sx) * XC * 2);      \
+  }
+  // prefetch cursor: step issued + PFD (held at the last step)
+  int ptap = 0, ppart = 0, pc = 0, pstep = 0;
+#define VAEP_ADVANCE(tp, pt, cc)                                                               \
+  if (++tp == TAPS) {                                                                          \
+    tp = 0;                                                                                    \
+    if (++pt == PARTS) {                                                                       \
+      pt = 0;                                                                                  \
+      cc += 64;                                                                                \
+    }                                                                                          \
+  }
+#pragma unroll
+  for (int i = 0; i < PFD; ++i)
+    if (pstep + 1 < nsteps) {
+      ++pstep;
+      VAEP_ADVANCE(ptap, ppart, pc);
+    }
+#define VAEP_SA(st) ((st) == 0 ? sA0 : (st) == 1 ? sA1 : sA2)
+#define VAEP_SB(st) ((st) == 0 ? sB0 : (st) == 1 ? sB1 : sB2)
+#define VAEP_ISSUE(st)                                                                         \
+  {                                                                                            \
+    {                                                                                          \
+      VAEP_TAP_GEO(itap, need, delta);                                                         \
+      _Pragma("unroll") for (int j = 0; j < NB; ++j)                                           \
+        bvo[j] = ((pmask[j] & need) == need) ? (unsigned)((int)pbase[j] + delta) : kPadOffset;  \
+    }                                                                                          \
+    const int aso = ((itap * WP + wpart(PARTS, ipart)) * C + ic) * 2;                          \
+    const int bso = (xpart(ipart) * C + ic) * 2;                                               \
+    _Pragma("unroll") for (int j = 0; j < NA; ++j)                                             \
+      dma16(j == 0, wrs, lds_addr(VAEP_SA(st)) + wrow + j * 4096, avo[j], aso);                 \
+    _Pragma("unroll") for (int j = 0; j < NB; ++j)                                             \
+      dma16(j == 0, xrs, lds_addr(VAEP_SB(st)) + wrow + j * 4096, bvo[j], bso);                 \
+    {                                                                                          \
+      VAEP_TAP_GEO(ptap, need, delta);                                                         \
+      const unsigned pbv = ((pf_mask & need) == need) ? (unsigned)((int)pf_base + delta) : kPadOffset; \
+      prefetch4(wrs, lds_addr((const unsigned short*)sPF), pf_avo,                             \
+                ((ptap * WP + wpart(PARTS, ppart)) * C + pc) * 2);                             \
+      prefetch4(xrs, lds_addr((const unsigned short*)sPF), pbv, (xpart(ppart) * C + pc) * 2);  \
+    }                                                                                          \
+    ++issued;                                                                                  \
+    VAEP_ADVANCE(itap, ipart, ic);                                                             \
+    if (pstep + 1 < nsteps) {                                                                  \
+      ++pstep;                                                                                 \
+      VAEP_ADVANCE(ptap, ppart, pc);                                                           \
+    }                                                                                          \
+  }
+
+  // matrix-core operand reads: row (block base + lane%32), logical chunk 2*kk + lane/32
+  const int fl = (lane & 7) ^ ((lane >> 3) & 1);
+  const int lr = (lane & 31) * 64;
+  int ko[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) ko[kk] = lr + (((2 * kk + (lane >> 5)) ^ fl) << 3);
+  const int wco = (wave >> 1) * (BM / 2);
+  const int wpx = (wave & 1) * 128;
+
+  // Step s computes from stage s % S and first issues step s + S - 1 into stage
+  // (s + S - 1) % S, which every wave finished reading before the barrier.  Loads complete
+  // in issue order; this thread's loads of step s have landed once at most the loads
+  // issued after them (the two prefetches of that step, and the next step's group when
+  // S is 3) are outstanding.  The barrier then publishes every thread's chunks.
+#define VAEP_STEP(cs, ns, si)                                                                    \
+  {                                                                                            \
+    if (S == 3 && (si) + 2 <= nsteps)                                                          \
+      __builtin_amdgcn_s_waitcnt(((NG + 2) & 15) | (((NG + 2) >> 4) << 14) | (7 << 4) | (15 << 8)); \
+    else                                                                                       \
+      __builtin_amdgcn_s_waitcnt(2 | (7 << 4) | (15 << 8));                                    \
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                            \
+    if (issued < nsteps) VAEP_ISSUE(ns);                                                       \
+    const unsigned short* A = VAEP_SA(cs);                                                     \
+    const unsigned short* B = VAEP_SB(cs);                                                     \
+    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                         \
+      bf16x8_t af[MI], bfr[NJ];                                                                \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i)                                           \
+        af[i] = *reinterpret_cast<const bf16x8_t*>(A + (wco + 32 * i) * 64 + ko[kk]);          \
+      _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                           \
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(B + (wpx + 32 * j) * 64 + ko[kk]);         \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i)                                           \
+        _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                         \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0); \
+    }                                                                                          \
+  }
+
+  // prologue: steps 0 .. S-2 into stages 0 .. S-2
+  VAEP_ISSUE(0);
+  if (S == 3 && issued < nsteps) VAEP_ISSUE(1);
+  // whole rounds of S steps, then the remainder (stage numbering restarts at 0)
+  const int nmain = nsteps - nsteps % S;
+  int s = 0;
+  for (; s < nmain; s += S) {
+    if (S == 2) {
+      VAEP_STEP(0, 1, s);
+      VAEP_STEP(1, 0, s + 1);
+    } else {
+      VAEP_STEP(0, 2, s);
+      VAEP_STEP(1, 0, s + 1);
+      VAEP_STEP(2, 1, s + 2);
+    }
+  }
+  if (s < nsteps) VAEP_STEP(0, S - 1, s);
+  if (S == 3 && s + 1 < nsteps) VAEP_STEP(1, 0, s + 1);
+#undef VAEP_STEP
+#undef VAEP_SA
+#undef VAEP_SB
+#undef VAEP_TAP_GEO
+#undef VAEP_ADVANCE
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // prefetches still in flight
+#undef VAEP_ISSUE
+#undef VAEP_SET_TAP
+
+  // Epilogue.  acc[i][j][v]: channel co0 + wco + 32i + 8(v/4) + 4(lane/32) + v%4, pixel
+  // tile*BN + wpx + 32j + lane%32 (source grid for sub-pixel convs).
+  const int half = a.cout;   // kModeBandSplit: lo parts start `cout` channels after the hi parts
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const long long p = (long long)tile * BN + wpx + 32 * j + (lane & 31);
+    if (p >= m_band) continue;
+    const int n = (int)(p / plane);
+    const int rem = (int)(p - (long long)n * plane);
+    int r = rem / W;
+    int c = rem - r * W;
+    if (SUB) {
+      r = 2 * r + py;
+      c = 2 * c + px;
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int co = co0 + wco + 32 * i + 8 * g + 4 * (lane >> 5);
+        if (co >= a.cout) continue;
+        const float4 bb = *reinterpret_cast<const float4*>(a.bias + co);
+        float v[4] = {acc[i][j][4 * g + 0] + bb.x, acc[i][j][4 * g + 1] + bb.y,
+                      acc[i][j][4 * g + 2] + bb.z, acc[i][j][4 * g + 3] + bb.w};
+        if (a.res) {
+          // residual: fp32 with `cout` channels in the output's band geometry
+          long long ro = band_offset(a.out, band, n, r, c);
+          if (MODE == kModeBandSplit) ro >>= 1;
+          const float4 rr = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.res) + ro + co);
+          v[0] += rr.x;
+          v[1] += rr.y;
+          v[2] += rr.z;
+          v[3] += rr.w;
+        }
+        store4<MODE>(a.out, a.y, half, band, n, r, c, co, v);
+      }
+    }
+  }
+}
+
+template <int KT, int KS, bool SUB, int PARTS, int MODE>
+hipError_t go_bm(const ConvArgs& a, int bm, hipStream_t s) {
+  const int ph = SUB ? 4 : 1;
+  const long long wgs = (long long)a.tiles_total * (a.cout_pad / bm) * ph;
+  if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (bm == 256)
+    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 256>), dim3((unsigned)wgs), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128>), dim3((unsigned)wgs), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int KT, int KS, bool SUB, int PARTS>
+hipError_t go_mode(const ConvArgs& a, int bm, hipStream_t s) {
+  if (a.mode == kModeBandSplit) return go_bm<KT, KS, SUB, PARTS, kModeBandSplit>(a, bm, s);
+  return go_bm<KT, KS, SUB, PARTS, kModeBand>(a, bm, s);
+}
+
+}  // namespace
+
+// Workgroups of 256 output channels when a layer still fills the 256 CUs with them.
+static int wide_bm(const ConvArgs& a, long long tiles) {
+  const int ph = a.sub ? 4 : 1;
+  return (a.cout_pad % 256 == 0 && tiles * (a.cout_pad / 256) * ph >= 512) ? 256 : 128;
+}
+
+static long long wide_tiles(const ConvArgs& a) {
+  long long t = 0;
+  for (int b = 0; b < a.in.nb; ++b)
+    t += ((long long)a.in.n_img * a.in.rows[b] * a.in.W + kWideTileM - 1) / kWideTileM;
+  return t;
+}
+
+bool conv_wide_fits(const ConvArgs& a) {
+  if (a.sub) return true;
+  if (a.x_f32 || a.x_split || a.ups) return false;
+  if (a.mode != kModeBand && a.mode != kModeBandSplit) return false;
+  if (a.cin % 64 != 0 || a.cout_pad % 128 != 0) return false;
+  const bool geo = (a.kt == 1 && (a.ks == 3 || a.ks == 1)) || (a.kt == 3 && a.ks == 3);
+  // With 128-channel tiles the 1-workgroup-per-CU kernel cannot hide its fp32 epilogue
+  // behind another workgroup's K loop; those layers stay on the 2-per-CU kernel.
+  return geo && wide_bm(a, wide_tiles(a)) == 256;
+}
+
+hipError_t launch_conv_wide(ConvArgs& a, hipStream_t s) {
+  if (a.cin % 64 != 0 || a.cout_pad % 128 != 0) return hipErrorInvalidValue;
+  // split operands feed the sub-pixel form only
+  if (a.sub != a.x_split || (a.sub && (a.kt != 1 || a.ks != 3))) return hipErrorInvalidValue;
+  if (a.in.C != (a.x_split ? 2 * a.cin : a.cin)) return hipErrorInvalidValue;
+  // buffer-resource addressing: the rows one tile reads and the weights stay below 2 GiB
+  for (int b = 0; b < a.in.nb; ++b)
+    if ((long long)a.kt * (a.in.rows[b] + 2) * a.in.W * a.in.C * 2 + 2LL * kWideTileM * a.in.C * 2 >=
+        (1LL << 31) - 4096)
+      return hipErrorInvalidValue;
+  const long long kw = (long long)a.kt * (a.sub ? 4 * 2 : a.ks * a.ks) * a.cin;
+  if ((long long)a.cout_pad * kw * 2 >= (1LL << 31)) return hipErrorInvalidValue;
+  // tiles over the compute pixels (the source grid for sub-pixel convs)
+  int t = 0;
+  for (int b = 0; b < a.in.nb; ++b) {
+    a.tile_start[b] = t;
+    const long long m = (long long)a.in.n_img * a.in.rows[b] * a.in.W;
+    t += (int)((m + kWideTileM - 1) / kWideTileM);
+  }
+  a.tile_start[a.in.nb] = t;
+  a.tiles_total = t;
+  if (t == 0) return hipSuccess;
+  const int bm = wide_bm(a, t);
+  if (a.sub) return go_mode<1, 3, true, 3>(a, bm, s);
+  if (a.kt == 1 && a.ks == 3) return go_mode<1, 3, false, 1>(a, bm, s);
+  if (a.kt == 1 && a.ks == 1) return go_mode<1, 1, false, 1>(a, bm, s);
+  if (a.kt == 3 && a.ks == 3) return go_mode<3, 3, false, 1>(a, bm, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace vaep

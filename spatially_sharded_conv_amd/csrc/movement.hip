@@ -76,6 +76,50 @@ __global__ void pack_weight_kernel(const T* src, int co, int ci, int taps, T* ds
   }
 }
 
+// Sub-pixel form of nearest-2x + 3x3 conv.  For output phase py (row parity), kernel row
+// dy reads source row offset floor((py + dy - 1) / 2), which is -1, 0, 0 for py = 0 and
+// 0, 0, 1 for py = 1; folded row tap a of phase py sums the kernel rows whose offset is
+// a - 1 + py (columns likewise).  The fp32 sum is stored as bf16 hi and lo parts.
+__global__ void fold_subpixel_kernel(const bf16* src, int co, int ci, bf16* dst, int co_pad) {
+  const long long total = 4LL * co_pad * 4 * ci;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int c = (int)(i % ci);
+    const int tap = (int)((i / ci) % 4);
+    const int o = (int)((i / (4LL * ci)) % co_pad);
+    const int ph = (int)(i / (4LL * ci * co_pad));
+    const int py = ph >> 1, px = ph & 1, ta = tap >> 1, tb = tap & 1;
+    float w = 0.f;
+    if (o < co) {
+      for (int dy = 0; dy < 3; ++dy) {
+        if (((py + dy - 1) >> 1) != ta - 1 + py) continue;
+        for (int dx = 0; dx < 3; ++dx) {
+          if (((px + dx - 1) >> 1) != tb - 1 + px) continue;
+          w += (float)src[(((long long)o * ci + c) * 3 + dy) * 3 + dx];
+        }
+      }
+    }
+    const bf16 hi = bf16(w);
+    const bf16 lo = bf16(w - (float)hi);
+    bf16* d = dst + ((((long long)ph * co_pad + o) * 4 + tap) * 2) * ci + c;
+    d[0] = hi;
+    d[ci] = lo;
+  }
+}
+
+// fp32 element -> bf16 hi at channel ch, lo at channel C + ch of a 2C-channel buffer.
+__global__ void split_kernel(const float* src, long long n, int C, bf16* dst) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (long long)gridDim.x * blockDim.x) {
+    const float v = src[i];
+    const long long pix = i / C;
+    const int ch = (int)(i - pix * C);
+    const bf16 hi = bf16(v);
+    dst[pix * 2 * C + ch] = hi;
+    dst[pix * 2 * C + C + ch] = bf16(v - (float)hi);
+  }
+}
+
 template <typename T>
 __global__ void to_f32_kernel(const T* src, int n, float* dst, int n_pad) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -140,6 +184,21 @@ hipError_t launch_pack_weight(const void* src, int co, int ci, int taps, void* d
   else
     hipLaunchKernelGGL(pack_weight_kernel<bf16>, dim3(grid_for(total)), dim3(256), 0, s,
                        (const bf16*)src, co, ci, taps, (bf16*)dst, co_pad, ci_pad);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold_subpixel_weight(const void* src, int co, int ci, void* dst, int co_pad,
+                                       hipStream_t s) {
+  const long long total = 4LL * co_pad * 4 * ci;
+  hipLaunchKernelGGL(fold_subpixel_kernel, dim3(grid_for(total)), dim3(256), 0, s, (const bf16*)src, co, ci,
+                     (bf16*)dst, co_pad);
+  return hipGetLastError();
+}
+
+hipError_t launch_split(const float* src, const BandLayout& L, void* dst, hipStream_t s) {
+  const long long n = layout_elems(L);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(split_kernel, dim3(grid_for(n)), dim3(256), 0, s, src, n, L.C, (bf16*)dst);
   return hipGetLastError();
 }
 

@@ -51,6 +51,8 @@ enum ConvMode : int {
   kModeQKV = 1,             // global token-major Q, K and transposed V
   kModeFinal = 2,           // NC[T]HW output, first `cout` channels
   kModeTimeInterleave = 3,  // causal temporal upsample frame layout, halo push
+  kModeBandSplit = 4,       // band-layout output stored as bf16 parts [hi (cout) | lo (cout)]
+                            // (+bias, +residual), halo push; the operand of a split-input conv
 };
 
 struct ConvArgs {
@@ -71,6 +73,10 @@ struct ConvArgs {
   int ups;              // nearest-2x fused into the load
   int mode;
   int x_f32;            // bf16 path: operand source stored as fp32 (rounded on load)
+  int x_split;          // bf16 path: operand source stored as bf16 [hi | lo] parts, channel
+                        // stride in.C = 2 * cin (written by a kModeBandSplit conv)
+  int sub;              // nearest-2x + 3x3 conv in sub-pixel form: w holds the phase-folded
+                        // weights of launch_fold_subpixel_weight; needs x_split
   int final_frames;     // kModeFinal: frames per sample of the output tensor
   int tiles_total;      // M tiles over all bands
   int tile_start[kMaxBands + 1];  // prefix of M tiles per band
@@ -81,6 +87,19 @@ hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s);
 // Pixel tile of the MFMA kernel along M and output-channel tile along N.
 constexpr int kConvTileM = 128;
 constexpr int kConvTileN = 128;
+// Pixel tile of the wide kernel (output-channel tile 128 or 256).
+constexpr int kWideTileM = 256;
+// Whether the wide kernel runs the conv described by `a` (bf16 path): K in steps of 64
+// channels, output channels a multiple of 128, band-layout epilogues.  Sub-pixel convs
+// always run there.
+bool conv_wide_fits(const ConvArgs& a);
+hipError_t launch_conv_wide(ConvArgs& a, hipStream_t s);
+// Phase-folded weights of a nearest-2x + 3x3 conv: src [co][ci][3][3] bf16 ->
+// dst [4 phases][co_pad][4 taps][2 parts (hi, lo)][ci] bf16; zero rows past co.
+hipError_t launch_fold_subpixel_weight(const void* src, int co, int ci, void* dst, int co_pad,
+                                       hipStream_t s);
+// fp32 band buffer (channels c) -> bf16 [hi | lo] band buffer (channels 2c), halo rows included.
+hipError_t launch_split(const float* src, const BandLayout& L, void* dst, hipStream_t s);
 
 // ------------------------------------------------------------------ norms
 // Local moments per (band, image, group): partial records of tiles, merged per band and

@@ -64,6 +64,30 @@ def test_conv3x3_step(gpu_lib, dtype, case):
     assert_close(got, ref, *ACC_TOL, what=f"conv3x3 {case}")
 
 
+def test_conv3x3_step_wide_tiles(gpu_lib):
+    # enough 256-pixel tiles for the 256-channel output tiles of the wide kernel (ragged
+    # rows, a one-row band, residual)
+    B, cin, cout, H, W, starts = 1, 64, 256, 130, 1030, (0, 40, 41, 130)
+    x = seeded((B, cin, H, W), 15, dtype="bf16")
+    w = seeded((cout, cin, 3, 3), 16, 1 / math.sqrt(cin * 9), dtype="bf16")
+    b = seeded((cout,), 17, 0.1, dtype="bf16")
+    r = seeded((B, cout, H, W), 18, dtype="f32")
+    ref = _conv_ref(x, w, b, False, r, "bf16")
+    got = vaep.step_conv(to_dev(x, "bf16"), to_dev(w, "bf16"), to_dev(b, "bf16"), starts, residual=r.cuda())
+    assert_close(got, ref, *ACC_TOL, what="conv3x3 wide tiles")
+
+
+def test_upsample_conv_from_fp32_wide_tiles(gpu_lib):
+    # sub-pixel upsample conv with 256-channel output tiles
+    x = seeded((1, 64, 130, 260), 27, dtype="f32")
+    w = seeded((256, 64, 3, 3), 28, 1 / math.sqrt(64 * 9), dtype="bf16")
+    b = seeded((256,), 29, 0.1, dtype="bf16")
+    ref = _conv_ref(x, w, b, False, None, "bf16", upsample=True, x_exact=True)
+    got = vaep.step_conv(x.cuda(), to_dev(w, "bf16"), to_dev(b, "bf16"), (0, 64, 65, 130), upsample=True)
+    assert got.shape == (1, 256, 260, 520)
+    assert_close(got, ref, *ACC_TOL, what="sub-pixel upsample conv, wide tiles")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_conv1x1_step(gpu_lib, dtype):
     x = seeded((2, 192, 7, 45), 21, dtype=dtype)
@@ -100,15 +124,28 @@ def test_upsample_conv_step(gpu_lib, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_causal_conv3d_step(gpu_lib, dtype):
-    x = seeded((1, 32, 4, 9, 11), 41, dtype=dtype)
-    w = seeded((64, 32, 3, 3, 3), 42, 1 / math.sqrt(32 * 27), dtype=dtype)
+@pytest.mark.parametrize("cin", [32, 64])
+def test_causal_conv3d_step(gpu_lib, dtype, cin):
+    x = seeded((1, cin, 4, 9, 11), 41, dtype=dtype)
+    w = seeded((64, cin, 3, 3, 3), 42, 1 / math.sqrt(cin * 27), dtype=dtype)
     b = seeded((64,), 43, 0.1, dtype=dtype)
     r = seeded((1, 64, 4, 9, 11), 44, dtype="f32")
     ref = _conv_ref(x, w, b, True, r, dtype)
     got = vaep.step_conv(to_dev(x, dtype), to_dev(w, dtype), to_dev(b, dtype), (0, 4, 9), causal=True,
                          residual=r.cuda())
     assert_close(got, ref, *ACC_TOL, what="causal conv3d")
+
+
+def test_causal_conv3d_step_wide_tiles(gpu_lib):
+    # causal 3x3x3 conv on 256-channel output tiles of the wide kernel
+    x = seeded((1, 64, 4, 130, 260), 45, dtype="bf16")
+    w = seeded((256, 64, 3, 3, 3), 46, 1 / math.sqrt(64 * 27), dtype="bf16")
+    b = seeded((256,), 47, 0.1, dtype="bf16")
+    r = seeded((1, 256, 4, 130, 260), 48, dtype="f32")
+    ref = _conv_ref(x, w, b, True, r, "bf16")
+    got = vaep.step_conv(to_dev(x, "bf16"), to_dev(w, "bf16"), to_dev(b, "bf16"), (0, 61, 62, 130), causal=True,
+                         residual=r.cuda())
+    assert_close(got, ref, *ACC_TOL, what="causal conv3d, wide tiles")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
