@@ -20,6 +20,7 @@ namespace vaep {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 namespace {
 
@@ -185,6 +186,204 @@ __global__ void __launch_bounds__(256) flash_bf16(const AttnArgs a) {
   }
 }
 
+// bf16 path, split-channel form (tokens a multiple of 8).  A workgroup owns 64 queries;
+// wave w owns channels [w*DS, (w+1)*DS) of both products (DS = d/4), so no K or V
+// element is read by two waves and both go straight from global memory into registers
+// (V of a tile loads while its S is formed, K of the next tile while its softmax and
+// P V run).  Per 32-key tile:
+//   1. each wave forms its partial S^T[key][q] = K[key][slice] Q^T[slice][q]
+//      (v_mfma_f32_32x32x16_bf16) and stores it to LDS;
+//   2. wave w sums the four partials for queries 16w .. 16w+15, runs the online softmax in
+//      fp32 (exp2 domain) and stores P (bf16) and the rescale factors;
+//   3. each wave accumulates O^T[slice][q] += V^T[slice][key] P^T[key][q].
+// The running max moves only when a row's tile max exceeds it by more than 8 (factor 256
+// in P); otherwise P is formed against the old max (still exact: numerator and
+// denominator use the same max), so the O rescale runs only on the rare tiles that move
+// a max.
+template <int DS>
+__global__ void __launch_bounds__(256, 1) attn_split(const AttnArgs a) {
+  constexpr int D = 4 * DS;
+  constexpr int KS = DS / 16;   // 16-channel steps of the S product
+  constexpr int CB = DS / 32;   // 32-channel blocks of O^T
+  constexpr int BK = 32;        // keys per tile
+  __shared__ __attribute__((aligned(16))) float sS[4][64][36];
+  __shared__ __attribute__((aligned(16))) unsigned short sP[64][40];
+  __shared__ float sAlpha[64];
+  __shared__ float sL[64];
+  __shared__ int sFlag[4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = band_of(a, blockIdx.x);
+  const int local = blockIdx.x - a.tile_start[b];
+  const int W = a.L.W;
+  const int nq = a.L.rows[b] * W;
+  const int qt_img = (nq + 63) / 64;
+  const int n = local / qt_img;
+  const int q0 = (local - n * qt_img) * 64;
+  const int tokens = a.tokens;
+  const long long tok0 = (long long)a.L.row0[b] * W;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int c0 = wave * DS;
+
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(a.q), 0, 0x7fffffff, 0x00020000);
+  const unsigned short* kbase = reinterpret_cast<const unsigned short*>(a.k) + (long long)n * tokens * D;
+  const unsigned short* vbase = reinterpret_cast<const unsigned short*>(a.vt) + (long long)n * D * tokens;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned short*>(kbase), 0, tokens * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned short*>(vbase), 0, tokens * D * 2, 0x00020000);
+
+  // Q^T fragments (B operand of S^T): query q0 + 32*qb + lane%32, channels c0 + 16*ks + 8*hi
+  bf16x8_t qf[2][KS];
+  {
+    const unsigned short* qbase = reinterpret_cast<const unsigned short*>(a.q) + (long long)n * tokens * D;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      int ql = q0 + 32 * qb + l32;
+      if (ql > nq - 1) ql = nq - 1;
+      const unsigned short* qr = qbase + (tok0 + ql) * D + c0 + 8 * hi;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = *reinterpret_cast<const bf16x8_t*>(qr + 16 * ks);
+    }
+  }
+  (void)qrs;
+
+  // K fragments (A operand of S^T): key k0 + lane%32 (clamped), channels c0 + 16*ks + 8*hi.
+  // V^T fragments (A operand of O^T): channel c0 + 32*cb + lane%32, keys k0 + 16*kk + 8*hi
+  // (clamped to the last 8 keys; those keys get P = 0).
+  bf16x8_t kf[KS], vf[CB][2];
+#define VAEP_LOAD_K(KF, k0)                                                                    \
+  {                                                                                            \
+    int kr = (k0) + l32;                                                                       \
+    if (kr > tokens - 1) kr = tokens - 1;                                                      \
+    _Pragma("unroll") for (int ks = 0; ks < KS; ++ks)                                          \
+      KF[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(             \
+          krs, (kr * D + c0 + 16 * ks + 8 * hi) * 2, 0, 0));                                   \
+  }
+#define VAEP_LOAD_V(VF, k0)                                                                    \
+  {                                                                                            \
+    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                         \
+      int kc = (k0) + 16 * kk + 8 * hi;                                                        \
+      if (kc > tokens - 8) kc = tokens - 8;                                                    \
+      _Pragma("unroll") for (int cb = 0; cb < CB; ++cb)                                        \
+        VF[cb][kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(       \
+            vrs, ((c0 + 32 * cb + l32) * tokens + kc) * 2, 0, 0));                             \
+    }                                                                                          \
+  }
+
+  f32x16_t oacc[CB][2];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[cb][qb][v] = 0.f;
+  // softmax rows of this lane: query 16*wave + lane/4, keys 8*(lane%4) .. +8 of a tile
+  const int qs = 16 * wave + (lane >> 2);
+  const int kq = (lane & 3) * 8;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = a.scale * 1.4426950408889634f;
+  const int ntiles = (tokens + BK - 1) / BK;
+
+#define VAEP_TILE(KF, VF, k0)                                                                  \
+  {                                                                                            \
+    VAEP_LOAD_V(VF, k0);                                                                       \
+    f32x16_t sacc[2];                                                                          \
+    _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                                         \
+      _Pragma("unroll") for (int v = 0; v < 16; ++v) sacc[qb][v] = 0.f;                        \
+      _Pragma("unroll") for (int ks = 0; ks < KS; ++ks)                                        \
+        sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(KF[ks], qf[qb][ks], sacc[qb], 0, 0, 0); \
+    }                                                                                          \
+    if ((k0) + BK < tokens) VAEP_LOAD_K(KF, (k0) + BK);                                        \
+    /* partial S^T: lane holds query 32qb + lane%32, keys 8g + 4hi + 0..3 */                   \
+    _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                                           \
+      _Pragma("unroll") for (int g = 0; g < 4; ++g)                                            \
+        *reinterpret_cast<f32x4_t*>(&sS[wave][32 * qb + l32][8 * g + 4 * hi]) =                \
+            f32x4_t{sacc[qb][4 * g], sacc[qb][4 * g + 1], sacc[qb][4 * g + 2], sacc[qb][4 * g + 3]}; \
+    __syncthreads();                                                                           \
+    {                                                                                          \
+      float sv[8];                                                                             \
+      _Pragma("unroll") for (int e = 0; e < 8; ++e) sv[e] = 0.f;                               \
+      _Pragma("unroll") for (int w = 0; w < 4; ++w) {                                          \
+        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(&sS[w][qs][kq]);                  \
+        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(&sS[w][qs][kq + 4]);              \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                        \
+          sv[e] += x0[e];                                                                      \
+          sv[4 + e] += x1[e];                                                                  \
+        }                                                                                      \
+      }                                                                                        \
+      float rmax = -INFINITY;                                                                  \
+      _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                          \
+        sv[e] = ((k0) + kq + e < tokens) ? sv[e] * sl2 : -INFINITY;                            \
+        rmax = fmaxf(rmax, sv[e]);                                                             \
+      }                                                                                        \
+      rmax = fmaxf(rmax, __shfl_xor(rmax, 1));                                                 \
+      rmax = fmaxf(rmax, __shfl_xor(rmax, 2));                                                 \
+      const bool need = rmax > m_run + 8.f;                                                    \
+      const float m_new = need ? rmax : m_run;                                                 \
+      const float alpha = need ? exp2f(m_run - m_new) : 1.f;                                   \
+      float rs = 0.f;                                                                          \
+      unsigned pk[4];                                                                          \
+      _Pragma("unroll") for (int e = 0; e < 8; e += 2) {                                       \
+        const float p0 = exp2f(sv[e] - m_new), p1 = exp2f(sv[e + 1] - m_new);                  \
+        rs += p0 + p1;                                                                         \
+        pk[e / 2] = (unsigned)f2bf(p0) | ((unsigned)f2bf(p1) << 16);                           \
+      }                                                                                        \
+      rs += __shfl_xor(rs, 1);                                                                 \
+      rs += __shfl_xor(rs, 2);                                                                 \
+      l_run = l_run * alpha + rs;                                                              \
+      m_run = m_new;                                                                           \
+      *reinterpret_cast<uint4*>(&sP[qs][kq]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);         \
+      if ((lane & 3) == 0) sAlpha[qs] = alpha;                                                 \
+      const bool anyw = __builtin_amdgcn_ballot_w64(need) != 0;                                \
+      if (lane == 0) sFlag[wave] = anyw ? 1 : 0;                                               \
+    }                                                                                          \
+    __syncthreads();                                                                           \
+    if (sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3]) {                                           \
+      _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                                       \
+        const float al = sAlpha[32 * qb + l32];                                                \
+        _Pragma("unroll") for (int cb = 0; cb < CB; ++cb) oacc[cb][qb] *= al;                  \
+      }                                                                                        \
+    }                                                                                          \
+    _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                                           \
+      _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                       \
+        const bf16x8_t pf = *reinterpret_cast<const bf16x8_t*>(&sP[32 * qb + l32][16 * kk + 8 * hi]); \
+        _Pragma("unroll") for (int cb = 0; cb < CB; ++cb)                                      \
+          oacc[cb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(VF[cb][kk], pf, oacc[cb][qb], 0, 0, 0); \
+      }                                                                                        \
+  }
+
+  VAEP_LOAD_K(kf, 0);
+  for (int t = 0; t < ntiles; ++t) VAEP_TILE(kf, vf, t * BK);
+#undef VAEP_TILE
+#undef VAEP_LOAD_K
+#undef VAEP_LOAD_V
+
+  if ((lane & 3) == 0) sL[qs] = l_run;
+  __syncthreads();
+  // O^T block (cb, qb): lane holds query 32qb + lane%32, channels c0 + 32cb + 8g + 4hi + 0..3
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int ql = q0 + 32 * qb + l32;
+    if (ql >= nq) continue;
+    const float inv = 1.f / sL[32 * qb + l32];
+    const int r = ql / W, c = ql - (ql / W) * W;
+    unsigned short* out = reinterpret_cast<unsigned short*>(a.o) + band_offset(a.L, b, n, r, c);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = c0 + 32 * cb + 8 * g + 4 * hi;
+        uint2 pk;
+        pk.x = (unsigned)f2bf(oacc[cb][qb][4 * g] * inv) | ((unsigned)f2bf(oacc[cb][qb][4 * g + 1] * inv) << 16);
+        pk.y = (unsigned)f2bf(oacc[cb][qb][4 * g + 2] * inv) | ((unsigned)f2bf(oacc[cb][qb][4 * g + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(out + d) = pk;
+      }
+  }
+}
+
 // fp32 path: one wave per query, keys in sequence with an online softmax; lanes split d.
 __global__ void __launch_bounds__(256) attn_f32(const AttnArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -239,7 +438,10 @@ __global__ void __launch_bounds__(256) attn_f32(const AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attention(AttnArgs& a, int dtype, hipStream_t s) {
-  const int per = dtype == VAEP_DTYPE_F32 ? 4 : kQ;
+  // split-channel kernel: 64 queries per workgroup, needs tokens % 8 == 0 (16-byte V^T rows)
+  const bool split = dtype != VAEP_DTYPE_F32 && a.tokens % 8 == 0 &&
+                     (long long)a.tokens * a.c * 2 < (1LL << 31);
+  const int per = dtype == VAEP_DTYPE_F32 ? 4 : (split ? 64 : kQ);
   int t = 0;
   for (int b = 0; b < a.L.nb; ++b) {
     a.tile_start[b] = t;
@@ -251,6 +453,16 @@ hipError_t launch_attention(AttnArgs& a, int dtype, hipStream_t s) {
   if (dtype == VAEP_DTYPE_F32) {
     if (a.c > 1024) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_f32, dim3(t), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  if (split) {
+    switch (a.c) {
+      case 128: hipLaunchKernelGGL(attn_split<32>, dim3(t), dim3(256), 0, s, a); break;
+      case 256: hipLaunchKernelGGL(attn_split<64>, dim3(t), dim3(256), 0, s, a); break;
+      case 384: hipLaunchKernelGGL(attn_split<96>, dim3(t), dim3(256), 0, s, a); break;
+      case 512: hipLaunchKernelGGL(attn_split<128>, dim3(t), dim3(256), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
   }
   switch (a.c) {

@@ -206,6 +206,8 @@ def _attn_ref(x, groups, g, be, wq, bq, wk, bk, wv, bv, wo, bo, dtype):
 @pytest.mark.parametrize("case", [
     ("bf16", 512, 32, (1, 8, 25), (0, 3, 8)),          # 200 tokens: ragged key and query tiles
     ("bf16", 384, 0, (2, 6, 10), (0, 1, 6)),           # per-frame span, RMSNorm pre-norm
+    ("bf16", 256, 32, (1, 16, 32), (0, 5, 16)),         # 512 tokens, 64-channel wave slices
+    ("bf16", 128, 32, (1, 12, 20), (0, 12)),            # 240 tokens, 32-channel wave slices
     ("f32", 64, 8, (1, 8, 8), (0, 3, 8)),
 ])
 def test_attention_step(gpu_lib, case):
