@@ -152,11 +152,8 @@ __global__ void __launch_bounds__(256, 1) conv_wide(const ConvArgs a) {
   constexpr int MI = BM / 64;                 // 32-row channel blocks per wave
   constexpr int NJ = 4;                       // 32-pixel blocks per wave
   constexpr int PH = SUB ? 4 : 1;
-  // one array per stage: the compiler's wait-count tracking of LDS-destination loads
-  // tells distinct arrays apart, so a read of one stage does not wait for the loads that
-  // are filling another
-  __shared__ __attribute__((aligned(1024))) unsigned short sA0[BM * 64], sA1[BM * 64], sA2[S == 3 ? BM * 64 : 8];
-  __shared__ __attribute__((aligned(1024))) unsigned short sB0[BN * 64], sB1[BN * 64], sB2[S == 3 ? BN * 64 : 8];
+  // S operand stages: A (BM x 64) then B (BN x 64) per stage; the epilogue reuses the space
+  __shared__ __attribute__((aligned(1024))) unsigned short smem[S * (BM + BN) * 64];
   __shared__ unsigned int sPF[64];             // prefetch landing words (never read)
   constexpr int PFD = 2;                       // prefetch target: PFD steps past the step issued
   constexpr int NG = NA + NB + 2;              // loads per thread per issued step
@@ -315,34 +312,44 @@ __global__ void __launch_bounds__(256, 1) conv_wide(const ConvArgs a) {
       ++pstep;
       VAEP_ADVANCE(ptap, ppart, pc);
     }
-#define VAEP_SA(st) ((st) == 0 ? sA0 : (st) == 1 ? sA1 : sA2)
-#define VAEP_SB(st) ((st) == 0 ? sB0 : (st) == 1 ? sB1 : sB2)
-#define VAEP_ISSUE(st)                                                                         \
+#define VAEP_SA(st) (smem + (st) * (BM * 64))
+#define VAEP_SB(st) (smem + S * (BM * 64) + (st) * (BN * 64))
+// The loads of one step go out in four parts, one before each group of MFMAs of the
+// current step, so that the wave never waits on a full load queue with the matrix cores
+// idle.  Part 0 also forms the tap's offsets; part 3 adds the prefetch and advances.
+#define VAEP_ISSUE_PART(st, q)                                                                 \
   {                                                                                            \
-    {                                                                                          \
+    if ((q) == 0) {                                                                            \
       VAEP_TAP_GEO(itap, need, delta);                                                         \
       _Pragma("unroll") for (int j = 0; j < NB; ++j)                                           \
         bvo[j] = ((pmask[j] & need) == need) ? (unsigned)((int)pbase[j] + delta) : kPadOffset;  \
     }                                                                                          \
     const int aso = ((itap * WP + wpart(PARTS, ipart)) * C + ic) * 2;                          \
     const int bso = (xpart(ipart) * C + ic) * 2;                                               \
-    _Pragma("unroll") for (int j = 0; j < NA; ++j)                                             \
-      dma16(j == 0, wrs, lds_addr(VAEP_SA(st)) + wrow + j * 4096, avo[j], aso);                 \
-    _Pragma("unroll") for (int j = 0; j < NB; ++j)                                             \
-      dma16(j == 0, xrs, lds_addr(VAEP_SB(st)) + wrow + j * 4096, bvo[j], bso);                 \
-    {                                                                                          \
+    _Pragma("unroll") for (int j = (q) * (NA / 4); j < ((q) + 1) * (NA / 4); ++j)              \
+      dma16(j == (q) * (NA / 4), wrs, lds_addr(VAEP_SA(st)) + wrow + j * 4096, avo[j], aso);    \
+    _Pragma("unroll") for (int j = (q) * (NB / 4); j < ((q) + 1) * (NB / 4); ++j)              \
+      dma16(j == (q) * (NB / 4), xrs, lds_addr(VAEP_SB(st)) + wrow + j * 4096, bvo[j], bso);    \
+    if ((q) == 3) {                                                                            \
       VAEP_TAP_GEO(ptap, need, delta);                                                         \
       const unsigned pbv = ((pf_mask & need) == need) ? (unsigned)((int)pf_base + delta) : kPadOffset; \
       prefetch4(wrs, lds_addr((const unsigned short*)sPF), pf_avo,                             \
                 ((ptap * WP + wpart(PARTS, ppart)) * C + pc) * 2);                             \
       prefetch4(xrs, lds_addr((const unsigned short*)sPF), pbv, (xpart(ppart) * C + pc) * 2);  \
+      ++issued;                                                                                \
+      VAEP_ADVANCE(itap, ipart, ic);                                                           \
+      if (pstep + 1 < nsteps) {                                                                \
+        ++pstep;                                                                               \
+        VAEP_ADVANCE(ptap, ppart, pc);                                                         \
+      }                                                                                        \
     }                                                                                          \
-    ++issued;                                                                                  \
-    VAEP_ADVANCE(itap, ipart, ic);                                                             \
-    if (pstep + 1 < nsteps) {                                                                  \
-      ++pstep;                                                                                 \
-      VAEP_ADVANCE(ptap, ppart, pc);                                                           \
-    }                                                                                          \
+  }
+#define VAEP_ISSUE(st)                                                                         \
+  {                                                                                            \
+    VAEP_ISSUE_PART(st, 0);                                                                    \
+    VAEP_ISSUE_PART(st, 1);                                                                    \
+    VAEP_ISSUE_PART(st, 2);                                                                    \
+    VAEP_ISSUE_PART(st, 3);                                                                    \
   }
 
   // matrix-core operand reads: row (block base + lane%32), logical chunk 2*kk + lane/32
@@ -366,18 +373,28 @@ __global__ void __launch_bounds__(256, 1) conv_wide(const ConvArgs a) {
     else                                                                                       \
       __builtin_amdgcn_s_waitcnt(2 | (7 << 4) | (15 << 8));                                    \
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                            \
-    if (issued < nsteps) VAEP_ISSUE(ns);                                                       \
+    const bool more = issued < nsteps;                                                         \
     const unsigned short* A = VAEP_SA(cs);                                                     \
     const unsigned short* B = VAEP_SB(cs);                                                     \
+    /* operand fragments double-buffered across the four 16-wide K slices: the reads of */    \
+    /* slice kk+1 are in flight while slice kk's MFMAs run */                                 \
+    bf16x8_t af[2][MI], bfr[2][NJ];                                                            \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i)                                             \
+      af[0][i] = *reinterpret_cast<const bf16x8_t*>(A + (wco + 32 * i) * 64 + ko[0]);          \
+    _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                             \
+      bfr[0][j] = *reinterpret_cast<const bf16x8_t*>(B + (wpx + 32 * j) * 64 + ko[0]);         \
     _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                         \
-      bf16x8_t af[MI], bfr[NJ];                                                                \
-      _Pragma("unroll") for (int i = 0; i < MI; ++i)                                           \
-        af[i] = *reinterpret_cast<const bf16x8_t*>(A + (wco + 32 * i) * 64 + ko[kk]);          \
-      _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                           \
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(B + (wpx + 32 * j) * 64 + ko[kk]);         \
+      const int cur = kk & 1;                                                                  \
+      if (kk < 3) {                                                                            \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i)                                         \
+          af[cur ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(A + (wco + 32 * i) * 64 + ko[kk + 1]); \
+        _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                         \
+          bfr[cur ^ 1][j] = *reinterpret_cast<const bf16x8_t*>(B + (wpx + 32 * j) * 64 + ko[kk + 1]); \
+      }                                                                                        \
+      if (more) VAEP_ISSUE_PART(ns, kk);                                                       \
       _Pragma("unroll") for (int i = 0; i < MI; ++i)                                           \
         _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                         \
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0); \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0); \
     }                                                                                          \
   }
 
@@ -404,6 +421,7 @@ __global__ void __launch_bounds__(256, 1) conv_wide(const ConvArgs a) {
 #undef VAEP_SB
 #undef VAEP_TAP_GEO
 #undef VAEP_ADVANCE
+#undef VAEP_ISSUE_PART
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // prefetches still in flight
 #undef VAEP_ISSUE
 #undef VAEP_SET_TAP
