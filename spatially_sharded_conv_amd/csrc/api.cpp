@@ -91,6 +91,12 @@ bool stage_sub(const vaep_config& c, int i) {
   return c.dtype == VAEP_DTYPE_BF16 && stage_ups(c, i) && !stage_time_ups(c, i) &&
          c.resnets_per_stage >= 1 && c.stage_channels[i] % 64 == 0;
 }
+// A sub-pixel upsample whose output feeds only GroupNorm/RMSNorm and a 1x1 shortcut (the
+// next stage changes the channel count) stores it as hi / lo halves: the shortcut is then
+// a plain bf16 conv over both halves.
+bool stage_up_split(const vaep_config& c, int i) {
+  return stage_sub(c, i) && i + 1 < c.n_stages && c.stage_channels[i + 1] != c.stage_channels[i];
+}
 
 // Canonical parameter list (names follow the decoder structure).
 std::vector<ParamDesc> param_list(const vaep_config& c) {
@@ -176,6 +182,7 @@ struct ConvW {
   float* b = nullptr;
   void* wsub = nullptr;   // phase-folded weights of a sub-pixel upsample conv (else NULL)
   int co = 0, ci = 0, co_pad = 0, ci_pad = 0, kt = 1, ks = 3;
+  int rep = 1;            // 2: input channels repeated for an operand stored as hi / lo halves
 };
 struct NormW {
   float* g = nullptr;
@@ -186,6 +193,7 @@ struct ResW {
   NormW n1, n2;
   ConvW c1, c2, sc;
   bool has_sc = false;
+  bool split_in = false;  // the block input arrives as bf16 hi / lo halves (norm1 and shortcut)
 };
 struct AttnW {
   NormW norm;
@@ -194,7 +202,8 @@ struct AttnW {
 struct StageW {
   std::vector<ResW> res;
   bool time_up = false, up = false;
-  bool sub = false;   // the last resnet writes a split stream and the upsample runs sub-pixel
+  bool sub = false;       // the last resnet writes a split stream and the upsample runs sub-pixel
+  bool up_split = false;  // the upsample writes its output as hi / lo halves for the next stage
   ConvW time_conv, up_conv;
 };
 
@@ -254,21 +263,23 @@ struct Builder {
     if (err == hipSuccess && e != hipSuccess) err = e;
   }
 
-  ConvW conv(const std::string& n, int co, int ci, int kt, int ks, int co_pad_to = 0) {
+  ConvW conv(const std::string& n, int co, int ci, int kt, int ks, int co_pad_to = 0, int rep = 1) {
     ConvW w;
     const bool bf = dtype == VAEP_DTYPE_BF16;
     w.co = co;
     w.ci = ci;
     w.kt = kt;
     w.ks = ks;
+    w.rep = rep;
     w.co_pad = bf ? round_up(co, kConvTileN) : co;
     if (co_pad_to) w.co_pad = co_pad_to;
-    w.ci_pad = bf ? round_up(ci, 32) : ci;
+    const int ci1 = bf ? round_up(ci, 32) : ci;
+    w.ci_pad = ci1 * rep;
     const int taps = kt * ks * ks;
     w.w = carve.take((size_t)w.co_pad * taps * w.ci_pad * dtype_bytes(dtype));
     w.b = (float*)carve.take((size_t)w.co_pad * sizeof(float));
     if (!dry) {
-      ok(launch_pack_weight(P(n + ".weight"), co, ci, taps, w.w, w.co_pad, w.ci_pad, dtype, st));
+      ok(launch_pack_weight(P(n + ".weight"), co, ci, taps, w.w, w.co_pad, ci1, dtype, st, rep));
       ok(launch_to_f32(P(n + ".bias"), co, w.b, w.co_pad, dtype, st));
     }
     return w;
@@ -284,7 +295,7 @@ struct Builder {
     }
     return w;
   }
-  ResW resnet(const std::string& p, int ci, int co) {
+  ResW resnet(const std::string& p, int ci, int co, bool split_in = false) {
     ResW r;
     const int kt = is_video(c) ? 3 : 1;
     r.n1 = norm(p + ".norm1", ci);
@@ -292,7 +303,8 @@ struct Builder {
     r.n2 = norm(p + ".norm2", co);
     r.c2 = conv(p + ".conv2", co, co, kt, 3);
     r.has_sc = ci != co;
-    if (r.has_sc) r.sc = conv(p + ".shortcut", co, ci, 1, 1);
+    r.split_in = split_in && r.has_sc;
+    if (r.has_sc) r.sc = conv(p + ".shortcut", co, ci, 1, 1, 0, r.split_in ? 2 : 1);
     return r;
   }
   AttnW attention(int ch) {
@@ -334,7 +346,8 @@ struct Builder {
       StageW s;
       const int co = c.stage_channels[i];
       for (int j = 0; j < c.resnets_per_stage; ++j) {
-        s.res.push_back(resnet("up" + std::to_string(i) + ".res" + std::to_string(j), prev, co));
+        const bool split_in = j == 0 && i > 0 && stage_up_split(c, i - 1);
+        s.res.push_back(resnet("up" + std::to_string(i) + ".res" + std::to_string(j), prev, co, split_in));
         prev = co;
       }
       s.time_up = stage_time_ups(c, i);
@@ -342,6 +355,7 @@ struct Builder {
       s.up = stage_ups(c, i);
       if (s.up) s.up_conv = conv("up" + std::to_string(i) + ".upsample", co, co, 1, 3);
       s.sub = stage_sub(c, i);
+      s.up_split = stage_up_split(c, i);
       if (s.sub) {
         ConvW& u = s.up_conv;
         u.wsub = carve.take((size_t)4 * u.co_pad * 4 * 2 * u.ci_pad * 2);
@@ -472,7 +486,7 @@ struct Exec {
       pe.mode = mode;
       pe.pixels = m;
       pe.flops = 2.0 * (double)m * w.co * (double)k;
-      const double in_b = (double)Lin.n_img * Lin.H * Lin.W * w.ci * (xk == kXOp ? eb() : 4.0);
+      const double in_b = (double)Lin.n_img * Lin.H * Lin.W * w.ci * (xk == kXOp && w.rep == 1 ? eb() : 4.0);
       const double out_elem = mode == kModeQKV ? (double)eb() : 4.0;
       pe.bytes = in_b + (double)w.co * k * eb() + (double)m * w.co * out_elem + (res ? (double)m * w.co * 4 : 0.0);
       rec_begin(pe);
@@ -484,7 +498,9 @@ struct Exec {
     return VAEP_OK;
   }
 
-  int norm(const NormW& w, const void* x, const BandLayout& L, void* y, int act, float* merged_out = nullptr) {
+  // x_split: x holds bf16 hi / lo halves of the fp32 input (L describes the logical tensor)
+  int norm(const NormW& w, const void* x, const BandLayout& L, void* y, int act, float* merged_out = nullptr,
+           bool x_split = false) {
     need_act(L, 4);
     // statistics tiles never straddle a row any band table of this decode can cut at
     const int slab_rows = base_rows > 0 ? L.H / base_rows : 1;
@@ -494,6 +510,7 @@ struct Exec {
     NormArgs a;
     std::memset(&a, 0, sizeof(a));
     a.x = x;
+    a.x_split = x_split ? 1 : 0;
     a.y = y;
     a.L = L;
     a.groups = groups;
@@ -564,19 +581,22 @@ void others(int cur, int* o) {
 
 // split_out: store the block output as bf16 hi/lo parts (layout with 2x the channels)
 // for a following split-input conv, instead of fp32.
+// If r.split_in, L arrives as the hi / lo layout (2 x the block's input channels).
 int resnet(Exec& E, const ResW& r, int& cur, BandLayout& L, bool split_out = false) {
   int o[3];
   others(cur, o);
-  const BandLayout Lx = L;
+  const BandLayout Lx = r.split_in ? reshaped(L, L.C / 2, L.n_img, L.frames) : L;
   const BandLayout Lh = reshaped(L, r.c1.co, L.n_img, L.frames);
   const BandLayout Ly = split_out ? reshaped(L, 2 * r.c1.co, L.n_img, L.frames) : Lh;
   int rc;
-  if ((rc = E.norm(r.n1, E.act[cur], Lx, E.act[o[0]], 1))) return rc;
+  if ((rc = E.norm(r.n1, E.act[cur], Lx, E.act[o[0]], 1, nullptr, r.split_in))) return rc;
   if ((rc = E.conv(r.c1, E.act[o[0]], Lx, kXOp, E.act[o[1]], Lh, kModeBand, nullptr, 0))) return rc;
   if ((rc = E.norm(r.n2, E.act[o[1]], Lh, E.act[o[0]], 1))) return rc;
   const void* res = E.act[cur];
   if (r.has_sc) {
-    if ((rc = E.conv(r.sc, E.act[cur], Lx, kXF32, E.act[o[2]], Lh, kModeBand, nullptr, 0))) return rc;
+    // a split input is a bf16 operand over both halves (weights repeated)
+    if ((rc = E.conv(r.sc, E.act[cur], L, r.split_in ? kXOp : kXF32, E.act[o[2]], Lh, kModeBand, nullptr, 0)))
+      return rc;
     res = E.act[o[2]];
   }
   if ((rc = E.conv(r.c2, E.act[o[0]], Lh, kXOp, E.act[o[1]], Ly, split_out ? kModeBandSplit : kModeBand, res, 0)))
@@ -637,8 +657,9 @@ int walk(Exec& E, const void* latent, int B, int T, int W, const int* rows, int 
     if (s.up) {
       int o[3];
       others(cur, o);
-      const BandLayout Lu = upsampled(L, s.up_conv.co);
-      if ((rc = E.conv(s.up_conv, E.act[cur], L, s.sub ? kXSplit : kXF32, E.act[o[0]], Lu, kModeBand, nullptr, 1)))
+      const BandLayout Lu = upsampled(L, (s.up_split ? 2 : 1) * s.up_conv.co);
+      if ((rc = E.conv(s.up_conv, E.act[cur], L, s.sub ? kXSplit : kXF32, E.act[o[0]], Lu,
+                       s.up_split ? kModeBandSplit : kModeBand, nullptr, 1)))
         return rc;
       cur = o[0];
       L = Lu;

@@ -138,6 +138,81 @@ __device__ __forceinline__ void store4(const BandLayout& L, void* y, int half, i
   }
 }
 
+// Split-output epilogue.  Lanes l and l+32 hold alternate 4-channel groups of one pixel;
+// v_permlane32_swap pairs them up so that each lane owns 8 consecutive channels and
+// stores their hi and lo parts as one 16-byte store each.
+template <bool SUB, int MI, int NJ>
+__device__ __forceinline__ void split_epilogue(const ConvArgs& a, const f32x16_t (&acc)[MI][NJ], int band,
+                                               int tile, int plane, long long m_band, int W, int py, int px,
+                                               int co0, int wco, int wpx, int lane) {
+  const int hi = lane >> 5;
+  const int half = a.cout;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const long long p = (long long)tile * kWideTileM + wpx + 32 * j + (lane & 31);
+    const bool pv = p < m_band;
+    long long o = 0, ho = 0;
+    bool halo = false;
+    if (pv) {
+      const int n = (int)(p / plane);
+      const int rem = (int)(p - (long long)n * plane);
+      int r = rem / W;
+      int c = rem - r * W;
+      if (SUB) {
+        r = 2 * r + py;
+        c = 2 * c + px;
+      }
+      o = band_offset(a.out, band, n, r, c);
+      const bool up = r == 0 && band > 0, dn = r == a.out.rows[band] - 1 && band + 1 < a.out.nb;
+      halo = up || dn;
+      ho = up ? band_offset(a.out, band - 1, n, a.out.rows[band - 1], c) : (dn ? band_offset(a.out, band + 1, n, -1, c) : 0);
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][j][8 * m + e]),
+                                                           __float_as_uint(acc[i][j][8 * m + 4 + e]), false, false);
+          v[e] = __uint_as_float(r2[0]);
+          v[4 + e] = __uint_as_float(r2[1]);
+        }
+        const int co = co0 + wco + 32 * i + 8 * (2 * m + hi);
+        if (!pv || co >= a.cout) continue;
+        const float4 b0 = *reinterpret_cast<const float4*>(a.bias + co);
+        const float4 b1 = *reinterpret_cast<const float4*>(a.bias + co + 4);
+        v[0] += b0.x; v[1] += b0.y; v[2] += b0.z; v[3] += b0.w;
+        v[4] += b1.x; v[5] += b1.y; v[6] += b1.z; v[7] += b1.w;
+        if (a.res) {
+          // residual: fp32 with `cout` channels in the output's band geometry
+          const float* rp = reinterpret_cast<const float*>(a.res) + (o >> 1) + co;
+          const float4 r0 = *reinterpret_cast<const float4*>(rp);
+          const float4 r1 = *reinterpret_cast<const float4*>(rp + 4);
+          v[0] += r0.x; v[1] += r0.y; v[2] += r0.z; v[3] += r0.w;
+          v[4] += r1.x; v[5] += r1.y; v[6] += r1.z; v[7] += r1.w;
+        }
+        unsigned hw[4], lw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const unsigned short h0 = f2bf(v[2 * e]), h1 = f2bf(v[2 * e + 1]);
+          const unsigned short l0 = f2bf(v[2 * e] - bf2f(h0)), l1 = f2bf(v[2 * e + 1] - bf2f(h1));
+          hw[e] = (unsigned)h0 | ((unsigned)h1 << 16);
+          lw[e] = (unsigned)l0 | ((unsigned)l1 << 16);
+        }
+        unsigned short* y = reinterpret_cast<unsigned short*>(a.y);
+        *reinterpret_cast<uint4*>(y + o + co) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(y + o + half + co) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        if (halo) {
+          *reinterpret_cast<uint4*>(y + ho + co) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+          *reinterpret_cast<uint4*>(y + ho + half + co) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        }
+      }
+    }
+  }
+}
+
 // Part p of a tap: weight part (0 = w or w_hi, 1 = w_lo) and operand part (0 = x or x_hi, 1 = x_lo).
 __device__ __forceinline__ constexpr int wpart(int parts, int p) { return parts == 3 && p == 2 ? 1 : 0; }
 __device__ __forceinline__ constexpr int xpart(int p) { return p == 1 ? 1 : 0; }
@@ -429,6 +504,10 @@ __global__ void __launch_bounds__(256, 1) conv_wide(const ConvArgs a) {
   // Epilogue.  acc[i][j][v]: channel co0 + wco + 32i + 8(v/4) + 4(lane/32) + v%4, pixel
   // tile*BN + wpx + 32j + lane%32 (source grid for sub-pixel convs).
   const int half = a.cout;   // kModeBandSplit: lo parts start `cout` channels after the hi parts
+  if (MODE == kModeBandSplit) {
+    split_epilogue<SUB, MI, NJ>(a, acc, band, tile, plane, m_band, W, py, px, co0, wco, wpx, lane);
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const long long p = (long long)tile * BN + wpx + 32 * j + (lane & 31);

@@ -63,13 +63,16 @@ __global__ void copy_frame0_kernel(const T* src, const BandLayout Ls, T* dst, co
 
 template <typename T>
 __global__ void pack_weight_kernel(const T* src, int co, int ci, int taps, T* dst, int co_pad,
-                                   int ci_pad) {
-  const long long total = (long long)co_pad * taps * ci_pad;
+                                   int ci_pad, int rep) {
+  // rep copies of the ci_pad input channels per tap (rep = 2: one per bf16 part of a
+  // split operand)
+  const int row = ci_pad * rep;
+  const long long total = (long long)co_pad * taps * row;
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (long long)gridDim.x * blockDim.x) {
-    const int c = (int)(i % ci_pad);
-    const int t = (int)((i / ci_pad) % taps);
-    const int o = (int)(i / ((long long)ci_pad * taps));
+    const int c = (int)(i % row) % ci_pad;
+    const int t = (int)((i / row) % taps);
+    const int o = (int)(i / ((long long)row * taps));
     T v = T(0.f);
     if (o < co && c < ci) v = src[((long long)o * ci + c) * taps + t];
     dst[i] = v;
@@ -176,14 +179,14 @@ hipError_t launch_copy_frame0(const void* src, const BandLayout& Ls, void* dst, 
 }
 
 hipError_t launch_pack_weight(const void* src, int co, int ci, int taps, void* dst, int co_pad,
-                              int ci_pad, int dtype, hipStream_t s) {
-  const long long total = (long long)co_pad * taps * ci_pad;
+                              int ci_pad, int dtype, hipStream_t s, int rep) {
+  const long long total = (long long)co_pad * taps * ci_pad * rep;
   if (dtype == VAEP_DTYPE_F32)
     hipLaunchKernelGGL(pack_weight_kernel<float>, dim3(grid_for(total)), dim3(256), 0, s,
-                       (const float*)src, co, ci, taps, (float*)dst, co_pad, ci_pad);
+                       (const float*)src, co, ci, taps, (float*)dst, co_pad, ci_pad, rep);
   else
     hipLaunchKernelGGL(pack_weight_kernel<bf16>, dim3(grid_for(total)), dim3(256), 0, s,
-                       (const bf16*)src, co, ci, taps, (bf16*)dst, co_pad, ci_pad);
+                       (const bf16*)src, co, ci, taps, (bf16*)dst, co_pad, ci_pad, rep);
   return hipGetLastError();
 }
 

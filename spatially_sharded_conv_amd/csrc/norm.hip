@@ -31,6 +31,31 @@ __device__ __forceinline__ void load4(const float* p, float* v) {
   const float4 q = *reinterpret_cast<const float4*>(p);
   v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
 }
+__device__ __forceinline__ float bf_at(unsigned w, int hi) { return __uint_as_float(hi ? (w & 0xffff0000u) : (w << 16)); }
+
+// Input element access.  `pix` is the element offset of a pixel's channel 0 in the
+// C-channel layout.  XS: the buffer holds bf16 hi / lo halves of the fp32 values (2C
+// channels per pixel, written by a split-output conv); x = hi + lo is exact in fp32.
+template <bool XS>
+__device__ __forceinline__ void loadx4(const void* x, long long pix, int C, int ch, float* v) {
+  if (!XS) {
+    load4(reinterpret_cast<const float*>(x) + pix + ch, v);
+  } else {
+    const unsigned short* s = reinterpret_cast<const unsigned short*>(x) + 2 * pix + ch;
+    const uint2 h = *reinterpret_cast<const uint2*>(s);
+    const uint2 l = *reinterpret_cast<const uint2*>(s + C);
+    v[0] = bf_at(h.x, 0) + bf_at(l.x, 0);
+    v[1] = bf_at(h.x, 1) + bf_at(l.x, 1);
+    v[2] = bf_at(h.y, 0) + bf_at(l.y, 0);
+    v[3] = bf_at(h.y, 1) + bf_at(l.y, 1);
+  }
+}
+template <bool XS>
+__device__ __forceinline__ float loadx1(const void* x, long long pix, int C, int ch) {
+  if (!XS) return reinterpret_cast<const float*>(x)[pix + ch];
+  const unsigned short* s = reinterpret_cast<const unsigned short*>(x) + 2 * pix + ch;
+  return __uint_as_float((unsigned)s[0] << 16) + __uint_as_float((unsigned)s[C] << 16);
+}
 
 template <typename T> struct Out;
 template <> struct Out<float> {
@@ -68,6 +93,7 @@ __device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); 
 // the tile's pixels accumulating sums shifted by the tile's first pixel (fp32 over 4
 // pixels, then fp64); the block then reduces per group in fp64.  The tiling is fixed,
 // so the result does not depend on the band table.
+template <bool XS>
 __global__ void __launch_bounds__(kThreads) gn_stats(const NormArgs a) {
   __shared__ double r1[kThreads * V];
   __shared__ double r2[kThreads * V];
@@ -90,10 +116,9 @@ __global__ void __launch_bounds__(kThreads) gn_stats(const NormArgs a) {
   const int tid = threadIdx.x;
   const int slot = tid % S, pl = tid / S;
   const bool active = pl < PL;
-  const float* tile_x = reinterpret_cast<const float*>(a.x) + row_offset(L, b, n, g0 - L.row0[b]) + p0 * C;
-  const float* base = tile_x + (long long)slot * V;
+  const long long tile_x = row_offset(L, b, n, g0 - L.row0[b]) + p0 * C;   // pixel offset
   // per-channel shift: the tile's first pixel
-  for (int c = tid; c < C; c += kThreads) shift[c] = tile_x[c];
+  for (int c = tid; c < C; c += kThreads) shift[c] = loadx1<XS>(a.x, tile_x, C, c);
   __syncthreads();
   float k[V];
 #pragma unroll
@@ -111,7 +136,7 @@ __global__ void __launch_bounds__(kThreads) gn_stats(const NormArgs a) {
         const long long q = p + (long long)u * PL;
         if (q < tp) {
           float x[V];
-          load4(base + q * C, x);
+          loadx4<XS>(a.x, tile_x + q * C, C, slot * V, x);
 #pragma unroll
           for (int e = 0; e < V; ++e) {
             const float d = x[e] - k[e];
@@ -261,7 +286,7 @@ __global__ void __launch_bounds__(kThreads) gn_merge(const NormArgs a, float* co
 // written into the neighbours' halo slots.  Workgroup = a run of kApplyPix pixels of one
 // (band, image); thread = fixed channel slot, pixels strided by the pixel lanes.
 constexpr int kApplyPix = 128;
-template <typename TO>
+template <typename TO, bool XS>
 __global__ void __launch_bounds__(kThreads) gn_apply(const NormArgs a, const float* coef) {
   const BandLayout& L = a.L;
   const int C = L.C, S = C / V, PL = kThreads / S;
@@ -275,7 +300,7 @@ __global__ void __launch_bounds__(kThreads) gn_apply(const NormArgs a, const flo
   const int tid = threadIdx.x;
   const int slot = tid % S, pl = tid / S;
   if (pl >= PL) return;
-  const float* X = reinterpret_cast<const float*>(a.x) + row_offset(L, b, n, 0) + slot * V;
+  const long long xrow = row_offset(L, b, n, 0);
   TO* Y = reinterpret_cast<TO*>(a.y);
   const long long ybase = row_offset(L, b, n, 0) + slot * V;
   float sc[V], sh[V];
@@ -292,7 +317,7 @@ __global__ void __launch_bounds__(kThreads) gn_apply(const NormArgs a, const flo
     const long long p = p0 + pl + (long long)k * PL;
     if (p >= p0 + kApplyPix || p >= npix) break;
     float x[V];
-    load4(X + p * C, x);
+    loadx4<XS>(a.x, xrow + p * C, C, slot * V, x);
 #pragma unroll
     for (int e = 0; e < V; ++e) {
       const float y = x[e] * sc[e] + sh[e];
@@ -305,7 +330,7 @@ __global__ void __launch_bounds__(kThreads) gn_apply(const NormArgs a, const flo
 }
 
 // Channel RMSNorm: y_c = gamma_c x_c / sqrt(mean_c x^2 + eps) (+SiLU), per pixel.
-template <typename TO>
+template <typename TO, bool XS>
 __global__ void __launch_bounds__(kThreads) rms_apply(const NormArgs a) {
   __shared__ float part[kThreads];
   __shared__ float rs[kThreads];
@@ -314,7 +339,6 @@ __global__ void __launch_bounds__(kThreads) rms_apply(const NormArgs a) {
   const int tid = threadIdx.x;
   const int slot = tid % S, px = tid / S;
   const long long ptotal = a.item_start[L.nb];
-  const float* X = reinterpret_cast<const float*>(a.x);
   TO* Y = reinterpret_cast<TO*>(a.y);
   for (long long base = (long long)blockIdx.x * PX; base < ptotal; base += (long long)gridDim.x * PX) {
     const long long gp = base + px;
@@ -332,7 +356,7 @@ __global__ void __launch_bounds__(kThreads) rms_apply(const NormArgs a) {
       r = (int)(rem / L.W);
       c = (int)(rem - (long long)r * L.W);
       off = row_offset(L, b, n, r) + (long long)c * C + slot * V;
-      load4(X + off, x);
+      loadx4<XS>(a.x, off - slot * V, C, slot * V, x);
 #pragma unroll
       for (int e = 0; e < V; ++e) ss += x[e] * x[e];
     }
@@ -430,7 +454,10 @@ hipError_t launch_groupnorm(NormArgs& a, int dtype, hipStream_t s) {
   a.band_moments = coef + 2LL * L.n_img * L.C;
   a.stats = a.band_moments + 3LL * L.nb * L.n_img * a.groups;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(gn_stats, dim3(blocks), dim3(kThreads), 0, s, a);
+  if (a.x_split)
+    hipLaunchKernelGGL(gn_stats<true>, dim3(blocks), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(gn_stats<false>, dim3(blocks), dim3(kThreads), 0, s, a);
   hipLaunchKernelGGL(gn_merge, dim3(L.n_img * a.groups), dim3(kThreads), 0, s, a, coef);
   long long nblk = 0;   // apply workgroups: runs of kApplyPix pixels per (band, image)
   for (int b = 0; b < L.nb; ++b) {
@@ -439,10 +466,14 @@ hipError_t launch_groupnorm(NormArgs& a, int dtype, hipStream_t s) {
   }
   a.item_start[L.nb] = nblk;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (dtype == VAEP_DTYPE_F32)
-    hipLaunchKernelGGL(gn_apply<float>, dim3((int)nblk), dim3(kThreads), 0, s, a, coef);
+  if (dtype == VAEP_DTYPE_F32 && !a.x_split)
+    hipLaunchKernelGGL((gn_apply<float, false>), dim3((int)nblk), dim3(kThreads), 0, s, a, coef);
+  else if (dtype == VAEP_DTYPE_F32)
+    return hipErrorInvalidValue;   // split inputs exist on the bf16 path only
+  else if (a.x_split)
+    hipLaunchKernelGGL((gn_apply<bf16, true>), dim3((int)nblk), dim3(kThreads), 0, s, a, coef);
   else
-    hipLaunchKernelGGL(gn_apply<bf16>, dim3((int)nblk), dim3(kThreads), 0, s, a, coef);
+    hipLaunchKernelGGL((gn_apply<bf16, false>), dim3((int)nblk), dim3(kThreads), 0, s, a, coef);
   return hipGetLastError();
 }
 
@@ -459,10 +490,14 @@ hipError_t launch_rmsnorm(NormArgs& a, int dtype, hipStream_t s) {
   long long nblk = (pt + PX - 1) / PX;
   if (nblk > 65536) nblk = 65536;
   if (nblk == 0) return hipSuccess;
-  if (dtype == VAEP_DTYPE_F32)
-    hipLaunchKernelGGL(rms_apply<float>, dim3((int)nblk), dim3(kThreads), 0, s, a);
+  if (dtype == VAEP_DTYPE_F32 && !a.x_split)
+    hipLaunchKernelGGL((rms_apply<float, false>), dim3((int)nblk), dim3(kThreads), 0, s, a);
+  else if (dtype == VAEP_DTYPE_F32)
+    return hipErrorInvalidValue;
+  else if (a.x_split)
+    hipLaunchKernelGGL((rms_apply<bf16, true>), dim3((int)nblk), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(rms_apply<bf16>, dim3((int)nblk), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((rms_apply<bf16, false>), dim3((int)nblk), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

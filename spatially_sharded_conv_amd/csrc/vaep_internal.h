@@ -105,7 +105,9 @@ hipError_t launch_split(const float* src, const BandLayout& L, void* dst, hipStr
 // Local moments per (band, image, group): partial records of tiles, merged per band and
 // then across bands with the element-count-weighted merge.
 struct NormArgs {
-  const void* x;         // fp32 input (conv outputs are fp32 in every configuration)
+  const void* x;         // fp32 input (conv outputs are fp32 in every configuration), or
+                         // with x_split its bf16 hi / lo halves (2C channels per pixel)
+  int x_split;
   void* y;               // output in the operand dtype
   BandLayout L;
   int groups;
@@ -163,9 +165,10 @@ hipError_t launch_unpack(const void* src, const BandLayout& L, void* dst, int c_
 // halo rows included.
 hipError_t launch_copy_frame0(const void* src, const BandLayout& Ls, void* dst,
                               const BandLayout& Ld, int dtype, hipStream_t s);
-// Conv weight [co][ci][taps] (dtype) -> [co_pad][taps][ci_pad] (dtype), zero padded.
+// Conv weight [co][ci][taps] (dtype) -> [co_pad][taps][rep * ci_pad] (dtype), zero padded;
+// rep = 2 repeats the input channels for an operand stored as bf16 hi / lo halves.
 hipError_t launch_pack_weight(const void* src, int co, int ci, int taps, void* dst, int co_pad,
-                              int ci_pad, int dtype, hipStream_t s);
+                              int ci_pad, int dtype, hipStream_t s, int rep = 1);
 // Any-dtype vector -> fp32 vector of n_pad entries (zero padded); src may be NULL (zeros).
 hipError_t launch_to_f32(const void* src, int n, float* dst, int n_pad, int dtype, hipStream_t s);
 
