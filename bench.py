@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-latent", type=int, default=48,
                     help="latent side of the oracle's bounded sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                    help="only run a device-to-device copy of MB MiB (reference dispatch for HBM counters)")
     return ap.parse_args()
 
 
@@ -54,11 +56,18 @@ def summarise(recs, steps):
 
     for r in recs:
         if r["step"] == L.STEP_CONV:
-            k = r["kt"] * r["ks"] * r["ks"] * r["cin"]
-            # MFMA-bound convolutions: spatial 3x3 (x3) with K >= 1152 and >= 96 outputs;
-            # conv_in, conv_out, 1x1 projections and time convs are reported apart
-            dense = r["ks"] == 3 and k >= 1152 and r["cout"] >= 96 and r["mode"] == 0
-            add("conv_mfma" if dense else "conv_other", r)
+            # the roofline kernel: the wide kernel's plain 3x3 (x3) form with 256-channel
+            # tiles and fp32 band output (one template instance of conv_wide); other wide
+            # launches (sub-pixel upsample, split output), the 128x128-tile kernel and the
+            # narrow conv_out are reported apart
+            if r["kernel"] == L.KERNEL_CONV_WIDE256 and r["ks"] == 3 and r["ups"] == 0 and r["mode"] == 0:
+                add("conv_wide_3x3", r)
+            elif r["kernel"] in (L.KERNEL_CONV_WIDE256, L.KERNEL_CONV_WIDE128):
+                add("conv_wide_other", r)
+            elif r["kernel"] == L.KERNEL_CONV_TILE128:
+                add("conv_tile128", r)
+            else:
+                add("conv_other", r)
         elif r["step"] == L.STEP_GROUPNORM:
             add("groupnorm", r)
         elif r["step"] == L.STEP_RMSNORM:
@@ -75,6 +84,22 @@ def summarise(recs, steps):
         d["gbs"] = d["bytes"] / (d["ms"] * 1e-3) / 1e9 if d["ms"] else 0.0
         d["avg_launch_ms"] = d["ms"] / d["launches"]
     return out
+
+
+def measured_traffic():
+    """HBM bytes per launch of the roofline kernel from the committed rocprofv3 counter summary,
+    if the kernel source is still the one the counters were taken on (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "conv_wide_3x3_1024_hbm_traffic.md")
+    src = os.path.join(ROOT, "spatially_sharded_conv_amd", "csrc", "conv_wide.hip")
+    try:
+        fields = dict(l.split(": ", 1) for l in open(path).read().splitlines() if ": " in l and " " not in l.split(": ", 1)[0])
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if fields.get("conv_wide_source_sha256", "").strip() != sha:
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(cfg_id, side):
@@ -108,6 +133,15 @@ def main():
     from synth import make_latent, make_params, preset
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
+        return
     cfg = preset(args.config)
     params = make_params(cfg)
     lc = vaep.make_config(cfg.family, cfg.dtype, cfg.z_channels, cfg.stage_channels,
@@ -153,17 +187,18 @@ def main():
     recs = vaep.profile_end(dec)
     ms_prof = p_start.elapsed_time(p_end) / args.steps
     cls = summarise(recs, args.steps)
-    conv = cls.get("conv_mfma", {"tflops": 0.0, "flops": 0.0, "launches": 1, "avg_launch_ms": 0.0})
+    conv = cls.get("conv_wide_3x3", {"tflops": 0.0, "flops": 0.0, "launches": 1, "avg_launch_ms": 0.0})
     gn = cls.get("groupnorm") or cls.get("rmsnorm") or {"gbs": 0.0}
 
     roofline = {
-        "kernel": "conv_mfma_bf16 (implicit-GEMM 3x3 / 3x3x3 halo conv, v_mfma_f32_32x32x16_bf16)",
+        "kernel": "conv_wide<1, 3, false, 1, 0, 256> (implicit-GEMM 3x3 halo conv, 256x256 tiles, "
+                  "LDS-DMA operands, v_mfma_f32_32x32x16_bf16)",
         "bound": "mfma",
         "achieved": round(conv["tflops"], 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(conv["tflops"] / PEAK_BF16_TFLOPS, 4),
-        "traffic": None,
+        "traffic": measured_traffic() if args.config == 3 else None,
         "launches_per_step": conv["launches"] // args.steps,
         "avg_launch_ms": round(conv["avg_launch_ms"], 4),
         "flops_per_launch": conv["flops"] / max(1, conv["launches"]),

@@ -169,6 +169,10 @@ int vaep_decode_bands(vaep_model* model, const void* latent, int batch, int fram
  * nothing beyond the caller's own stream order. */
 enum { VAEP_STEP_CONV = 1, VAEP_STEP_GROUPNORM = 2, VAEP_STEP_RMSNORM = 3,
        VAEP_STEP_ATTENTION = 4, VAEP_STEP_MOVE = 5 };
+/* Convolution kernel that ran a conv step: 128x128 tiles two per CU, the wide kernel
+ * with 256- or 128-channel tiles, the narrow-output kernel, the fp32 kernel. */
+enum { VAEP_KERNEL_OTHER = 0, VAEP_KERNEL_CONV_TILE128 = 1, VAEP_KERNEL_CONV_WIDE256 = 2,
+       VAEP_KERNEL_CONV_WIDE128 = 3, VAEP_KERNEL_CONV_NARROW = 4, VAEP_KERNEL_CONV_F32 = 5 };
 typedef struct vaep_profile_entry {
   int32_t step;        /* VAEP_STEP_* */
   int32_t n_kernels;   /* kernels inside the bracket */
@@ -179,7 +183,7 @@ typedef struct vaep_profile_entry {
   double flops;        /* algorithmic flops */
   double bytes;        /* algorithmic HBM bytes */
   float ms;            /* time between the bracketing events */
-  int32_t reserved;
+  int32_t kernel;      /* conv: VAEP_KERNEL_* */
 } vaep_profile_entry;
 int vaep_profile_begin(vaep_model* model, int max_launches);
 int vaep_profile_end(vaep_model* model, vaep_profile_entry* out, int cap, int* n_out);

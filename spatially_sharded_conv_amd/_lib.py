@@ -36,6 +36,8 @@ EXPORTS = [
 ]
 
 STEP_CONV, STEP_GROUPNORM, STEP_RMSNORM, STEP_ATTENTION, STEP_MOVE = 1, 2, 3, 4, 5
+(KERNEL_OTHER, KERNEL_CONV_TILE128, KERNEL_CONV_WIDE256, KERNEL_CONV_WIDE128, KERNEL_CONV_NARROW,
+ KERNEL_CONV_F32) = 0, 1, 2, 3, 4, 5
 
 
 class VaepConfig(C.Structure):
@@ -59,7 +61,7 @@ class VaepProfileEntry(C.Structure):
         ("step", C.c_int32), ("n_kernels", C.c_int32), ("kt", C.c_int32), ("ks", C.c_int32),
         ("cin", C.c_int32), ("cout", C.c_int32), ("ups", C.c_int32), ("mode", C.c_int32),
         ("pixels", C.c_int64), ("flops", C.c_double), ("bytes", C.c_double), ("ms", C.c_float),
-        ("reserved", C.c_int32),
+        ("kernel", C.c_int32),
     ]
 
 

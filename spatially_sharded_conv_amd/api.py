@@ -145,7 +145,7 @@ def profile_end(dec: "Decoder"):
     arr = (L.VaepProfileEntry * cap)()
     n = C.c_int()
     L.check(L.load().vaep_profile_end(dec._h, arr, cap, C.byref(n)))
-    keys = [f[0] for f in L.VaepProfileEntry._fields_ if f[0] != "reserved"]
+    keys = [f[0] for f in L.VaepProfileEntry._fields_]
     return [{k: getattr(arr[i], k) for k in keys} for i in range(min(n.value, cap))]
 
 

@@ -492,6 +492,7 @@ struct Exec {
       rec_begin(pe);
     }
     hipError_t e = launch_conv(a, dtype, st);
+    if (recording) pending.kernel = a.kernel_used;
     rec_end();
     if (e != hipSuccess) return hip_fail(e, "conv launch");
     ++launches;

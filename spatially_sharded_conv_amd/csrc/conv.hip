@@ -501,6 +501,7 @@ hipError_t go(const ConvArgs& a, hipStream_t s) {
 hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s) {
   const bool ups = a.ups != 0;
   if (dtype != VAEP_DTYPE_F32 && conv_wide_fits(a)) return launch_conv_wide(a, s);
+  if (dtype != VAEP_DTYPE_F32 && conv_narrow_fits(a)) return launch_conv_narrow(a, s);
   // split operands and sub-pixel weights exist only on the wide kernel
   if (a.x_split || a.sub || (a.mode == kModeBandSplit && dtype == VAEP_DTYPE_F32)) return hipErrorInvalidValue;
   if (dtype != VAEP_DTYPE_F32) {
@@ -521,6 +522,7 @@ hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s) {
   }
   a.tile_start[a.in.nb] = t;
   a.tiles_total = t;
+  a.kernel_used = dtype == VAEP_DTYPE_F32 ? VAEP_KERNEL_CONV_F32 : VAEP_KERNEL_CONV_TILE128;
   if (t == 0) return hipSuccess;
   if (dtype == VAEP_DTYPE_F32) {
     dim3 grid(t, a.cout);

@@ -612,6 +612,7 @@ hipError_t launch_conv_wide(ConvArgs& a, hipStream_t s) {
   a.tiles_total = t;
   if (t == 0) return hipSuccess;
   const int bm = wide_bm(a, t);
+  a.kernel_used = bm == 256 ? VAEP_KERNEL_CONV_WIDE256 : VAEP_KERNEL_CONV_WIDE128;
   if (a.sub) return go_mode<1, 3, true, 3>(a, bm, s);
   if (a.kt == 1 && a.ks == 3) return go_mode<1, 3, false, 1>(a, bm, s);
   if (a.kt == 1 && a.ks == 1) return go_mode<1, 1, false, 1>(a, bm, s);

@@ -80,6 +80,7 @@ struct ConvArgs {
   int final_frames;     // kModeFinal: frames per sample of the output tensor
   int tiles_total;      // M tiles over all bands
   int tile_start[kMaxBands + 1];  // prefix of M tiles per band
+  int kernel_used;      // set by the launch: VAEP_KERNEL_*
 };
 
 // Launch the convolution described by `a` (fills tile fields).  dtype: VAEP_DTYPE_*.
@@ -94,6 +95,9 @@ constexpr int kWideTileM = 256;
 // always run there.
 bool conv_wide_fits(const ConvArgs& a);
 hipError_t launch_conv_wide(ConvArgs& a, hipStream_t s);
+// The final conv (kModeFinal) with at most 16 output channels: pixels on the MFMA rows.
+bool conv_narrow_fits(const ConvArgs& a);
+hipError_t launch_conv_narrow(ConvArgs& a, hipStream_t s);
 // Phase-folded weights of a nearest-2x + 3x3 conv: src [co][ci][3][3] bf16 ->
 // dst [4 phases][co_pad][4 taps][2 parts (hi, lo)][ci] bf16; zero rows past co.
 hipError_t launch_fold_subpixel_weight(const void* src, int co, int ci, void* dst, int co_pad,
