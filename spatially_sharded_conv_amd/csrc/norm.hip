@@ -235,28 +235,31 @@ __device__ void merge_tiles(const NormArgs& a, int n, int g, int t0, int t1, dou
   __syncthreads();
 }
 
-// Pass 2: one workgroup per (image n, group g).  Reports each band's moments (its own
-// tiles merged) and merges all tiles of the image into the statistics the apply uses;
-// the merged mean and variance are rounded to fp32 once.  Writes the per-channel
-// scale/shift of the apply.
+// Pass 2: one workgroup per (image n, group g, k): k < nb reports band k's moments (its
+// own tiles merged); k = nb merges all tiles of the image into the statistics the apply
+// uses, rounded to fp32 once, and writes the per-channel scale/shift of the apply.  Each
+// result is a fixed function of the tiles, whatever workgroup computes it.
 __global__ void __launch_bounds__(kThreads) gn_merge(const NormArgs a, float* coef) {
   __shared__ double sh[kThreads];
   __shared__ float fin[2];
   const BandLayout& L = a.L;
   const int G = a.groups, C = L.C, cpg = C / G;
-  const int n = blockIdx.x / G, g = blockIdx.x - (blockIdx.x / G) * G;
+  const int k = blockIdx.x % (L.nb + 1);
+  const int ng = blockIdx.x / (L.nb + 1);
+  const int n = ng / G, g = ng - (ng / G) * G;
   const int tid = threadIdx.x;
   const int s_idx = n * G + g, ns = L.n_img * G;
-  for (int b = 0; b < L.nb; ++b) {
+  if (k < L.nb) {
     double cb, mb, vb;
-    const int t0 = (L.row0[b] / a.slab_rows) * a.chunks;
-    const int t1 = ((L.row0[b] + L.rows[b]) / a.slab_rows) * a.chunks;
+    const int t0 = (L.row0[k] / a.slab_rows) * a.chunks;
+    const int t1 = ((L.row0[k] + L.rows[k]) / a.slab_rows) * a.chunks;
     merge_tiles(a, n, g, t0, t1, sh, &cb, &mb, &vb);
     if (tid == 0) {
-      a.band_moments[(0 * L.nb + b) * (long long)ns + s_idx] = (float)cb;
-      a.band_moments[(1 * L.nb + b) * (long long)ns + s_idx] = (float)mb;
-      a.band_moments[(2 * L.nb + b) * (long long)ns + s_idx] = (float)vb;
+      a.band_moments[(0 * L.nb + k) * (long long)ns + s_idx] = (float)cb;
+      a.band_moments[(1 * L.nb + k) * (long long)ns + s_idx] = (float)mb;
+      a.band_moments[(2 * L.nb + k) * (long long)ns + s_idx] = (float)vb;
     }
+    return;
   }
   double cnt, mean, var;
   merge_tiles(a, n, g, 0, a.slabs * a.chunks, sh, &cnt, &mean, &var);
@@ -283,9 +286,8 @@ __global__ void __launch_bounds__(kThreads) gn_merge(const NormArgs a, float* co
 }
 
 // Pass 3: y = act(x * scale_c + shift_c) over every owned row; boundary rows are also
-// written into the neighbours' halo slots.  Workgroup = a run of kApplyPix pixels of one
-// (band, image); thread = fixed channel slot, pixels strided by the pixel lanes.
-constexpr int kApplyPix = 128;
+// written into the neighbours' halo slots.  Workgroup = a run of a.apply_pix pixels of
+// one (band, image); thread = fixed channel slot, pixels strided by the pixel lanes.
 template <typename TO, bool XS>
 __global__ void __launch_bounds__(kThreads) gn_apply(const NormArgs a, const float* coef) {
   const BandLayout& L = a.L;
@@ -293,9 +295,10 @@ __global__ void __launch_bounds__(kThreads) gn_apply(const NormArgs a, const flo
   int b = 0;
   while (b + 1 < L.nb && (long long)blockIdx.x >= a.item_start[b + 1]) ++b;
   const long long local = blockIdx.x - a.item_start[b];
-  const long long runs = ((long long)L.rows[b] * L.W + kApplyPix - 1) / kApplyPix;
+  const int run = a.apply_pix;
+  const long long runs = ((long long)L.rows[b] * L.W + run - 1) / run;
   const int n = (int)(local / runs);
-  const long long p0 = (local - n * runs) * kApplyPix;
+  const long long p0 = (local - n * runs) * run;
   const long long npix = (long long)L.rows[b] * L.W;
   const int tid = threadIdx.x;
   const int slot = tid % S, pl = tid / S;
@@ -313,9 +316,7 @@ __global__ void __launch_bounds__(kThreads) gn_apply(const NormArgs a, const flo
   const long long row_up = b > 0 ? row_offset(L, b - 1, n, L.rows[b - 1]) + slot * V : 0;
   const long long row_dn = b + 1 < L.nb ? row_offset(L, b + 1, n, -1) + slot * V : 0;
   const long long last_row_start = (long long)(L.rows[b] - 1) * L.W;
-  for (int k = 0; k < kApplyPix / PL + 1; ++k) {
-    const long long p = p0 + pl + (long long)k * PL;
-    if (p >= p0 + kApplyPix || p >= npix) break;
+  for (long long p = p0 + pl; p < p0 + run && p < npix; p += PL) {
     float x[V];
     loadx4<XS>(a.x, xrow + p * C, C, slot * V, x);
 #pragma unroll
@@ -416,9 +417,24 @@ __global__ void moment_merge(int n_shards, int n_stats, const float* mean, const
 
 
 // Stats tiling of a layout: slabs of a.slab_rows rows (set by the caller), cut into
-// chunks of chunk_pixels(C) pixels.
-// ~128 KiB of fp32 per statistics tile
-static int chunk_pixels(int C) { return (32768 + C - 1) / C; }
+// chunks of chunk_pixels() pixels: about 2048 tiles per layer, each between 64 KiB and
+// 512 KiB of fp32.  A function of the layer's shape only, never of the band table.
+static int chunk_pixels(const BandLayout& L) {
+  const long long bytes = (long long)L.n_img * L.H * L.W * L.C * 4;
+  long long tb = bytes / 2048;
+  if (tb < (64 << 10)) tb = 64 << 10;
+  if (tb > (512 << 10)) tb = 512 << 10;
+  const long long pix = tb / (4LL * L.C);
+  return (int)(pix < 1 ? 1 : pix);
+}
+// Apply run length: enough workgroups to fill the GPU on small layers.
+static int apply_pixels(const BandLayout& L) {
+  const long long pix = (long long)L.n_img * L.H * L.W;
+  long long run = pix / 2048;
+  if (run < 32) run = 32;
+  if (run > 256) run = 256;
+  return (int)run;
+}
 
 static bool plan_stats(NormArgs& a) {
   const BandLayout& L = a.L;
@@ -426,7 +442,7 @@ static bool plan_stats(NormArgs& a) {
   for (int b = 0; b < L.nb; ++b)
     if (L.row0[b] % a.slab_rows != 0 || L.rows[b] % a.slab_rows != 0) return false;
   a.slabs = L.H / a.slab_rows;
-  a.chunk_pix = chunk_pixels(L.C);
+  a.chunk_pix = chunk_pixels(L);
   const long long slab_pix = (long long)a.slab_rows * L.W;
   a.chunks = (int)((slab_pix + a.chunk_pix - 1) / a.chunk_pix);
   return true;
@@ -434,7 +450,7 @@ static bool plan_stats(NormArgs& a) {
 
 size_t gn_partials_floats(const BandLayout& L, int groups, int slab_rows) {
   // (in floats) fp64 partials, per-channel coefficients, per-band moments, merged stats
-  const int pix = chunk_pixels(L.C);
+  const int pix = chunk_pixels(L);
   const long long slab_pix = (long long)slab_rows * L.W;
   const long long tiles = (long long)L.n_img * (L.H / slab_rows) * ((slab_pix + pix - 1) / pix);
   return (size_t)(tiles * groups * 4 + 2LL * L.n_img * L.C + 3LL * L.nb * L.n_img * groups +
@@ -458,11 +474,12 @@ hipError_t launch_groupnorm(NormArgs& a, int dtype, hipStream_t s) {
     hipLaunchKernelGGL(gn_stats<true>, dim3(blocks), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL(gn_stats<false>, dim3(blocks), dim3(kThreads), 0, s, a);
-  hipLaunchKernelGGL(gn_merge, dim3(L.n_img * a.groups), dim3(kThreads), 0, s, a, coef);
-  long long nblk = 0;   // apply workgroups: runs of kApplyPix pixels per (band, image)
+  hipLaunchKernelGGL(gn_merge, dim3(L.n_img * a.groups * (L.nb + 1)), dim3(kThreads), 0, s, a, coef);
+  a.apply_pix = apply_pixels(L);
+  long long nblk = 0;   // apply workgroups: runs of apply_pix pixels per (band, image)
   for (int b = 0; b < L.nb; ++b) {
     a.item_start[b] = nblk;
-    nblk += (long long)L.n_img * (((long long)L.rows[b] * L.W + kApplyPix - 1) / kApplyPix);
+    nblk += (long long)L.n_img * (((long long)L.rows[b] * L.W + a.apply_pix - 1) / a.apply_pix);
   }
   a.item_start[L.nb] = nblk;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;

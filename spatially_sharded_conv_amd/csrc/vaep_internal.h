@@ -131,6 +131,7 @@ struct NormArgs {
   int slabs;             // slabs per image = H / slab_rows
   int chunks;            // chunks per slab
   int chunk_pix;         // pixels per chunk (last chunk of a slab may be shorter)
+  int apply_pix;         // pixels per apply workgroup
   long long item_start[kMaxBands + 1];  // apply pass: first vector (GN) / pixel (RMS) of band i
 };
 
