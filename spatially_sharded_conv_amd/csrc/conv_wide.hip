@@ -217,26 +217,33 @@ __device__ __forceinline__ void split_epilogue(const ConvArgs& a, const f32x16_t
 __device__ __forceinline__ constexpr int wpart(int parts, int p) { return parts == 3 && p == 2 ? 1 : 0; }
 __device__ __forceinline__ constexpr int xpart(int p) { return p == 1 ? 1 : 0; }
 
-template <int KT, int KS, bool SUB, int PARTS, int MODE, int BM>
-__global__ void __launch_bounds__(256, 1) conv_wide(const ConvArgs a) {
+template <int KT, int KS, bool SUB, int PARTS, int MODE, int BM, int NW>
+__global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
+  // NW waves: 2 along the output channels x NW/2 along the pixels.  With 8 waves two
+  // share each SIMD, so one wave's loads, LDS reads and barrier waits hide behind the
+  // other's MFMAs.
   constexpr int S = BM == 256 ? 2 : 3;        // LDS stages
   constexpr int TAPS = SUB ? 4 : KT * KS * KS;
   constexpr int WP = PARTS == 3 ? 2 : 1;      // weight parts per tap in the packed rows
-  constexpr int NA = BM / 32;                 // A (weight) chunk loads per thread per step
-  constexpr int NB = BN / 32;                 // B (pixel) chunk loads per thread per step
+  constexpr int WPX = NW / 2;                 // waves along the pixels
+  constexpr int NA = BM / (8 * NW);           // A (weight) chunk loads per thread per step
+  constexpr int NB = BN / (8 * NW);           // B (pixel) chunk loads per thread per step
   constexpr int MI = BM / 64;                 // 32-row channel blocks per wave
-  constexpr int NJ = 4;                       // 32-pixel blocks per wave
+  constexpr int NJ = BN / (32 * WPX);         // 32-pixel blocks per wave
+  static_assert(NA % 4 == 0 && NB % 4 == 0, "loads per quarter step");
   constexpr int PH = SUB ? 4 : 1;
   // S operand stages: A (BM x 64) then B (BN x 64) per stage; the epilogue reuses the space
   __shared__ __attribute__((aligned(1024))) unsigned short smem[S * (BM + BN) * 64];
   __shared__ unsigned int sPF[64];             // prefetch landing words (never read)
   constexpr int PFD = 2;                       // prefetch target: PFD steps past the step issued
   constexpr int NG = NA + NB + 2;              // loads per thread per issued step
+  constexpr int LPP = (NA + NB) / 4;           // operand loads per quarter step
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const unsigned wrow = wave * 8 * 64 * 2;   // LDS byte offset of this wave's first row block
+  constexpr unsigned kRowStep = NW * 8 * 64 * 2;   // LDS bytes between a wave's row blocks
   // work id -> (output-channel tile, pixel tile, phase); the phases of a pixel tile are adjacent
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int phase = lin % PH;
@@ -278,12 +285,12 @@ __global__ void __launch_bounds__(256, 1) conv_wide(const ConvArgs a) {
       reinterpret_cast<const unsigned short*>(a.w) + (long long)phase * a.cout_pad * kw,
       (unsigned)((long long)a.cout_pad * kw * 2));
 
-  // This thread's chunk: LDS rows (j*4 + wave)*8 + lane/8, slot lane%8, logical chunk ck.
+  // This thread's chunk: LDS rows (j*NW + wave)*8 + lane/8, slot lane%8, logical chunk ck.
   const int ck = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
   unsigned avo[NA];
 #pragma unroll
   for (int j = 0; j < NA; ++j)
-    avo[j] = (unsigned)(((long long)(co0 + (j * 4 + wave) * 8 + (lane >> 3)) * kw + ck * 8) * 2);
+    avo[j] = (unsigned)(((long long)(co0 + (j * NW + wave) * 8 + (lane >> 3)) * kw + ck * 8) * 2);
   // Pixel rows: byte offset of the pixel's own position and validity bits
   // (0..2: row shift -1..1 inside the image, 3..5: column shift -1..1, 6..8: frame shift
   // -(KT-1)+dt not before frame 0).
@@ -293,7 +300,7 @@ __global__ void __launch_bounds__(256, 1) conv_wide(const ConvArgs a) {
   const int g0 = a.in.row0[band];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const long long p = (long long)tile * BN + (j * 4 + wave) * 8 + (lane >> 3);
+    const long long p = (long long)tile * BN + (j * NW + wave) * 8 + (lane >> 3);
     const bool ok = p < m_band;
     const long long q = ok ? p : 0;
     const int n = (int)(q / plane);
@@ -318,10 +325,11 @@ __global__ void __launch_bounds__(256, 1) conv_wide(const ConvArgs a) {
   unsigned bvo[NB];
   // prefetch roles: weight row (wave*64 + lane) % BM, tile pixel wave*64 + lane
   const unsigned pf_avo = (unsigned)((long long)(co0 + (wave * 64 + lane) % BM) * kw * 2);
+  const int pf_px = (wave * 64 + lane) % BN;
   unsigned pf_base;
   int pf_mask;
   {
-    const long long p = (long long)tile * BN + wave * 64 + lane;
+    const long long p = (long long)tile * BN + pf_px;
     const bool ok = p < m_band;
     const long long q = ok ? p : 0;
     const int n = (int)(q / plane);
@@ -392,20 +400,26 @@ __global__ void __launch_bounds__(256, 1) conv_wide(const ConvArgs a) {
 // The loads of one step go out in four parts, one before each group of MFMAs of the
 // current step, so that the wave never waits on a full load queue with the matrix cores
 // idle.  Part 0 also forms the tap's offsets; part 3 adds the prefetch and advances.
-#define VAEP_ISSUE_PART(st, q)                                                                 \
+// One load of a step: part q (0..3), index m within the part (A chunks first, then B).
+// Part 0's first load also forms the tap's offsets; part 3's last load adds the prefetch
+// and advances the step counters.
+#define VAEP_ISSUE_ONE(st, q, m)                                                               \
   {                                                                                            \
-    if ((q) == 0) {                                                                            \
+    if ((q) == 0 && (m) == 0) {                                                                \
       VAEP_TAP_GEO(itap, need, delta);                                                         \
       _Pragma("unroll") for (int j = 0; j < NB; ++j)                                           \
         bvo[j] = ((pmask[j] & need) == need) ? (unsigned)((int)pbase[j] + delta) : kPadOffset;  \
     }                                                                                          \
-    const int aso = ((itap * WP + wpart(PARTS, ipart)) * C + ic) * 2;                          \
-    const int bso = (xpart(ipart) * C + ic) * 2;                                               \
-    _Pragma("unroll") for (int j = (q) * (NA / 4); j < ((q) + 1) * (NA / 4); ++j)              \
-      dma16(j == (q) * (NA / 4), wrs, lds_addr(VAEP_SA(st)) + wrow + j * 4096, avo[j], aso);    \
-    _Pragma("unroll") for (int j = (q) * (NB / 4); j < ((q) + 1) * (NB / 4); ++j)              \
-      dma16(j == (q) * (NB / 4), xrs, lds_addr(VAEP_SB(st)) + wrow + j * 4096, bvo[j], bso);    \
-    if ((q) == 3) {                                                                            \
+    if ((m) < NA / 4) {                                                                        \
+      const int j = (q) * (NA / 4) + (m);                                                      \
+      const int aso = ((itap * WP + wpart(PARTS, ipart)) * C + ic) * 2;                        \
+      dma16((m) == 0, wrs, lds_addr(VAEP_SA(st)) + wrow + j * kRowStep, avo[j], aso);           \
+    } else {                                                                                   \
+      const int j = (q) * (NB / 4) + (m) - NA / 4;                                             \
+      const int bso = (xpart(ipart) * C + ic) * 2;                                             \
+      dma16((m) == NA / 4, xrs, lds_addr(VAEP_SB(st)) + wrow + j * kRowStep, bvo[j], bso);     \
+    }                                                                                          \
+    if ((q) == 3 && (m) == LPP - 1) {                                                          \
       VAEP_TAP_GEO(ptap, need, delta);                                                         \
       const unsigned pbv = ((pf_mask & need) == need) ? (unsigned)((int)pf_base + delta) : kPadOffset; \
       prefetch4(wrs, lds_addr((const unsigned short*)sPF), pf_avo,                             \
@@ -418,6 +432,10 @@ __global__ void __launch_bounds__(256, 1) conv_wide(const ConvArgs a) {
         VAEP_ADVANCE(ptap, ppart, pc);                                                         \
       }                                                                                        \
     }                                                                                          \
+  }
+#define VAEP_ISSUE_PART(st, q)                                                                 \
+  {                                                                                            \
+    _Pragma("unroll") for (int m = 0; m < LPP; ++m) VAEP_ISSUE_ONE(st, q, m);                  \
   }
 #define VAEP_ISSUE(st)                                                                         \
   {                                                                                            \
@@ -433,8 +451,8 @@ __global__ void __launch_bounds__(256, 1) conv_wide(const ConvArgs a) {
   int ko[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) ko[kk] = lr + (((2 * kk + (lane >> 5)) ^ fl) << 3);
-  const int wco = (wave >> 1) * (BM / 2);
-  const int wpx = (wave & 1) * 128;
+  const int wco = (wave / WPX) * (BM / 2);
+  const int wpx = (wave % WPX) * (BN / WPX);
 
   // Step s computes from stage s % S and first issues step s + S - 1 into stage
   // (s + S - 1) % S, which every wave finished reading before the barrier.  Loads complete
@@ -466,10 +484,18 @@ __global__ void __launch_bounds__(256, 1) conv_wide(const ConvArgs a) {
         _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                         \
           bfr[cur ^ 1][j] = *reinterpret_cast<const bf16x8_t*>(B + (wpx + 32 * j) * 64 + ko[kk + 1]); \
       }                                                                                        \
-      if (more) VAEP_ISSUE_PART(ns, kk);                                                       \
+      /* the quarter step's loads go out one at a time between groups of MFMAs */             \
       _Pragma("unroll") for (int i = 0; i < MI; ++i)                                           \
-        _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                         \
+        _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                       \
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0); \
+          constexpr int per = (MI * NJ) / LPP;                                                 \
+          const int idx = i * NJ + j;                                                          \
+          if (idx % per == per - 1 && idx / per < LPP) {                                       \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            if (more) VAEP_ISSUE_ONE(ns, kk, idx / per);                                       \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+          }                                                                                    \
+        }                                                                                      \
     }                                                                                          \
   }
 
@@ -497,6 +523,7 @@ __global__ void __launch_bounds__(256, 1) conv_wide(const ConvArgs a) {
 #undef VAEP_TAP_GEO
 #undef VAEP_ADVANCE
 #undef VAEP_ISSUE_PART
+#undef VAEP_ISSUE_ONE
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // prefetches still in flight
 #undef VAEP_ISSUE
 #undef VAEP_SET_TAP
@@ -551,9 +578,9 @@ hipError_t go_bm(const ConvArgs& a, int bm, hipStream_t s) {
   const long long wgs = (long long)a.tiles_total * (a.cout_pad / bm) * ph;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
   if (bm == 256)
-    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 256>), dim3((unsigned)wgs), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 256, 8>), dim3((unsigned)wgs), dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128>), dim3((unsigned)wgs), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128, 4>), dim3((unsigned)wgs), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
