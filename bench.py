@@ -42,6 +42,31 @@ def parse():
     return ap.parse_args()
 
 
+def aggregates(recs, steps):
+    """Whole-decode figures: conv MFMA utilisation over every MFMA-bound conv (3x3 / 3x3x3 with
+    K >= 1152 and >= 96 outputs, any kernel, algorithmic flops) and GroupNorm bandwidth over the
+    tensors of at least 512 MiB (fp32 input; larger than the 256 MB last-level cache)."""
+    import spatially_sharded_conv_amd._lib as L
+    cf = cm = nb = nm = 0.0
+    for r in recs:
+        if r["step"] == L.STEP_CONV and r["ks"] == 3 and r["kt"] * 9 * r["cin"] >= 1152 and r["cout"] >= 96:
+            cf += r["flops"]
+            cm += r["ms"]
+        if r["step"] == L.STEP_GROUPNORM and r["pixels"] * r["cin"] * 4 >= 512 << 20:
+            nb += r["bytes"]
+            nm += r["ms"]
+    return {
+        "conv_mfma_util": {"convs": "3x3 / 3x3x3, K >= 1152, N >= 96, all kernels",
+                           "tflops": round(cf / (cm * 1e-3) / 1e12, 2) if cm else 0.0,
+                           "frac": round(cf / (cm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4) if cm else 0.0,
+                           "ms_per_step": round(cm / steps, 4)},
+        "groupnorm_large": {"tensors": ">= 512 MiB fp32",
+                            "gbs": round(nb / (nm * 1e-3) / 1e9, 1) if nm else 0.0,
+                            "frac": round(nb / (nm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if nm else 0.0,
+                            "ms_per_step": round(nm / steps, 4)},
+    }
+
+
 def summarise(recs, steps):
     """Group per-launch records into the classes the roofline reports."""
     import spatially_sharded_conv_amd._lib as L
@@ -191,7 +216,7 @@ def main():
     gn = cls.get("groupnorm") or cls.get("rmsnorm") or {"gbs": 0.0}
 
     roofline = {
-        "kernel": "conv_wide<1, 3, false, 1, 0, 256> (implicit-GEMM 3x3 halo conv, 256x256 tiles, "
+        "kernel": "conv_wide<1, 3, false, 1, 0, 256, 8> (implicit-GEMM 3x3 halo conv, 256x256 tiles, 8 waves, "
                   "LDS-DMA operands, v_mfma_f32_32x32x16_bf16)",
         "bound": "mfma",
         "achieved": round(conv["tflops"], 2),
@@ -236,6 +261,7 @@ def main():
                           "tflops": round(v["tflops"], 2), "gbs": round(v["gbs"], 1)}
                       for k, v in sorted(cls.items())},
         "profiled_ms_per_step": round(ms_prof, 4),
+        **aggregates(recs, args.steps),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
