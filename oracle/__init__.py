@@ -12,6 +12,9 @@ What it computes follows the pages on the method:
   attention.
 * ChituDiffusion, "Static Layer-Wise VAE Decode" (validation page) -- the
   "Semantics and Communication" operator table and the merge formula below it.
+* The distributed-VAE strategy page -- "Strategy Selection Contract" and the
+  Wan spatial-shard notes (height or width sharding, the ``auto`` axis
+  policy).
 
 Both pages state that the layer-wise decode keeps full-image semantics, so the
 oracle's primary output is the plain full-image decoder forward
@@ -28,10 +31,11 @@ Parity status of every function is listed in ``oracle/PINS.md``.
 from .ops import (conv_padded, conv_full, conv_band, groupnorm_moments, merge_moments,
                   groupnorm_apply, rmsnorm, silu, attention_rows, upsample_nearest2x,
                   temporal_upsample_interleave)
-from .decoder import decode_full, decode_bands, Precision
+from .decoder import decode_full, decode_bands, decode_auto, choose_axis, even_starts, Precision
 
 __all__ = [
     "conv_padded", "conv_full", "conv_band", "groupnorm_moments", "merge_moments",
     "groupnorm_apply", "rmsnorm", "silu", "attention_rows", "upsample_nearest2x",
-    "temporal_upsample_interleave", "decode_full", "decode_bands", "Precision",
+    "temporal_upsample_interleave", "decode_full", "decode_bands", "decode_auto", "choose_axis",
+    "even_starts", "Precision",
 ]

@@ -16,12 +16,13 @@ blocks):
   2-D attention spans the whole image, video attention spans one frame.
 
 ``decode_full`` is the plain whole-tensor forward.  ``decode_bands`` runs the
-same graph on disjoint latent row bands as the pages describe: band rows
-double with every upsample, convs read kernel-radius halo rows from the
-neighbouring bands' buffers, GroupNorm merges local moments with
-element-count weights, attention uses the band's Q against K/V concatenated
-from all bands, and everything else stays local.  The final output is the
-bands' rows stacked in order (the leader gather).
+same graph on disjoint latent row bands (or column bands: the width-sharded
+mode) as the pages describe: band rows double with every upsample, convs read
+kernel-radius halo rows from the neighbouring bands' buffers, GroupNorm merges
+local moments with element-count weights, attention uses the band's Q against
+K/V concatenated from all bands, and everything else stays local.  The final
+output is the bands' rows (columns) stacked in order (the leader gather).
+``choose_axis`` is the per-request ``auto`` policy of the strategy page.
 """
 from __future__ import annotations
 
@@ -124,17 +125,24 @@ class FullOps(_Ops):
 
 
 class BandOps(_Ops):
-    """Per-band operators; an activation is the list of band tensors in row order."""
+    """Per-band operators; an activation is the list of band tensors in band order.
 
-    def __init__(self, cfg, prec, starts: Sequence[int]):
+    ``axis`` 3 cuts latent rows (height bands), 4 cuts latent columns (width
+    bands); every other rule is the same on either axis.
+    """
+
+    def __init__(self, cfg, prec, starts: Sequence[int], axis: int = 3):
         super().__init__(cfg, prec)
+        assert axis in (3, 4)
         self.starts = list(starts)
+        self.axis = axis
 
     def conv(self, xb, w, b, causal=None, residual=None):
         causal = self.video and w.dim() == 5 if causal is None else causal
         w5 = _as5d(w)
         return [ops.conv_band(xb, i, w5, b, causal, self.acc,
-                              None if residual is None else residual[i]) for i in range(len(xb))]
+                              None if residual is None else residual[i], axis=self.axis)
+                for i in range(len(xb))]
 
     def norm(self, xb, p, prefix, act):
         if self.video:   # channel-only normalisation: local to each band
@@ -159,7 +167,7 @@ class BandOps(_Ops):
                     qs.append(q)
                     ks.append(k)
                     vs.append(v)
-                k_all = torch.cat(ks, dim=0)   # the gathered global K/V, bands in row order
+                k_all = torch.cat(ks, dim=0)   # the gathered global K/V, bands in band order
                 v_all = torch.cat(vs, dim=0)
                 for i, x in enumerate(xb):
                     o = self.fin(ops.attention_rows(qs[i], k_all, v_all, 1.0 / math.sqrt(c)))
@@ -182,10 +190,10 @@ class BandOps(_Ops):
     def enter(self, z):
         z5 = z.unsqueeze(2) if z.dim() == 4 else z
         s = self.starts
-        return [z5[:, :, :, s[i]:s[i + 1], :].contiguous() for i in range(len(s) - 1)]
+        return [z5.narrow(self.axis, s[i], s[i + 1] - s[i]).contiguous() for i in range(len(s) - 1)]
 
     def leave(self, yb):
-        y = torch.cat(yb, dim=3)
+        y = torch.cat(yb, dim=self.axis)
         return y[:, :, 0] if not self.video else y
 
 
@@ -228,10 +236,55 @@ def decode_full(cfg, params: Dict[str, torch.Tensor], latent: torch.Tensor,
 
 
 def decode_bands(cfg, params: Dict[str, torch.Tensor], latent: torch.Tensor,
-                 starts: Sequence[int], prec: Precision = None) -> torch.Tensor:
-    """Band-mode decode on latent row bands [starts[i], starts[i+1])."""
+                 starts: Sequence[int], prec: Precision = None, axis: str = "height") -> torch.Tensor:
+    """Band-mode decode on latent bands [starts[i], starts[i+1]) of the given axis.
+
+    ``axis="height"`` cuts latent rows, ``axis="width"`` latent columns.
+    """
     prec = prec or Precision(cfg.dtype)
+    dim = {"height": 3, "width": 4}[axis]
     s = list(starts)
-    assert s[0] == 0 and s[-1] == latent.shape[-2] and all(a < b for a, b in zip(s, s[1:]))
+    assert s[0] == 0 and s[-1] == latent.shape[dim - 5] and all(a < b for a, b in zip(s, s[1:]))
     with torch.no_grad():
-        return _graph(BandOps(cfg, prec, s), cfg, params, latent)
+        return _graph(BandOps(cfg, prec, s, dim), cfg, params, latent)
+
+
+def choose_axis(latent_h: int, latent_w: int, n_shards: int) -> str:
+    """The ``auto`` strategy of the Wan spatial-shard decode, per request.
+
+    Model-specific notes on the strategy page: auto takes the longer axis
+    that can cover every shard, width winning ties; when neither axis can
+    cover the shards it falls back.  A shard needs at least one latent row
+    (the kernel radius at the latent level), so an axis covers ``n_shards``
+    when its length is at least ``n_shards``.  Returns "height", "width" or
+    "dense" (the fallback: one band).
+    """
+    assert n_shards >= 1
+    if n_shards == 1:
+        return "dense"
+    cover_h, cover_w = latent_h >= n_shards, latent_w >= n_shards
+    if cover_w and (latent_w >= latent_h or not cover_h):
+        return "width"
+    if cover_h:
+        return "height"
+    return "dense"
+
+
+def even_starts(length: int, n_shards: int) -> List[int]:
+    """Shard boundaries splitting ``length`` into n nearly equal parts, larger parts first."""
+    q, r = divmod(length, n_shards)
+    starts = [0]
+    for i in range(n_shards):
+        starts.append(starts[-1] + q + (1 if i < r else 0))
+    return starts
+
+
+def decode_auto(cfg, params: Dict[str, torch.Tensor], latent: torch.Tensor, n_shards: int,
+                prec: Precision = None):
+    """Decode with the axis ``choose_axis`` picks and even shards; returns (output, axis)."""
+    h, w = latent.shape[-2:]
+    axis = choose_axis(h, w, n_shards)
+    if axis == "dense":
+        return decode_full(cfg, params, latent, prec), axis
+    starts = even_starts(h if axis == "height" else w, n_shards)
+    return decode_bands(cfg, params, latent, starts, prec, axis), axis

@@ -83,7 +83,7 @@ def conv_full(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor], causa
 
 
 def conv_band(bands: Sequence[torch.Tensor], i: int, w: torch.Tensor, b: Optional[torch.Tensor],
-              causal: bool, finish, residual=None) -> torch.Tensor:
+              causal: bool, finish, residual=None, axis: int = 3) -> torch.Tensor:
     """Conv of band i: its own rows plus kernel-radius halo rows from the neighbours.
 
     The feature page's conv section: each conv fetches the boundary rows it
@@ -91,28 +91,46 @@ def conv_band(bands: Sequence[torch.Tensor], i: int, w: torch.Tensor, b: Optiona
     of the whole image; a shard keeps only the output rows it owns.  The
     validation page's operator table says the same (kernel-radius rows, zero
     padding only at the global image edges).
+
+    ``axis`` is the dimension the bands cut: 3 (height, row bands) or 4
+    (width, column bands -- the width-sharded mode of the Wan page's strategy
+    table).  Along the cut axis the halo comes from the neighbour bands;
+    along the other spatial axis and in time the padding is the plain zero /
+    causal padding of ``conv_full``.
     """
+    assert axis in (3, 4)
     _, _, kt, kh, kw = w.shape
     ph, pw = (kh - 1) // 2, (kw - 1) // 2
     pt = (kt - 1) if causal else 0
+    halo = ph if axis == 3 else pw
     x = bands[i]
+
+    def zeros():
+        shape = list(x.shape)
+        shape[axis] = halo
+        return torch.zeros(shape, dtype=x.dtype)
+
     parts = []
-    if ph:
+    if halo:
         if i > 0:
-            above = bands[i - 1]
-            assert above.shape[3] >= ph, "neighbour band thinner than the halo"
-            parts.append(above[:, :, :, above.shape[3] - ph:, :])
+            before = bands[i - 1]
+            assert before.shape[axis] >= halo, "neighbour band thinner than the halo"
+            parts.append(before.narrow(axis, before.shape[axis] - halo, halo))
         else:
-            parts.append(torch.zeros(x.shape[:3] + (ph, x.shape[4]), dtype=x.dtype))
+            parts.append(zeros())
     parts.append(x)
-    if ph:
+    if halo:
         if i + 1 < len(bands):
-            below = bands[i + 1]
-            assert below.shape[3] >= ph, "neighbour band thinner than the halo"
-            parts.append(below[:, :, :, :ph, :])
+            after = bands[i + 1]
+            assert after.shape[axis] >= halo, "neighbour band thinner than the halo"
+            parts.append(after.narrow(axis, 0, halo))
         else:
-            parts.append(torch.zeros(x.shape[:3] + (ph, x.shape[4]), dtype=x.dtype))
-    xp = _pad_tw(torch.cat(parts, dim=3), pt, pw)
+            parts.append(zeros())
+    xc = torch.cat(parts, dim=axis)
+    if axis == 3:
+        xp = _pad_tw(xc, pt, pw)
+    else:   # zero rows at both H edges, causal zero frames in front
+        xp = torch.nn.functional.pad(xc, (0, 0, ph, ph, pt, 0)) if (ph or pt) else xc
     return conv_padded(xp, w, b, finish, residual)
 
 

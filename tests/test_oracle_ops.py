@@ -115,6 +115,24 @@ def test_conv_band_equals_full_bitwise():
     assert torch.equal(torch.cat(parts, dim=3), full)
 
 
+def test_conv_width_band_equals_full():
+    # column bands (the width-sharded mode): halo columns from the neighbours, zero rows
+    # at the H edges; uneven bands including 1-column bands
+    x = _rand((2, 4, 3, 7, 10), 21).float()
+    w = _rand((5, 4, 3, 3, 3), 22).float()
+    b = _rand((5,), 23).float()
+    r = _rand((2, 5, 3, 7, 10), 24).float()
+    for causal, wk in ((True, w), (False, w[:, :, 2:])):
+        full = ops.conv_full(x, wk, b, causal, fin32, r)
+        starts = [0, 1, 4, 5, 10]
+        bands = [x[:, :, :, :, s:e].contiguous() for s, e in zip(starts, starts[1:])]
+        parts = [ops.conv_band(bands, i, wk, b, causal, fin32, r[..., s:e], axis=4)
+                 for i, (s, e) in enumerate(zip(starts, starts[1:]))]
+        y = torch.cat(parts, dim=4)
+        assert y.shape == full.shape
+        assert (y - full).abs().max().item() <= 1e-6 * full.abs().max().item()
+
+
 def test_conv_linearity():
     x1 = _rand((1, 3, 1, 6, 6), 14).float()
     x2 = _rand((1, 3, 1, 6, 6), 15).float()
