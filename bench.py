@@ -1,4 +1,4 @@
-"""Throughput of the layer-wise, height-sharded VAE decode on one MI355X.
+"""Throughput of the layer-wise, spatially sharded VAE decode on one MI355X.
 
 One step = one band decode (vaep_decode_bands) of the 1024x1024 bf16 preset:
 latent 1x16x128x128 split into 4 uneven latent row bands (31/33/32/32), every
@@ -11,6 +11,8 @@ of K decodes brackets every kernel launch with HIP events on the decode stream
 (vaep_profile_begin/_end) to give each kernel's average duration, from which
 the roofline fractions are computed with algorithmic flops / bytes per launch.
 The CPU baseline times the oracle on a bounded sample of the same decoder.
+`shard_axes` times the same latent decoded on column bands of the same sizes
+(vaep_decode_sharded, width axis) and with the per-request `auto` axis policy.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
 """
@@ -228,6 +230,28 @@ def main():
         "avg_launch_ms": round(conv["avg_launch_ms"], 4),
         "flops_per_launch": conv["flops"] / max(1, conv["launches"]),
     }
+    # the same workload sharded along the width (the row bands' sizes laid across the
+    # columns when they fit) and with the per-request axis policy
+    axes = {}
+    sizes = [b - a for a, b in zip(starts, starts[1:])]
+    col = [0]
+    for v in sizes:
+        col.append(col[-1] + v)
+    for name, st in (("width", tuple(col) if col[-1] == cfg.latent_w else None), ("auto", None)):
+        for _ in range(args.warmup):
+            dec.decode_sharded(latent, name, nb, out, ws, st, stream)
+        torch.cuda.synchronize()
+        a_start = torch.cuda.Event(enable_timing=True)
+        a_end = torch.cuda.Event(enable_timing=True)
+        a_start.record(stream)
+        for _ in range(args.steps):
+            _, ainfo = dec.decode_sharded(latent, name, nb, out, ws, st, stream)
+        a_end.record(stream)
+        torch.cuda.synchronize()
+        a_ms = a_start.elapsed_time(a_end) / args.steps
+        axes[name] = {"axis": {1: "height", 2: "width", 3: "dense"}[ainfo.axis],
+                      "bands": list(st) if st else ainfo.bands_used,
+                      "ms_per_step": round(a_ms, 4), "mpixel_s": round(pixels / (a_ms * 1e-3) / 1e6, 3)}
     norm_key = "groupnorm" if "groupnorm" in cls else "rmsnorm"
     line = {
         "metric": METRIC,
@@ -261,6 +285,7 @@ def main():
                           "tflops": round(v["tflops"], 2), "gbs": round(v["gbs"], 1)}
                       for k, v in sorted(cls.items())},
         "profiled_ms_per_step": round(ms_prof, 4),
+        "shard_axes": axes,
         **aggregates(recs, args.steps),
         "cpu_baseline": None,
     }

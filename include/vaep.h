@@ -1,5 +1,5 @@
 /*
- * vaep.h -- C ABI of the layer-wise, height-sharded VAE decoder for MI355X (gfx950).
+ * vaep.h -- C ABI of the layer-wise, spatially sharded VAE decoder for MI355X (gfx950).
  *
  * The method (ChituDiffusion, "VAEP: VAE 并行解码", sections on height sharding,
  * conv halos, the GroupNorm merge and AGKV; and "Static Layer-Wise VAE Decode",
@@ -15,7 +15,9 @@
  *   - activations, pointwise ops, channel RMSNorm and nearest upsampling stay local;
  *   - the decoded rows of every band land in one output (the leader's).
  * On one GPU every band is a share of this device: halo rows, statistics and K/V pass
- * through device memory; there are no collectives.
+ * through device memory; there are no collectives.  vaep_decode_sharded cuts latent
+ * columns instead (the width-sharded mode of the distributed-VAE strategy page) or lets
+ * the per-request `auto` policy choose the axis.
  *
  * Conventions for every entry point:
  *   - Pointers named "device" are HIP device pointers owned by the caller, unless a
@@ -80,12 +82,18 @@ typedef struct vaep_config {
   float eps;                                /* norm epsilon */
 } vaep_config;
 
-/* Optional report filled by vaep_decode_bands. */
+/* Shard axes (vaep_decode_sharded, vaep_select_axis, vaep_decode_info.axis). */
+enum { VAEP_AXIS_AUTO = 0,     /* pick per request (vaep_select_axis) */
+       VAEP_AXIS_HEIGHT = 1,   /* bands of latent rows */
+       VAEP_AXIS_WIDTH = 2,    /* bands of latent columns */
+       VAEP_AXIS_DENSE = 3 };  /* result only: one dense band */
+
+/* Optional report filled by the decode entry points. */
 typedef struct vaep_decode_info {
   int32_t bands_used;        /* number of bands actually decoded */
-  int32_t fell_back;         /* 1 if the dense one-band path was taken */
+  int32_t fell_back;         /* 1 if the dense one-band path replaced a multi-shard request */
   int32_t n_launches;        /* kernels enqueued by the call */
-  int32_t reserved;
+  int32_t axis;              /* VAEP_AXIS_HEIGHT / _WIDTH of the bands, or _DENSE */
   uint64_t workspace_bytes;  /* bytes of the workspace the call used */
 } vaep_decode_info;
 
@@ -128,7 +136,8 @@ int vaep_model_destroy(vaep_model* model);
 
 /* Workspace needed to decode a latent of `batch` x [frames x] latent_h x latent_w
  * with up to `n_bands` bands (frames = 1 for KL2D).  The same size serves
- * vaep_decode_full and every band table with at most n_bands bands. */
+ * vaep_decode_full, every band table with at most n_bands bands, and
+ * vaep_decode_sharded with at most n_bands shards on either axis. */
 int vaep_workspace_bytes(const vaep_model* model, int batch, int frames, int latent_h,
                          int latent_w, int n_bands, size_t* bytes_out);
 
@@ -157,6 +166,41 @@ int vaep_decode_bands(vaep_model* model, const void* latent, int batch, int fram
                       int latent_h, int latent_w, const int32_t* row_starts, int n_bands,
                       void* out, void* ws, size_t ws_bytes, void* stream,
                       vaep_decode_info* info);
+
+/* Axis policy of a sharded decode (the distributed-VAE strategy page, "Strategy
+ * Selection Contract" and the Wan spatial-shard notes: `auto` takes the longer axis
+ * that can cover every shard, width winning ties, and falls back when neither can).
+ * A shard needs at least one latent row or column (the 3x3 kernels' radius at latent
+ * resolution), so an axis covers n_shards when its length is >= n_shards.  Writes
+ * VAEP_AXIS_HEIGHT, VAEP_AXIS_WIDTH or VAEP_AXIS_DENSE (n_shards = 1, or neither axis
+ * covers) to *axis_out.  Host only: touches no device.  Deterministic and free of state.
+ * Errors: INVALID_ARG (NULL axis_out, sizes < 1). */
+int vaep_select_axis(int latent_h, int latent_w, int n_shards, int32_t* axis_out);
+
+/* Sharded decode along a chosen axis (strategy page: explicit height or width
+ * sharding, or `auto`, decided per request).
+ * axis = VAEP_AXIS_HEIGHT: bands of latent rows, exactly vaep_decode_bands.
+ * axis = VAEP_AXIS_WIDTH: bands of latent columns; every rule of the band decode holds
+ *   with rows and columns exchanged (convs read one halo column from each neighbour
+ *   band, zero padding at the global edges; GroupNorm merges the bands' moments;
+ *   attention runs each band's queries against the K/V of every band).  Internally the
+ *   decode runs on the transposed image with transposed 3x3 kernels (built by
+ *   vaep_model_create); latent and output keep their NC[T]HW layout.
+ * axis = VAEP_AXIS_AUTO: vaep_select_axis picks the axis; starts must be NULL.
+ * starts: host array of n_shards+1 indices along the axis (0 = starts[0] < ... <
+ *   starts[n_shards] = axis length), or NULL for even shards (sizes differ by at most
+ *   one, larger shards first).
+ * Fallback: an explicit axis with NULL starts that is shorter than n_shards, or more
+ *   than VAEP_MAX_BANDS shards, decodes one dense band and returns VAEP_WARN_FELL_BACK;
+ *   `auto` with neither axis covering decodes one dense band and returns VAEP_OK
+ *   (info->axis = VAEP_AXIS_DENSE, info->fell_back = 1 when n_shards > 1).
+ * Other arguments as for vaep_decode_bands; ws >= vaep_workspace_bytes(..., n_shards).
+ * Errors: INVALID_ARG (unknown axis, starts with AUTO, bad table, NULL pointers),
+ * WORKSPACE, HIP. */
+int vaep_decode_sharded(vaep_model* model, const void* latent, int batch, int frames,
+                        int latent_h, int latent_w, int axis, const int32_t* starts,
+                        int n_shards, void* out, void* ws, size_t ws_bytes, void* stream,
+                        vaep_decode_info* info);
 
 /* Launch timing.  While profiling is on for a model, every kernel launch of its decodes
  * is bracketed by two HIP events on the caller's stream and the library records the

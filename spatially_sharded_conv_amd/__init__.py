@@ -1,6 +1,7 @@
-"""Layer-wise, height-sharded VAE decode for MI355X (gfx950).
+"""Layer-wise, spatially sharded VAE decode for MI355X (gfx950).
 
-The decoder runs band by band on disjoint latent row bands: convolutions read
+The decoder runs band by band on disjoint latent row bands (or column bands,
+or the axis a per-request policy picks): convolutions read
 halo rows from the neighbouring bands, GroupNorm merges per-band moments with
 element-count weights, attention runs band-local queries against the global
 K/V, and every kernel is hand-written HIP for gfx950 behind the C ABI of
@@ -8,12 +9,12 @@ K/V, and every kernel is hand-written HIP for gfx950 behind the C ABI of
 """
 from . import _lib
 from .api import (Decoder, config_preset, make_config, param_info, groupnorm_merge, profile_begin,
-                  profile_end, step_conv,
+                  profile_end, select_axis, step_conv,
                   step_groupnorm, step_rmsnorm, step_attention, step_temporal_upsample, version)
 
 __all__ = [
     "_lib", "Decoder", "config_preset", "make_config", "param_info", "groupnorm_merge",
-    "profile_begin", "profile_end",
+    "profile_begin", "profile_end", "select_axis",
     "step_conv", "step_groupnorm", "step_rmsnorm", "step_attention", "step_temporal_upsample",
     "version",
 ]

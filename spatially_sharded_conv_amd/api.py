@@ -134,6 +134,33 @@ class Decoder:
                                                 _stream(stream), C.byref(info)))
         return rc, info
 
+    def decode_sharded(self, latent, axis: str, n_shards: int, out, ws, starts=None, stream=None):
+        """axis: 'height', 'width' or 'auto'; starts: shard boundaries along the axis or None."""
+        b, t, h, w = self._dims(latent)
+        _dev(latent, self.dtype, "latent")
+        _dev(out, torch.float32, "out")
+        code = AXES[axis]
+        info = L.VaepDecodeInfo()
+        st = None
+        if starts is not None:
+            assert len(starts) == n_shards + 1
+            st = _starts(starts)
+        rc = L.check(L.load().vaep_decode_sharded(self._h, _p(latent), b, t, h, w, code, st, n_shards,
+                                                  _p(out), _p(ws), ws.numel(), _stream(stream),
+                                                  C.byref(info)))
+        return rc, info
+
+
+AXES = {"auto": L.AXIS_AUTO, "height": L.AXIS_HEIGHT, "width": L.AXIS_WIDTH}
+AXIS_NAMES = {L.AXIS_HEIGHT: "height", L.AXIS_WIDTH: "width", L.AXIS_DENSE: "dense"}
+
+
+def select_axis(latent_h: int, latent_w: int, n_shards: int) -> str:
+    """The library's per-request axis policy: 'height', 'width' or 'dense'."""
+    a = C.c_int32()
+    L.check(L.load().vaep_select_axis(latent_h, latent_w, n_shards, C.byref(a)), allow_warning=False)
+    return AXIS_NAMES[a.value]
+
 
 def profile_begin(dec: "Decoder", max_launches: int = 4096):
     L.check(L.load().vaep_profile_begin(dec._h, max_launches))

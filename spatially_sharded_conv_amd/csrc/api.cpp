@@ -181,6 +181,10 @@ struct ConvW {
   void* w = nullptr;
   float* b = nullptr;
   void* wsub = nullptr;   // phase-folded weights of a sub-pixel upsample conv (else NULL)
+  // The same kernels for a decode on the transposed image (width bands): 3x3 spatial taps
+  // transposed.  NULL for convs without spatial taps, which serve both orientations.
+  void* wT = nullptr;
+  void* wsubT = nullptr;
   int co = 0, ci = 0, co_pad = 0, ci_pad = 0, kt = 1, ks = 3;
   int rep = 1;            // 2: input channels repeated for an operand stored as hi / lo halves
 };
@@ -276,10 +280,13 @@ struct Builder {
     const int ci1 = bf ? round_up(ci, 32) : ci;
     w.ci_pad = ci1 * rep;
     const int taps = kt * ks * ks;
-    w.w = carve.take((size_t)w.co_pad * taps * w.ci_pad * dtype_bytes(dtype));
+    const size_t wbytes = (size_t)w.co_pad * taps * w.ci_pad * dtype_bytes(dtype);
+    w.w = carve.take(wbytes);
+    if (ks == 3) w.wT = carve.take(wbytes);
     w.b = (float*)carve.take((size_t)w.co_pad * sizeof(float));
     if (!dry) {
       ok(launch_pack_weight(P(n + ".weight"), co, ci, taps, w.w, w.co_pad, ci1, dtype, st, rep));
+      if (ks == 3) ok(launch_pack_weight(P(n + ".weight"), co, ci, taps, w.wT, w.co_pad, ci1, dtype, st, rep, true));
       ok(launch_to_f32(P(n + ".bias"), co, w.b, w.co_pad, dtype, st));
     }
     return w;
@@ -358,8 +365,14 @@ struct Builder {
       s.up_split = stage_up_split(c, i);
       if (s.sub) {
         ConvW& u = s.up_conv;
-        u.wsub = carve.take((size_t)4 * u.co_pad * 4 * 2 * u.ci_pad * 2);
-        if (!dry) ok(launch_fold_subpixel_weight(P("up" + std::to_string(i) + ".upsample.weight"), co, co, u.wsub, u.co_pad, st));
+        const size_t fbytes = (size_t)4 * u.co_pad * 4 * 2 * u.ci_pad * 2;
+        u.wsub = carve.take(fbytes);
+        u.wsubT = carve.take(fbytes);
+        if (!dry) {
+          const std::string wn = "up" + std::to_string(i) + ".upsample.weight";
+          ok(launch_fold_subpixel_weight(P(wn), co, co, u.wsub, u.co_pad, st));
+          ok(launch_fold_subpixel_weight(P(wn), co, co, u.wsubT, u.co_pad, st, true));
+        }
       }
       m.stages.push_back(s);
     }
@@ -414,6 +427,9 @@ struct Exec {
   }
   int groups = 0;      // GroupNorm groups; 0 selects channel RMSNorm
   float eps = 1e-6f;
+  // Width bands: the decode runs on the transposed image (layout rows = image columns) with
+  // the transposed 3x3 kernels; the latent is read and the output written transposed.
+  bool transposed = false;
   int base_rows = 0;   // rows of the band table's own resolution (latent rows of a decode)
 
   size_t eb() const { return dtype_bytes(dtype); }   // operand (normalised activation) element
@@ -448,11 +464,12 @@ struct Exec {
     need_act(Lin, xk == kXOp ? eb() : (xk == kXF32 ? 4 : 2));
     if (dry) return VAEP_OK;
     const bool sub = xk == kXSplit && ups;
-    if (sub && !w.wsub) return fail(VAEP_ERR_INVALID_ARG, "internal: sub-pixel conv without folded weights");
+    const void* wsel = sub ? (transposed ? w.wsubT : w.wsub) : (transposed && w.ks == 3 ? w.wT : w.w);
+    if (!wsel) return fail(VAEP_ERR_INVALID_ARG, "internal: conv weights missing for this orientation");
     ConvArgs a;
     std::memset(&a, 0, sizeof(a));
     a.x = x;
-    a.w = sub ? w.wsub : w.w;
+    a.w = wsel;
     a.bias = w.b;
     a.res = res;
     a.y = y;
@@ -472,6 +489,7 @@ struct Exec {
     a.x_split = xk == kXSplit ? 1 : 0;
     a.sub = sub ? 1 : 0;
     a.final_frames = final_frames;
+    a.out_transposed = transposed && mode == kModeFinal ? 1 : 0;
     if (Lin.C != (xk == kXSplit ? 2 : 1) * w.ci_pad)
       return fail(VAEP_ERR_INVALID_ARG, "internal: conv input has %d channels, weight %d", Lin.C, w.ci_pad);
     {
@@ -622,7 +640,7 @@ int walk(Exec& E, const void* latent, int B, int T, int W, const int* rows, int 
   int cur = 0;
   E.need_act(L, E.eb());
   if (!E.dry) {
-    hipError_t e = launch_pack(latent, c.z_channels, E.act[0], L, E.dtype, E.st);
+    hipError_t e = launch_pack(latent, c.z_channels, E.act[0], L, E.dtype, E.st, E.transposed);
     if (e != hipSuccess) return hip_fail(e, "latent pack");
     ++E.launches;
   }
@@ -703,16 +721,72 @@ int check_latent_dims(const vaep_model* m, int batch, int frames, int h, int w) 
   return VAEP_OK;
 }
 
-int plan_bytes(const vaep_model* m, int batch, int frames, int h, int w, int nb, size_t* bytes) {
+// Workspace of a decode whose nb bands cut an axis of length `cut` (the other axis `other`).
+int plan_bytes(const vaep_model* m, int batch, int frames, int cut, int other, int nb, bool transposed,
+               size_t* bytes) {
   Exec E;
   E.m = m;
   E.dtype = m->cfg.dtype;
   E.dry = true;
-  std::vector<int> rows = even_rows(h, nb);
-  int rc = walk(E, nullptr, batch, frames, w, rows.data(), nb, nullptr);
+  E.transposed = transposed;
+  std::vector<int> rows = even_rows(cut, nb);
+  int rc = walk(E, nullptr, batch, frames, other, rows.data(), nb, nullptr);
   if (rc) return rc;
   *bytes = E.total();
   return VAEP_OK;
+}
+
+// Dry pass (sizing), workspace check and the decode itself on `rows` bands of the cut axis.
+int run_decode(vaep_model* model, const void* latent, int batch, int frames, int other, bool transposed,
+               const std::vector<int>& rows, int axis_code, int status, void* out, void* ws, size_t ws_bytes,
+               void* stream, vaep_decode_info* info) {
+  const int nb = (int)rows.size();
+  Exec E;
+  E.m = model;
+  E.dtype = model->cfg.dtype;
+  E.st = (hipStream_t)stream;
+  E.dry = true;
+  E.transposed = transposed;
+  E.prof = &model->prof;
+  int rc;
+  if ((rc = walk(E, latent, batch, frames, other, rows.data(), nb, out))) return rc;
+  const size_t need = E.total();
+  if (!ws || ws_bytes < need)
+    return fail(VAEP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  E.assign((char*)ws);
+  E.dry = false;
+  if ((rc = walk(E, latent, batch, frames, other, rows.data(), nb, out))) return rc;
+  if (info) {
+    info->bands_used = nb;
+    info->fell_back = status == VAEP_WARN_FELL_BACK || axis_code == VAEP_AXIS_DENSE;
+    info->n_launches = E.launches;
+    info->axis = axis_code;
+    info->workspace_bytes = need;
+  }
+  return VAEP_OK;
+}
+
+// Row counts of a validated band table along an axis of length `len`.
+int table_rows(const int32_t* starts, int n, int len, const char* what, std::vector<int>& rows) {
+  if (starts[0] != 0 || starts[n] != len)
+    return fail(VAEP_ERR_INVALID_ARG, "%s bands must cover 0..%d (got %d..%d)", what, len, starts[0], starts[n]);
+  rows.clear();
+  for (int i = 0; i < n; ++i) {
+    if (starts[i + 1] <= starts[i])
+      return fail(VAEP_ERR_INVALID_ARG, "%s band %d is empty or reversed (%d..%d)", what, i, starts[i], starts[i + 1]);
+    rows.push_back(starts[i + 1] - starts[i]);
+  }
+  return VAEP_OK;
+}
+
+// The per-request axis policy: the longer axis that gives every shard at least one latent
+// row (the kernel radius at latent resolution), width on ties; otherwise one dense band.
+int select_axis(int h, int w, int n) {
+  if (n <= 1) return VAEP_AXIS_DENSE;
+  const bool cover_h = h >= n, cover_w = w >= n;
+  if (cover_w && (w >= h || !cover_h)) return VAEP_AXIS_WIDTH;
+  if (cover_h) return VAEP_AXIS_HEIGHT;
+  return VAEP_AXIS_DENSE;
 }
 
 
@@ -880,8 +954,16 @@ int vaep_workspace_bytes(const vaep_model* model, int batch, int frames, int lat
   if (rc) return rc;
   if (!bytes_out) return fail(VAEP_ERR_INVALID_ARG, "bytes_out is NULL");
   if (n_bands < 1) return fail(VAEP_ERR_INVALID_ARG, "n_bands must be >= 1");
-  const int nb = std::min(std::min(n_bands, kMaxBands), latent_h);
-  return plan_bytes(model, batch, frames, latent_h, latent_w, nb, bytes_out);
+  // row bands, and column bands of the same count (the larger of the two)
+  size_t rows_b = 0, cols_b = 0;
+  rc = plan_bytes(model, batch, frames, latent_h, latent_w, std::min(std::min(n_bands, kMaxBands), latent_h),
+                  false, &rows_b);
+  if (rc) return rc;
+  rc = plan_bytes(model, batch, frames, latent_w, latent_h, std::min(std::min(n_bands, kMaxBands), latent_w),
+                  true, &cols_b);
+  if (rc) return rc;
+  *bytes_out = std::max(rows_b, cols_b);
+  return VAEP_OK;
 }
 
 int vaep_decode_bands(vaep_model* model, const void* latent, int batch, int frames, int latent_h,
@@ -892,42 +974,69 @@ int vaep_decode_bands(vaep_model* model, const void* latent, int batch, int fram
   if (!latent || !out) return fail(VAEP_ERR_INVALID_ARG, "latent and out must be device pointers");
   if (!row_starts) return fail(VAEP_ERR_INVALID_ARG, "row_starts is NULL");
   if (n_bands < 1) return fail(VAEP_ERR_INVALID_ARG, "n_bands must be >= 1");
-  if (row_starts[0] != 0 || row_starts[n_bands] != latent_h)
-    return fail(VAEP_ERR_INVALID_ARG, "bands must cover rows 0..%d (got %d..%d)", latent_h, row_starts[0], row_starts[n_bands]);
-  for (int i = 0; i < n_bands; ++i)
-    if (row_starts[i + 1] <= row_starts[i])
-      return fail(VAEP_ERR_INVALID_ARG, "band %d is empty or reversed (%d..%d)", i, row_starts[i], row_starts[i + 1]);
-  int status = VAEP_OK;
   std::vector<int> rows;
+  if ((rc = table_rows(row_starts, n_bands, latent_h, "row", rows))) return rc;
+  int status = VAEP_OK;
   if (n_bands > kMaxBands) {
     rows.assign(1, latent_h);      // dense fallback: one band
     status = VAEP_WARN_FELL_BACK;
-  } else {
-    for (int i = 0; i < n_bands; ++i) rows.push_back(row_starts[i + 1] - row_starts[i]);
   }
-  const int nb = (int)rows.size();
-  Exec E;
-  E.m = model;
-  E.dtype = model->cfg.dtype;
-  E.st = (hipStream_t)stream;
-  E.dry = true;
-  E.prof = &model->prof;
-  if ((rc = walk(E, latent, batch, frames, latent_w, rows.data(), nb, out))) return rc;
-  const size_t need = E.total();
-  if (!ws || ws_bytes < need)
-    return fail(VAEP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
-  E.assign((char*)ws);
-  E.dry = false;
-  if ((rc = walk(E, latent, batch, frames, latent_w, rows.data(), nb, out))) return rc;
-  if (info) {
-    info->bands_used = nb;
-    info->fell_back = status == VAEP_WARN_FELL_BACK;
-    info->n_launches = E.launches;
-    info->reserved = 0;
-    info->workspace_bytes = need;
-  }
+  rc = run_decode(model, latent, batch, frames, latent_w, false, rows,
+                  status == VAEP_OK ? VAEP_AXIS_HEIGHT : VAEP_AXIS_DENSE, status, out, ws, ws_bytes, stream, info);
+  if (rc) return rc;
   if (status == VAEP_WARN_FELL_BACK)
     fail(VAEP_WARN_FELL_BACK, "%d bands exceed the %d-band limit: decoded as one dense band", n_bands, kMaxBands);
+  return status;
+}
+
+int vaep_select_axis(int latent_h, int latent_w, int n_shards, int32_t* axis_out) {
+  if (!axis_out) return fail(VAEP_ERR_INVALID_ARG, "axis_out is NULL");
+  if (latent_h < 1 || latent_w < 1 || n_shards < 1)
+    return fail(VAEP_ERR_INVALID_ARG, "latent %dx%d and n_shards %d must be >= 1", latent_h, latent_w, n_shards);
+  *axis_out = select_axis(latent_h, latent_w, n_shards);
+  return VAEP_OK;
+}
+
+int vaep_decode_sharded(vaep_model* model, const void* latent, int batch, int frames, int latent_h,
+                        int latent_w, int axis, const int32_t* starts, int n_shards, void* out, void* ws,
+                        size_t ws_bytes, void* stream, vaep_decode_info* info) {
+  int rc = check_latent_dims(model, batch, frames, latent_h, latent_w);
+  if (rc) return rc;
+  if (!latent || !out) return fail(VAEP_ERR_INVALID_ARG, "latent and out must be device pointers");
+  if (n_shards < 1) return fail(VAEP_ERR_INVALID_ARG, "n_shards must be >= 1");
+  if (axis != VAEP_AXIS_AUTO && axis != VAEP_AXIS_HEIGHT && axis != VAEP_AXIS_WIDTH)
+    return fail(VAEP_ERR_INVALID_ARG, "axis %d is not VAEP_AXIS_AUTO, _HEIGHT or _WIDTH", axis);
+  if (axis == VAEP_AXIS_AUTO && starts)
+    return fail(VAEP_ERR_INVALID_ARG, "VAEP_AXIS_AUTO picks the axis per request: starts must be NULL");
+  int status = VAEP_OK;
+  int chosen = axis;
+  const char* why = nullptr;
+  if (axis == VAEP_AXIS_AUTO) {
+    chosen = select_axis(latent_h, latent_w, n_shards);
+    if (chosen != VAEP_AXIS_DENSE && n_shards > kMaxBands) chosen = VAEP_AXIS_DENSE;
+  }
+  const int len = chosen == VAEP_AXIS_WIDTH ? latent_w : latent_h;
+  std::vector<int> rows;
+  if (chosen != VAEP_AXIS_DENSE && starts) {
+    if ((rc = table_rows(starts, n_shards, len, chosen == VAEP_AXIS_WIDTH ? "column" : "row", rows))) return rc;
+  } else if (chosen != VAEP_AXIS_DENSE) {
+    if (len < n_shards) why = "the axis is shorter than the shard count";
+    else rows = even_rows(len, n_shards);
+  }
+  if (chosen != VAEP_AXIS_DENSE && !why && n_shards > kMaxBands) why = "the shard count exceeds the band limit";
+  if (why) {              // an explicit axis that cannot be honoured: warn and decode dense
+    chosen = VAEP_AXIS_DENSE;
+    status = VAEP_WARN_FELL_BACK;
+  }
+  if (chosen == VAEP_AXIS_DENSE) rows.assign(1, latent_h);
+  const bool tr = chosen == VAEP_AXIS_WIDTH;
+  rc = run_decode(model, latent, batch, frames, tr ? latent_h : latent_w, tr, rows, chosen, status, out, ws,
+                  ws_bytes, stream, info);
+  if (rc) return rc;
+  if (info) info->fell_back = chosen == VAEP_AXIS_DENSE && n_shards > 1;
+  if (status == VAEP_WARN_FELL_BACK)
+    fail(VAEP_WARN_FELL_BACK, "%d shards along the %s: %s; decoded as one dense band", n_shards,
+         axis == VAEP_AXIS_WIDTH ? "width" : "height", why);
   return status;
 }
 

@@ -402,7 +402,8 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
           const int T = a.final_frames;
           const int bsm = n / T, t = n - bsm * T;
           const long long hw = (long long)a.in.H * a.in.W;
-          const long long pix = (long long)(a.in.row0[band] + r) * a.in.W + c;
+          const long long pix = a.out_transposed ? (long long)c * a.in.H + (a.in.row0[band] + r)
+                                                : (long long)(a.in.row0[band] + r) * a.in.W + c;
           float* o = reinterpret_cast<float*>(a.y);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -475,7 +476,8 @@ __global__ void __launch_bounds__(128) conv_f32(const ConvArgs a) {
     const int T = a.final_frames;
     const int bsm = n / T, t = n - bsm * T;
     const long long hw = (long long)a.in.H * a.in.W;
-    const long long pix = (long long)(a.in.row0[band] + r) * a.in.W + c;
+    const long long pix = a.out_transposed ? (long long)c * a.in.H + (a.in.row0[band] + r)
+                                                : (long long)(a.in.row0[band] + r) * a.in.W + c;
     reinterpret_cast<float*>(a.y)[(((long long)bsm * a.cout + co) * T + t) * hw + pix] = v;
   }
 }

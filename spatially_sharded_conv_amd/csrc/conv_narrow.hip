@@ -141,7 +141,8 @@ __global__ void __launch_bounds__(256) conv_narrow(const ConvArgs a) {
       const int rem = (int)(p - (long long)n * plane);
       const int r = rem / W, c = rem - (rem / W) * W;
       const int bs = n / T, t = n - bs * T;
-      out[(((long long)bs * a.cout + co) * T + t) * hw + (long long)(g0 + r) * W + c] = acc[rb][v] + bias;
+      const long long pix = a.out_transposed ? (long long)c * a.in.H + (g0 + r) : (long long)(g0 + r) * W + c;
+      out[(((long long)bs * a.cout + co) * T + t) * hw + pix] = acc[rb][v] + bias;
     }
 }
 

@@ -7,7 +7,7 @@ namespace vaep {
 namespace {
 
 template <typename T>
-__global__ void pack_kernel(const T* src, int c_src, T* dst, const BandLayout L) {
+__global__ void pack_kernel(const T* src, int c_src, T* dst, const BandLayout L, int tr) {
   const int b = blockIdx.y;
   const long long total = (long long)L.n_img * (L.rows[b] + 2) * L.W * L.C;
   const long long HW = (long long)L.H * L.W;
@@ -23,7 +23,8 @@ __global__ void pack_kernel(const T* src, int c_src, T* dst, const BandLayout L)
     T v = T(0.f);
     if (ch < c_src && g >= 0 && g < L.H) {
       const int bs = n / L.frames, t = n - bs * L.frames;
-      v = src[(((long long)bs * c_src + ch) * L.frames + t) * HW + (long long)g * L.W + c];
+      const long long pix = tr ? (long long)c * L.H + g : (long long)g * L.W + c;
+      v = src[(((long long)bs * c_src + ch) * L.frames + t) * HW + pix];
     }
     dst[L.off[b] + i] = v;
   }
@@ -63,7 +64,7 @@ __global__ void copy_frame0_kernel(const T* src, const BandLayout Ls, T* dst, co
 
 template <typename T>
 __global__ void pack_weight_kernel(const T* src, int co, int ci, int taps, T* dst, int co_pad,
-                                   int ci_pad, int rep) {
+                                   int ci_pad, int rep, int tr) {
   // rep copies of the ci_pad input channels per tap (rep = 2: one per bf16 part of a
   // split operand)
   const int row = ci_pad * rep;
@@ -74,7 +75,9 @@ __global__ void pack_weight_kernel(const T* src, int co, int ci, int taps, T* ds
     const int t = (int)((i / row) % taps);
     const int o = (int)(i / ((long long)row * taps));
     T v = T(0.f);
-    if (o < co && c < ci) v = src[((long long)o * ci + c) * taps + t];
+    // the transposed kernel swaps the two spatial tap indices within each time tap
+    const int ts = tr ? (t / 9) * 9 + (t % 3) * 3 + (t % 9) / 3 : t;
+    if (o < co && c < ci) v = src[((long long)o * ci + c) * taps + ts];
     dst[i] = v;
   }
 }
@@ -83,7 +86,7 @@ __global__ void pack_weight_kernel(const T* src, int co, int ci, int taps, T* ds
 // dy reads source row offset floor((py + dy - 1) / 2), which is -1, 0, 0 for py = 0 and
 // 0, 0, 1 for py = 1; folded row tap a of phase py sums the kernel rows whose offset is
 // a - 1 + py (columns likewise).  The fp32 sum is stored as bf16 hi and lo parts.
-__global__ void fold_subpixel_kernel(const bf16* src, int co, int ci, bf16* dst, int co_pad) {
+__global__ void fold_subpixel_kernel(const bf16* src, int co, int ci, bf16* dst, int co_pad, int tr) {
   const long long total = 4LL * co_pad * 4 * ci;
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (long long)gridDim.x * blockDim.x) {
@@ -98,7 +101,7 @@ __global__ void fold_subpixel_kernel(const bf16* src, int co, int ci, bf16* dst,
         if (((py + dy - 1) >> 1) != ta - 1 + py) continue;
         for (int dx = 0; dx < 3; ++dx) {
           if (((px + dx - 1) >> 1) != tb - 1 + px) continue;
-          w += (float)src[(((long long)o * ci + c) * 3 + dy) * 3 + dx];
+          w += (float)src[(((long long)o * ci + c) * 3 + (tr ? dx : dy)) * 3 + (tr ? dy : dx)];
         }
       }
     }
@@ -138,7 +141,7 @@ int grid_for(long long n) {
 }  // namespace
 
 hipError_t launch_pack(const void* src, int c_src, void* dst, const BandLayout& L, int dtype,
-                       hipStream_t s) {
+                       hipStream_t s, bool transposed) {
   long long mx = 0;
   for (int b = 0; b < L.nb; ++b) {
     const long long e = (long long)L.n_img * (L.rows[b] + 2) * L.W * L.C;
@@ -146,9 +149,11 @@ hipError_t launch_pack(const void* src, int c_src, void* dst, const BandLayout& 
   }
   dim3 grid(grid_for(mx), L.nb);
   if (dtype == VAEP_DTYPE_F32)
-    hipLaunchKernelGGL(pack_kernel<float>, grid, dim3(256), 0, s, (const float*)src, c_src, (float*)dst, L);
+    hipLaunchKernelGGL(pack_kernel<float>, grid, dim3(256), 0, s, (const float*)src, c_src, (float*)dst, L,
+                       transposed ? 1 : 0);
   else
-    hipLaunchKernelGGL(pack_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)src, c_src, (bf16*)dst, L);
+    hipLaunchKernelGGL(pack_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)src, c_src, (bf16*)dst, L,
+                       transposed ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -179,22 +184,24 @@ hipError_t launch_copy_frame0(const void* src, const BandLayout& Ls, void* dst, 
 }
 
 hipError_t launch_pack_weight(const void* src, int co, int ci, int taps, void* dst, int co_pad,
-                              int ci_pad, int dtype, hipStream_t s, int rep) {
+                              int ci_pad, int dtype, hipStream_t s, int rep, bool transposed) {
+  if (transposed && taps % 9 != 0) return hipErrorInvalidValue;
   const long long total = (long long)co_pad * taps * ci_pad * rep;
+  const int tr = transposed ? 1 : 0;
   if (dtype == VAEP_DTYPE_F32)
     hipLaunchKernelGGL(pack_weight_kernel<float>, dim3(grid_for(total)), dim3(256), 0, s,
-                       (const float*)src, co, ci, taps, (float*)dst, co_pad, ci_pad, rep);
+                       (const float*)src, co, ci, taps, (float*)dst, co_pad, ci_pad, rep, tr);
   else
     hipLaunchKernelGGL(pack_weight_kernel<bf16>, dim3(grid_for(total)), dim3(256), 0, s,
-                       (const bf16*)src, co, ci, taps, (bf16*)dst, co_pad, ci_pad, rep);
+                       (const bf16*)src, co, ci, taps, (bf16*)dst, co_pad, ci_pad, rep, tr);
   return hipGetLastError();
 }
 
 hipError_t launch_fold_subpixel_weight(const void* src, int co, int ci, void* dst, int co_pad,
-                                       hipStream_t s) {
+                                       hipStream_t s, bool transposed) {
   const long long total = 4LL * co_pad * 4 * ci;
   hipLaunchKernelGGL(fold_subpixel_kernel, dim3(grid_for(total)), dim3(256), 0, s, (const bf16*)src, co, ci,
-                     (bf16*)dst, co_pad);
+                     (bf16*)dst, co_pad, transposed ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -78,6 +78,8 @@ struct ConvArgs {
   int sub;              // nearest-2x + 3x3 conv in sub-pixel form: w holds the phase-folded
                         // weights of launch_fold_subpixel_weight; needs x_split
   int final_frames;     // kModeFinal: frames per sample of the output tensor
+  int out_transposed;   // kModeFinal: the bands cut the output's columns -- band-layout row g,
+                        // column c is output pixel (row c, column g) of an in.W x in.H image
   int tiles_total;      // M tiles over all bands
   int tile_start[kMaxBands + 1];  // prefix of M tiles per band
   int kernel_used;      // set by the launch: VAEP_KERNEL_*
@@ -100,8 +102,9 @@ bool conv_narrow_fits(const ConvArgs& a);
 hipError_t launch_conv_narrow(ConvArgs& a, hipStream_t s);
 // Phase-folded weights of a nearest-2x + 3x3 conv: src [co][ci][3][3] bf16 ->
 // dst [4 phases][co_pad][4 taps][2 parts (hi, lo)][ci] bf16; zero rows past co.
+// transposed: fold the transposed 3x3 kernel (for decodes on the transposed image).
 hipError_t launch_fold_subpixel_weight(const void* src, int co, int ci, void* dst, int co_pad,
-                                       hipStream_t s);
+                                       hipStream_t s, bool transposed = false);
 // fp32 band buffer (channels c) -> bf16 [hi | lo] band buffer (channels 2c), halo rows included.
 hipError_t launch_split(const float* src, const BandLayout& L, void* dst, hipStream_t s);
 
@@ -160,9 +163,11 @@ hipError_t launch_attention(AttnArgs& a, int dtype, hipStream_t s);
 
 // ------------------------------------------------------------------ data movement
 // NC[T]HW tensor -> band layout (halo rows filled from neighbours, zeros at image
-// edges, channels >= c_src zero).  n_img = B*T.
+// edges, channels >= c_src zero).  n_img = B*T.  transposed: the bands cut the source's
+// columns -- layout row g, column c reads source pixel (row c, column g) of an L.W x L.H
+// image.
 hipError_t launch_pack(const void* src, int c_src, void* dst, const BandLayout& L, int dtype,
-                       hipStream_t s);
+                       hipStream_t s, bool transposed = false);
 // band layout -> NC[T]HW tensor with c_dst channels.
 hipError_t launch_unpack(const void* src, const BandLayout& L, void* dst, int c_dst, int dtype,
                          hipStream_t s);
@@ -172,8 +177,10 @@ hipError_t launch_copy_frame0(const void* src, const BandLayout& Ls, void* dst,
                               const BandLayout& Ld, int dtype, hipStream_t s);
 // Conv weight [co][ci][taps] (dtype) -> [co_pad][taps][rep * ci_pad] (dtype), zero padded;
 // rep = 2 repeats the input channels for an operand stored as bf16 hi / lo halves.
+// transposed (3x3 spatial taps only, taps = kt * 9): packed tap (dt, a, b) takes source
+// tap (dt, b, a), the kernel of the same conv on the transposed image.
 hipError_t launch_pack_weight(const void* src, int co, int ci, int taps, void* dst, int co_pad,
-                              int ci_pad, int dtype, hipStream_t s, int rep = 1);
+                              int ci_pad, int dtype, hipStream_t s, int rep = 1, bool transposed = false);
 // Any-dtype vector -> fp32 vector of n_pad entries (zero padded); src may be NULL (zeros).
 hipError_t launch_to_f32(const void* src, int n, float* dst, int n_pad, int dtype, hipStream_t s);
 

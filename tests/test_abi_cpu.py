@@ -145,3 +145,33 @@ def test_too_many_bands_rejected_by_steps():
     starts = list(range(0, 66))
     rc, _ = _size_query_conv(starts, h=65)
     assert rc == L.VAEP_ERR_INVALID_ARG
+
+
+def test_select_axis_matches_the_oracle_policy():
+    # the library's per-request axis policy against the oracle's reading of the strategy
+    # page (host-only call, no device)
+    from oracle import choose_axis
+    for h in range(1, 13):
+        for w in range(1, 13):
+            for n in range(1, 14):
+                assert api.select_axis(h, w, n) == choose_axis(h, w, n), (h, w, n)
+    assert api.select_axis(60, 104, 4) == "width"
+    assert api.select_axis(128, 128, 8) == "width"
+
+
+def test_select_axis_argument_checks():
+    lib = L.load()
+    a = C.c_int32()
+    assert lib.vaep_select_axis(8, 8, 2, None) == L.VAEP_ERR_INVALID_ARG
+    assert lib.vaep_select_axis(0, 8, 2, C.byref(a)) == L.VAEP_ERR_INVALID_ARG
+    assert lib.vaep_select_axis(8, 8, 0, C.byref(a)) == L.VAEP_ERR_INVALID_ARG
+
+
+def test_sharded_decode_argument_checks_without_gpu_work():
+    lib = L.load()
+    bad = C.c_void_p(1)
+
+    # NULL model, then NULL pointers, unknown axis and starts with auto on a NULL model
+    assert lib.vaep_decode_sharded(None, bad, 1, 1, 8, 8, L.AXIS_WIDTH, None, 2, bad, bad, 0, None,
+                                   None) == L.VAEP_ERR_INVALID_ARG
+    assert "model" in L.last_error()
