@@ -85,17 +85,20 @@ bool stage_ups(const vaep_config& c, int i) { return i < c.n_stages - 1; }
 bool stage_time_ups(const vaep_config& c, int i) {
   return is_video(c) && stage_ups(c, i) && i < c.temporal_up_stages;
 }
-// bf16 stages whose spatial upsample runs in sub-pixel form on the wide conv kernel: the
-// stage's last resnet stores its output as bf16 hi/lo parts (64-channel K steps).
-bool stage_sub(const vaep_config& c, int i) {
-  return c.dtype == VAEP_DTYPE_BF16 && stage_ups(c, i) && !stage_time_ups(c, i) &&
-         c.resnets_per_stage >= 1 && c.stage_channels[i] % 64 == 0;
+// bf16 stages whose spatial upsample runs in sub-pixel form on the wide conv kernel
+// (64-channel K steps); its operand is the stream as bf16 hi/lo parts.
+bool stage_sub_up(const vaep_config& c, int i) {
+  return c.dtype == VAEP_DTYPE_BF16 && stage_ups(c, i) && c.stage_channels[i] % 64 == 0 &&
+         (stage_time_ups(c, i) || c.resnets_per_stage >= 1);
 }
+// ... where the stage's last resnet stores its output directly as those parts.  After a
+// temporal upsample the stream is split by a separate pass instead.
+bool stage_sub(const vaep_config& c, int i) { return stage_sub_up(c, i) && !stage_time_ups(c, i); }
 // A sub-pixel upsample whose output feeds only GroupNorm/RMSNorm and a 1x1 shortcut (the
 // next stage changes the channel count) stores it as hi / lo halves: the shortcut is then
 // a plain bf16 conv over both halves.
 bool stage_up_split(const vaep_config& c, int i) {
-  return stage_sub(c, i) && i + 1 < c.n_stages && c.stage_channels[i + 1] != c.stage_channels[i];
+  return stage_sub_up(c, i) && i + 1 < c.n_stages && c.stage_channels[i + 1] != c.stage_channels[i];
 }
 
 // Canonical parameter list (names follow the decoder structure).
@@ -206,7 +209,8 @@ struct AttnW {
 struct StageW {
   std::vector<ResW> res;
   bool time_up = false, up = false;
-  bool sub = false;       // the last resnet writes a split stream and the upsample runs sub-pixel
+  bool sub_up = false;    // the upsample runs sub-pixel on a split stream
+  bool sub = false;       // the last resnet writes that split stream (else a split pass does)
   bool up_split = false;  // the upsample writes its output as hi / lo halves for the next stage
   ConvW time_conv, up_conv;
 };
@@ -361,9 +365,10 @@ struct Builder {
       if (s.time_up) s.time_conv = conv("up" + std::to_string(i) + ".time_conv", 2 * co, co, 3, 1);
       s.up = stage_ups(c, i);
       if (s.up) s.up_conv = conv("up" + std::to_string(i) + ".upsample", co, co, 1, 3);
+      s.sub_up = stage_sub_up(c, i);
       s.sub = stage_sub(c, i);
       s.up_split = stage_up_split(c, i);
-      if (s.sub) {
+      if (s.sub_up) {
         ConvW& u = s.up_conv;
         const size_t fbytes = (size_t)4 * u.co_pad * 4 * 2 * u.ci_pad * 2;
         u.wsub = carve.take(fbytes);
@@ -556,6 +561,21 @@ struct Exec {
     return VAEP_OK;
   }
 
+  // fp32 band buffer -> bf16 hi / lo halves (2C channels), halo rows included
+  int split(const void* x, const BandLayout& L, void* y) {
+    if (dry) return VAEP_OK;
+    vaep_profile_entry pe = entry(VAEP_STEP_MOVE, 1);
+    pe.cin = pe.cout = L.C;
+    pe.pixels = (long long)L.n_img * L.H * L.W;
+    pe.bytes = (double)layout_elems(L) * 8.0;
+    rec_begin(pe);
+    hipError_t e = launch_split(reinterpret_cast<const float*>(x), L, y, st);
+    rec_end();
+    if (e != hipSuccess) return hip_fail(e, "split launch");
+    ++launches;
+    return VAEP_OK;
+  }
+
   int attention(const AttnW& w, const void* x, const BandLayout& L, void* a_buf, void* o_buf, void* y) {
     const int c = L.C;
     qkv_bytes = std::max(qkv_bytes, (size_t)L.n_img * L.H * L.W * c * eb());
@@ -677,7 +697,15 @@ int walk(Exec& E, const void* latent, int B, int T, int W, const int* rows, int 
       int o[3];
       others(cur, o);
       const BandLayout Lu = upsampled(L, (s.up_split ? 2 : 1) * s.up_conv.co);
-      if ((rc = E.conv(s.up_conv, E.act[cur], L, s.sub ? kXSplit : kXF32, E.act[o[0]], Lu,
+      int src = cur;
+      BandLayout Ls = L;
+      if (s.sub_up && !s.sub) {   // split the fp32 stream (halo rows included) for the sub-pixel conv
+        Ls = reshaped(L, 2 * L.C, L.n_img, L.frames);
+        E.need_act(Ls, 2);
+        src = o[1];
+        if ((rc = E.split(E.act[cur], L, E.act[src]))) return rc;
+      }
+      if ((rc = E.conv(s.up_conv, E.act[src], Ls, s.sub_up ? kXSplit : kXF32, E.act[o[0]], Lu,
                        s.up_split ? kModeBandSplit : kModeBand, nullptr, 1)))
         return rc;
       cur = o[0];
