@@ -102,7 +102,11 @@ __device__ __forceinline__ int band_of_block(const int* start, int nb, int blk) 
   return b;
 }
 
-__device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
+// SiLU(v) = v / (1 + e^-v), with the hardware reciprocal (1 ulp) instead of an IEEE
+// division: the result is rounded to the bf16 operand format (or feeds an fp32 conv
+// operand) and the division's ten-instruction sequence made the norm passes VALU-bound.
+// v -> -inf: e^-v = inf, rcp(inf) = 0, result -0 as with the division.
+__device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.f + __expf(-v)); }
 
 // Pass 1: central moments of one tile (a pixel chunk of one slab of one image):
 // partials[tile][g] = (mean, M2) of group g.  Each thread streams its channel slot over
@@ -402,6 +406,93 @@ __global__ void __launch_bounds__(kThreads) rms_apply(const NormArgs a) {
   }
 }
 
+// Channel RMSNorm, one wave per run of P pixels: the run's P*C fp32 values are K float4
+// per lane, contiguous (P*C = 256*K), so every load and store of a wave covers one
+// contiguous span.  The per-pixel sums of squares are combined through the wave's own
+// LDS rows (no workgroup barrier), then every lane scales its values by the rstd of
+// their pixel.  A run never crosses an image or band (the last run of one is partial).
+// item_start holds the first run of each band.
+template <typename TO, bool XS, bool NT, int K>
+__global__ void __launch_bounds__(kThreads) rms_wave(const NormArgs a, int runs_total) {
+  constexpr int P4 = 64 * K;                 // float4 slots of one run
+  __shared__ float part[kThreads / 64][P4];
+  __shared__ float rsq[kThreads / 64][64];
+  const BandLayout& L = a.L;
+  const int C = L.C, Q = C / V;              // float4 slots of one pixel
+  const int P = P4 / Q;                      // pixels of one run
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  TO* Y = reinterpret_cast<TO*>(a.y);
+  const int stride = gridDim.x * (kThreads / 64);
+  // a lane's slots sit at the same (pixel, channel) of every run
+  int spix[K], sch[K];
+  float gam[K][V];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int slot = j * 64 + lane;
+    spix[j] = slot / Q;
+    sch[j] = (slot - spix[j] * Q) * V;
+#pragma unroll
+    for (int e = 0; e < V; ++e) gam[j][e] = a.gamma[sch[j] + e];
+  }
+  for (int u = blockIdx.x * (kThreads / 64) + wv; u < runs_total; u += stride) {
+    int b = 0;
+    while (b + 1 < L.nb && u >= (int)a.item_start[b + 1]) ++b;
+    const int lu = u - (int)a.item_start[b];
+    const int img_pix = L.rows[b] * L.W;
+    const int runs_img = (img_pix + P - 1) / P;
+    const int n = lu / runs_img;
+    const int p0 = (lu - n * runs_img) * P;
+    const int np = img_pix - p0 < P ? img_pix - p0 : P;
+    const long long base = row_offset(L, b, n, 0);
+    float x[K][V];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      if (spix[j] < np) {
+        loadx4<XS, NT>(a.x, base + (long long)(p0 + spix[j]) * C, C, sch[j], x[j]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) x[j][e] = 0.f;
+      }
+      float q = 0.f;
+#pragma unroll
+      for (int e = 0; e < V; ++e) q = fmaf(x[j][e], x[j][e], q);
+      part[wv][j * 64 + lane] = q;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < P) {
+      float t = 0.f;
+      for (int i = 0; i < Q; ++i) t += part[wv][lane * Q + i];
+      rsq[wv][lane] = rsqrtf(t / (float)C + a.eps);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int last_row = (L.rows[b] - 1) * L.W;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      if (spix[j] >= np) continue;
+      const float rr = rsq[wv][spix[j]];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float y = x[j][e] * rr * gam[j][e];
+        x[j][e] = a.act ? silu(y) : y;
+      }
+      const int p = p0 + spix[j];
+      Out<TO>::store4(Y + base + (long long)p * C + sch[j], x[j]);
+      if (p < L.W && b > 0)
+        Out<TO>::store4(Y + row_offset(L, b - 1, n, L.rows[b - 1]) + (long long)p * C + sch[j], x[j]);
+      if (p >= last_row && b + 1 < L.nb)
+        Out<TO>::store4(Y + row_offset(L, b + 1, n, -1) + (long long)(p - last_row) * C + sch[j], x[j]);
+    }
+    // the next run reuses part / rsq
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
 // Standalone merge of caller-supplied shard moments (one thread per statistic).
 __global__ void moment_merge(int n_shards, int n_stats, const float* mean, const float* var,
                              const int64_t* counts, float* mean_out, float* var_out) {
@@ -520,9 +611,53 @@ hipError_t launch_groupnorm(NormArgs& a, int dtype, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename TO, bool XS, bool NT>
+static hipError_t go_rms_wave(NormArgs& a, int k, hipStream_t s) {
+  const BandLayout& L = a.L;
+  const int P = 64 * k / (L.C / V);
+  long long runs = 0;
+  for (int b = 0; b < L.nb; ++b) {
+    a.item_start[b] = runs;
+    runs += (long long)L.n_img * (((long long)L.rows[b] * L.W + P - 1) / P);
+  }
+  a.item_start[L.nb] = runs;
+  if (runs == 0) return hipSuccess;
+  // 32-bit run and pixel indices in the kernel
+  if (runs > 0x7fffffffLL) return hipErrorInvalidValue;
+  for (int b = 0; b < L.nb; ++b)
+    if ((long long)L.rows[b] * L.W + P > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int r32 = (int)runs;
+  long long nblk = (runs + 3) / 4;
+  if (nblk > 4096) nblk = 4096;
+  if (k == 1) hipLaunchKernelGGL((rms_wave<TO, XS, NT, 1>), dim3((int)nblk), dim3(kThreads), 0, s, a, r32);
+  if (k == 2) hipLaunchKernelGGL((rms_wave<TO, XS, NT, 2>), dim3((int)nblk), dim3(kThreads), 0, s, a, r32);
+  if (k == 3) hipLaunchKernelGGL((rms_wave<TO, XS, NT, 3>), dim3((int)nblk), dim3(kThreads), 0, s, a, r32);
+  if (k == 4) hipLaunchKernelGGL((rms_wave<TO, XS, NT, 4>), dim3((int)nblk), dim3(kThreads), 0, s, a, r32);
+  return hipGetLastError();
+}
+
+// float4 slots per lane of the wave-per-run RMSNorm for C channels: the smallest k with
+// 64 * k a multiple of C / 4, if it is at most 4 (else 0: the per-pixel kernel runs).
+static int rms_wave_k(int C) {
+  const int q = C / V;
+  for (int k = 1; k <= 4; ++k)
+    if ((64 * k) % q == 0 && 64 * k / q <= 64) return k;
+  return 0;
+}
+
 hipError_t launch_rmsnorm(NormArgs& a, int dtype, hipStream_t s) {
   const BandLayout& L = a.L;
   if (L.C % V != 0 || L.C / V > kThreads) return hipErrorInvalidValue;
+  const int k = rms_wave_k(L.C);
+  if (k > 0 && dtype == VAEP_DTYPE_BF16) {
+    long long elems = 0;
+    for (int b = 0; b < L.nb; ++b) elems += (long long)L.n_img * L.rows[b] * L.W * L.C;
+    const bool nt = elems * 4 >= kStreamBytes;
+    if (a.x_split && nt) return go_rms_wave<bf16, true, true>(a, k, s);
+    if (a.x_split) return go_rms_wave<bf16, true, false>(a, k, s);
+    if (nt) return go_rms_wave<bf16, false, true>(a, k, s);
+    return go_rms_wave<bf16, false, false>(a, k, s);
+  }
   long long pt = 0;
   for (int b = 0; b < L.nb; ++b) {
     a.item_start[b] = pt;
