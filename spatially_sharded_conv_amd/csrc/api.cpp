@@ -435,6 +435,11 @@ struct Exec {
   // Width bands: the decode runs on the transposed image (layout rows = image columns) with
   // the transposed 3x3 kernels; the latent is read and the output written transposed.
   bool transposed = false;
+  // The last conv's output whose GroupNorm tile records it wrote into `scratch` (in its
+  // epilogue), and their chunk width; the next norm of exactly that buffer uses them.
+  const void* gn_src = nullptr;
+  int gn_src_chunk = 0;
+  static constexpr int kMinGnChunk = kConvTileM;   // narrowest conv pixel tile
   int base_rows = 0;   // rows of the band table's own resolution (latent rows of a decode)
 
   size_t eb() const { return dtype_bytes(dtype); }   // operand (normalised activation) element
@@ -462,12 +467,21 @@ struct Exec {
   // xk: what the input buffer holds (kXOp: a normalised activation in the operand dtype;
   // kXF32: an fp32 conv output; kXSplit: bf16 hi/lo parts of an fp32 conv output, 2x the
   // channels).  A split input with ups runs the sub-pixel form with w.wsub.
+  // gn_next: a GroupNorm reads the output next; the conv may then form its tile statistics.
   int conv(const ConvW& w, const void* x, const BandLayout& Lin, int xk, void* y,
-           const BandLayout& Lout, int mode, const void* res, int ups, int final_frames = 1) {
+           const BandLayout& Lout, int mode, const void* res, int ups, int final_frames = 1,
+           bool gn_next = false) {
     if (mode == kModeBand || mode == kModeTimeInterleave) need_act(Lout, 4);
     if (mode == kModeBandSplit) need_act(Lout, 2);
     need_act(Lin, xk == kXOp ? eb() : (xk == kXF32 ? 4 : 2));
+    gn_next = gn_next && groups > 0 && dtype == VAEP_DTYPE_BF16 &&
+              (mode == kModeBand || mode == kModeBandSplit);
+    if (gn_next) {
+      const BandLayout Lg = mode == kModeBandSplit ? reshaped(Lout, Lout.C / 2, Lout.n_img, Lout.frames) : Lout;
+      scratch_bytes = std::max(scratch_bytes, gn_partials_floats(Lg, groups, 1, kMinGnChunk) * sizeof(float));
+    }
     if (dry) return VAEP_OK;
+    gn_src = nullptr;
     const bool sub = xk == kXSplit && ups;
     const void* wsel = sub ? (transposed ? w.wsubT : w.wsub) : (transposed && w.ks == 3 ? w.wT : w.w);
     if (!wsel) return fail(VAEP_ERR_INVALID_ARG, "internal: conv weights missing for this orientation");
@@ -495,6 +509,8 @@ struct Exec {
     a.sub = sub ? 1 : 0;
     a.final_frames = final_frames;
     a.out_transposed = transposed && mode == kModeFinal ? 1 : 0;
+    a.gn_part = gn_next ? reinterpret_cast<double*>(scratch) : nullptr;
+    a.gn_groups = gn_next ? groups : 0;
     if (Lin.C != (xk == kXSplit ? 2 : 1) * w.ci_pad)
       return fail(VAEP_ERR_INVALID_ARG, "internal: conv input has %d channels, weight %d", Lin.C, w.ci_pad);
     {
@@ -519,6 +535,10 @@ struct Exec {
     rec_end();
     if (e != hipSuccess) return hip_fail(e, "conv launch");
     ++launches;
+    if (a.gn_part && a.gn_chunk > 0) {
+      gn_src = y;
+      gn_src_chunk = a.gn_chunk;
+    }
     return VAEP_OK;
   }
 
@@ -531,8 +551,12 @@ struct Exec {
     if (groups > 0)
       scratch_bytes = std::max(scratch_bytes, gn_partials_floats(L, groups, slab_rows) * sizeof(float));
     if (dry) return VAEP_OK;
+    // statistics already formed by the conv that wrote x
+    const int pre = (groups > 0 && x == gn_src) ? gn_src_chunk : 0;
+    gn_src = nullptr;
     NormArgs a;
     std::memset(&a, 0, sizeof(a));
+    a.pre_chunk = pre;
     a.x = x;
     a.x_split = x_split ? 1 : 0;
     a.y = y;
@@ -546,18 +570,20 @@ struct Exec {
     a.merged_out = merged_out;
     a.slab_rows = slab_rows;
     {
-      vaep_profile_entry pe = entry(groups > 0 ? VAEP_STEP_GROUPNORM : VAEP_STEP_RMSNORM, groups > 0 ? 3 : 1);
+      vaep_profile_entry pe = entry(groups > 0 ? VAEP_STEP_GROUPNORM : VAEP_STEP_RMSNORM,
+                                    groups > 0 ? (pre ? 2 : 3) : 1);
       const double elems = (double)L.n_img * L.H * L.W * L.C;
       pe.cin = pe.cout = L.C;
       pe.pixels = (long long)L.n_img * L.H * L.W;
-      // GroupNorm: statistics read + apply read (fp32) + apply write; RMSNorm: one read + write
-      pe.bytes = elems * ((groups > 0 ? 8.0 : 4.0) + (double)eb());
+      // GroupNorm: statistics read (unless the producing conv formed them) + apply read
+      // (fp32) + apply write; RMSNorm: one read + write
+      pe.bytes = elems * ((groups > 0 && !pre ? 8.0 : 4.0) + (double)eb());
       rec_begin(pe);
     }
     hipError_t e = groups > 0 ? launch_groupnorm(a, dtype, st) : launch_rmsnorm(a, dtype, st);
     rec_end();
     if (e != hipSuccess) return hip_fail(e, "norm launch");
-    launches += groups > 0 ? 3 : 1;
+    launches += groups > 0 ? (pre ? 2 : 3) : 1;
     return VAEP_OK;
   }
 
@@ -607,7 +633,7 @@ struct Exec {
       if (e != hipSuccess) return hip_fail(e, "attention launch");
       ++launches;
     }
-    return conv(w.out, o_buf, L, kXOp, y, L, kModeBand, x, 0);
+    return conv(w.out, o_buf, L, kXOp, y, L, kModeBand, x, 0, 1, true);
   }
 };
 
@@ -629,7 +655,7 @@ int resnet(Exec& E, const ResW& r, int& cur, BandLayout& L, bool split_out = fal
   const BandLayout Ly = split_out ? reshaped(L, 2 * r.c1.co, L.n_img, L.frames) : Lh;
   int rc;
   if ((rc = E.norm(r.n1, E.act[cur], Lx, E.act[o[0]], 1, nullptr, r.split_in))) return rc;
-  if ((rc = E.conv(r.c1, E.act[o[0]], Lx, kXOp, E.act[o[1]], Lh, kModeBand, nullptr, 0))) return rc;
+  if ((rc = E.conv(r.c1, E.act[o[0]], Lx, kXOp, E.act[o[1]], Lh, kModeBand, nullptr, 0, 1, true))) return rc;
   if ((rc = E.norm(r.n2, E.act[o[1]], Lh, E.act[o[0]], 1))) return rc;
   const void* res = E.act[cur];
   if (r.has_sc) {
@@ -638,7 +664,9 @@ int resnet(Exec& E, const ResW& r, int& cur, BandLayout& L, bool split_out = fal
       return rc;
     res = E.act[o[2]];
   }
-  if ((rc = E.conv(r.c2, E.act[o[0]], Lh, kXOp, E.act[o[1]], Ly, split_out ? kModeBandSplit : kModeBand, res, 0)))
+  // every resnet output but a split one (read by the upsample conv) feeds a norm next
+  if ((rc = E.conv(r.c2, E.act[o[0]], Lh, kXOp, E.act[o[1]], Ly, split_out ? kModeBandSplit : kModeBand, res, 0, 1,
+                   !split_out)))
     return rc;
   cur = o[1];
   L = Ly;
@@ -665,7 +693,7 @@ int walk(Exec& E, const void* latent, int B, int T, int W, const int* rows, int 
     ++E.launches;
   }
   BandLayout L1 = reshaped(L, m.conv_in.co, L.n_img, T);
-  if ((rc = E.conv(m.conv_in, E.act[0], L, kXOp, E.act[1], L1, kModeBand, nullptr, 0))) return rc;
+  if ((rc = E.conv(m.conv_in, E.act[0], L, kXOp, E.act[1], L1, kModeBand, nullptr, 0, 1, true))) return rc;
   cur = 1;
   L = L1;
   if ((rc = resnet(E, m.mid0, cur, L))) return rc;
@@ -706,7 +734,7 @@ int walk(Exec& E, const void* latent, int B, int T, int W, const int* rows, int 
         if ((rc = E.split(E.act[cur], L, E.act[src]))) return rc;
       }
       if ((rc = E.conv(s.up_conv, E.act[src], Ls, s.sub_up ? kXSplit : kXF32, E.act[o[0]], Lu,
-                       s.up_split ? kModeBandSplit : kModeBand, nullptr, 1)))
+                       s.up_split ? kModeBandSplit : kModeBand, nullptr, 1, 1, true)))
         return rc;
       cur = o[0];
       L = Lu;

@@ -17,6 +17,7 @@
 // tap per step through a double-buffered LDS tile (global -> registers -> LDS while the
 // previous tile feeds the MFMAs).
 #include "vaep_internal.h"
+#include "conv_gn_stats.h"
 
 namespace vaep {
 
@@ -337,10 +338,50 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
 #undef VAEP_CONV_STASH
 #undef VAEP_CONV_COMPUTE
 #undef VAEP_MFMA_K
-  const f32x16_t acc[2][2] = {{acc00, acc01}, {acc10, acc11}};
+  f32x16_t acc[2][2] = {{acc00, acc01}, {acc10, acc11}};
 
   // Epilogue.  acc[i][j][v]: channel co0+wco+32i+8(v/4)+4(lane/32)+(v%4), pixel
   // tile*BN+wpx+32j+(lane%32).
+  // When a GroupNorm consumes the output (a.gn_part set by the launch, whole-row tiles),
+  // bias and residual are folded into the accumulators first and the tile's moments are
+  // formed from the final values before they are stored.
+  bool folded = false;
+  if constexpr (MODE == kModeBand) {
+    if (a.gn_part) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const long long p = (long long)tile * BN + wpx + 32 * j + (lane & 31);
+        const int n = (int)(p / plane);
+        const int rem = (int)(p - (long long)n * plane);
+        const int r = rem / wc;
+        const int c = rem - r * wc;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int co = co0 + wco + 32 * i + 8 * g + 4 * (lane >> 5);
+            const float4 bb = *reinterpret_cast<const float4*>(a.bias + co);
+            float4 rr = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (a.res)
+              rr = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.res) +
+                                                    band_offset(a.out, band, n, r, c) + co);
+            acc[i][j][4 * g + 0] += bb.x + rr.x;
+            acc[i][j][4 * g + 1] += bb.y + rr.y;
+            acc[i][j][4 * g + 2] += bb.z + rr.z;
+            acc[i][j][4 * g + 3] += bb.w + rr.w;
+          }
+      }
+      folded = true;
+      const long long p0 = (long long)tile * BN;
+      const int n0 = (int)(p0 / plane);
+      const int rem0 = (int)(p0 - (long long)n0 * plane);
+      const int cg = a.cout / a.gn_groups;
+      const long long rec = gnstats::tile_record(a.out, band, n0, rem0 / wc, (rem0 % wc) / BN, wc / BN);
+      gnstats::tile_stats<2, 2, 4, 2, BM, false>(acc, wave, lane, cg, BN,
+                                                 a.gn_part + (rec * a.gn_groups + co0 / cg) * 2,
+                                                 reinterpret_cast<float*>(&sW[0][0]));
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const long long p = (long long)tile * BN + wpx + 32 * j + (lane & 31);
@@ -356,13 +397,13 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
         const int co = co0 + wco + 32 * i + 8 * g + 4 * (lane >> 5);
         if (co >= a.cout) continue;
         float v[4];
-        const float4 bb = *reinterpret_cast<const float4*>(a.bias + co);
+        const float4 bb = folded ? make_float4(0.f, 0.f, 0.f, 0.f) : *reinterpret_cast<const float4*>(a.bias + co);
         v[0] = acc[i][j][4 * g + 0] + bb.x;
         v[1] = acc[i][j][4 * g + 1] + bb.y;
         v[2] = acc[i][j][4 * g + 2] + bb.z;
         v[3] = acc[i][j][4 * g + 3] + bb.w;
         if (MODE == kModeBand || MODE == kModeBandSplit) {
-          if (a.res) {
+          if (a.res && !folded) {
             // residual: fp32 with `cout` channels in the output's band geometry
             long long ro = band_offset(a.out, band, n, r, c);
             if (MODE == kModeBandSplit) ro >>= 1;
@@ -502,8 +543,12 @@ hipError_t go(const ConvArgs& a, hipStream_t s) {
 
 hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s) {
   const bool ups = a.ups != 0;
+  a.gn_chunk = 0;
   if (dtype != VAEP_DTYPE_F32 && conv_wide_fits(a)) return launch_conv_wide(a, s);
-  if (dtype != VAEP_DTYPE_F32 && conv_narrow_fits(a)) return launch_conv_narrow(a, s);
+  if (dtype != VAEP_DTYPE_F32 && conv_narrow_fits(a)) {
+    a.gn_part = nullptr;
+    return launch_conv_narrow(a, s);
+  }
   // split operands and sub-pixel weights exist only on the wide kernel
   if (a.x_split || a.sub || (a.mode == kModeBandSplit && dtype == VAEP_DTYPE_F32)) return hipErrorInvalidValue;
   if (dtype != VAEP_DTYPE_F32) {
@@ -525,6 +570,15 @@ hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s) {
   a.tile_start[a.in.nb] = t;
   a.tiles_total = t;
   a.kernel_used = dtype == VAEP_DTYPE_F32 ? VAEP_KERNEL_CONV_F32 : VAEP_KERNEL_CONV_TILE128;
+  // GroupNorm tile statistics in the epilogue: whole-row pixel tiles, every group inside
+  // one channel tile
+  const int wout = (ups ? 2 : 1) * a.in.W;
+  a.gn_chunk = 0;
+  if (a.gn_part && dtype != VAEP_DTYPE_F32 && a.mode == kModeBand && !a.x_f32 && wout % kConvTileM == 0 &&
+      a.cout == a.cout_pad && a.gn_groups > 0 && a.cout % a.gn_groups == 0 && (a.cout / a.gn_groups) % 4 == 0 &&
+      kConvTileN % (a.cout / a.gn_groups) == 0)
+    a.gn_chunk = kConvTileM;
+  if (!a.gn_chunk) a.gn_part = nullptr;
   if (t == 0) return hipSuccess;
   if (dtype == VAEP_DTYPE_F32) {
     dim3 grid(t, a.cout);

@@ -28,6 +28,7 @@
 // three parts per tap: x_hi * w_hi, x_lo * w_hi, x_hi * w_lo (the dropped x_lo * w_lo is
 // below 2^-18 of the product).  Other convs have one part: x * w.
 #include "vaep_internal.h"
+#include "conv_gn_stats.h"
 
 namespace vaep {
 
@@ -141,10 +142,11 @@ __device__ __forceinline__ void store4(const BandLayout& L, void* y, int half, i
 // Split-output epilogue.  Lanes l and l+32 hold alternate 4-channel groups of one pixel;
 // v_permlane32_swap pairs them up so that each lane owns 8 consecutive channels and
 // stores their hi and lo parts as one 16-byte store each.
+// folded: bias and residual are already in acc.
 template <bool SUB, int MI, int NJ>
 __device__ __forceinline__ void split_epilogue(const ConvArgs& a, const f32x16_t (&acc)[MI][NJ], int band,
                                                int tile, int plane, long long m_band, int W, int py, int px,
-                                               int co0, int wco, int wpx, int lane) {
+                                               int co0, int wco, int wpx, int lane, bool folded) {
   const int hi = lane >> 5;
   const int half = a.cout;
 #pragma unroll
@@ -181,11 +183,13 @@ __device__ __forceinline__ void split_epilogue(const ConvArgs& a, const f32x16_t
         }
         const int co = co0 + wco + 32 * i + 8 * (2 * m + hi);
         if (!pv || co >= a.cout) continue;
-        const float4 b0 = *reinterpret_cast<const float4*>(a.bias + co);
-        const float4 b1 = *reinterpret_cast<const float4*>(a.bias + co + 4);
-        v[0] += b0.x; v[1] += b0.y; v[2] += b0.z; v[3] += b0.w;
-        v[4] += b1.x; v[5] += b1.y; v[6] += b1.z; v[7] += b1.w;
-        if (a.res) {
+        if (!folded) {
+          const float4 b0 = *reinterpret_cast<const float4*>(a.bias + co);
+          const float4 b1 = *reinterpret_cast<const float4*>(a.bias + co + 4);
+          v[0] += b0.x; v[1] += b0.y; v[2] += b0.z; v[3] += b0.w;
+          v[4] += b1.x; v[5] += b1.y; v[6] += b1.z; v[7] += b1.w;
+        }
+        if (a.res && !folded) {
           // residual: fp32 with `cout` channels in the output's band geometry
           const float* rp = reinterpret_cast<const float*>(a.res) + (o >> 1) + co;
           const float4 r0 = *reinterpret_cast<const float4*>(rp);
@@ -531,8 +535,48 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   // Epilogue.  acc[i][j][v]: channel co0 + wco + 32i + 8(v/4) + 4(lane/32) + v%4, pixel
   // tile*BN + wpx + 32j + lane%32 (source grid for sub-pixel convs).
   const int half = a.cout;   // kModeBandSplit: lo parts start `cout` channels after the hi parts
+  // When a GroupNorm consumes the output (a.gn_part set by the launch: whole-row tiles),
+  // the tile's moments are formed from the final values (hi + lo for split outputs):
+  // split outputs (no residual) get the bias folded into the accumulators, as hi + lo,
+  // before the statistics and the stores (bf16 parts of hi + lo are hi and lo again);
+  // plain outputs write each final value back into the accumulators as they store it and
+  // form the statistics afterwards.
+  const bool gn = a.gn_part != nullptr;
+  bool folded = false;
+  auto gn_stats = [&]() {
+    __syncthreads();   // every wave is done with the operand stages: the LDS is scratch now
+    const long long p0 = (long long)tile * BN;
+    const int n0 = (int)(p0 / plane);
+    const int rem0 = (int)(p0 - (long long)n0 * plane);
+    const int r0 = rem0 / W, c0 = rem0 - (rem0 / W) * W;
+    const int chunks = (SUB ? 2 : 1) * (W / BN);
+    const long long rec = gnstats::tile_record(a.out, band, n0, SUB ? 2 * r0 + py : r0,
+                                               (SUB ? px * (W / BN) : 0) + c0 / BN, chunks);
+    const int cg = a.cout / a.gn_groups;
+    gnstats::tile_stats<MI, NJ, NW, WPX, BM, false>(
+        acc, wave, lane, cg, BN, a.gn_part + (rec * a.gn_groups + co0 / cg) * 2, reinterpret_cast<float*>(smem));
+  };
+  if (MODE == kModeBandSplit && gn) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int co = co0 + wco + 32 * i + 8 * g + 4 * (lane >> 5);
+        const float4 bb = *reinterpret_cast<const float4*>(a.bias + co);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          // hi + lo of the value: what the norm reads, and it splits into the same parts
+          acc[i][j][4 * g + 0] = gnstats::seen<true>(acc[i][j][4 * g + 0] + bb.x);
+          acc[i][j][4 * g + 1] = gnstats::seen<true>(acc[i][j][4 * g + 1] + bb.y);
+          acc[i][j][4 * g + 2] = gnstats::seen<true>(acc[i][j][4 * g + 2] + bb.z);
+          acc[i][j][4 * g + 3] = gnstats::seen<true>(acc[i][j][4 * g + 3] + bb.w);
+        }
+      }
+    folded = true;
+    gn_stats();
+  }
   if (MODE == kModeBandSplit) {
-    split_epilogue<SUB, MI, NJ>(a, acc, band, tile, plane, m_band, W, py, px, co0, wco, wpx, lane);
+    split_epilogue<SUB, MI, NJ>(a, acc, band, tile, plane, m_band, W, py, px, co0, wco, wpx, lane, folded);
     return;
   }
 #pragma unroll
@@ -567,9 +611,16 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
           v[3] += rr.w;
         }
         store4<MODE>(a.out, a.y, half, band, n, r, c, co, v);
+        if (gn) {
+          acc[i][j][4 * g + 0] = v[0];
+          acc[i][j][4 * g + 1] = v[1];
+          acc[i][j][4 * g + 2] = v[2];
+          acc[i][j][4 * g + 3] = v[3];
+        }
       }
     }
   }
+  if (gn) gn_stats();
 }
 
 template <int KT, int KS, bool SUB, int PARTS, int MODE>
@@ -617,6 +668,7 @@ bool conv_wide_fits(const ConvArgs& a) {
 }
 
 hipError_t launch_conv_wide(ConvArgs& a, hipStream_t s) {
+  a.gn_chunk = 0;
   if (a.cin % 64 != 0 || a.cout_pad % 128 != 0) return hipErrorInvalidValue;
   // split operands feed the sub-pixel form only
   if (a.sub != a.x_split || (a.sub && (a.kt != 1 || a.ks != 3))) return hipErrorInvalidValue;
@@ -640,6 +692,14 @@ hipError_t launch_conv_wide(ConvArgs& a, hipStream_t s) {
   if (t == 0) return hipSuccess;
   const int bm = wide_bm(a, t);
   a.kernel_used = bm == 256 ? VAEP_KERNEL_CONV_WIDE256 : VAEP_KERNEL_CONV_WIDE128;
+  // GroupNorm tile statistics in the epilogue: whole-row pixel tiles, every group inside
+  // one channel tile
+  a.gn_chunk = 0;
+  if (a.gn_part && (a.mode == kModeBand || (a.mode == kModeBandSplit && !a.res)) && a.in.W % kWideTileM == 0 &&
+      a.cout == a.cout_pad && a.gn_groups > 0 && a.cout % a.gn_groups == 0 && (a.cout / a.gn_groups) % 4 == 0 &&
+      bm % (a.cout / a.gn_groups) == 0)
+    a.gn_chunk = kWideTileM;
+  if (!a.gn_chunk) a.gn_part = nullptr;
   if (a.sub) return go_mode<1, 3, true, 3>(a, bm, s);
   if (a.kt == 1 && a.ks == 3) return go_mode<1, 3, false, 1>(a, bm, s);
   if (a.kt == 1 && a.ks == 1) return go_mode<1, 1, false, 1>(a, bm, s);

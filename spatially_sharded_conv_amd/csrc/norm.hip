@@ -545,19 +545,24 @@ static int apply_pixels(const BandLayout& L) {
 
 static bool plan_stats(NormArgs& a) {
   const BandLayout& L = a.L;
+  if (a.pre_chunk > 0) {       // records of the producing conv: one-row slabs, whole chunks
+    if (L.W % a.pre_chunk != 0) return false;
+    a.slab_rows = 1;
+  }
   if (a.slab_rows < 1 || L.H % a.slab_rows != 0) return false;
   for (int b = 0; b < L.nb; ++b)
     if (L.row0[b] % a.slab_rows != 0 || L.rows[b] % a.slab_rows != 0) return false;
   a.slabs = L.H / a.slab_rows;
-  a.chunk_pix = chunk_pixels(L);
+  a.chunk_pix = a.pre_chunk > 0 ? a.pre_chunk : chunk_pixels(L);
   const long long slab_pix = (long long)a.slab_rows * L.W;
   a.chunks = (int)((slab_pix + a.chunk_pix - 1) / a.chunk_pix);
   return true;
 }
 
-size_t gn_partials_floats(const BandLayout& L, int groups, int slab_rows) {
+size_t gn_partials_floats(const BandLayout& L, int groups, int slab_rows, int chunk) {
   // (in floats) fp64 partials, per-channel coefficients, per-band moments, merged stats
-  const int pix = chunk_pixels(L);
+  const int pix = chunk > 0 ? chunk : chunk_pixels(L);
+  if (chunk > 0) slab_rows = 1;
   const long long slab_pix = (long long)slab_rows * L.W;
   const long long tiles = (long long)L.n_img * (L.H / slab_rows) * ((slab_pix + pix - 1) / pix);
   return (size_t)(tiles * groups * 4 + 2LL * L.n_img * L.C + 3LL * L.nb * L.n_img * groups +
@@ -579,14 +584,16 @@ hipError_t launch_groupnorm(NormArgs& a, int dtype, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   // the input's size: fp32, or bf16 hi / lo halves (the same bytes)
   const bool nt = (long long)L.n_img * L.H * L.W * L.C * 4 >= kStreamBytes;
-  if (a.x_split && nt)
-    hipLaunchKernelGGL((gn_stats<true, true>), dim3(blocks), dim3(kThreads), 0, s, a);
-  else if (a.x_split)
-    hipLaunchKernelGGL((gn_stats<true, false>), dim3(blocks), dim3(kThreads), 0, s, a);
-  else if (nt)
-    hipLaunchKernelGGL((gn_stats<false, true>), dim3(blocks), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((gn_stats<false, false>), dim3(blocks), dim3(kThreads), 0, s, a);
+  if (a.pre_chunk <= 0) {   // else the producing conv already wrote the tile records
+    if (a.x_split && nt)
+      hipLaunchKernelGGL((gn_stats<true, true>), dim3(blocks), dim3(kThreads), 0, s, a);
+    else if (a.x_split)
+      hipLaunchKernelGGL((gn_stats<true, false>), dim3(blocks), dim3(kThreads), 0, s, a);
+    else if (nt)
+      hipLaunchKernelGGL((gn_stats<false, true>), dim3(blocks), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((gn_stats<false, false>), dim3(blocks), dim3(kThreads), 0, s, a);
+  }
   hipLaunchKernelGGL(gn_merge, dim3(L.n_img * a.groups * (L.nb + 1)), dim3(kThreads), 0, s, a, coef);
   a.apply_pix = apply_pixels(L);
   long long nblk = 0;   // apply workgroups: runs of apply_pix pixels per (band, image)

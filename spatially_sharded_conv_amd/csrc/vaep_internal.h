@@ -83,6 +83,15 @@ struct ConvArgs {
   int tiles_total;      // M tiles over all bands
   int tile_start[kMaxBands + 1];  // prefix of M tiles per band
   int kernel_used;      // set by the launch: VAEP_KERNEL_*
+  // GroupNorm statistics of the output for the norm that consumes it (kModeBand /
+  // kModeBandSplit).  The caller sets gn_part (fp64 tile records, [tiles][gn_groups][2]
+  // mean and M2) and gn_groups; the launch keeps gn_part only if the kernel it picks forms
+  // the records in its epilogue (pixel tiles of whole rows), sets gn_chunk to the tile
+  // width in pixels, and else clears gn_part and gn_chunk.  Tile index:
+  // (image * out.H + row) * (out.W / gn_chunk) + column / gn_chunk.
+  double* gn_part;
+  int gn_groups;
+  int gn_chunk;
 };
 
 // Launch the convolution described by `a` (fills tile fields).  dtype: VAEP_DTYPE_*.
@@ -135,11 +144,15 @@ struct NormArgs {
   int chunks;            // chunks per slab
   int chunk_pix;         // pixels per chunk (last chunk of a slab may be shorter)
   int apply_pix;         // pixels per apply workgroup
+  // > 0: the producing conv already wrote the tile records into `partials` (one-row slabs,
+  // chunks of pre_chunk pixels, see ConvArgs::gn_part); the statistics pass is skipped.
+  int pre_chunk;
   long long item_start[kMaxBands + 1];  // apply pass: first vector (GN) / pixel (RMS) of band i
 };
 
-// Scratch of a GroupNorm launch in floats; slab_rows as in NormArgs.
-size_t gn_partials_floats(const BandLayout& L, int groups, int slab_rows);
+// Scratch of a GroupNorm launch in floats; slab_rows as in NormArgs; chunk > 0: tile
+// records of `chunk` pixels of one row (statistics formed by the producing conv).
+size_t gn_partials_floats(const BandLayout& L, int groups, int slab_rows, int chunk = 0);
 hipError_t launch_groupnorm(NormArgs& a, int dtype, hipStream_t s);
 hipError_t launch_rmsnorm(NormArgs& a, int dtype, hipStream_t s);
 hipError_t launch_moment_merge(int n_shards, int n_stats, const float* mean, const float* var,
