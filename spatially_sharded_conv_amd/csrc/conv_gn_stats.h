@@ -19,11 +19,27 @@ namespace gnstats {
 
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
-// Sum over the 32 lanes of each half-wave (lanes 0-31 and 32-63 separately).
+// Workgroup barrier for LDS traffic only: every wave's LDS operations have completed, but
+// its global stores (the epilogue's output) stay in flight.  __syncthreads would also wait
+// for those, serialising the store latency of the whole tile.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// Sum over the 32 lanes of each half-wave (lanes 0-31 and 32-63 separately), in the VALU:
+// DPP butterflies within each row of 16 lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror), then rows 0+1 and 2+3 through v_permlane16_swap.
 __device__ __forceinline__ float half_sum(float v) {
-#pragma unroll
-  for (int k = 16; k >= 1; k >>= 1) v += __shfl_xor(v, k, 64);
-  return v;
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // val[i][j][v] holds the final value (what the norm reads) of local channel
@@ -32,7 +48,8 @@ __device__ __forceinline__ float half_sum(float v) {
 // lds: at least NWAVES*MI*8 + BM floats + BM/4 doubles of workgroup scratch no other thread
 // uses meanwhile.  cg: channels per group (multiple of 4, divides BM).  part: the tile's
 // record, [G][2] doubles (mean, M2), already offset to the workgroup's first group.
-// Contains two __syncthreads; every thread of the workgroup must call it.
+// Contains LDS barriers (lds_barrier); every thread of the workgroup must call it, and
+// the caller must have passed an lds_barrier since the last use of `lds` for anything else.
 // SPLITV: the output is stored as bf16 hi / lo parts, which the norm reads back as
 // hi + lo (exact in fp32); the moments are taken of that value.
 __device__ __forceinline__ float bf16_round(float v) {
@@ -59,7 +76,7 @@ __device__ __forceinline__ void tile_stats(const f32x16_t (&val)[MI][NJ], int wa
   // group sums over quads of waves: quad q of wave w covers local channel
   // (w / WPX) * WAVE_CH + 32 (q / 8) + 8 ((q % 8) / 2) + 4 (q % 2)
   auto reduce_groups = [&](bool second) {
-    __syncthreads();
+    lds_barrier();
     if ((int)threadIdx.x < ngroups) {
       const int gi = threadIdx.x;
       double s = 0.0;
@@ -80,7 +97,7 @@ __device__ __forceinline__ void tile_stats(const f32x16_t (&val)[MI][NJ], int wa
         part[2 * gi + 1] = m2 > 0.0 ? m2 : 0.0;
       }
     }
-    __syncthreads();
+    if (!second) lds_barrier();   // the group means are read by every lane next
   };
   // pass 1: sums
 #pragma unroll

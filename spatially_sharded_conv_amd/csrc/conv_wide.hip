@@ -544,7 +544,7 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   const bool gn = a.gn_part != nullptr;
   bool folded = false;
   auto gn_stats = [&]() {
-    __syncthreads();   // every wave is done with the operand stages: the LDS is scratch now
+    gnstats::lds_barrier();   // every wave is done with the operand stages: the LDS is scratch now
     const long long p0 = (long long)tile * BN;
     const int n0 = (int)(p0 / plane);
     const int rem0 = (int)(p0 - (long long)n0 * plane);
