@@ -14,7 +14,8 @@ What it computes follows the pages on the method:
   "Semantics and Communication" operator table and the merge formula below it.
 * The distributed-VAE strategy page -- "Strategy Selection Contract" and the
   Wan spatial-shard notes (height or width sharding, the ``auto`` axis
-  policy).
+  policy), and the tile/patch decode (split / exec / merge with overlap
+  blending), the comparison baseline in ``tiled.py``.
 
 Both pages state that the layer-wise decode keeps full-image semantics, so the
 oracle's primary output is the plain full-image decoder forward
@@ -32,10 +33,11 @@ from .ops import (conv_padded, conv_full, conv_band, groupnorm_moments, merge_mo
                   groupnorm_apply, rmsnorm, silu, attention_rows, upsample_nearest2x,
                   temporal_upsample_interleave)
 from .decoder import decode_full, decode_bands, decode_auto, choose_axis, even_starts, Precision
+from .tiled import blend_h, blend_v, decode_tiled, row_seam, tile_origins
 
 __all__ = [
     "conv_padded", "conv_full", "conv_band", "groupnorm_moments", "merge_moments",
     "groupnorm_apply", "rmsnorm", "silu", "attention_rows", "upsample_nearest2x",
     "temporal_upsample_interleave", "decode_full", "decode_bands", "decode_auto", "choose_axis",
-    "even_starts", "Precision",
+    "even_starts", "Precision", "blend_h", "blend_v", "decode_tiled", "row_seam", "tile_origins",
 ]
