@@ -12,7 +12,9 @@ of K decodes brackets every kernel launch with HIP events on the decode stream
 the roofline fractions are computed with algorithmic flops / bytes per launch.
 The CPU baseline times the oracle on a bounded sample of the same decoder.
 `shard_axes` times the same latent decoded on column bands of the same sizes
-(vaep_decode_sharded, width axis) and with the per-request `auto` axis policy.
+(vaep_decode_sharded, width axis) and with the per-request `auto` axis policy;
+`tiled_baseline` times the overlap-blending tile decode (vaep_decode_tiled) and
+reports its distance from the band decode and its row-seam diagnostic.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
 """
@@ -252,6 +254,42 @@ def main():
         axes[name] = {"axis": {1: "height", 2: "width", 3: "dense"}[ainfo.axis],
                       "bands": list(st) if st else ainfo.bands_used,
                       "ms_per_step": round(a_ms, 4), "mpixel_s": round(pixels / (a_ms * 1e-3) / 1e6, 3)}
+    # the overlap-blending tile decode the sharded decode replaces (latent tiles of 32 with
+    # stride 24: 256-pixel tiles every 192 output pixels at 8x upsampling), same latent
+    tiled = None
+    if not cfg.is_video:
+        tile, tstride = 32, 24
+        band_out = torch.empty_like(out)
+        dec.decode_bands(latent, starts, band_out, ws, stream)
+        tws = dec.tiled_workspace(cfg.batch, cfg.frames, cfg.latent_h, cfg.latent_w, tile, tstride)
+        tout = torch.empty_like(out)
+        for _ in range(args.warmup):
+            dec.decode_tiled(latent, tile, tstride, tout, tws, stream)
+        torch.cuda.synchronize()
+        t_a = torch.cuda.Event(enable_timing=True)
+        t_b = torch.cuda.Event(enable_timing=True)
+        t_a.record(stream)
+        for _ in range(args.steps):
+            dec.decode_tiled(latent, tile, tstride, tout, tws, stream)
+        t_b.record(stream)
+        torch.cuda.synchronize()
+        t_ms = t_a.elapsed_time(t_b) / args.steps
+        # seam diagnostic (validation page): mean absolute jump between adjacent rows of the
+        # per-pixel RGB mean, 0-255 units; at the tiles' row boundaries and over all rows
+        def row_jumps(y):
+            m = (y.double().mean(dim=1) + 1.0) * 127.5
+            return (m[:, 1:, :] - m[:, :-1, :]).abs().mean(dim=(0, 2))
+        keep = tstride * (out.shape[-1] // cfg.latent_w)
+        bnd = torch.arange(keep - 1, out.shape[-2] - 1, keep, device=out.device)
+        jt, jb = row_jumps(tout), row_jumps(band_out)
+        d = (tout.double() - band_out.double())
+        del tws
+        tiled = {"tile_latent": tile, "stride_latent": tstride, "ms_per_step": round(t_ms, 4),
+                 "mpixel_s": round(pixels / (t_ms * 1e-3) / 1e6, 3),
+                 "rel_l2_vs_band_decode": round((d.norm() / band_out.double().norm()).item(), 5),
+                 "row_jump_at_tile_rows": round(jt[bnd].mean().item(), 4),
+                 "row_jump_at_those_rows_band_decode": round(jb[bnd].mean().item(), 4),
+                 "row_jump_all_rows": round(jt.mean().item(), 4)}
     norm_key = "groupnorm" if "groupnorm" in cls else "rmsnorm"
     line = {
         "metric": METRIC,
@@ -286,6 +324,7 @@ def main():
                       for k, v in sorted(cls.items())},
         "profiled_ms_per_step": round(ms_prof, 4),
         "shard_axes": axes,
+        "tiled_baseline": tiled,
         **aggregates(recs, args.steps),
         "cpu_baseline": None,
     }

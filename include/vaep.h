@@ -202,6 +202,26 @@ int vaep_decode_sharded(vaep_model* model, const void* latent, int batch, int fr
                         int n_shards, void* out, void* ws, size_t ws_bytes, void* stream,
                         vaep_decode_info* info);
 
+/* Tiled decode with overlap blending -- the comparison baseline the sharded decode
+ * replaces (distributed-VAE strategy page, "Tile/Patch Implementation (Decode)"):
+ * latent tiles of tile x tile rows and columns start every `stride` rows and columns
+ * (clipped at the image edge); each is decoded on its own as a whole image (its own
+ * GroupNorm statistics and attention tokens); the merge walks the tiles in raster order,
+ * cross-fades each tile's first (tile - stride) * 2^(n_stages-1) output rows linearly
+ * from its upper neighbour's last ones (weight of the neighbour 1 - k/e at row k of
+ * e = min(neighbour rows, tile rows, overlap)), then its first columns from its left
+ * neighbour likewise, keeps stride * 2^(n_stages-1) rows and columns of every tile and
+ * crops to the image.  The blend is a reading (the page names it without printing it).
+ * Unlike the band decodes this does not reproduce the full-image decode; it exists to be
+ * measured against it (seams, time).  latent / out as for vaep_decode_full; ws of at
+ * least vaep_tiled_workspace_bytes(...) bytes (it holds every decoded tile).
+ * Errors: INVALID_ARG (1 <= stride <= tile violated, NULL pointers), WORKSPACE, HIP. */
+int vaep_tiled_workspace_bytes(const vaep_model* model, int batch, int frames, int latent_h,
+                               int latent_w, int tile, int stride, size_t* bytes_out);
+int vaep_decode_tiled(vaep_model* model, const void* latent, int batch, int frames, int latent_h,
+                      int latent_w, int tile, int stride, void* out, void* ws, size_t ws_bytes,
+                      void* stream);
+
 /* Launch timing.  While profiling is on for a model, every kernel launch of its decodes
  * is bracketed by two HIP events on the caller's stream and the library records the
  * step's kind, shape and algorithmic work (each tensor counted once; convolution flops

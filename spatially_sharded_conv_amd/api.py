@@ -151,6 +151,21 @@ class Decoder:
         return rc, info
 
 
+    def tiled_workspace(self, batch, frames, latent_h, latent_w, tile, stride, device="cuda") -> torch.Tensor:
+        n = C.c_size_t()
+        L.check(L.load().vaep_tiled_workspace_bytes(self._h, batch, frames, latent_h, latent_w, tile, stride,
+                                                    C.byref(n)))
+        return torch.empty(n.value, dtype=torch.uint8, device=device)
+
+    def decode_tiled(self, latent, tile: int, stride: int, out, ws, stream=None) -> int:
+        """Tiled decode with overlap blending (the comparison baseline of the sharded decode)."""
+        b, t, h, w = self._dims(latent)
+        _dev(latent, self.dtype, "latent")
+        _dev(out, torch.float32, "out")
+        return L.check(L.load().vaep_decode_tiled(self._h, _p(latent), b, t, h, w, tile, stride, _p(out), _p(ws),
+                                                  ws.numel(), _stream(stream)))
+
+
 AXES = {"auto": L.AXIS_AUTO, "height": L.AXIS_HEIGHT, "width": L.AXIS_WIDTH}
 AXIS_NAMES = {L.AXIS_HEIGHT: "height", L.AXIS_WIDTH: "width", L.AXIS_DENSE: "dense"}
 

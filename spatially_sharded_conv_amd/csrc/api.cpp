@@ -835,6 +835,51 @@ int table_rows(const int32_t* starts, int n, int len, const char* what, std::vec
   return VAEP_OK;
 }
 
+// Tiled decode (overlap-blending baseline): tile grid, workspace carve-up.
+struct TilePlan {
+  int nr = 0, nc = 0;          // tile rows and columns
+  int nfull = 0;               // tiles of the full tile size (decoded together as one batch)
+  int full_r = 0, full_c = 0;  // ... the first full_r tile rows x full_c tile columns
+  int up = 1;                  // output pixels per latent pixel
+  int blend = 0;               // overlap in output rows / columns
+  long long planes = 0;        // output planes: batch * 3 * output frames
+  long long slot_elems = 0;    // fp32 elements of one tile slot (largest tile)
+  size_t dec_bytes = 0, lat_bytes = 0, store_bytes = 0, total = 0;
+};
+
+int tile_plan(const vaep_model* m, int batch, int frames, int h, int w, int tile, int stride, TilePlan* tp) {
+  if (tile < 1 || stride < 1 || stride > tile)
+    return fail(VAEP_ERR_INVALID_ARG, "tile %d and stride %d must satisfy 1 <= stride <= tile", tile, stride);
+  tp->nr = (h + stride - 1) / stride;
+  tp->nc = (w + stride - 1) / stride;
+  tp->up = 1 << (m->cfg.n_stages - 1);
+  tp->blend = (tile - stride) * tp->up;
+  int t_out = frames;
+  for (int i = 0; i < m->cfg.n_stages; ++i)
+    if (stage_time_ups(m->cfg, i)) t_out = 2 * t_out - 1;
+  tp->planes = (long long)batch * 3 * t_out;
+  const int th = std::min(tile, h), tw = std::min(tile, w);
+  tp->slot_elems = tp->planes * (long long)th * tp->up * tw * tp->up;
+  // tiles lying wholly inside the image share one size and decode as one batch; the
+  // clipped edge tiles decode one at a time
+  int full_r = 0, full_c = 0;
+  for (int i = 0; i < h; i += stride) full_r += i + tile <= h ? 1 : 0;
+  for (int j = 0; j < w; j += stride) full_c += j + tile <= w ? 1 : 0;
+  tp->full_r = full_r;
+  tp->full_c = full_c;
+  tp->nfull = full_r * full_c;
+  const int nb = std::max(tp->nfull, 1);
+  size_t one = 0, many = 0;
+  int rc = plan_bytes(m, batch, frames, th, tw, 1, false, &one);
+  if (rc) return rc;
+  if (tp->nfull > 0 && (rc = plan_bytes(m, batch * tp->nfull, frames, tile, tile, 1, false, &many))) return rc;
+  tp->dec_bytes = align_up(std::max(one, many), 256);
+  tp->lat_bytes = align_up((size_t)nb * batch * m->cfg.z_channels * frames * th * tw * dtype_bytes(m->cfg.dtype), 256);
+  tp->store_bytes = (size_t)tp->nr * tp->nc * tp->slot_elems * sizeof(float);
+  tp->total = tp->dec_bytes + tp->lat_bytes + tp->store_bytes;
+  return VAEP_OK;
+}
+
 // The per-request axis policy: the longer axis that gives every shard at least one latent
 // row (the kernel radius at latent resolution), width on ties; otherwise one dense band.
 int select_axis(int h, int w, int n) {
@@ -1043,6 +1088,93 @@ int vaep_decode_bands(vaep_model* model, const void* latent, int batch, int fram
   if (status == VAEP_WARN_FELL_BACK)
     fail(VAEP_WARN_FELL_BACK, "%d bands exceed the %d-band limit: decoded as one dense band", n_bands, kMaxBands);
   return status;
+}
+
+int vaep_tiled_workspace_bytes(const vaep_model* model, int batch, int frames, int latent_h, int latent_w,
+                               int tile, int stride, size_t* bytes_out) {
+  int rc = check_latent_dims(model, batch, frames, latent_h, latent_w);
+  if (rc) return rc;
+  if (!bytes_out) return fail(VAEP_ERR_INVALID_ARG, "bytes_out is NULL");
+  TilePlan tp;
+  if ((rc = tile_plan(model, batch, frames, latent_h, latent_w, tile, stride, &tp))) return rc;
+  *bytes_out = tp.total;
+  return VAEP_OK;
+}
+
+int vaep_decode_tiled(vaep_model* model, const void* latent, int batch, int frames, int latent_h, int latent_w,
+                      int tile, int stride, void* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_latent_dims(model, batch, frames, latent_h, latent_w);
+  if (rc) return rc;
+  if (!latent || !out) return fail(VAEP_ERR_INVALID_ARG, "latent and out must be device pointers");
+  TilePlan tp;
+  if ((rc = tile_plan(model, batch, frames, latent_h, latent_w, tile, stride, &tp))) return rc;
+  if (!ws || ws_bytes < tp.total)
+    return fail(VAEP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", tp.total, ws ? ws_bytes : (size_t)0);
+  hipStream_t st = (hipStream_t)stream;
+  char* base = (char*)ws;
+  void* dec_ws = base;
+  void* lat = base + tp.dec_bytes;
+  float* slots = (float*)(base + tp.dec_bytes + tp.lat_bytes);
+  const int cz = model->cfg.z_channels;
+  const long long lat_planes = (long long)batch * cz * frames;
+  // split / exec: every tile decoded on its own (its own statistics and attention), the
+  // full-size ones together as a batch of images whose outputs land in consecutive slots
+  // (the slots of full tiles are ordered first: slot k of the batch, then the edge tiles)
+  std::vector<int> slot_of(tp.nr * tp.nc);
+  for (int gi = 0; gi < tp.nr; ++gi)
+    for (int gj = 0; gj < tp.nc; ++gj) slot_of[gi * tp.nc + gj] = tile_slot(gi, gj, tp.nc, tp.full_r, tp.full_c);
+  const size_t lat_tile = (size_t)lat_planes * tile * tile * dtype_bytes(model->cfg.dtype);
+  if (tp.nfull > 0) {
+    for (int gi = 0; gi < tp.nr; ++gi)
+      for (int gj = 0; gj < tp.nc; ++gj) {
+        const int k = slot_of[gi * tp.nc + gj];
+        if (k >= tp.nfull) continue;
+        hipError_t e = launch_crop(latent, lat_planes, latent_h, latent_w, gi * stride, gj * stride, tile, tile,
+                                   (char*)lat + k * lat_tile, model->cfg.dtype, st);
+        if (e != hipSuccess) return hip_fail(e, "latent tile crop");
+      }
+    const std::vector<int> rows(1, tile);
+    rc = run_decode(model, lat, batch * tp.nfull, frames, tile, false, rows, VAEP_AXIS_DENSE, VAEP_OK, slots, dec_ws,
+                    tp.dec_bytes, stream, nullptr);
+    if (rc) return rc;
+  }
+  for (int gi = 0; gi < tp.nr; ++gi)
+    for (int gj = 0; gj < tp.nc; ++gj) {
+      const int k = slot_of[gi * tp.nc + gj];
+      if (k < tp.nfull) continue;
+      const int i = gi * stride, j = gj * stride;
+      const int th = std::min(tile, latent_h - i), tw = std::min(tile, latent_w - j);
+      hipError_t e = launch_crop(latent, lat_planes, latent_h, latent_w, i, j, th, tw, lat, model->cfg.dtype, st);
+      if (e != hipSuccess) return hip_fail(e, "latent tile crop");
+      const std::vector<int> rows(1, th);
+      rc = run_decode(model, lat, batch, frames, tw, false, rows, VAEP_AXIS_DENSE, VAEP_OK,
+                      slots + (long long)k * tp.slot_elems, dec_ws, tp.dec_bytes, stream, nullptr);
+      if (rc) return rc;
+    }
+  // merge: raster order, upper neighbour over the overlap rows, then left over the columns
+  auto out_len = [&](int g, int len) { return std::min(tile, len - g * stride) * tp.up; };
+  for (int gi = 0; gi < tp.nr; ++gi)
+    for (int gj = 0; gj < tp.nc; ++gj) {
+      float* t = slots + (long long)slot_of[gi * tp.nc + gj] * tp.slot_elems;
+      const int th = out_len(gi, latent_h), tw = out_len(gj, latent_w);
+      hipError_t e = hipSuccess;
+      if (gi > 0) {
+        const int uh = out_len(gi - 1, latent_h);
+        e = launch_blend(slots + (long long)slot_of[(gi - 1) * tp.nc + gj] * tp.slot_elems, t, tp.planes, th, tw, uh,
+                         std::min(std::min(uh, th), tp.blend), 0, st);
+      }
+      if (e == hipSuccess && gj > 0) {
+        const int lw = out_len(gj - 1, latent_w);
+        e = launch_blend(slots + (long long)slot_of[gi * tp.nc + gj - 1] * tp.slot_elems, t, tp.planes, th, tw, lw,
+                         std::min(std::min(lw, tw), tp.blend), 1, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "tile blend");
+    }
+  hipError_t e = launch_tiles_gather(slots, tp.slot_elems, tp.planes, latent_h * tp.up, latent_w * tp.up,
+                                     stride * tp.up, tile * tp.up, tp.nc, tp.full_r, tp.full_c, latent_h, latent_w,
+                                     stride, tp.up, (float*)out, st);
+  if (e != hipSuccess) return hip_fail(e, "tile gather");
+  return VAEP_OK;
 }
 
 int vaep_select_axis(int latent_h, int latent_w, int n_shards, int32_t* axis_out) {

@@ -138,7 +138,98 @@ int grid_for(long long n) {
   return g < 1 ? 1 : (int)g;
 }
 
+// Latent tile: rows [i, i + th), columns [j, j + tw) of every (sample, channel, frame)
+// plane of an NC[T]HW tensor, stored contiguously.
+template <typename T>
+__global__ void crop_kernel(const T* src, long long planes, int h, int w, int i, int j, int th, int tw, T* dst) {
+  const long long total = planes * th * tw;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (long long)gridDim.x * blockDim.x) {
+    const int x = (int)(e % tw);
+    const int y = (int)((e / tw) % th);
+    const long long p = e / ((long long)th * tw);
+    dst[e] = src[(p * h + i + y) * w + j + x];
+  }
+}
+
+// Linear cross-fade of a tile's first e rows (axis 0) or columns (axis 1) from the last
+// ones of its neighbour, in place: v = nb * (1 - k / e) + v * (k / e), k = row / column.
+// Tiles are [planes][th][tw] fp32; the neighbour has the same width (rows) or height
+// (columns) and nb_len rows / columns.
+__global__ void blend_kernel(const float* nb, float* tile, long long planes, int th, int tw, int nb_len, int e,
+                             int axis) {
+  const int other = axis == 0 ? tw : th;
+  const long long total = planes * e * other;
+  for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (long long)gridDim.x * blockDim.x) {
+    const int o = (int)(idx % other);
+    const int k = (int)((idx / other) % e);
+    const long long p = idx / ((long long)e * other);
+    const float wt = (float)k / (float)e;
+    float* v;
+    float n;
+    if (axis == 0) {
+      v = tile + (p * th + k) * tw + o;
+      n = nb[(p * nb_len + nb_len - e + k) * tw + o];
+    } else {
+      v = tile + (p * th + o) * tw + k;
+      n = nb[(p * th + o) * nb_len + nb_len - e + k];
+    }
+    *v = n * (1.f - wt) + *v * wt;
+  }
+}
+
+// Output of the tiled decode: output row y, column x comes from tile (y / keep, x / keep)
+// at (y % keep, x % keep).  Tile (gi, gj) sits in slot tile_slot(...), [planes][th][tw].
+__global__ void tiles_gather_kernel(const float* slots, long long slot_elems, long long planes, int H, int W,
+                                    int keep, int tile_out, int nc, int full_r, int full_c, int lat_h, int lat_w,
+                                    int stride, int up, float* out) {
+  const long long total = planes * H * W;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (long long)gridDim.x * blockDim.x) {
+    const int x = (int)(e % W);
+    const int y = (int)((e / W) % H);
+    const long long p = e / ((long long)H * W);
+    const int gi = y / keep, gj = x / keep;
+    const int th = min(tile_out, (lat_h - gi * stride) * up);
+    const int tw = min(tile_out, (lat_w - gj * stride) * up);
+    const float* t = slots + (long long)tile_slot(gi, gj, nc, full_r, full_c) * slot_elems;
+    out[e] = t[(p * th + (y - gi * keep)) * tw + (x - gj * keep)];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_crop(const void* src, long long planes, int h, int w, int i, int j, int th, int tw, void* dst,
+                       int dtype, hipStream_t s) {
+  const long long total = planes * th * tw;
+  if (total == 0) return hipSuccess;
+  if (dtype == VAEP_DTYPE_F32)
+    hipLaunchKernelGGL(crop_kernel<float>, dim3(grid_for(total)), dim3(256), 0, s, (const float*)src, planes, h, w,
+                       i, j, th, tw, (float*)dst);
+  else
+    hipLaunchKernelGGL(crop_kernel<bf16>, dim3(grid_for(total)), dim3(256), 0, s, (const bf16*)src, planes, h, w,
+                       i, j, th, tw, (bf16*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_blend(const float* nb, float* tile, long long planes, int th, int tw, int nb_len, int e, int axis,
+                        hipStream_t s) {
+  const long long total = planes * e * (axis == 0 ? tw : th);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(blend_kernel, dim3(grid_for(total)), dim3(256), 0, s, nb, tile, planes, th, tw, nb_len, e, axis);
+  return hipGetLastError();
+}
+
+hipError_t launch_tiles_gather(const float* slots, long long slot_elems, long long planes, int H, int W, int keep,
+                               int tile_out, int nc, int full_r, int full_c, int lat_h, int lat_w, int stride, int up,
+                               float* out, hipStream_t s) {
+  const long long total = planes * H * W;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(tiles_gather_kernel, dim3(grid_for(total)), dim3(256), 0, s, slots, slot_elems, planes, H, W,
+                     keep, tile_out, nc, full_r, full_c, lat_h, lat_w, stride, up, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack(const void* src, int c_src, void* dst, const BandLayout& L, int dtype,
                        hipStream_t s, bool transposed) {

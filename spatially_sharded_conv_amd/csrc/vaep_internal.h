@@ -197,6 +197,28 @@ hipError_t launch_pack_weight(const void* src, int co, int ci, int taps, void* d
 // Any-dtype vector -> fp32 vector of n_pad entries (zero padded); src may be NULL (zeros).
 hipError_t launch_to_f32(const void* src, int n, float* dst, int n_pad, int dtype, hipStream_t s);
 
+// Slot of tile (gi, gj) of a tiled decode: the full-size tiles (gi < full_r, gj < full_c)
+// first in raster order (they decode as one batch), then the clipped edge tiles in raster
+// order.
+__host__ __device__ inline int tile_slot(int gi, int gj, int nc, int full_r, int full_c) {
+  if (gi < full_r && gj < full_c) return gi * full_c + gj;
+  const int before = (gi < full_r ? gi : full_r) * (nc - full_c) + (gi > full_r ? gi - full_r : 0) * nc;
+  return full_r * full_c + before + (gi < full_r ? gj - full_c : gj);
+}
+
+// Tiled decode (overlap-blending baseline).  crop: rows [i, i+th), columns [j, j+tw) of
+// each of `planes` h x w planes -> contiguous [planes][th][tw] (dtype).  blend: linear
+// cross-fade of the first e rows (axis 0) / columns (axis 1) of an fp32 [planes][th][tw]
+// tile from the last ones of its neighbour (nb_len rows / columns), in place.  gather:
+// the merged output from the tile slots (see movement.hip).
+hipError_t launch_crop(const void* src, long long planes, int h, int w, int i, int j, int th, int tw, void* dst,
+                       int dtype, hipStream_t s);
+hipError_t launch_blend(const float* nb, float* tile, long long planes, int th, int tw, int nb_len, int e, int axis,
+                        hipStream_t s);
+hipError_t launch_tiles_gather(const float* slots, long long slot_elems, long long planes, int H, int W, int keep,
+                               int tile_out, int nc, int full_r, int full_c, int lat_h, int lat_w, int stride, int up,
+                               float* out, hipStream_t s);
+
 inline size_t dtype_bytes(int dtype) { return dtype == VAEP_DTYPE_F32 ? 4 : 2; }
 
 }  // namespace vaep
