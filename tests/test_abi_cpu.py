@@ -175,3 +175,12 @@ def test_sharded_decode_argument_checks_without_gpu_work():
     assert lib.vaep_decode_sharded(None, bad, 1, 1, 8, 8, L.AXIS_WIDTH, None, 2, bad, bad, 0, None,
                                    None) == L.VAEP_ERR_INVALID_ARG
     assert "model" in L.last_error()
+
+
+def test_tiled_entry_points_check_arguments_without_gpu_work():
+    lib = L.load()
+    n = C.c_size_t()
+    bad = C.c_void_p(1)
+    assert lib.vaep_tiled_workspace_bytes(None, 1, 1, 8, 8, 4, 3, C.byref(n)) == L.VAEP_ERR_INVALID_ARG
+    assert lib.vaep_decode_tiled(None, bad, 1, 1, 8, 8, 4, 3, bad, bad, 0, None) == L.VAEP_ERR_INVALID_ARG
+    assert "model" in L.last_error()
