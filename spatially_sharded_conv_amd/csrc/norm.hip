@@ -208,10 +208,25 @@ __global__ void __launch_bounds__(kThreads) gn_stats(const NormArgs a) {
   }
 }
 
+// Sum of one fp64 value per thread of the workgroup, in a fixed order: a butterfly within
+// each wave (every lane ends with the same sum), then the wave sums in wave order.  sh:
+// kThreads / 64 doubles of LDS.
+__device__ __forceinline__ double block_sum(double v, double* sh) {
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) v += __shfl_xor(v, k, 64);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double r = 0.0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) r += sh[w];
+  __syncthreads();
+  return r;
+}
+
 // Count-weighted merge (feature page, GroupNorm section) of the tiles [t0, t1) of
 // image n, group g: mean = sum w_t mean_t, var = sum w_t (var_t + (mean_t - mean)^2),
-// w_t = n_t / sum n_t.  Fixed thread striding and a fixed tree: the result depends only
-// on the tiles.  Every thread returns (count, mean, var).
+// w_t = n_t / sum n_t.  Fixed thread striding and a fixed reduction order: the result
+// depends only on the tiles.  Every thread returns (count, mean, var).
 __device__ void merge_tiles(const NormArgs& a, int n, int g, int t0, int t1, double* sh,
                             double* cnt, double* mean, double* var) {
   const int tid = threadIdx.x;
@@ -228,14 +243,7 @@ __device__ void merge_tiles(const NormArgs& a, int n, int g, int t0, int t1, dou
   const double total = (double)((t1 - t0) / a.chunks) * (double)slab_pix * cpg;
   double s = 0.0;
   for (int t = t0 + tid; t < t1; t += kThreads) s += (tile_n(t) / total) * P[((long long)t * G + g) * 2];
-  sh[tid] = s;
-  __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) sh[tid] += sh[tid + w];
-    __syncthreads();
-  }
-  const double m = sh[0];
-  __syncthreads();
+  const double m = block_sum(s, sh);
   s = 0.0;
   for (int t = t0 + tid; t < t1; t += kThreads) {
     const double nt = tile_n(t);
@@ -243,16 +251,10 @@ __device__ void merge_tiles(const NormArgs& a, int n, int g, int t0, int t1, dou
     const double d = pr[0] - m;
     s += (nt / total) * (pr[1] / nt + d * d);
   }
-  sh[tid] = s;
-  __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) sh[tid] += sh[tid + w];
-    __syncthreads();
-  }
+  const double v = block_sum(s, sh);
   *cnt = total;
   *mean = m;
-  *var = sh[0];
-  __syncthreads();
+  *var = v;
 }
 
 // Pass 2: one workgroup per (image n, group g, k): k < nb reports band k's moments (its
