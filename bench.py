@@ -91,6 +91,8 @@ def summarise(recs, steps):
             # narrow conv_out are reported apart
             if r["kernel"] == L.KERNEL_CONV_WIDE256 and r["ks"] == 3 and r["ups"] == 0 and r["mode"] == 0:
                 add("conv_wide_3x3", r)
+            elif r["kernel"] == L.KERNEL_CONV_WIDE128X512:
+                add("conv_wide_512px", r)
             elif r["kernel"] in (L.KERNEL_CONV_WIDE256, L.KERNEL_CONV_WIDE128):
                 add("conv_wide_other", r)
             elif r["kernel"] == L.KERNEL_CONV_TILE128:
@@ -220,7 +222,7 @@ def main():
     gn = cls.get("groupnorm") or cls.get("rmsnorm") or {"gbs": 0.0}
 
     roofline = {
-        "kernel": "conv_wide<1, 3, false, 1, 0, 256, 8> (implicit-GEMM 3x3 halo conv, 256x256 tiles, 8 waves, "
+        "kernel": "conv_wide<1, 3, false, 1, 0, 256, 256, 8> (implicit-GEMM 3x3 halo conv, 256x256 tiles, 8 waves, "
                   "LDS-DMA operands, v_mfma_f32_32x32x16_bf16)",
         "bound": "mfma",
         "achieved": round(conv["tflops"], 2),

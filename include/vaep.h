@@ -234,9 +234,11 @@ int vaep_decode_tiled(vaep_model* model, const void* latent, int batch, int fram
 enum { VAEP_STEP_CONV = 1, VAEP_STEP_GROUPNORM = 2, VAEP_STEP_RMSNORM = 3,
        VAEP_STEP_ATTENTION = 4, VAEP_STEP_MOVE = 5 };
 /* Convolution kernel that ran a conv step: 128x128 tiles two per CU, the wide kernel
- * with 256- or 128-channel tiles, the narrow-output kernel, the fp32 kernel. */
+ * with 256 x 256, 128 x 256 or 128 x 512 (channels x pixels) tiles, the narrow-output
+ * kernel, the fp32 kernel. */
 enum { VAEP_KERNEL_OTHER = 0, VAEP_KERNEL_CONV_TILE128 = 1, VAEP_KERNEL_CONV_WIDE256 = 2,
-       VAEP_KERNEL_CONV_WIDE128 = 3, VAEP_KERNEL_CONV_NARROW = 4, VAEP_KERNEL_CONV_F32 = 5 };
+       VAEP_KERNEL_CONV_WIDE128 = 3, VAEP_KERNEL_CONV_NARROW = 4, VAEP_KERNEL_CONV_F32 = 5,
+       VAEP_KERNEL_CONV_WIDE128X512 = 6 };
 typedef struct vaep_profile_entry {
   int32_t step;        /* VAEP_STEP_* */
   int32_t n_kernels;   /* kernels inside the bracket */

@@ -243,12 +243,51 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
   const __amdgpu_buffer_rsrc_t xrs =
       make_rsrc(reinterpret_cast<const char*>(a.x) + x_base * XB,
                 (unsigned)((last_slot - first_slot + 1) * row_elems * XB));
-  f32x16_t acc00, acc01, acc10, acc11;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc00[v] = acc01[v] = acc10[v] = acc11[v] = 0.f;
-
   const int wco = (wave >> 1) * 64;
   const int wpx = (wave & 1) * 64;
+  // Accumulators acc<i><j>: channel co0+wco+32i+8(v/4)+4(lane/32)+(v%4), pixel
+  // tile*BN+wpx+32j+(lane%32).  They start at bias + residual (band modes: fp32 with `cout`
+  // channels in the output's band geometry, split outputs at half their offset), so the
+  // epilogue only stores; the residual's latency overlaps the first operand loads.  (An
+  // opaque copy of the lane index keeps the compiler from carrying these addresses through
+  // the K loop for the epilogue.)
+  f32x16_t acc00, acc01, acc10, acc11;
+  {
+    int ilane = lane;
+    asm volatile("" : "+v"(ilane));
+    auto init = [&](f32x16_t& acc, int i, int j) {
+      const long long p = (long long)tile * BN + wpx + 32 * j + (ilane & 31);
+      long long ro = -1;
+      if ((MODE == kModeBand || MODE == kModeBandSplit) && a.res && p < m_band) {
+        const int n = (int)(p / plane);
+        const int rem = (int)(p - (long long)n * plane);
+        const int r = rem / wc;
+        const int c = rem - r * wc;
+        ro = band_offset(a.out, band, n, r, c);
+        if (MODE == kModeBandSplit) ro >>= 1;
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int co = co0 + wco + 32 * i + 8 * g + 4 * (ilane >> 5);
+        float4 v = *reinterpret_cast<const float4*>(a.bias + co);   // cout_pad entries
+        if (ro >= 0 && co < a.cout) {
+          const float4 rr = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.res) + ro + co);
+          v.x += rr.x;
+          v.y += rr.y;
+          v.z += rr.z;
+          v.w += rr.w;
+        }
+        acc[4 * g + 0] = v.x;
+        acc[4 * g + 1] = v.y;
+        acc[4 * g + 2] = v.z;
+        acc[4 * g + 3] = v.w;
+      }
+    };
+    init(acc00, 0, 0);
+    init(acc01, 0, 1);
+    init(acc10, 1, 0);
+    init(acc11, 1, 1);
+  }
   const int frag = (lane & 31) * LDK + (lane >> 5) * 8;
   const int srow = rs * LDK + q8;
 
@@ -340,38 +379,11 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
 #undef VAEP_MFMA_K
   f32x16_t acc[2][2] = {{acc00, acc01}, {acc10, acc11}};
 
-  // Epilogue.  acc[i][j][v]: channel co0+wco+32i+8(v/4)+4(lane/32)+(v%4), pixel
-  // tile*BN+wpx+32j+(lane%32).
-  // When a GroupNorm consumes the output (a.gn_part set by the launch, whole-row tiles),
-  // bias and residual are folded into the accumulators first and the tile's moments are
-  // formed from the final values before they are stored.
-  bool folded = false;
+  // Epilogue: the accumulators hold the final values.  When a GroupNorm consumes the
+  // output (a.gn_part set by the launch, whole-row tiles), the tile's moments are formed
+  // before the values are stored.
   if constexpr (MODE == kModeBand) {
     if (a.gn_part) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const long long p = (long long)tile * BN + wpx + 32 * j + (lane & 31);
-        const int n = (int)(p / plane);
-        const int rem = (int)(p - (long long)n * plane);
-        const int r = rem / wc;
-        const int c = rem - r * wc;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int co = co0 + wco + 32 * i + 8 * g + 4 * (lane >> 5);
-            const float4 bb = *reinterpret_cast<const float4*>(a.bias + co);
-            float4 rr = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (a.res)
-              rr = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.res) +
-                                                    band_offset(a.out, band, n, r, c) + co);
-            acc[i][j][4 * g + 0] += bb.x + rr.x;
-            acc[i][j][4 * g + 1] += bb.y + rr.y;
-            acc[i][j][4 * g + 2] += bb.z + rr.z;
-            acc[i][j][4 * g + 3] += bb.w + rr.w;
-          }
-      }
-      folded = true;
       const long long p0 = (long long)tile * BN;
       const int n0 = (int)(p0 / plane);
       const int rem0 = (int)(p0 - (long long)n0 * plane);
@@ -396,23 +408,8 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int co = co0 + wco + 32 * i + 8 * g + 4 * (lane >> 5);
         if (co >= a.cout) continue;
-        float v[4];
-        const float4 bb = folded ? make_float4(0.f, 0.f, 0.f, 0.f) : *reinterpret_cast<const float4*>(a.bias + co);
-        v[0] = acc[i][j][4 * g + 0] + bb.x;
-        v[1] = acc[i][j][4 * g + 1] + bb.y;
-        v[2] = acc[i][j][4 * g + 2] + bb.z;
-        v[3] = acc[i][j][4 * g + 3] + bb.w;
+        const float v[4] = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
         if (MODE == kModeBand || MODE == kModeBandSplit) {
-          if (a.res && !folded) {
-            // residual: fp32 with `cout` channels in the output's band geometry
-            long long ro = band_offset(a.out, band, n, r, c);
-            if (MODE == kModeBandSplit) ro >>= 1;
-            const float4 rr = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.res) + ro + co);
-            v[0] += rr.x;
-            v[1] += rr.y;
-            v[2] += rr.z;
-            v[3] += rr.w;
-          }
           if (MODE == kModeBandSplit)
             store_split4(a.out, a.y, a.cout, band, n, r, c, co, v);
           else

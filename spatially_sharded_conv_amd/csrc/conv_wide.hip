@@ -6,12 +6,13 @@
 // output rows (ChituDiffusion "VAEP" feature page, conv section; "Static Layer-Wise VAE
 // Decode", operator table, "Spatial convolution" row).
 //
-// Layout of the work: one 256-thread workgroup computes BM (128 or 256) output channels
-// x 256 pixels of one band as an implicit GEMM D[co][pixel] = W[co][k] X[k][pixel] with
-// v_mfma_f32_32x32x16_bf16; the four waves own (BM/2) x 128 each.  K advances one tap
-// and 64 channels per step, taps fastest.  Both operand tiles go global -> LDS directly (buffer loads
-// with the LDS destination), through S stages (2 for BM 256, 3 for BM 128), with one
-// barrier per step and no staging registers.  A lane's 16-byte chunk lands at a fixed
+// Layout of the work: one workgroup of NW waves computes BM output channels x BN pixels
+// of one band (256 x 256 and 128 x 512 with 8 waves, 128 x 256 with 4) as an implicit
+// GEMM D[co][pixel] = W[co][k] X[k][pixel] with v_mfma_f32_32x32x16_bf16; the waves own
+// (BM/2) x (2 BN/NW) each.  K advances one tap and 64 channels per step, taps fastest.
+// Both operand tiles go global -> LDS directly (buffer loads with the LDS destination),
+// through S stages (3 for 128 x 256, else 2), with one barrier per step and no staging
+// registers.  A lane's 16-byte chunk lands at a fixed
 // LDS slot, so the XOR swizzle that keeps the matrix-core reads free of bank conflicts is
 // applied on the global side: LDS slot (row, p) holds logical chunk p ^ f(row),
 // f(row) = (row & 7) ^ ((row >> 3) & 1).
@@ -39,7 +40,6 @@ typedef __attribute__((address_space(3))) unsigned short lds_u16;
 
 namespace {
 
-constexpr int BN = kWideTileM;              // pixels per workgroup
 constexpr unsigned kPadOffset = 0x80000000u; // past every buffer resource (< 2 GiB, host-checked)
 
 // Raw buffer resource over [base, base + bytes): loads past the end return zeros, which is
@@ -139,19 +139,18 @@ __device__ __forceinline__ void store4(const BandLayout& L, void* y, int half, i
   }
 }
 
-// Split-output epilogue.  Lanes l and l+32 hold alternate 4-channel groups of one pixel;
-// v_permlane32_swap pairs them up so that each lane owns 8 consecutive channels and
-// stores their hi and lo parts as one 16-byte store each.
-// folded: bias and residual are already in acc.
-template <bool SUB, int MI, int NJ>
+// Split-output epilogue (acc holds the final values).  Lanes l and l+32 hold alternate
+// 4-channel groups of one pixel; v_permlane32_swap pairs them up so that each lane owns 8
+// consecutive channels and stores their hi and lo parts as one 16-byte store each.
+template <bool SUB, int MI, int NJ, int BN>
 __device__ __forceinline__ void split_epilogue(const ConvArgs& a, const f32x16_t (&acc)[MI][NJ], int band,
                                                int tile, int plane, long long m_band, int W, int py, int px,
-                                               int co0, int wco, int wpx, int lane, bool folded) {
+                                               int co0, int wco, int wpx, int lane) {
   const int hi = lane >> 5;
   const int half = a.cout;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const long long p = (long long)tile * kWideTileM + wpx + 32 * j + (lane & 31);
+    const long long p = (long long)tile * BN + wpx + 32 * j + (lane & 31);
     const bool pv = p < m_band;
     long long o = 0, ho = 0;
     bool halo = false;
@@ -183,20 +182,6 @@ __device__ __forceinline__ void split_epilogue(const ConvArgs& a, const f32x16_t
         }
         const int co = co0 + wco + 32 * i + 8 * (2 * m + hi);
         if (!pv || co >= a.cout) continue;
-        if (!folded) {
-          const float4 b0 = *reinterpret_cast<const float4*>(a.bias + co);
-          const float4 b1 = *reinterpret_cast<const float4*>(a.bias + co + 4);
-          v[0] += b0.x; v[1] += b0.y; v[2] += b0.z; v[3] += b0.w;
-          v[4] += b1.x; v[5] += b1.y; v[6] += b1.z; v[7] += b1.w;
-        }
-        if (a.res && !folded) {
-          // residual: fp32 with `cout` channels in the output's band geometry
-          const float* rp = reinterpret_cast<const float*>(a.res) + (o >> 1) + co;
-          const float4 r0 = *reinterpret_cast<const float4*>(rp);
-          const float4 r1 = *reinterpret_cast<const float4*>(rp + 4);
-          v[0] += r0.x; v[1] += r0.y; v[2] += r0.z; v[3] += r0.w;
-          v[4] += r1.x; v[5] += r1.y; v[6] += r1.z; v[7] += r1.w;
-        }
         unsigned hw[4], lw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -221,12 +206,34 @@ __device__ __forceinline__ void split_epilogue(const ConvArgs& a, const f32x16_t
 __device__ __forceinline__ constexpr int wpart(int parts, int p) { return parts == 3 && p == 2 ? 1 : 0; }
 __device__ __forceinline__ constexpr int xpart(int p) { return p == 1 ? 1 : 0; }
 
-template <int KT, int KS, bool SUB, int PARTS, int MODE, int BM, int NW>
+// Load g (0 .. NL-1) of a step is an A (weight) chunk load for g < NA, else a B (pixel)
+// chunk load; the loads go out in four quarters, quarter q issuing loads QB(q) .. QB(q+1)-1.
+// When both counts divide by four each quarter interleaves NA/4 A and NB/4 B loads.
+template <int NA, int NB>
+struct LoadOrder {
+  static constexpr int NL = NA + NB;
+  static constexpr bool even = NA % 4 == 0 && NB % 4 == 0;
+  static constexpr int QB(int q) { return q * NL / 4; }
+  static constexpr int count(int q) { return QB(q + 1) - QB(q); }
+  // flat index of the t-th load of quarter q
+  static constexpr int at(int q, int t) {
+    return !even ? QB(q) + t : (t < NA / 4 ? q * (NA / 4) + t : NA + q * (NB / 4) + t - NA / 4);
+  }
+  // the load starts a run that shares one scalar offset (A loads, or B loads, of a quarter)
+  static constexpr bool first(int q, int t) {
+    return even ? (t == 0 || t == NA / 4) : (at(q, t) == QB(q) || at(q, t) == (QB(q) > NA ? QB(q) : NA));
+  }
+};
+
+template <int KT, int KS, bool SUB, int PARTS, int MODE, int BM, int BN, int NW>
 __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   // NW waves: 2 along the output channels x NW/2 along the pixels.  With 8 waves two
   // share each SIMD, so one wave's loads, LDS reads and barrier waits hide behind the
   // other's MFMAs.
-  constexpr int S = BM == 256 ? 2 : 3;        // LDS stages
+  constexpr int S = (BM == 128 && BN == 256) ? 3 : 2;   // LDS stages
+  // L2 prefetch of the step PFD ahead needs 256 bytes of LDS beyond the stages (its landing
+  // words); the 128 x 512 tile fills the 160 KiB with its two stages and goes without.
+  constexpr bool PF = S * (BM + BN) * 64 * 2 + 256 <= 160 * 1024;
   constexpr int TAPS = SUB ? 4 : KT * KS * KS;
   constexpr int WP = PARTS == 3 ? 2 : 1;      // weight parts per tap in the packed rows
   constexpr int WPX = NW / 2;                 // waves along the pixels
@@ -234,14 +241,17 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   constexpr int NB = BN / (8 * NW);           // B (pixel) chunk loads per thread per step
   constexpr int MI = BM / 64;                 // 32-row channel blocks per wave
   constexpr int NJ = BN / (32 * WPX);         // 32-pixel blocks per wave
-  static_assert(NA % 4 == 0 && NB % 4 == 0, "loads per quarter step");
+  typedef LoadOrder<NA, NB> LO;
+  static_assert(LO::NL >= 4 && LO::count(0) >= 1 && MI * NJ >= 3, "loads per quarter step");
   constexpr int PH = SUB ? 4 : 1;
-  // S operand stages: A (BM x 64) then B (BN x 64) per stage; the epilogue reuses the space
-  __shared__ __attribute__((aligned(1024))) unsigned short smem[S * (BM + BN) * 64];
-  __shared__ unsigned int sPF[64];             // prefetch landing words (never read)
+  // S operand stages: A (BM x 64) then B (BN x 64) per stage, then the prefetch landing
+  // words (never read); the epilogue reuses the space
+  constexpr int kStageElems = S * (BM + BN) * 64;
+  __shared__ __attribute__((aligned(1024))) unsigned short smem[kStageElems + (PF ? 128 : 0)];
+  const unsigned short* sPF = smem + kStageElems;
   constexpr int PFD = 2;                       // prefetch target: PFD steps past the step issued
-  constexpr int NG = NA + NB + 2;              // loads per thread per issued step
-  constexpr int LPP = (NA + NB) / 4;           // operand loads per quarter step
+  constexpr int PFN = PF ? 2 : 0;              // prefetch loads per issued step
+  constexpr int NG = LO::NL + PFN;             // loads per thread per issued step
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -354,13 +364,54 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
     pf_mask = ok ? m : 0;
   }
 
+  // acc[i][j][v]: channel co0 + wco + 32i + 8(v/4) + 4(lane/32) + v%4, pixel
+  // tile*BN + wpx + 32j + lane%32 (source grid for sub-pixel convs).
+  const int wco = (wave / WPX) * (BM / 2);
+  const int wpx = (wave % WPX) * (BN / WPX);
+  // The accumulators start at bias + residual (fp32 with `cout` channels in the output's
+  // band geometry; split outputs address it at half their offset), so the epilogue only
+  // stores: the residual's HBM latency overlaps the first operand loads instead of
+  // stalling the stores.
+  // (an opaque copy of the lane index keeps the compiler from carrying these addresses
+  // through the K loop for the epilogue, which forms them again)
   f32x16_t acc[MI][NJ];
+  int ilane = lane;
+  asm volatile("" : "+v"(ilane));
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int j = 0; j < NJ; ++j) {
+    const long long p = (long long)tile * BN + wpx + 32 * j + (ilane & 31);
+    long long ro = -1;
+    if (a.res && p < m_band) {
+      const int n = (int)(p / plane);
+      const int rem = (int)(p - (long long)n * plane);
+      int r = rem / W;
+      int c = rem - r * W;
+      if (SUB) {
+        r = 2 * r + py;
+        c = 2 * c + px;
+      }
+      ro = band_offset(a.out, band, n, r, c);
+      if (MODE == kModeBandSplit) ro >>= 1;
+    }
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+      for (int g = 0; g < 4; ++g) {
+        const int co = co0 + wco + 32 * i + 8 * g + 4 * (ilane >> 5);
+        float4 v = *reinterpret_cast<const float4*>(a.bias + co);   // cout_pad entries
+        if (ro >= 0 && co < a.cout) {
+          const float4 rr = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.res) + ro + co);
+          v.x += rr.x;
+          v.y += rr.y;
+          v.z += rr.z;
+          v.w += rr.w;
+        }
+        acc[i][j][4 * g + 0] = v.x;
+        acc[i][j][4 * g + 1] = v.y;
+        acc[i][j][4 * g + 2] = v.z;
+        acc[i][j][4 * g + 3] = v.w;
+      }
+  }
 
   // Issue the loads of step (c0, part, tap) into LDS stage st; taps vary fastest, so
   // consecutive steps read shifted windows of the same rows and channels (L2 and the
@@ -403,32 +454,33 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
 #define VAEP_SB(st) (smem + S * (BM * 64) + (st) * (BN * 64))
 // The loads of one step go out in four parts, one before each group of MFMAs of the
 // current step, so that the wave never waits on a full load queue with the matrix cores
-// idle.  Part 0 also forms the tap's offsets; part 3 adds the prefetch and advances.
-// One load of a step: part q (0..3), index m within the part (A chunks first, then B).
-// Part 0's first load also forms the tap's offsets; part 3's last load adds the prefetch
-// and advances the step counters.
-#define VAEP_ISSUE_ONE(st, q, m)                                                               \
+// idle.  One load of a step: quarter q (0..3), index t within the quarter (LoadOrder).
+// Quarter 0's first load also forms the tap's offsets; quarter 3's last load adds the
+// prefetch and advances the step counters.
+#define VAEP_ISSUE_ONE(st, q, t)                                                               \
   {                                                                                            \
-    if ((q) == 0 && (m) == 0) {                                                                \
+    if ((q) == 0 && (t) == 0) {                                                                \
       VAEP_TAP_GEO(itap, need, delta);                                                         \
       _Pragma("unroll") for (int j = 0; j < NB; ++j)                                           \
         bvo[j] = ((pmask[j] & need) == need) ? (unsigned)((int)pbase[j] + delta) : kPadOffset;  \
     }                                                                                          \
-    if ((m) < NA / 4) {                                                                        \
-      const int j = (q) * (NA / 4) + (m);                                                      \
+    const int g = LO::at((q), (t));                                                            \
+    if (g < NA) {                                                                              \
+      const int j = g;                                                                         \
       const int aso = ((itap * WP + wpart(PARTS, ipart)) * C + ic) * 2;                        \
-      dma16((m) == 0, wrs, lds_addr(VAEP_SA(st)) + wrow + j * kRowStep, avo[j], aso);           \
+      dma16(LO::first((q), (t)), wrs, lds_addr(VAEP_SA(st)) + wrow + j * kRowStep, avo[j], aso); \
     } else {                                                                                   \
-      const int j = (q) * (NB / 4) + (m) - NA / 4;                                             \
+      const int j = g - NA;                                                                    \
       const int bso = (xpart(ipart) * C + ic) * 2;                                             \
-      dma16((m) == NA / 4, xrs, lds_addr(VAEP_SB(st)) + wrow + j * kRowStep, bvo[j], bso);     \
+      dma16(LO::first((q), (t)), xrs, lds_addr(VAEP_SB(st)) + wrow + j * kRowStep, bvo[j], bso); \
     }                                                                                          \
-    if ((q) == 3 && (m) == LPP - 1) {                                                          \
-      VAEP_TAP_GEO(ptap, need, delta);                                                         \
-      const unsigned pbv = ((pf_mask & need) == need) ? (unsigned)((int)pf_base + delta) : kPadOffset; \
-      prefetch4(wrs, lds_addr((const unsigned short*)sPF), pf_avo,                             \
-                ((ptap * WP + wpart(PARTS, ppart)) * C + pc) * 2);                             \
-      prefetch4(xrs, lds_addr((const unsigned short*)sPF), pbv, (xpart(ppart) * C + pc) * 2);  \
+    if ((q) == 3 && (t) == LO::count(3) - 1) {                                                 \
+      if constexpr (PF) {                                                                      \
+        VAEP_TAP_GEO(ptap, need, delta);                                                       \
+        const unsigned pbv = ((pf_mask & need) == need) ? (unsigned)((int)pf_base + delta) : kPadOffset; \
+        prefetch4(wrs, lds_addr(sPF), pf_avo, ((ptap * WP + wpart(PARTS, ppart)) * C + pc) * 2); \
+        prefetch4(xrs, lds_addr(sPF), pbv, (xpart(ppart) * C + pc) * 2);                       \
+      }                                                                                        \
       ++issued;                                                                                \
       VAEP_ADVANCE(itap, ipart, ic);                                                           \
       if (pstep + 1 < nsteps) {                                                                \
@@ -439,7 +491,7 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   }
 #define VAEP_ISSUE_PART(st, q)                                                                 \
   {                                                                                            \
-    _Pragma("unroll") for (int m = 0; m < LPP; ++m) VAEP_ISSUE_ONE(st, q, m);                  \
+    _Pragma("unroll") for (int t = 0; t < LO::count(q); ++t) VAEP_ISSUE_ONE(st, q, t);         \
   }
 #define VAEP_ISSUE(st)                                                                         \
   {                                                                                            \
@@ -455,20 +507,18 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   int ko[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) ko[kk] = lr + (((2 * kk + (lane >> 5)) ^ fl) << 3);
-  const int wco = (wave / WPX) * (BM / 2);
-  const int wpx = (wave % WPX) * (BN / WPX);
 
   // Step s computes from stage s % S and first issues step s + S - 1 into stage
   // (s + S - 1) % S, which every wave finished reading before the barrier.  Loads complete
   // in issue order; this thread's loads of step s have landed once at most the loads
-  // issued after them (the two prefetches of that step, and the next step's group when
-  // S is 3) are outstanding.  The barrier then publishes every thread's chunks.
+  // issued after them (the prefetches of that step, if any, and the next step's group
+  // when S is 3) are outstanding.  The barrier then publishes every thread's chunks.
 #define VAEP_STEP(cs, ns, si)                                                                    \
   {                                                                                            \
     if (S == 3 && (si) + 2 <= nsteps)                                                          \
-      __builtin_amdgcn_s_waitcnt(((NG + 2) & 15) | (((NG + 2) >> 4) << 14) | (7 << 4) | (15 << 8)); \
+      __builtin_amdgcn_s_waitcnt(((NG + PFN) & 15) | (((NG + PFN) >> 4) << 14) | (7 << 4) | (15 << 8)); \
     else                                                                                       \
-      __builtin_amdgcn_s_waitcnt(2 | (7 << 4) | (15 << 8));                                    \
+      __builtin_amdgcn_s_waitcnt(PFN | (7 << 4) | (15 << 8));                                  \
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                            \
     const bool more = issued < nsteps;                                                         \
     const unsigned short* A = VAEP_SA(cs);                                                     \
@@ -492,9 +542,9 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
       _Pragma("unroll") for (int i = 0; i < MI; ++i)                                           \
         _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                       \
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0); \
-          constexpr int per = (MI * NJ) / LPP;                                                 \
+          const int per = (MI * NJ) / LO::count(kk);                                           \
           const int idx = i * NJ + j;                                                          \
-          if (idx % per == per - 1 && idx / per < LPP) {                                       \
+          if (idx % per == per - 1 && idx / per < LO::count(kk)) {                             \
             __builtin_amdgcn_sched_barrier(0);                                                 \
             if (more) VAEP_ISSUE_ONE(ns, kk, idx / per);                                       \
             __builtin_amdgcn_sched_barrier(0);                                                 \
@@ -532,18 +582,13 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
 #undef VAEP_ISSUE
 #undef VAEP_SET_TAP
 
-  // Epilogue.  acc[i][j][v]: channel co0 + wco + 32i + 8(v/4) + 4(lane/32) + v%4, pixel
-  // tile*BN + wpx + 32j + lane%32 (source grid for sub-pixel convs).
+  // Epilogue: the accumulators hold the final values.
   const int half = a.cout;   // kModeBandSplit: lo parts start `cout` channels after the hi parts
   // When a GroupNorm consumes the output (a.gn_part set by the launch: whole-row tiles),
-  // the tile's moments are formed from the final values (hi + lo for split outputs):
-  // split outputs (no residual) get the bias folded into the accumulators, as hi + lo,
-  // before the statistics and the stores (bf16 parts of hi + lo are hi and lo again);
-  // plain outputs write each final value back into the accumulators as they store it and
-  // form the statistics afterwards.
+  // the tile's moments are formed from the values the norm reads (hi + lo for split
+  // outputs); plain outputs are stored first and the statistics formed afterwards.
   const bool gn = a.gn_part != nullptr;
-  bool folded = false;
-  auto gn_stats = [&]() {
+  auto gn_stats = [&](auto splitv) {
     gnstats::lds_barrier();   // every wave is done with the operand stages: the LDS is scratch now
     const long long p0 = (long long)tile * BN;
     const int n0 = (int)(p0 / plane);
@@ -553,30 +598,12 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
     const long long rec = gnstats::tile_record(a.out, band, n0, SUB ? 2 * r0 + py : r0,
                                                (SUB ? px * (W / BN) : 0) + c0 / BN, chunks);
     const int cg = a.cout / a.gn_groups;
-    gnstats::tile_stats<MI, NJ, NW, WPX, BM, false>(
+    gnstats::tile_stats<MI, NJ, NW, WPX, BM, decltype(splitv)::value>(
         acc, wave, lane, cg, BN, a.gn_part + (rec * a.gn_groups + co0 / cg) * 2, reinterpret_cast<float*>(smem));
   };
-  if (MODE == kModeBandSplit && gn) {
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int co = co0 + wco + 32 * i + 8 * g + 4 * (lane >> 5);
-        const float4 bb = *reinterpret_cast<const float4*>(a.bias + co);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          // hi + lo of the value: what the norm reads, and it splits into the same parts
-          acc[i][j][4 * g + 0] = gnstats::seen<true>(acc[i][j][4 * g + 0] + bb.x);
-          acc[i][j][4 * g + 1] = gnstats::seen<true>(acc[i][j][4 * g + 1] + bb.y);
-          acc[i][j][4 * g + 2] = gnstats::seen<true>(acc[i][j][4 * g + 2] + bb.z);
-          acc[i][j][4 * g + 3] = gnstats::seen<true>(acc[i][j][4 * g + 3] + bb.w);
-        }
-      }
-    folded = true;
-    gn_stats();
-  }
+  if (MODE == kModeBandSplit && gn) gn_stats(std::true_type{});
   if (MODE == kModeBandSplit) {
-    split_epilogue<SUB, MI, NJ>(a, acc, band, tile, plane, m_band, W, py, px, co0, wco, wpx, lane, folded);
+    split_epilogue<SUB, MI, NJ, BN>(a, acc, band, tile, plane, m_band, W, py, px, co0, wco, wpx, lane);
     return;
   }
 #pragma unroll
@@ -597,63 +624,48 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int co = co0 + wco + 32 * i + 8 * g + 4 * (lane >> 5);
         if (co >= a.cout) continue;
-        const float4 bb = *reinterpret_cast<const float4*>(a.bias + co);
-        float v[4] = {acc[i][j][4 * g + 0] + bb.x, acc[i][j][4 * g + 1] + bb.y,
-                      acc[i][j][4 * g + 2] + bb.z, acc[i][j][4 * g + 3] + bb.w};
-        if (a.res) {
-          // residual: fp32 with `cout` channels in the output's band geometry
-          long long ro = band_offset(a.out, band, n, r, c);
-          if (MODE == kModeBandSplit) ro >>= 1;
-          const float4 rr = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.res) + ro + co);
-          v[0] += rr.x;
-          v[1] += rr.y;
-          v[2] += rr.z;
-          v[3] += rr.w;
-        }
+        const float v[4] = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
         store4<MODE>(a.out, a.y, half, band, n, r, c, co, v);
-        if (gn) {
-          acc[i][j][4 * g + 0] = v[0];
-          acc[i][j][4 * g + 1] = v[1];
-          acc[i][j][4 * g + 2] = v[2];
-          acc[i][j][4 * g + 3] = v[3];
-        }
       }
     }
   }
-  if (gn) gn_stats();
+  if (gn) gn_stats(std::false_type{});
 }
 
 template <int KT, int KS, bool SUB, int PARTS, int MODE>
-hipError_t go_bm(const ConvArgs& a, int bm, hipStream_t s) {
+hipError_t go_tile(const ConvArgs& a, WideTile t, hipStream_t s) {
   const int ph = SUB ? 4 : 1;
-  const long long wgs = (long long)a.tiles_total * (a.cout_pad / bm) * ph;
+  const long long wgs = (long long)a.tiles_total * (a.cout_pad / t.bm) * ph;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (bm == 256)
-    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 256, 8>), dim3((unsigned)wgs), dim3(512), 0, s, a);
+  if (t.bm == 256)
+    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 256, 256, 8>), dim3((unsigned)wgs), dim3(512), 0, s, a);
+  else if (t.bn == 256)
+    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128, 256, 4>), dim3((unsigned)wgs), dim3(256), 0, s, a);
+  else if constexpr (!SUB)
+    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128, 512, 8>), dim3((unsigned)wgs), dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128, 4>), dim3((unsigned)wgs), dim3(256), 0, s, a);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 template <int KT, int KS, bool SUB, int PARTS>
-hipError_t go_mode(const ConvArgs& a, int bm, hipStream_t s) {
-  if (a.mode == kModeBandSplit) return go_bm<KT, KS, SUB, PARTS, kModeBandSplit>(a, bm, s);
-  return go_bm<KT, KS, SUB, PARTS, kModeBand>(a, bm, s);
+hipError_t go_mode(const ConvArgs& a, WideTile t, hipStream_t s) {
+  if (a.mode == kModeBandSplit) return go_tile<KT, KS, SUB, PARTS, kModeBandSplit>(a, t, s);
+  return go_tile<KT, KS, SUB, PARTS, kModeBand>(a, t, s);
 }
 
 }  // namespace
 
-// Workgroups of 256 output channels when a layer still fills the 256 CUs with them.
-static int wide_bm(const ConvArgs& a, long long tiles) {
+// Workgroup tile (output channels x pixels) of the wide kernel: 256 x 256 when a layer
+// still fills the 256 CUs with two workgroups each; else, for plain convs, 128 x 512 with
+// 8 waves when that does; else 128 x 256 with 4 waves.  Decided on the whole image, so
+// every band table of an image runs the same kernel.
+WideTile wide_tile(const ConvArgs& a) {
   const int ph = a.sub ? 4 : 1;
-  return (a.cout_pad % 256 == 0 && tiles * (a.cout_pad / 256) * ph >= 512) ? 256 : 128;
-}
-
-static long long wide_tiles(const ConvArgs& a) {
-  long long t = 0;
-  for (int b = 0; b < a.in.nb; ++b)
-    t += ((long long)a.in.n_img * a.in.rows[b] * a.in.W + kWideTileM - 1) / kWideTileM;
-  return t;
+  const long long px = (long long)a.in.n_img * a.in.H * a.in.W;
+  if (a.cout_pad % 256 == 0 && (px + 255) / 256 * (a.cout_pad / 256) * ph >= 512) return {256, 256};
+  if (!a.sub && a.cout_pad % 128 == 0 && (px + 511) / 512 * (a.cout_pad / 128) >= 512) return {128, 512};
+  return {128, 256};
 }
 
 bool conv_wide_fits(const ConvArgs& a) {
@@ -662,9 +674,10 @@ bool conv_wide_fits(const ConvArgs& a) {
   if (a.mode != kModeBand && a.mode != kModeBandSplit) return false;
   if (a.cin % 64 != 0 || a.cout_pad % 128 != 0) return false;
   const bool geo = (a.kt == 1 && (a.ks == 3 || a.ks == 1)) || (a.kt == 3 && a.ks == 3);
-  // With 128-channel tiles the 1-workgroup-per-CU kernel cannot hide its fp32 epilogue
+  // With 128 x 256 tiles the 1-workgroup-per-CU kernel cannot hide its fp32 epilogue
   // behind another workgroup's K loop; those layers stay on the 2-per-CU kernel.
-  return geo && wide_bm(a, wide_tiles(a)) == 256;
+  const WideTile t = wide_tile(a);
+  return geo && !(t.bm == 128 && t.bn == 256);
 }
 
 hipError_t launch_conv_wide(ConvArgs& a, hipStream_t s) {
@@ -673,9 +686,11 @@ hipError_t launch_conv_wide(ConvArgs& a, hipStream_t s) {
   // split operands feed the sub-pixel form only
   if (a.sub != a.x_split || (a.sub && (a.kt != 1 || a.ks != 3))) return hipErrorInvalidValue;
   if (a.in.C != (a.x_split ? 2 * a.cin : a.cin)) return hipErrorInvalidValue;
+  const WideTile wt = wide_tile(a);
+  const int bn = wt.bn;
   // buffer-resource addressing: the rows one tile reads and the weights stay below 2 GiB
   for (int b = 0; b < a.in.nb; ++b)
-    if ((long long)a.kt * (a.in.rows[b] + 2) * a.in.W * a.in.C * 2 + 2LL * kWideTileM * a.in.C * 2 >=
+    if ((long long)a.kt * (a.in.rows[b] + 2) * a.in.W * a.in.C * 2 + 2LL * bn * a.in.C * 2 >=
         (1LL << 31) - 4096)
       return hipErrorInvalidValue;
   const long long kw = (long long)a.kt * (a.sub ? 4 * 2 : a.ks * a.ks) * a.cin;
@@ -685,25 +700,26 @@ hipError_t launch_conv_wide(ConvArgs& a, hipStream_t s) {
   for (int b = 0; b < a.in.nb; ++b) {
     a.tile_start[b] = t;
     const long long m = (long long)a.in.n_img * a.in.rows[b] * a.in.W;
-    t += (int)((m + kWideTileM - 1) / kWideTileM);
+    t += (int)((m + bn - 1) / bn);
   }
   a.tile_start[a.in.nb] = t;
   a.tiles_total = t;
   if (t == 0) return hipSuccess;
-  const int bm = wide_bm(a, t);
-  a.kernel_used = bm == 256 ? VAEP_KERNEL_CONV_WIDE256 : VAEP_KERNEL_CONV_WIDE128;
+  const int bm = wt.bm;
+  a.kernel_used = bm == 256 ? VAEP_KERNEL_CONV_WIDE256
+                            : (bn == 512 ? VAEP_KERNEL_CONV_WIDE128X512 : VAEP_KERNEL_CONV_WIDE128);
   // GroupNorm tile statistics in the epilogue: whole-row pixel tiles, every group inside
   // one channel tile
   a.gn_chunk = 0;
-  if (a.gn_part && (a.mode == kModeBand || (a.mode == kModeBandSplit && !a.res)) && a.in.W % kWideTileM == 0 &&
+  if (a.gn_part && (a.mode == kModeBand || (a.mode == kModeBandSplit && !a.res)) && a.in.W % bn == 0 &&
       a.cout == a.cout_pad && a.gn_groups > 0 && a.cout % a.gn_groups == 0 && (a.cout / a.gn_groups) % 4 == 0 &&
       bm % (a.cout / a.gn_groups) == 0)
-    a.gn_chunk = kWideTileM;
+    a.gn_chunk = bn;
   if (!a.gn_chunk) a.gn_part = nullptr;
-  if (a.sub) return go_mode<1, 3, true, 3>(a, bm, s);
-  if (a.kt == 1 && a.ks == 3) return go_mode<1, 3, false, 1>(a, bm, s);
-  if (a.kt == 1 && a.ks == 1) return go_mode<1, 1, false, 1>(a, bm, s);
-  if (a.kt == 3 && a.ks == 3) return go_mode<3, 3, false, 1>(a, bm, s);
+  if (a.sub) return go_mode<1, 3, true, 3>(a, wt, s);
+  if (a.kt == 1 && a.ks == 3) return go_mode<1, 3, false, 1>(a, wt, s);
+  if (a.kt == 1 && a.ks == 1) return go_mode<1, 1, false, 1>(a, wt, s);
+  if (a.kt == 3 && a.ks == 3) return go_mode<3, 3, false, 1>(a, wt, s);
   return hipErrorInvalidValue;
 }
 

@@ -99,8 +99,12 @@ hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s);
 // Pixel tile of the MFMA kernel along M and output-channel tile along N.
 constexpr int kConvTileM = 128;
 constexpr int kConvTileN = 128;
-// Pixel tile of the wide kernel (output-channel tile 128 or 256).
-constexpr int kWideTileM = 256;
+// Workgroup tile of the wide kernel, output channels x pixels: 256 x 256, 128 x 256 or
+// 128 x 512.
+struct WideTile {
+  int bm, bn;
+};
+WideTile wide_tile(const ConvArgs& a);
 // Whether the wide kernel runs the conv described by `a` (bf16 path): K in steps of 64
 // channels, output channels a multiple of 128, band-layout epilogues.  Sub-pixel convs
 // always run there.

@@ -178,6 +178,27 @@ def test_repeat_and_alternating_calls(gpu_lib):
     dec.close()
 
 
+def test_full_size_bands_bit_identical_and_kernels(gpu_lib):
+    # The 1024^2 decode runs every conv kernel family (128x128 tiles, 256x256 and 128x512
+    # wide tiles with GroupNorm moments in the epilogue, sub-pixel upsample, narrow
+    # conv_out); its band decode must equal the full decode bit for bit.
+    cfg = preset(3)
+    dec, _ = make_decoder(cfg)
+    z = make_latent(cfg)
+    ws = dec.workspace(1, 1, cfg.latent_h, cfg.latent_w, len(cfg.band_starts) - 1)
+    y_full, rc, _ = gpu_decode(dec, cfg, z, (0, cfg.latent_h), ws)
+    assert rc == 0
+    vaep.profile_begin(dec)
+    y_band, rc, _ = gpu_decode(dec, cfg, z, cfg.band_starts, ws)
+    recs = vaep.profile_end(dec)
+    assert rc == 0
+    used = {r["kernel"] for r in recs if r["step"] == L.STEP_CONV}
+    for k in (L.KERNEL_CONV_TILE128, L.KERNEL_CONV_WIDE256, L.KERNEL_CONV_WIDE128X512, L.KERNEL_CONV_NARROW):
+        assert k in used, (k, used)
+    assert torch.equal(y_band, y_full)
+    dec.close()
+
+
 @pytest.mark.parametrize("shape", [(10, 12), (12, 20), (9, 16)])
 def test_band_decode_is_bit_identical_to_full(gpu_lib, shape):
     # convs and attention compute each element identically on any band table, and the

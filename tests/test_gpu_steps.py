@@ -88,6 +88,31 @@ def test_upsample_conv_from_fp32_wide_tiles(gpu_lib):
     assert_close(got, ref, *ACC_TOL, what="sub-pixel upsample conv, wide tiles")
 
 
+@pytest.mark.parametrize("kind", ["3x3_res_cout96", "1x1_cout128", "3x3x3_causal_cout128"])
+def test_conv_128x512_tiles(gpu_lib, kind):
+    # 128-channel output tiles over 512 pixels (8 waves): enough pixels that the layer fills
+    # the CUs with them, rows that are not a multiple of 512 (tiles straddle rows), a one-row
+    # band, a ragged channel tile (96 of 128), and a second band table that must give the
+    # same bits
+    video = kind.startswith("3x3x3")
+    cout = 96 if "cout96" in kind else 128
+    ks = 1 if kind.startswith("1x1") else 3
+    shape = (1, 64, 4, 130, 520) if video else (1, 64, 260, 1030)
+    H = shape[-2]
+    x = seeded(shape, 51, dtype="bf16")
+    wshape = (cout, 64, 3, 3, 3) if video else (cout, 64, ks, ks)
+    w = seeded(wshape, 52, 1 / math.sqrt(64 * ks * ks * (3 if video else 1)), dtype="bf16")
+    b = seeded((cout,), 53, 0.1, dtype="bf16")
+    r = seeded((shape[0], cout) + shape[2:], 54, dtype="f32") if kind.startswith("3x3_res") else None
+    ref = _conv_ref(x, w, b, video, r, "bf16")
+    args = (to_dev(x, "bf16"), to_dev(w, "bf16"), to_dev(b, "bf16"))
+    res = None if r is None else r.cuda()
+    got = vaep.step_conv(*args, (0, 77, 78, H), causal=video, residual=res)
+    assert_close(got, ref, *ACC_TOL, what=f"conv {kind}, 128x512 tiles")
+    again = vaep.step_conv(*args, (0, H // 2, H), causal=video, residual=res)
+    assert torch.equal(again, got)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_conv1x1_step(gpu_lib, dtype):
     x = seeded((2, 192, 7, 45), 21, dtype=dtype)
