@@ -30,11 +30,15 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
+# Per-file flags.  conv_wide.hip: without machine sinking -- the backend otherwise moves
+# the sub-pixel conv's fp8 matrix products past the load-issue blocks that follow them,
+# keeping every operand fragment of a step live, and the 8-wave kernel spills.
+FILE_FLAGS = {"conv_wide.hip": ["-mllvm", "-disable-machine-sink"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + FLAGS + FILE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile of {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -184,6 +184,7 @@ struct ConvW {
   void* w = nullptr;
   float* b = nullptr;
   void* wsub = nullptr;   // phase-folded weights of a sub-pixel upsample conv (else NULL)
+  int* sub_scale = nullptr;  // its fp8 products' MFMA scale (2 ints, launch_fold_subpixel_weight)
   // The same kernels for a decode on the transposed image (width bands): 3x3 spatial taps
   // transposed.  NULL for convs without spatial taps, which serve both orientations.
   void* wT = nullptr;
@@ -373,10 +374,11 @@ struct Builder {
         const size_t fbytes = (size_t)4 * u.co_pad * 4 * 2 * u.ci_pad * 2;
         u.wsub = carve.take(fbytes);
         u.wsubT = carve.take(fbytes);
+        u.sub_scale = (int*)carve.take(2 * sizeof(int));
         if (!dry) {
           const std::string wn = "up" + std::to_string(i) + ".upsample.weight";
-          ok(launch_fold_subpixel_weight(P(wn), co, co, u.wsub, u.co_pad, st));
-          ok(launch_fold_subpixel_weight(P(wn), co, co, u.wsubT, u.co_pad, st, true));
+          ok(launch_fold_subpixel_weight(P(wn), co, co, u.wsub, u.co_pad, u.sub_scale, st));
+          ok(launch_fold_subpixel_weight(P(wn), co, co, u.wsubT, u.co_pad, u.sub_scale, st, true));
         }
       }
       m.stages.push_back(s);
@@ -465,12 +467,15 @@ struct Exec {
   }
 
   // xk: what the input buffer holds (kXOp: a normalised activation in the operand dtype;
-  // kXF32: an fp32 conv output; kXSplit: bf16 hi/lo parts of an fp32 conv output, 2x the
-  // channels).  A split input with ups runs the sub-pixel form with w.wsub.
+  // kXF32: an fp32 conv output; kXSplit: an fp32 conv output in the sub-pixel operand
+  // encoding, 4 bytes per channel).  A split input with ups runs the sub-pixel form with
+  // w.wsub.
   // gn_next: a GroupNorm reads the output next; the conv may then form its tile statistics.
+  // split8: a kModeBandSplit output is written in the sub-pixel operand encoding (its only
+  // reader is a sub-pixel upsample conv) instead of bf16 hi / lo halves.
   int conv(const ConvW& w, const void* x, const BandLayout& Lin, int xk, void* y,
            const BandLayout& Lout, int mode, const void* res, int ups, int final_frames = 1,
-           bool gn_next = false) {
+           bool gn_next = false, bool split8 = false) {
     if (mode == kModeBand || mode == kModeTimeInterleave) need_act(Lout, 4);
     if (mode == kModeBandSplit) need_act(Lout, 2);
     need_act(Lin, xk == kXOp ? eb() : (xk == kXF32 ? 4 : 2));
@@ -507,6 +512,8 @@ struct Exec {
     a.x_f32 = xk == kXF32 ? 1 : 0;
     a.x_split = xk == kXSplit ? 1 : 0;
     a.sub = sub ? 1 : 0;
+    a.sub_scale = sub ? w.sub_scale : nullptr;
+    a.split8 = split8 && mode == kModeBandSplit ? 1 : 0;
     a.final_frames = final_frames;
     a.out_transposed = transposed && mode == kModeFinal ? 1 : 0;
     a.gn_part = gn_next ? reinterpret_cast<double*>(scratch) : nullptr;
@@ -666,7 +673,7 @@ int resnet(Exec& E, const ResW& r, int& cur, BandLayout& L, bool split_out = fal
   }
   // every resnet output but a split one (read by the upsample conv) feeds a norm next
   if ((rc = E.conv(r.c2, E.act[o[0]], Lh, kXOp, E.act[o[1]], Ly, split_out ? kModeBandSplit : kModeBand, res, 0, 1,
-                   !split_out)))
+                   !split_out, split_out)))
     return rc;
   cur = o[1];
   L = Ly;
@@ -1338,6 +1345,7 @@ int vaep_step_conv(int dtype, int x_dtype, const void* x, int batch, int frames,
   cw.w = cv.take((size_t)co_pad * taps * cin_pad * eb);
   cw.b = (float*)cv.take((size_t)co_pad * sizeof(float));
   if (sub) cw.wsub = cv.take((size_t)4 * co_pad * 4 * 2 * cin_pad * 2);
+  if (sub) cw.sub_scale = (int*)cv.take(2 * sizeof(int));
   bool sized;
   if ((rc = step_finish_sizing(cv, ws, ws_bytes, bytes_out, &sized)) || sized) return rc;
   if (!x || !weight || !y) return fail(VAEP_ERR_INVALID_ARG, "x, weight and y must be device pointers");
@@ -1347,7 +1355,7 @@ int vaep_step_conv(int dtype, int x_dtype, const void* x, int batch, int frames,
   if (e == hipSuccess) e = launch_pack_weight(weight, cout, cin, taps, cw.w, co_pad, cin_pad, dtype, st);
   if (e == hipSuccess) e = launch_to_f32(bias, cout, cw.b, co_pad, dtype, st);
   if (e == hipSuccess && sub) e = launch_split((const float*)xin, Lin, xs, st);
-  if (e == hipSuccess && sub) e = launch_fold_subpixel_weight(weight, cout, cin, cw.wsub, co_pad, st);
+  if (e == hipSuccess && sub) e = launch_fold_subpixel_weight(weight, cout, cin, cw.wsub, co_pad, cw.sub_scale, st);
   if (e != hipSuccess) return hip_fail(e, "step conv staging");
   Exec E;
   E.dtype = dtype;

@@ -18,6 +18,7 @@
 // previous tile feeds the MFMAs).
 #include "vaep_internal.h"
 #include "conv_gn_stats.h"
+#include "split8.h"
 
 namespace vaep {
 
@@ -107,12 +108,36 @@ __device__ __forceinline__ void store_band4(const BandLayout& L, void* y, int b,
   if (r == 0 && b > 0) st4f(y, band_offset(L, b - 1, n, L.rows[b - 1], c) + ch, v);
   if (r == L.rows[b] - 1 && b + 1 < L.nb) st4f(y, band_offset(L, b + 1, n, -1, c) + ch, v);
 }
-// The same as bf16 hi / lo parts in a layout of 2 x `half` channels.
+// 4 channels in the sub-pixel operand encoding (split8.h) of a pixel starting at element
+// `pix` of a layout of 2 x `half` bf16 elements per pixel.
+__device__ __forceinline__ void st4split8(void* base, long long pix, int half, int ch, const float* v) {
+  uint2 p;
+  p.x = (unsigned)f2bf(v[0]) | ((unsigned)f2bf(v[1]) << 16);
+  p.y = (unsigned)f2bf(v[2]) | ((unsigned)f2bf(v[3]) << 16);
+  unsigned short* px = reinterpret_cast<unsigned short*>(base) + pix;
+  *reinterpret_cast<uint2*>(px + ch) = p;
+  unsigned lo, xs;
+  split8::operand_bytes4(v, &lo, &xs);
+  unsigned char* f = reinterpret_cast<unsigned char*>(px) + split8::lo_byte(half, ch);
+  *reinterpret_cast<unsigned*>(f) = lo;
+  *reinterpret_cast<unsigned*>(f + 64) = xs;
+}
+// The same as bf16 hi / lo parts in a layout of 2 x `half` channels, or (s8) in the
+// sub-pixel operand encoding.
 __device__ __forceinline__ void store_split4(const BandLayout& L, void* y, int half, int b, int n, int r,
-                                             int c, int ch, const float* v) {
-  st4split(y, band_offset(L, b, n, r, c) + ch, half, v);
-  if (r == 0 && b > 0) st4split(y, band_offset(L, b - 1, n, L.rows[b - 1], c) + ch, half, v);
-  if (r == L.rows[b] - 1 && b + 1 < L.nb) st4split(y, band_offset(L, b + 1, n, -1, c) + ch, half, v);
+                                             int c, int ch, const float* v, bool s8) {
+  const long long o = band_offset(L, b, n, r, c);
+  // a one-row band pushes its row into both neighbours' halos
+  const bool up = r == 0 && b > 0, dn = r == L.rows[b] - 1 && b + 1 < L.nb;
+  if (s8) {
+    st4split8(y, o, half, ch, v);
+    if (up) st4split8(y, band_offset(L, b - 1, n, L.rows[b - 1], c), half, ch, v);
+    if (dn) st4split8(y, band_offset(L, b + 1, n, -1, c), half, ch, v);
+  } else {
+    st4split(y, o + ch, half, v);
+    if (up) st4split(y, band_offset(L, b - 1, n, L.rows[b - 1], c) + ch, half, v);
+    if (dn) st4split(y, band_offset(L, b + 1, n, -1, c) + ch, half, v);
+  }
 }
 
 // bf16 part of an fp32 value: hi = bf16(v); lo = bf16(v - hi).  hi + lo carries 16
@@ -411,7 +436,7 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
         const float v[4] = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
         if (MODE == kModeBand || MODE == kModeBandSplit) {
           if (MODE == kModeBandSplit)
-            store_split4(a.out, a.y, a.cout, band, n, r, c, co, v);
+            store_split4(a.out, a.y, a.cout, band, n, r, c, co, v, a.split8 != 0);
           else
             store_band4(a.out, a.y, band, n, r, c, co, v);
         } else if (MODE == kModeTimeInterleave) {
@@ -546,8 +571,10 @@ hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s) {
     a.gn_part = nullptr;
     return launch_conv_narrow(a, s);
   }
-  // split operands and sub-pixel weights exist only on the wide kernel
+  // split operands and sub-pixel weights exist only on the wide kernel; the fp8 split
+  // output needs 64-channel blocks
   if (a.x_split || a.sub || (a.mode == kModeBandSplit && dtype == VAEP_DTYPE_F32)) return hipErrorInvalidValue;
+  if (a.split8 && (a.mode != kModeBandSplit || a.cout % 64 != 0)) return hipErrorInvalidValue;
   if (dtype != VAEP_DTYPE_F32) {
     // buffer-resource addressing: the rows one tile can read (at most KT frames of a
     // band) and the weights stay below 2 GiB, so the padding offset reads out of range

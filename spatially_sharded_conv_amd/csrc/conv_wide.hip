@@ -24,12 +24,18 @@
 // is exactly a tap outside the source image, so zero padding carries over unchanged.  The
 // summed weights are no longer bf16 values and are applied as bf16 hi + lo parts.
 //
-// The operand of the sub-pixel form is the fp32 residual stream, pre-split into bf16
-// [hi | lo] channel halves (kModeBandSplit output or launch_split); K then runs over
-// three parts per tap: x_hi * w_hi, x_lo * w_hi, x_hi * w_lo (the dropped x_lo * w_lo is
-// below 2^-18 of the product).  Other convs have one part: x * w.
+// The operand of the sub-pixel form is the fp32 residual stream in the encoding of
+// split8.h (kModeBandSplit output with split8 set, or launch_split): bf16 hi parts, then
+// per 64-channel block fp8 bytes of x_lo and of x.  K runs over two parts per tap: x_hi *
+// w_hi as bf16 products, then the correction terms x_lo * w + x * w_lo as one fp8 step of
+// K = 128 per 64 channels (v_mfma_scale_f32_32x32x64_f8f6f4, A e4m3 weights, B e5m2
+// operand, A's E8M0 scale removing the power of two both were stored with).  That fp8
+// step reads LDS exactly like a bf16 step: its 32-byte operands are the fragments of two
+// consecutive 16-wide bf16 slices, taken in the same order for A and B, so every weight
+// byte meets the operand byte of its channel.  Other convs have one part: x * w.
 #include "vaep_internal.h"
 #include "conv_gn_stats.h"
+#include "split8.h"
 
 namespace vaep {
 
@@ -152,8 +158,7 @@ __device__ __forceinline__ void split_epilogue(const ConvArgs& a, const f32x16_t
   for (int j = 0; j < NJ; ++j) {
     const long long p = (long long)tile * BN + wpx + 32 * j + (lane & 31);
     const bool pv = p < m_band;
-    long long o = 0, ho = 0;
-    bool halo = false;
+    long long o = 0, hu = -1, hd = -1;   // own slot; halo slots in the bands above / below
     if (pv) {
       const int n = (int)(p / plane);
       const int rem = (int)(p - (long long)n * plane);
@@ -164,9 +169,9 @@ __device__ __forceinline__ void split_epilogue(const ConvArgs& a, const f32x16_t
         c = 2 * c + px;
       }
       o = band_offset(a.out, band, n, r, c);
-      const bool up = r == 0 && band > 0, dn = r == a.out.rows[band] - 1 && band + 1 < a.out.nb;
-      halo = up || dn;
-      ho = up ? band_offset(a.out, band - 1, n, a.out.rows[band - 1], c) : (dn ? band_offset(a.out, band + 1, n, -1, c) : 0);
+      // a one-row band pushes its row into both neighbours' halos
+      if (r == 0 && band > 0) hu = band_offset(a.out, band - 1, n, a.out.rows[band - 1], c);
+      if (r == a.out.rows[band] - 1 && band + 1 < a.out.nb) hd = band_offset(a.out, band + 1, n, -1, c);
     }
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
@@ -182,6 +187,26 @@ __device__ __forceinline__ void split_epilogue(const ConvArgs& a, const f32x16_t
         }
         const int co = co0 + wco + 32 * i + 8 * (2 * m + hi);
         if (!pv || co >= a.cout) continue;
+        unsigned short* y = reinterpret_cast<unsigned short*>(a.y);
+        if (a.split8) {
+          // bf16 hi parts, then the fp8 bytes of x_lo and x (split8.h)
+          unsigned hw[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hw[e] = (unsigned)f2bf(v[2 * e]) | ((unsigned)f2bf(v[2 * e + 1]) << 16);
+          uint2 lo, xs;
+          split8::operand_bytes4(v, &lo.x, &xs.x);
+          split8::operand_bytes4(v + 4, &lo.y, &xs.y);
+          const long long f = split8::lo_byte(half, co);
+          auto put8 = [&](long long q) {
+            *reinterpret_cast<uint4*>(y + q + co) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            *reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(y + q) + f) = lo;
+            *reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(y + q) + f + 64) = xs;
+          };
+          put8(o);
+          if (hu >= 0) put8(hu);
+          if (hd >= 0) put8(hd);
+          continue;
+        }
         unsigned hw[4], lw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -190,21 +215,30 @@ __device__ __forceinline__ void split_epilogue(const ConvArgs& a, const f32x16_t
           hw[e] = (unsigned)h0 | ((unsigned)h1 << 16);
           lw[e] = (unsigned)l0 | ((unsigned)l1 << 16);
         }
-        unsigned short* y = reinterpret_cast<unsigned short*>(a.y);
-        *reinterpret_cast<uint4*>(y + o + co) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        *reinterpret_cast<uint4*>(y + o + half + co) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        if (halo) {
-          *reinterpret_cast<uint4*>(y + ho + co) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-          *reinterpret_cast<uint4*>(y + ho + half + co) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        }
+        auto put = [&](long long q) {
+          *reinterpret_cast<uint4*>(y + q + co) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+          *reinterpret_cast<uint4*>(y + q + half + co) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        };
+        put(o);
+        if (hu >= 0) put(hu);
+        if (hd >= 0) put(hd);
       }
     }
   }
 }
 
-// Part p of a tap: weight part (0 = w or w_hi, 1 = w_lo) and operand part (0 = x or x_hi, 1 = x_lo).
-__device__ __forceinline__ constexpr int wpart(int parts, int p) { return parts == 3 && p == 2 ? 1 : 0; }
-__device__ __forceinline__ constexpr int xpart(int p) { return p == 1 ? 1 : 0; }
+// Part p of a tap selects the weight and operand halves of its packed rows: 0 = the bf16
+// values (w or w_hi; x or x_hi), 1 = the fp8 correction block of split8.h.
+__device__ __forceinline__ constexpr int wpart(int, int p) { return p; }
+__device__ __forceinline__ constexpr int xpart(int p) { return p; }
+
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+// Two 16-byte fragments as one 32-byte fp8 operand.
+__device__ __forceinline__ i32x8_t cat32(bf16x8_t a, bf16x8_t b) {
+  const i32x4_t x = __builtin_bit_cast(i32x4_t, a), y = __builtin_bit_cast(i32x4_t, b);
+  return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 // Load g (0 .. NL-1) of a step is an A (weight) chunk load for g < NA, else a B (pixel)
 // chunk load; the loads go out in four quarters, quarter q issuing loads QB(q) .. QB(q+1)-1.
@@ -235,7 +269,8 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   // words); the 128 x 512 tile fills the 160 KiB with its two stages and goes without.
   constexpr bool PF = S * (BM + BN) * 64 * 2 + 256 <= 160 * 1024;
   constexpr int TAPS = SUB ? 4 : KT * KS * KS;
-  constexpr int WP = PARTS == 3 ? 2 : 1;      // weight parts per tap in the packed rows
+  static_assert(SUB ? PARTS == 2 : PARTS == 1, "sub-pixel convs run a bf16 and an fp8 part");
+  constexpr int WP = PARTS;                   // weight parts per tap in the packed rows
   constexpr int WPX = NW / 2;                 // waves along the pixels
   constexpr int NA = BM / (8 * NW);           // A (weight) chunk loads per thread per step
   constexpr int NB = BN / (8 * NW);           // B (pixel) chunk loads per thread per step
@@ -366,6 +401,10 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
 
   // acc[i][j][v]: channel co0 + wco + 32i + 8(v/4) + 4(lane/32) + v%4, pixel
   // tile*BN + wpx + 32j + lane%32 (source grid for sub-pixel convs).
+  // fp8 step scales (E8M0 in every byte): A's removes the weights' and the operand's
+  // power-of-two factors; B's is 1
+  const int f8_scale_a = SUB ? *a.sub_scale : 0;
+  constexpr int f8_scale_b = 127 * 0x01010101;
   const int wco = (wave / WPX) * (BM / 2);
   const int wpx = (wave % WPX) * (BN / WPX);
   // The accumulators start at bias + residual (fp32 with `cout` channels in the output's
@@ -464,13 +503,13 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
       _Pragma("unroll") for (int j = 0; j < NB; ++j)                                           \
         bvo[j] = ((pmask[j] & need) == need) ? (unsigned)((int)pbase[j] + delta) : kPadOffset;  \
     }                                                                                          \
-    const int g = LO::at((q), (t));                                                            \
-    if (g < NA) {                                                                              \
-      const int j = g;                                                                         \
+    const int lg_ = LO::at((q), (t));                                                          \
+    if (lg_ < NA) {                                                                            \
+      const int j = lg_;                                                                       \
       const int aso = ((itap * WP + wpart(PARTS, ipart)) * C + ic) * 2;                        \
       dma16(LO::first((q), (t)), wrs, lds_addr(VAEP_SA(st)) + wrow + j * kRowStep, avo[j], aso); \
     } else {                                                                                   \
-      const int j = g - NA;                                                                    \
+      const int j = lg_ - NA;                                                                  \
       const int bso = (xpart(ipart) * C + ic) * 2;                                             \
       dma16(LO::first((q), (t)), xrs, lds_addr(VAEP_SB(st)) + wrow + j * kRowStep, bvo[j], bso); \
     }                                                                                          \
@@ -513,7 +552,7 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   // in issue order; this thread's loads of step s have landed once at most the loads
   // issued after them (the prefetches of that step, if any, and the next step's group
   // when S is 3) are outstanding.  The barrier then publishes every thread's chunks.
-#define VAEP_STEP(cs, ns, si)                                                                    \
+#define VAEP_STEP_K(cs, ns, si, F8)                                                              \
   {                                                                                            \
     if (S == 3 && (si) + 2 <= nsteps)                                                          \
       __builtin_amdgcn_s_waitcnt(((NG + PFN) & 15) | (((NG + PFN) >> 4) << 14) | (7 << 4) | (15 << 8)); \
@@ -523,55 +562,104 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
     const bool more = issued < nsteps;                                                         \
     const unsigned short* A = VAEP_SA(cs);                                                     \
     const unsigned short* B = VAEP_SB(cs);                                                     \
-    /* operand fragments double-buffered across the four 16-wide K slices: the reads of */    \
-    /* slice kk+1 are in flight while slice kk's MFMAs run */                                 \
-    bf16x8_t af[2][MI], bfr[2][NJ];                                                            \
-    _Pragma("unroll") for (int i = 0; i < MI; ++i)                                             \
-      af[0][i] = *reinterpret_cast<const bf16x8_t*>(A + (wco + 32 * i) * 64 + ko[0]);          \
-    _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                             \
-      bfr[0][j] = *reinterpret_cast<const bf16x8_t*>(B + (wpx + 32 * j) * 64 + ko[0]);         \
-    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                         \
-      const int cur = kk & 1;                                                                  \
-      if (kk < 3) {                                                                            \
-        _Pragma("unroll") for (int i = 0; i < MI; ++i)                                         \
-          af[cur ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(A + (wco + 32 * i) * 64 + ko[kk + 1]); \
-        _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                         \
-          bfr[cur ^ 1][j] = *reinterpret_cast<const bf16x8_t*>(B + (wpx + 32 * j) * 64 + ko[kk + 1]); \
-      }                                                                                        \
-      /* the quarter step's loads go out one at a time between groups of MFMAs */             \
-      _Pragma("unroll") for (int i = 0; i < MI; ++i)                                           \
+    if (F8) {                                                                                  \
+      /* fp8 correction step: slices 2g and 2g+1 form the 32-byte operands of group g */      \
+      _Pragma("unroll") for (int grp = 0; grp < 2; ++grp) {                                    \
+        /* one A operand at a time keeps the operand registers at (1 + NJ) x 8; the two */    \
+        /* 16-byte reads land in the halves of the 32-byte operand */                          \
+        const int k0 = ko[2 * grp], k1 = ko[2 * grp + 1];                                      \
+        i32x8_t fb[NJ];                                                                        \
         _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                       \
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0); \
-          const int per = (MI * NJ) / LO::count(kk);                                           \
-          const int idx = i * NJ + j;                                                          \
-          if (idx % per == per - 1 && idx / per < LO::count(kk)) {                             \
-            __builtin_amdgcn_sched_barrier(0);                                                 \
-            if (more) VAEP_ISSUE_ONE(ns, kk, idx / per);                                       \
-            __builtin_amdgcn_sched_barrier(0);                                                 \
+          fb[j].lo = *reinterpret_cast<const i32x4_t*>(B + (wpx + 32 * j) * 64 + k0);          \
+          fb[j].hi = *reinterpret_cast<const i32x4_t*>(B + (wpx + 32 * j) * 64 + k1);          \
+        }                                                                                      \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                       \
+          i32x8_t fa;                                                                          \
+          fa.lo = *reinterpret_cast<const i32x4_t*>(A + (wco + 32 * i) * 64 + k0);             \
+          fa.hi = *reinterpret_cast<const i32x4_t*>(A + (wco + 32 * i) * 64 + k1);             \
+          _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                     \
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                       \
+                fa, fb[j], acc[i][j], 0, 1, 0, f8_scale_a, 0, f8_scale_b);                     \
           }                                                                                    \
         }                                                                                      \
+        /* the group's MFMAs (64 cycles each) run while quarters 2g, 2g+1 issue */            \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        if (more) {                                                                            \
+          VAEP_ISSUE_PART(ns, 2 * grp);                                                        \
+          VAEP_ISSUE_PART(ns, 2 * grp + 1);                                                    \
+        }                                                                                      \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+      }                                                                                        \
+    } else {                                                                                   \
+      /* operand fragments double-buffered across the four 16-wide K slices: the reads of */  \
+      /* slice kk+1 are in flight while slice kk's MFMAs run */                               \
+      bf16x8_t af[2][MI], bfr[2][NJ];                                                          \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i)                                           \
+        af[0][i] = *reinterpret_cast<const bf16x8_t*>(A + (wco + 32 * i) * 64 + ko[0]);        \
+      _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                           \
+        bfr[0][j] = *reinterpret_cast<const bf16x8_t*>(B + (wpx + 32 * j) * 64 + ko[0]);       \
+      _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                       \
+        const int cur = kk & 1;                                                                \
+        if (kk < 3) {                                                                          \
+          _Pragma("unroll") for (int i = 0; i < MI; ++i)                                       \
+            af[cur ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(A + (wco + 32 * i) * 64 + ko[kk + 1]); \
+          _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                       \
+            bfr[cur ^ 1][j] = *reinterpret_cast<const bf16x8_t*>(B + (wpx + 32 * j) * 64 + ko[kk + 1]); \
+        }                                                                                      \
+        /* the quarter step's loads go out one at a time between groups of MFMAs */           \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i)                                         \
+          _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                     \
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0); \
+            const int per = (MI * NJ) / LO::count(kk);                                         \
+            const int idx = i * NJ + j;                                                        \
+            if (idx % per == per - 1 && idx / per < LO::count(kk)) {                           \
+              __builtin_amdgcn_sched_barrier(0);                                               \
+              if (more) VAEP_ISSUE_ONE(ns, kk, idx / per);                                     \
+              __builtin_amdgcn_sched_barrier(0);                                               \
+            }                                                                                  \
+          }                                                                                    \
+      }                                                                                        \
     }                                                                                          \
   }
 
+  // step si of a sub-pixel conv is an fp8 step when its part is 1
+#define VAEP_STEP(cs, ns, si) VAEP_STEP_K(cs, ns, si, SUB && ((si) / TAPS) % PARTS == 1)
   // prologue: steps 0 .. S-2 into stages 0 .. S-2
   VAEP_ISSUE(0);
   if (S == 3 && issued < nsteps) VAEP_ISSUE(1);
-  // whole rounds of S steps, then the remainder (stage numbering restarts at 0)
+  // whole rounds of S steps, then the remainder (stage numbering restarts at 0).  A
+  // two-stage sub-pixel conv runs rounds of 8 steps (4 taps of the bf16 part, then 4 of the
+  // fp8 part) whose kinds are known at compile time: with both kinds behind a run-time
+  // branch in every step the register allocation does not fit 2 waves per SIMD.
   const int nmain = nsteps - nsteps % S;
   int s = 0;
-  for (; s < nmain; s += S) {
-    if (S == 2) {
-      VAEP_STEP(0, 1, s);
-      VAEP_STEP(1, 0, s + 1);
-    } else {
-      VAEP_STEP(0, 2, s);
-      VAEP_STEP(1, 0, s + 1);
-      VAEP_STEP(2, 1, s + 2);
+  if constexpr (SUB && S == 2) {
+    for (; s < nsteps; s += 8) {
+      VAEP_STEP_K(0, 1, s, false);
+      VAEP_STEP_K(1, 0, s + 1, false);
+      VAEP_STEP_K(0, 1, s + 2, false);
+      VAEP_STEP_K(1, 0, s + 3, false);
+      VAEP_STEP_K(0, 1, s + 4, true);
+      VAEP_STEP_K(1, 0, s + 5, true);
+      VAEP_STEP_K(0, 1, s + 6, true);
+      VAEP_STEP_K(1, 0, s + 7, true);
     }
+  } else {
+    for (; s < nmain; s += S) {
+      if (S == 2) {
+        VAEP_STEP(0, 1, s);
+        VAEP_STEP(1, 0, s + 1);
+      } else {
+        VAEP_STEP(0, 2, s);
+        VAEP_STEP(1, 0, s + 1);
+        VAEP_STEP(2, 1, s + 2);
+      }
+    }
+    if (s < nsteps) VAEP_STEP(0, S - 1, s);
+    if (S == 3 && s + 1 < nsteps) VAEP_STEP(1, 0, s + 1);
   }
-  if (s < nsteps) VAEP_STEP(0, S - 1, s);
-  if (S == 3 && s + 1 < nsteps) VAEP_STEP(1, 0, s + 1);
 #undef VAEP_STEP
+#undef VAEP_STEP_K
 #undef VAEP_SA
 #undef VAEP_SB
 #undef VAEP_TAP_GEO
@@ -657,9 +745,10 @@ hipError_t go_mode(const ConvArgs& a, WideTile t, hipStream_t s) {
 }  // namespace
 
 // Workgroup tile (output channels x pixels) of the wide kernel: 256 x 256 when a layer
-// still fills the 256 CUs with two workgroups each; else, for plain convs, 128 x 512 with
-// 8 waves when that does; else 128 x 256 with 4 waves.  Decided on the whole image, so
-// every band table of an image runs the same kernel.
+// still fills the 256 CUs with two workgroups each (sub-pixel convs count their four
+// phases); else, for plain convs, 128 x 512 with 8 waves when that does; else 128 x 256
+// with 4 waves.  Decided on the whole image, so every band table of an image runs the same
+// kernel.
 WideTile wide_tile(const ConvArgs& a) {
   const int ph = a.sub ? 4 : 1;
   const long long px = (long long)a.in.n_img * a.in.H * a.in.W;
@@ -683,8 +772,11 @@ bool conv_wide_fits(const ConvArgs& a) {
 hipError_t launch_conv_wide(ConvArgs& a, hipStream_t s) {
   a.gn_chunk = 0;
   if (a.cin % 64 != 0 || a.cout_pad % 128 != 0) return hipErrorInvalidValue;
-  // split operands feed the sub-pixel form only
-  if (a.sub != a.x_split || (a.sub && (a.kt != 1 || a.ks != 3))) return hipErrorInvalidValue;
+  // split operands feed the sub-pixel form only, whose fp8 part needs 64-channel blocks and
+  // its scale; the fp8 split output likewise needs 64-channel blocks
+  if (a.sub != a.x_split || (a.sub && (a.kt != 1 || a.ks != 3 || a.cin % 64 != 0 || !a.sub_scale)))
+    return hipErrorInvalidValue;
+  if (a.split8 && (a.mode != kModeBandSplit || a.cout % 64 != 0)) return hipErrorInvalidValue;
   if (a.in.C != (a.x_split ? 2 * a.cin : a.cin)) return hipErrorInvalidValue;
   const WideTile wt = wide_tile(a);
   const int bn = wt.bn;
@@ -716,7 +808,7 @@ hipError_t launch_conv_wide(ConvArgs& a, hipStream_t s) {
       bm % (a.cout / a.gn_groups) == 0)
     a.gn_chunk = bn;
   if (!a.gn_chunk) a.gn_part = nullptr;
-  if (a.sub) return go_mode<1, 3, true, 3>(a, wt, s);
+  if (a.sub) return go_mode<1, 3, true, 2>(a, wt, s);
   if (a.kt == 1 && a.ks == 3) return go_mode<1, 3, false, 1>(a, wt, s);
   if (a.kt == 1 && a.ks == 1) return go_mode<1, 1, false, 1>(a, wt, s);
   if (a.kt == 3 && a.ks == 3) return go_mode<3, 3, false, 1>(a, wt, s);

@@ -2,6 +2,7 @@
 // neighbours' boundary rows in the halo slots), gather bands back, the first frame of
 // the causal temporal upsample, and weight repacking.
 #include "vaep_internal.h"
+#include "split8.h"
 
 namespace vaep {
 namespace {
@@ -86,7 +87,29 @@ __global__ void pack_weight_kernel(const T* src, int co, int ci, int taps, T* ds
 // dy reads source row offset floor((py + dy - 1) / 2), which is -1, 0, 0 for py = 0 and
 // 0, 0, 1 for py = 1; folded row tap a of phase py sums the kernel rows whose offset is
 // a - 1 + py (columns likewise).  The fp32 sum is stored as bf16 hi and lo parts.
-__global__ void fold_subpixel_kernel(const bf16* src, int co, int ci, bf16* dst, int co_pad, int tr) {
+// Largest |w| of n bf16 weights (one workgroup of 256) -> scale[1] (float bits).
+__global__ void __launch_bounds__(256) absmax_kernel(const bf16* src, long long n, int* scale) {
+  __shared__ float part[256];
+  float m = 0.f;
+  for (long long i = threadIdx.x; i < n; i += 256) m = fmaxf(m, fabsf((float)src[i]));
+  part[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) part[threadIdx.x] = fmaxf(part[threadIdx.x], part[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) scale[1] = __float_as_int(part[0]);
+}
+
+// Folded weights in the encoding of split8.h.  A folded weight sums at most four
+// weights, so 4 max |w| bounds it; s follows from that bound.  Thread 0 stores the MFMA
+// scale of A, E8M0 of 2^-(s+9) in every byte, at scale[0].
+__global__ void fold_subpixel_kernel(const bf16* src, int co, int ci, unsigned char* dst, int co_pad, int tr,
+                                     int* scale) {
+  const int sh = split8::weight_shift(4.f * __int_as_float(scale[1]));
+  const float up = ldexpf(1.f, sh), up_lo = ldexpf(1.f, sh + split8::kLoShift);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && !tr)
+    scale[0] = (127 - sh - split8::kLoShift) * 0x01010101;
   const long long total = 4LL * co_pad * 4 * ci;
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (long long)gridDim.x * blockDim.x) {
@@ -106,23 +129,36 @@ __global__ void fold_subpixel_kernel(const bf16* src, int co, int ci, bf16* dst,
       }
     }
     const bf16 hi = bf16(w);
-    const bf16 lo = bf16(w - (float)hi);
-    bf16* d = dst + ((((long long)ph * co_pad + o) * 4 + tap) * 2) * ci + c;
-    d[0] = hi;
-    d[ci] = lo;
+    // row of this (phase, output channel, tap): ci bf16 hi parts, then 2 ci fp8 bytes
+    unsigned char* d = dst + ((((long long)ph * co_pad + o) * 4 + tap) * 4LL) * ci;
+    *reinterpret_cast<bf16*>(d + 2LL * c) = hi;
+    const long long f = split8::lo_byte(ci, c);
+    d[f] = (unsigned char)split8::to_e4m3(w * up);
+    d[f + 64] = (unsigned char)split8::to_e4m3((w - (float)hi) * up_lo);
   }
 }
 
-// fp32 element -> bf16 hi at channel ch, lo at channel C + ch of a 2C-channel buffer.
-__global__ void split_kernel(const float* src, long long n, int C, bf16* dst) {
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+// fp32 pixel of C channels -> the operand encoding of split8.h (4C bytes), four channels
+// per thread.
+__global__ void split_kernel(const float* src, long long n4, int C, unsigned char* dst) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
        i += (long long)gridDim.x * blockDim.x) {
-    const float v = src[i];
-    const long long pix = i / C;
-    const int ch = (int)(i - pix * C);
-    const bf16 hi = bf16(v);
-    dst[pix * 2 * C + ch] = hi;
-    dst[pix * 2 * C + C + ch] = bf16(v - (float)hi);
+    const float4 f = reinterpret_cast<const float4*>(src)[i];
+    const float v[4] = {f.x, f.y, f.z, f.w};
+    const long long pix = (4 * i) / C;
+    const int ch = (int)(4 * i - pix * C);
+    unsigned char* d = dst + pix * 4LL * C;
+    uint2 h;
+    h.x = (unsigned)__bfloat16_as_ushort(__float2bfloat16(v[0])) |
+          ((unsigned)__bfloat16_as_ushort(__float2bfloat16(v[1])) << 16);
+    h.y = (unsigned)__bfloat16_as_ushort(__float2bfloat16(v[2])) |
+          ((unsigned)__bfloat16_as_ushort(__float2bfloat16(v[3])) << 16);
+    *reinterpret_cast<uint2*>(d + 2LL * ch) = h;
+    unsigned lo, xs;
+    split8::operand_bytes4(v, &lo, &xs);
+    const long long fb = split8::lo_byte(C, ch);
+    *reinterpret_cast<unsigned*>(d + fb) = lo;
+    *reinterpret_cast<unsigned*>(d + fb + 64) = xs;
   }
 }
 
@@ -288,18 +324,25 @@ hipError_t launch_pack_weight(const void* src, int co, int ci, int taps, void* d
   return hipGetLastError();
 }
 
-hipError_t launch_fold_subpixel_weight(const void* src, int co, int ci, void* dst, int co_pad,
+hipError_t launch_fold_subpixel_weight(const void* src, int co, int ci, void* dst, int co_pad, int* scale,
                                        hipStream_t s, bool transposed) {
+  if (ci % 64 != 0) return hipErrorInvalidValue;
+  if (!transposed) {
+    hipLaunchKernelGGL(absmax_kernel, dim3(1), dim3(256), 0, s, (const bf16*)src, 9LL * co * ci, scale);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const long long total = 4LL * co_pad * 4 * ci;
   hipLaunchKernelGGL(fold_subpixel_kernel, dim3(grid_for(total)), dim3(256), 0, s, (const bf16*)src, co, ci,
-                     (bf16*)dst, co_pad, transposed ? 1 : 0);
+                     (unsigned char*)dst, co_pad, transposed ? 1 : 0, scale);
   return hipGetLastError();
 }
 
 hipError_t launch_split(const float* src, const BandLayout& L, void* dst, hipStream_t s) {
+  if (L.C % 64 != 0) return hipErrorInvalidValue;
   const long long n = layout_elems(L);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(split_kernel, dim3(grid_for(n)), dim3(256), 0, s, src, n, L.C, (bf16*)dst);
+  hipLaunchKernelGGL(split_kernel, dim3(grid_for(n / 4)), dim3(256), 0, s, src, n / 4, L.C, (unsigned char*)dst);
   return hipGetLastError();
 }
 

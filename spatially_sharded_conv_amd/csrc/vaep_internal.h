@@ -77,6 +77,9 @@ struct ConvArgs {
                         // stride in.C = 2 * cin (written by a kModeBandSplit conv)
   int sub;              // nearest-2x + 3x3 conv in sub-pixel form: w holds the phase-folded
                         // weights of launch_fold_subpixel_weight; needs x_split
+  const int* sub_scale; // sub: the fp8 products' MFMA scale (launch_fold_subpixel_weight)
+  int split8;           // kModeBandSplit output in the sub-pixel operand encoding (split8.h)
+                        // instead of bf16 [hi | lo]
   int final_frames;     // kModeFinal: frames per sample of the output tensor
   int out_transposed;   // kModeFinal: the bands cut the output's columns -- band-layout row g,
                         // column c is output pixel (row c, column g) of an in.W x in.H image
@@ -114,11 +117,15 @@ hipError_t launch_conv_wide(ConvArgs& a, hipStream_t s);
 bool conv_narrow_fits(const ConvArgs& a);
 hipError_t launch_conv_narrow(ConvArgs& a, hipStream_t s);
 // Phase-folded weights of a nearest-2x + 3x3 conv: src [co][ci][3][3] bf16 ->
-// dst [4 phases][co_pad][4 taps][2 parts (hi, lo)][ci] bf16; zero rows past co.
-// transposed: fold the transposed 3x3 kernel (for decodes on the transposed image).
-hipError_t launch_fold_subpixel_weight(const void* src, int co, int ci, void* dst, int co_pad,
+// dst [4 phases][co_pad][4 taps][4 ci bytes in the weight encoding of split8.h]; zero rows
+// past co; ci a multiple of 64.  scale: 2 ints of device memory: the untransposed fold
+// stores the largest |w| at scale[1] and the MFMA scale of the fp8 products at scale[0]
+// (run it first).  transposed: fold the transposed 3x3 kernel (decodes on the
+// transposed image).
+hipError_t launch_fold_subpixel_weight(const void* src, int co, int ci, void* dst, int co_pad, int* scale,
                                        hipStream_t s, bool transposed = false);
-// fp32 band buffer (channels c) -> bf16 [hi | lo] band buffer (channels 2c), halo rows included.
+// fp32 band buffer (channels C, a multiple of 64) -> the sub-pixel operand encoding of
+// split8.h (4C bytes per pixel, C bf16 elements of channel stride 2C), halo rows included.
 hipError_t launch_split(const float* src, const BandLayout& L, void* dst, hipStream_t s);
 
 // ------------------------------------------------------------------ norms
