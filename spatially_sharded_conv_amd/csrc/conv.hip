@@ -122,23 +122,6 @@ __device__ __forceinline__ void st4split8(void* base, long long pix, int half, i
   *reinterpret_cast<unsigned*>(f) = lo;
   *reinterpret_cast<unsigned*>(f + 64) = xs;
 }
-// The same as bf16 hi / lo parts in a layout of 2 x `half` channels, or (s8) in the
-// sub-pixel operand encoding.
-__device__ __forceinline__ void store_split4(const BandLayout& L, void* y, int half, int b, int n, int r,
-                                             int c, int ch, const float* v, bool s8) {
-  const long long o = band_offset(L, b, n, r, c);
-  // a one-row band pushes its row into both neighbours' halos
-  const bool up = r == 0 && b > 0, dn = r == L.rows[b] - 1 && b + 1 < L.nb;
-  if (s8) {
-    st4split8(y, o, half, ch, v);
-    if (up) st4split8(y, band_offset(L, b - 1, n, L.rows[b - 1], c), half, ch, v);
-    if (dn) st4split8(y, band_offset(L, b + 1, n, -1, c), half, ch, v);
-  } else {
-    st4split(y, o + ch, half, v);
-    if (up) st4split(y, band_offset(L, b - 1, n, L.rows[b - 1], c) + ch, half, v);
-    if (dn) st4split(y, band_offset(L, b + 1, n, -1, c) + ch, half, v);
-  }
-}
 
 // bf16 part of an fp32 value: hi = bf16(v); lo = bf16(v - hi).  hi + lo carries 16
 // significand bits, so a product pass over each part recovers the fp32 operand to
@@ -427,6 +410,20 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
     const int rem = (int)(p - (long long)n * plane);
     const int r = rem / wc;
     const int c = rem - r * wc;
+    // band modes: this pixel's own slot and its halo slots in the neighbours (boundary
+    // rows; a one-row band has both), formed once per pixel block -- formed per store, the
+    // band fields are re-read from the kernel arguments with a scalar-load wait each time
+    long long own = 0, hu = -1, hd = -1;
+    if (MODE == kModeBand || MODE == kModeBandSplit) {
+      const BandLayout& L = a.out;
+      const long long OC = L.C;
+      const int rows_b = L.rows[band];
+      own = L.off[band] + (((long long)n * (rows_b + 2) + r + 1) * L.W + c) * OC;
+      if (band > 0 && r == 0)
+        hu = L.off[band - 1] + (((long long)n * (L.rows[band - 1] + 2) + L.rows[band - 1] + 1) * L.W + c) * OC;
+      if (band + 1 < L.nb && r == rows_b - 1)
+        hd = L.off[band + 1] + ((long long)n * (L.rows[band + 1] + 2) * L.W + c) * OC;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -434,11 +431,20 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
         const int co = co0 + wco + 32 * i + 8 * g + 4 * (lane >> 5);
         if (co >= a.cout) continue;
         const float v[4] = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-        if (MODE == kModeBand || MODE == kModeBandSplit) {
-          if (MODE == kModeBandSplit)
-            store_split4(a.out, a.y, a.cout, band, n, r, c, co, v, a.split8 != 0);
-          else
-            store_band4(a.out, a.y, band, n, r, c, co, v);
+        if (MODE == kModeBandSplit) {
+          auto put = [&](long long q) {
+            if (a.split8)
+              st4split8(a.y, q, a.cout, co, v);
+            else
+              st4split(a.y, q + co, a.cout, v);
+          };
+          put(own);
+          if (hu >= 0) put(hu);
+          if (hd >= 0) put(hd);
+        } else if (MODE == kModeBand) {
+          st4f(a.y, own + co, v);
+          if (hu >= 0) st4f(a.y, hu + co, v);
+          if (hd >= 0) st4f(a.y, hd + co, v);
         } else if (MODE == kModeTimeInterleave) {
           const int T = a.in.frames;
           const int t = n % T;

@@ -112,39 +112,6 @@ __device__ __forceinline__ unsigned short f2bf(float v) {
 }
 __device__ __forceinline__ float bf2f(unsigned short u) { return __uint_as_float(((unsigned)u) << 16); }
 
-__device__ __forceinline__ void st4f(void* base, long long off, const float* v) {
-  *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + off) = make_float4(v[0], v[1], v[2], v[3]);
-}
-// 4 channels as bf16 hi parts at `off` and lo parts at `off + half`.
-__device__ __forceinline__ void st4split(void* base, long long off, int half, const float* v) {
-  unsigned short h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    h[e] = f2bf(v[e]);
-    l[e] = f2bf(v[e] - bf2f(h[e]));
-  }
-  unsigned short* p = reinterpret_cast<unsigned short*>(base) + off;
-  *reinterpret_cast<uint2*>(p) = make_uint2((unsigned)h[0] | ((unsigned)h[1] << 16), (unsigned)h[2] | ((unsigned)h[3] << 16));
-  *reinterpret_cast<uint2*>(p + half) = make_uint2((unsigned)l[0] | ((unsigned)l[1] << 16), (unsigned)l[2] | ((unsigned)l[3] << 16));
-}
-
-// Store 4 channels of pixel (b, n, r, c) and push boundary rows into the neighbours' halos.
-template <int MODE>
-__device__ __forceinline__ void store4(const BandLayout& L, void* y, int half, int b, int n, int r, int c,
-                                       int ch, const float* v) {
-  const long long o = band_offset(L, b, n, r, c) + ch;
-  const bool up = r == 0 && b > 0, dn = r == L.rows[b] - 1 && b + 1 < L.nb;
-  if (MODE == kModeBandSplit) {
-    st4split(y, o, half, v);
-    if (up) st4split(y, band_offset(L, b - 1, n, L.rows[b - 1], c) + ch, half, v);
-    if (dn) st4split(y, band_offset(L, b + 1, n, -1, c) + ch, half, v);
-  } else {
-    st4f(y, o, v);
-    if (up) st4f(y, band_offset(L, b - 1, n, L.rows[b - 1], c) + ch, v);
-    if (dn) st4f(y, band_offset(L, b + 1, n, -1, c) + ch, v);
-  }
-}
-
 // Split-output epilogue (acc holds the final values).  Lanes l and l+32 hold alternate
 // 4-channel groups of one pixel; v_permlane32_swap pairs them up so that each lane owns 8
 // consecutive channels and stores their hi and lo parts as one 16-byte store each.
@@ -694,26 +661,46 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
     split_epilogue<SUB, MI, NJ, BN>(a, acc, band, tile, plane, m_band, W, py, px, co0, wco, wpx, lane);
     return;
   }
+  // Each pixel's own slot and its halo slots in the neighbours (boundary rows; a one-row
+  // band has both) are formed once per pixel block: formed per store, the band fields are
+  // re-read from the kernel arguments with a scalar-load wait before every store.
+  {
+    const BandLayout& L = a.out;
+    const long long off_b = L.off[band];
+    const int rows_b = L.rows[band];
+    const bool has_u = band > 0, has_d = band + 1 < L.nb;
+    const long long off_u = has_u ? L.off[band - 1] : 0, off_d = has_d ? L.off[band + 1] : 0;
+    const int rows_u = has_u ? L.rows[band - 1] : 0;
+    const int OW = L.W;
+    const long long OC = L.C;
+    float* y = reinterpret_cast<float*>(a.y);
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const long long p = (long long)tile * BN + wpx + 32 * j + (lane & 31);
-    if (p >= m_band) continue;
-    const int n = (int)(p / plane);
-    const int rem = (int)(p - (long long)n * plane);
-    int r = rem / W;
-    int c = rem - r * W;
-    if (SUB) {
-      r = 2 * r + py;
-      c = 2 * c + px;
-    }
+    for (int j = 0; j < NJ; ++j) {
+      const long long p = (long long)tile * BN + wpx + 32 * j + (lane & 31);
+      if (p >= m_band) continue;
+      const int n = (int)(p / plane);
+      const int rem = (int)(p - (long long)n * plane);
+      int r = rem / W;
+      int c = rem - r * W;
+      if (SUB) {
+        r = 2 * r + py;
+        c = 2 * c + px;
+      }
+      const long long own = off_b + (((long long)n * (rows_b + 2) + r + 1) * OW + c) * OC;
+      const long long hu = (has_u && r == 0) ? off_u + (((long long)n * (rows_u + 2) + rows_u + 1) * OW + c) * OC : -1;
+      const long long hd = (has_d && r == rows_b - 1) ? off_d + ((long long)n * (L.rows[band + 1] + 2) * OW + c) * OC : -1;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
+      for (int i = 0; i < MI; ++i) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int co = co0 + wco + 32 * i + 8 * g + 4 * (lane >> 5);
-        if (co >= a.cout) continue;
-        const float v[4] = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-        store4<MODE>(a.out, a.y, half, band, n, r, c, co, v);
+        for (int g = 0; g < 4; ++g) {
+          const int co = co0 + wco + 32 * i + 8 * g + 4 * (lane >> 5);
+          if (co >= a.cout) continue;
+          const float4 v = make_float4(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                       acc[i][j][4 * g + 3]);
+          *reinterpret_cast<float4*>(y + own + co) = v;
+          if (hu >= 0) *reinterpret_cast<float4*>(y + hu + co) = v;
+          if (hd >= 0) *reinterpret_cast<float4*>(y + hd + co) = v;
+        }
       }
     }
   }
