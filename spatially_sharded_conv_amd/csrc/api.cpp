@@ -191,6 +191,9 @@ struct ConvW {
   void* wsubT = nullptr;
   int co = 0, ci = 0, co_pad = 0, ci_pad = 0, kt = 1, ks = 3;
   int rep = 1;            // 2: input channels repeated for an operand stored as hi / lo halves
+  int kext = 0;           // K of a folded 1x1 conv on a second operand: its weights follow the
+                          // taps' in every packed row (see ConvArgs::x2)
+  int kext_ci = 0;        // that conv's true input channels (kext counts the hi / lo halves)
 };
 struct NormW {
   float* g = nullptr;
@@ -200,6 +203,9 @@ struct NormW {
 struct ResW {
   NormW n1, n2;
   ConvW c1, c2, sc;
+  // conv2 with the shortcut folded in (split input, bf16): K = conv2's taps, then the
+  // shortcut's 2 x ci channels of the block input; bias = conv2's + the shortcut's
+  ConvW c2x;
   bool has_sc = false;
   bool split_in = false;  // the block input arrives as bf16 hi / lo halves (norm1 and shortcut)
 };
@@ -317,7 +323,28 @@ struct Builder {
     r.has_sc = ci != co;
     r.split_in = split_in && r.has_sc;
     if (r.has_sc) r.sc = conv(p + ".shortcut", co, ci, 1, 1, 0, r.split_in ? 2 : 1);
+    if (r.split_in && dtype == VAEP_DTYPE_BF16 && r.sc.ci_pad % 64 == 0) r.c2x = folded(r.c2, r.sc);
     return r;
+  }
+  // conv2 with a 1x1 conv on a second operand appended to its K (packed rows side by side)
+  ConvW folded(const ConvW& c2, const ConvW& sc) {
+    ConvW x = c2;
+    x.kext = sc.ci_pad;
+    x.kext_ci = sc.ci;
+    const size_t row = (size_t)c2.kt * c2.ks * c2.ks * c2.ci_pad * 2, row2 = row + (size_t)x.kext * 2;
+    x.w = carve.take(c2.co_pad * row2);
+    x.wT = carve.take(c2.co_pad * row2);
+    x.b = (float*)carve.take((size_t)c2.co_pad * sizeof(float));
+    if (!dry) {
+      for (void* dst : {x.w, x.wT}) {
+        const void* src = dst == x.w ? c2.w : c2.wT;
+        ok(hipMemcpy2DAsync(dst, row2, src, row, row, c2.co_pad, hipMemcpyDeviceToDevice, st));
+        ok(hipMemcpy2DAsync((char*)dst + row, row2, sc.w, (size_t)x.kext * 2, (size_t)x.kext * 2, c2.co_pad,
+                            hipMemcpyDeviceToDevice, st));
+      }
+      ok(launch_add_f32(c2.b, sc.b, x.b, c2.co_pad, st));
+    }
+    return x;
   }
   AttnW attention(int ch) {
     AttnW a;
@@ -473,9 +500,12 @@ struct Exec {
   // gn_next: a GroupNorm reads the output next; the conv may then form its tile statistics.
   // split8: a kModeBandSplit output is written in the sub-pixel operand encoding (its only
   // reader is a sub-pixel upsample conv) instead of bf16 hi / lo halves.
+  // x2: the second operand of a conv with a folded 1x1 part (w.kext > 0): bf16, w.kext
+  // channels per pixel in Lin's band geometry.
   int conv(const ConvW& w, const void* x, const BandLayout& Lin, int xk, void* y,
            const BandLayout& Lout, int mode, const void* res, int ups, int final_frames = 1,
-           bool gn_next = false, bool split8 = false) {
+           bool gn_next = false, bool split8 = false, const void* x2 = nullptr) {
+    if (w.kext > 0) need_act(reshaped(Lin, w.kext, Lin.n_img, Lin.frames), 2);
     if (mode == kModeBand || mode == kModeTimeInterleave) need_act(Lout, 4);
     if (mode == kModeBandSplit) need_act(Lout, 2);
     need_act(Lin, xk == kXOp ? eb() : (xk == kXF32 ? 4 : 2));
@@ -514,6 +544,9 @@ struct Exec {
     a.sub = sub ? 1 : 0;
     a.sub_scale = sub ? w.sub_scale : nullptr;
     a.split8 = split8 && mode == kModeBandSplit ? 1 : 0;
+    if ((w.kext > 0) != (x2 != nullptr)) return fail(VAEP_ERR_INVALID_ARG, "internal: folded conv operand mismatch");
+    a.x2 = x2;
+    a.cin2 = w.kext;
     a.final_frames = final_frames;
     a.out_transposed = transposed && mode == kModeFinal ? 1 : 0;
     a.gn_part = gn_next ? reinterpret_cast<double*>(scratch) : nullptr;
@@ -523,7 +556,7 @@ struct Exec {
     {
       vaep_profile_entry pe = entry(VAEP_STEP_CONV, 1);
       const long long m = (long long)Lin.n_img * Lin.H * Lin.W * (ups ? 4 : 1);
-      const long long k = (long long)w.kt * w.ks * w.ks * w.ci;
+      const long long k = (long long)w.kt * w.ks * w.ks * w.ci + w.kext_ci;
       pe.kt = w.kt;
       pe.ks = w.ks;
       pe.cin = w.ci;
@@ -654,6 +687,28 @@ void others(int cur, int* o) {
 // split_out: store the block output as bf16 hi/lo parts (layout with 2x the channels)
 // for a following split-input conv, instead of fp32.
 // If r.split_in, L arrives as the hi / lo layout (2 x the block's input channels).
+// Whether conv2 of a resnet runs with its shortcut folded in: the folded weights exist
+// (split input, bf16) and conv2 runs on the wide kernel, which alone reads a second operand.
+bool shortcut_folds(const ResW& r, const BandLayout& Lh, bool split_out) {
+  if (!r.c2x.w || split_out) return false;
+  ConvArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.in = Lh;
+  a.cin = r.c2x.ci_pad;
+  a.cout = r.c2x.co;
+  a.cout_pad = r.c2x.co_pad;
+  a.kt = r.c2x.kt;
+  a.ks = r.c2x.ks;
+  a.mode = kModeBand;
+  if (!conv_wide_fits(a)) return false;
+  // the second operand's rows one tile reads stay within a buffer resource (2 GiB)
+  const long long bn = wide_tile(a).bn;
+  for (int b = 0; b < Lh.nb; ++b)
+    if ((long long)a.kt * (Lh.rows[b] + 2) * Lh.W * r.c2x.kext * 2 + 2 * bn * r.c2x.kext * 2 >= (1LL << 31) - 4096)
+      return false;
+  return true;
+}
+
 int resnet(Exec& E, const ResW& r, int& cur, BandLayout& L, bool split_out = false) {
   int o[3];
   others(cur, o);
@@ -664,6 +719,16 @@ int resnet(Exec& E, const ResW& r, int& cur, BandLayout& L, bool split_out = fal
   if ((rc = E.norm(r.n1, E.act[cur], Lx, E.act[o[0]], 1, nullptr, r.split_in))) return rc;
   if ((rc = E.conv(r.c1, E.act[o[0]], Lx, kXOp, E.act[o[1]], Lh, kModeBand, nullptr, 0, 1, true))) return rc;
   if ((rc = E.norm(r.n2, E.act[o[1]], Lh, E.act[o[0]], 1))) return rc;
+  if (shortcut_folds(r, Lh, split_out)) {
+    // conv2 + shortcut in one conv: K runs over conv2's taps, then the block input's
+    // hi / lo channels at the pixel itself; no residual pass
+    if ((rc = E.conv(r.c2x, E.act[o[0]], Lh, kXOp, E.act[o[1]], Ly, kModeBand, nullptr, 0, 1, true, false,
+                     E.act[cur])))
+      return rc;
+    cur = o[1];
+    L = Ly;
+    return VAEP_OK;
+  }
   const void* res = E.act[cur];
   if (r.has_sc) {
     // a split input is a bf16 operand over both halves (weights repeated)

@@ -581,6 +581,7 @@ hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s) {
   // output needs 64-channel blocks
   if (a.x_split || a.sub || (a.mode == kModeBandSplit && dtype == VAEP_DTYPE_F32)) return hipErrorInvalidValue;
   if (a.split8 && (a.mode != kModeBandSplit || a.cout % 64 != 0)) return hipErrorInvalidValue;
+  if (a.x2 || a.cin2) return hipErrorInvalidValue;   // a folded second operand needs the wide kernel
   if (dtype != VAEP_DTYPE_F32) {
     // buffer-resource addressing: the rows one tile can read (at most KT frames of a
     // band) and the weights stay below 2 GiB, so the padding offset reads out of range

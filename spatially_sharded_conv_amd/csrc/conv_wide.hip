@@ -277,8 +277,12 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   const int C = a.cin;                                 // input channels
   const int XC = a.in.C;                               // channel stride of the input buffer
   const int csteps = C >> 6;
-  const int nsteps = TAPS * PARTS * csteps;
-  const int kw = TAPS * WP * C;                        // packed weight row length (elements)
+  // K: the taps of the operand, then (a.x2) the channels of a second operand read at the
+  // pixel itself -- a 1x1 conv folded into this one (a resnet's shortcut): its weights
+  // follow the taps' in every packed row
+  const int nsteps1 = TAPS * PARTS * csteps;
+  const int nsteps = nsteps1 + (a.cin2 >> 6);
+  const int kw = TAPS * WP * C + a.cin2;               // packed weight row length (elements)
 
   // Input rows the tile can read: from its first pixel's row - 1 (KT - 1 frames back) to
   // its last pixel's row + 1; halo slots cover the rows beyond the band.
@@ -312,6 +316,13 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   // -(KT-1)+dt not before frame 0).
   unsigned pbase[NB];
   int pmask[NB];
+  // second operand (a.x2): cin2 channels per pixel in the input's band geometry (band
+  // offsets scale with the channel count), over the same rows as the first
+  unsigned pbase2[NB];
+  const u32x4_t x2rs = make_rsrc(
+      a.x2 ? reinterpret_cast<const unsigned short*>(a.x2) + a.in.off[band] / XC * a.cin2 + first_slot * W * a.cin2
+           : nullptr,
+      a.x2 ? (unsigned)((last_slot - first_slot + 1) * W * a.cin2 * 2) : 0u);
   const int H = a.in.H;
   const int g0 = a.in.row0[band];
 #pragma unroll
@@ -325,6 +336,7 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
     const int c = rem - r * W;
     const long long slot = (long long)n * (rows_in + 2) + r + 1;
     pbase[j] = (unsigned)(((slot - first_slot) * W + c) * XC * 2 + ck * 16);
+    pbase2[j] = (unsigned)(((slot - first_slot) * W + c) * a.cin2 * 2 + ck * 16);
     const int g = g0 + r;
     int m = 0;
     m |= (g - 1 >= 0) ? 1 : 0;
@@ -440,7 +452,7 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
     need = (1 << (sy + 1)) | (8 << (sx + 1)) | (64 << dt);                                     \
     delta = (int)((((long long)(dt - (KT - 1)) * (rows_in + 2) + sy) * W + sx) * XC * 2);      \
   }
-  // prefetch cursor: step issued + PFD (held at the last step)
+  // prefetch cursor: step issued + PFD (held at the last step of the taps)
   int ptap = 0, ppart = 0, pc = 0, pstep = 0;
 #define VAEP_ADVANCE(tp, pt, cc)                                                               \
   if (++tp == TAPS) {                                                                          \
@@ -452,7 +464,7 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   }
 #pragma unroll
   for (int i = 0; i < PFD; ++i)
-    if (pstep + 1 < nsteps) {
+    if (pstep + 1 < nsteps1) {
       ++pstep;
       VAEP_ADVANCE(ptap, ppart, pc);
     }
@@ -465,20 +477,26 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
 // prefetch and advances the step counters.
 #define VAEP_ISSUE_ONE(st, q, t)                                                               \
   {                                                                                            \
+    const bool ext_ = !SUB && issued >= nsteps1;   /* a step of the second operand */         \
     if ((q) == 0 && (t) == 0) {                                                                \
-      VAEP_TAP_GEO(itap, need, delta);                                                         \
-      _Pragma("unroll") for (int j = 0; j < NB; ++j)                                           \
-        bvo[j] = ((pmask[j] & need) == need) ? (unsigned)((int)pbase[j] + delta) : kPadOffset;  \
+      if (ext_) {                                                                              \
+        _Pragma("unroll") for (int j = 0; j < NB; ++j) bvo[j] = pmask[j] ? pbase2[j] : kPadOffset; \
+      } else {                                                                                 \
+        VAEP_TAP_GEO(itap, need, delta);                                                       \
+        _Pragma("unroll") for (int j = 0; j < NB; ++j)                                         \
+          bvo[j] = ((pmask[j] & need) == need) ? (unsigned)((int)pbase[j] + delta) : kPadOffset; \
+      }                                                                                        \
     }                                                                                          \
     const int lg_ = LO::at((q), (t));                                                          \
     if (lg_ < NA) {                                                                            \
       const int j = lg_;                                                                       \
-      const int aso = ((itap * WP + wpart(PARTS, ipart)) * C + ic) * 2;                        \
+      const int aso = ext_ ? (TAPS * WP * C + (issued - nsteps1) * 64) * 2                     \
+                           : ((itap * WP + wpart(PARTS, ipart)) * C + ic) * 2;                 \
       dma16(LO::first((q), (t)), wrs, lds_addr(VAEP_SA(st)) + wrow + j * kRowStep, avo[j], aso); \
     } else {                                                                                   \
       const int j = lg_ - NA;                                                                  \
-      const int bso = (xpart(ipart) * C + ic) * 2;                                             \
-      dma16(LO::first((q), (t)), xrs, lds_addr(VAEP_SB(st)) + wrow + j * kRowStep, bvo[j], bso); \
+      const int bso = ext_ ? (issued - nsteps1) * 128 : (xpart(ipart) * C + ic) * 2;           \
+      dma16(LO::first((q), (t)), ext_ ? x2rs : xrs, lds_addr(VAEP_SB(st)) + wrow + j * kRowStep, bvo[j], bso); \
     }                                                                                          \
     if ((q) == 3 && (t) == LO::count(3) - 1) {                                                 \
       if constexpr (PF) {                                                                      \
@@ -489,7 +507,7 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
       }                                                                                        \
       ++issued;                                                                                \
       VAEP_ADVANCE(itap, ipart, ic);                                                           \
-      if (pstep + 1 < nsteps) {                                                                \
+      if (pstep + 1 < nsteps1) {   /* the prefetch covers the taps' steps */                  \
         ++pstep;                                                                               \
         VAEP_ADVANCE(ptap, ppart, pc);                                                         \
       }                                                                                        \
@@ -764,15 +782,23 @@ hipError_t launch_conv_wide(ConvArgs& a, hipStream_t s) {
   if (a.sub != a.x_split || (a.sub && (a.kt != 1 || a.ks != 3 || a.cin % 64 != 0 || !a.sub_scale)))
     return hipErrorInvalidValue;
   if (a.split8 && (a.mode != kModeBandSplit || a.cout % 64 != 0)) return hipErrorInvalidValue;
+  // a second operand: plain band output, 64-channel steps (and, below, the rows one tile
+  // reads below 2 GiB)
+  if (a.x2 && (a.sub || a.mode != kModeBand || a.cin2 <= 0 || a.cin2 % 64 != 0)) return hipErrorInvalidValue;
+  if (!a.x2 && a.cin2 != 0) return hipErrorInvalidValue;
   if (a.in.C != (a.x_split ? 2 * a.cin : a.cin)) return hipErrorInvalidValue;
   const WideTile wt = wide_tile(a);
   const int bn = wt.bn;
+  if (a.x2)
+    for (int b = 0; b < a.in.nb; ++b)
+      if ((long long)a.kt * (a.in.rows[b] + 2) * a.in.W * a.cin2 * 2 + 2LL * bn * a.cin2 * 2 >= (1LL << 31) - 4096)
+        return hipErrorInvalidValue;
   // buffer-resource addressing: the rows one tile reads and the weights stay below 2 GiB
   for (int b = 0; b < a.in.nb; ++b)
     if ((long long)a.kt * (a.in.rows[b] + 2) * a.in.W * a.in.C * 2 + 2LL * bn * a.in.C * 2 >=
         (1LL << 31) - 4096)
       return hipErrorInvalidValue;
-  const long long kw = (long long)a.kt * (a.sub ? 4 * 2 : a.ks * a.ks) * a.cin;
+  const long long kw = (long long)a.kt * (a.sub ? 4 * 2 : a.ks * a.ks) * a.cin + a.cin2;
   if ((long long)a.cout_pad * kw * 2 >= (1LL << 31)) return hipErrorInvalidValue;
   // tiles over the compute pixels (the source grid for sub-pixel convs)
   int t = 0;

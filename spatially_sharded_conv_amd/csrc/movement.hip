@@ -162,6 +162,11 @@ __global__ void split_kernel(const float* src, long long n4, int C, unsigned cha
   }
 }
 
+__global__ void add_f32_kernel(const float* a, const float* b, float* out, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = a[i] + b[i];
+}
+
 template <typename T>
 __global__ void to_f32_kernel(const T* src, int n, float* dst, int n_pad) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -343,6 +348,12 @@ hipError_t launch_split(const float* src, const BandLayout& L, void* dst, hipStr
   const long long n = layout_elems(L);
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(split_kernel, dim3(grid_for(n / 4)), dim3(256), 0, s, src, n / 4, L.C, (unsigned char*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_f32(const float* a, const float* b, float* out, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(add_f32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, a, b, out, n);
   return hipGetLastError();
 }
 

@@ -80,6 +80,10 @@ struct ConvArgs {
   const int* sub_scale; // sub: the fp8 products' MFMA scale (launch_fold_subpixel_weight)
   int split8;           // kModeBandSplit output in the sub-pixel operand encoding (split8.h)
                         // instead of bf16 [hi | lo]
+  const void* x2;       // wide kernel, kModeBand: a second bf16 operand in the input's band
+  int cin2;             // geometry with cin2 channels, read at the output pixel itself (a 1x1
+                        // conv folded in: K grows by cin2, its weights follow the taps' in
+                        // every packed row); NULL / 0 for none
   int final_frames;     // kModeFinal: frames per sample of the output tensor
   int out_transposed;   // kModeFinal: the bands cut the output's columns -- band-layout row g,
                         // column c is output pixel (row c, column g) of an in.W x in.H image
@@ -127,6 +131,8 @@ hipError_t launch_fold_subpixel_weight(const void* src, int co, int ci, void* ds
 // fp32 band buffer (channels C, a multiple of 64) -> the sub-pixel operand encoding of
 // split8.h (4C bytes per pixel, C bf16 elements of channel stride 2C), halo rows included.
 hipError_t launch_split(const float* src, const BandLayout& L, void* dst, hipStream_t s);
+// out[i] = a[i] + b[i], i < n (fp32 device arrays).
+hipError_t launch_add_f32(const float* a, const float* b, float* out, int n, hipStream_t s);
 
 // ------------------------------------------------------------------ norms
 // Local moments per (band, image, group): partial records of tiles, merged per band and
