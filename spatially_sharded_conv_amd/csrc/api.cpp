@@ -645,6 +645,10 @@ struct Exec {
   int attention(const AttnW& w, const void* x, const BandLayout& L, void* a_buf, void* o_buf, void* y) {
     const int c = L.C;
     qkv_bytes = std::max(qkv_bytes, (size_t)L.n_img * L.H * L.W * c * eb());
+    // the key-split attention's halves live in the statistics scratch, which no GroupNorm
+    // holds between the QKV projection and the output projection
+    if (dtype == VAEP_DTYPE_BF16)
+      scratch_bytes = std::max(scratch_bytes, (size_t)attn_part_floats(L.n_img, L.H * L.W, c) * sizeof(float));
     int rc = norm(w.norm, x, L, a_buf, 0);
     if (rc) return rc;
     rc = conv(w.qkv, a_buf, L, kXOp, nullptr, L, kModeQKV, nullptr, 0);
@@ -661,6 +665,7 @@ struct Exec {
       aa.c = c;
       aa.tokens = L.H * L.W;
       aa.scale = 1.0f / std::sqrt((float)c);
+      aa.part = dtype == VAEP_DTYPE_BF16 ? scratch : nullptr;
       vaep_profile_entry pe = entry(VAEP_STEP_ATTENTION, 1);
       const double nq = (double)L.n_img * L.H * L.W, nk = (double)L.H * L.W;
       pe.cin = pe.cout = c;
@@ -1543,7 +1548,10 @@ int vaep_step_attention(int dtype, const void* x, int batch, int frames, int c, 
   void* qb = cv.take(qkv);
   void* kb = cv.take(qkv);
   void* vb = cv.take(qkv);
-  float* scratch = groups > 0 ? (float*)cv.take(gn_partials_floats(L, groups, 1) * sizeof(float)) : nullptr;
+  // statistics records, and the key-split attention's halves (bf16)
+  const long long sc_floats = std::max<long long>(groups > 0 ? (long long)gn_partials_floats(L, groups, 1) : 0,
+                                                  bf ? attn_part_floats(L.n_img, h * w, c) : 0);
+  float* scratch = sc_floats > 0 ? (float*)cv.take((size_t)sc_floats * sizeof(float)) : nullptr;
   AttnW aw;
   aw.norm.g = const_cast<float*>(norm_gamma);
   aw.norm.b = const_cast<float*>(norm_beta);

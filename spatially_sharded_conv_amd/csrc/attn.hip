@@ -200,8 +200,13 @@ __global__ void __launch_bounds__(256) flash_bf16(const AttnArgs a) {
 // in P); otherwise P is formed against the old max (still exact: numerator and
 // denominator use the same max), so the O rescale runs only on the rare tiles that move
 // a max.
+// Split keys (a.part set, d <= 384): workgroup 2i + s takes query block i against the s-th
+// half of the key tiles and writes its unnormalised O, running max and sum (fp32) to
+// a.part; attn_merge combines the halves.  Two workgroups then share each CU, one's
+// barrier and softmax phases overlapping the other's products.  At d = 512 the registers
+// of two workgroups per CU do not hold Q, K, V and O without spilling: one per CU.
 template <int DS>
-__global__ void __launch_bounds__(256, 1) attn_split(const AttnArgs a) {
+__global__ void __launch_bounds__(256, DS <= 96 ? 2 : 1) attn_split(const AttnArgs a) {
   constexpr int D = 4 * DS;
   constexpr int KS = DS / 16;   // 16-channel steps of the S product
   constexpr int CB = DS / 32;   // 32-channel blocks of O^T
@@ -214,8 +219,11 @@ __global__ void __launch_bounds__(256, 1) attn_split(const AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = band_of(a, blockIdx.x);
-  const int local = blockIdx.x - a.tile_start[b];
+  constexpr bool kSplit = DS <= 96;   // the key-split form exists for d <= 384
+  const int nsplit = kSplit && a.part ? 2 : 1;
+  const int blk = blockIdx.x / nsplit, half = blockIdx.x - blk * nsplit;
+  const int b = band_of(a, blk);
+  const int local = blk - a.tile_start[b];
   const int W = a.L.W;
   const int nq = a.L.rows[b] * W;
   const int qt_img = (nq + 63) / 64;
@@ -286,6 +294,9 @@ __global__ void __launch_bounds__(256, 1) attn_split(const AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * 1.4426950408889634f;
   const int ntiles = (tokens + BK - 1) / BK;
+  const int tper = (ntiles + nsplit - 1) / nsplit;
+  const int tbeg = half * tper;
+  const int tend = tbeg + tper < ntiles ? tbeg + tper : ntiles;
 
 #define VAEP_TILE(KF, VF, k0)                                                                  \
   {                                                                                            \
@@ -355,12 +366,33 @@ __global__ void __launch_bounds__(256, 1) attn_split(const AttnArgs a) {
       }                                                                                        \
   }
 
-  VAEP_LOAD_K(kf, 0);
-  for (int t = 0; t < ntiles; ++t) VAEP_TILE(kf, vf, t * BK);
+  VAEP_LOAD_K(kf, tbeg * BK);
+  for (int t = tbeg; t < tend; ++t) VAEP_TILE(kf, vf, t * BK);
 #undef VAEP_TILE
 #undef VAEP_LOAD_K
 #undef VAEP_LOAD_V
 
+  if (kSplit && a.part) {
+    // this half's unnormalised O^T, and (m, l) per query, at the query's global token
+    float* po = a.part + ((long long)(half * a.L.n_img + n) * tokens + tok0) * D;
+    float* pml = a.part + (long long)2 * a.L.n_img * tokens * D + ((long long)(half * a.L.n_img + n) * tokens + tok0) * 2;
+    if ((lane & 3) == 0 && q0 + qs < nq) {
+      pml[(long long)(q0 + qs) * 2] = m_run;
+      pml[(long long)(q0 + qs) * 2 + 1] = l_run;
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int ql = q0 + 32 * qb + l32;
+      if (ql >= nq) continue;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4_t*>(po + (long long)ql * D + c0 + 32 * cb + 8 * g + 4 * hi) =
+              f32x4_t{oacc[cb][qb][4 * g], oacc[cb][qb][4 * g + 1], oacc[cb][qb][4 * g + 2], oacc[cb][qb][4 * g + 3]};
+    }
+    return;
+  }
   if ((lane & 3) == 0) sL[qs] = l_run;
   __syncthreads();
   // O^T block (cb, qb): lane holds query 32qb + lane%32, channels c0 + 32cb + 8g + 4hi + 0..3
@@ -381,6 +413,42 @@ __global__ void __launch_bounds__(256, 1) attn_split(const AttnArgs a) {
         pk.y = (unsigned)f2bf(oacc[cb][qb][4 * g + 2] * inv) | ((unsigned)f2bf(oacc[cb][qb][4 * g + 3] * inv) << 16);
         *reinterpret_cast<uint2*>(out + d) = pk;
       }
+  }
+}
+
+// Combine the two key halves of attn_split: per query, m = max(m0, m1),
+// O = (O0 2^(m0-m) + O1 2^(m1-m)) / (l0 2^(m0-m) + l1 2^(m1-m)), stored as bf16 in the band
+// layout.  One workgroup per 64-query block, 4 channels per thread and step.
+__global__ void __launch_bounds__(256) attn_merge(const AttnArgs a) {
+  const int b = band_of(a, blockIdx.x);
+  const int local = blockIdx.x - a.tile_start[b];
+  const int W = a.L.W, D = a.c, tokens = a.tokens;
+  const int nq = a.L.rows[b] * W;
+  const int qt_img = (nq + 63) / 64;
+  const int n = local / qt_img;
+  const int q0 = (local - n * qt_img) * 64;
+  const long long tok0 = (long long)a.L.row0[b] * W;
+  const int n_img = a.L.n_img;
+  const float* ml = a.part + (long long)2 * n_img * tokens * D;
+  const int per_q = D / 4;                          // float4 steps per query
+  for (int e = threadIdx.x; e < 64 * per_q; e += 256) {
+    const int qi = e / per_q, d = (e - qi * per_q) * 4;
+    const int ql = q0 + qi;
+    if (ql >= nq) break;
+    const long long t0 = (long long)n * tokens + tok0 + ql;               // half 0
+    const long long t1 = (long long)(n_img + n) * tokens + tok0 + ql;     // half 1
+    const float m0 = ml[t0 * 2], l0 = ml[t0 * 2 + 1], m1 = ml[t1 * 2], l1 = ml[t1 * 2 + 1];
+    const float m = fmaxf(m0, m1);
+    const float f0 = l0 > 0.f ? exp2f(m0 - m) : 0.f, f1 = l1 > 0.f ? exp2f(m1 - m) : 0.f;
+    const float inv = 1.f / (l0 * f0 + l1 * f1);
+    const f32x4_t o0 = *reinterpret_cast<const f32x4_t*>(a.part + t0 * D + d);
+    const f32x4_t o1 = *reinterpret_cast<const f32x4_t*>(a.part + t1 * D + d);
+    const int r = ql / W, c = ql - (ql / W) * W;
+    unsigned short* out = reinterpret_cast<unsigned short*>(a.o) + band_offset(a.L, b, n, r, c) + d;
+    uint2 pk;
+    pk.x = (unsigned)f2bf((o0[0] * f0 + o1[0] * f1) * inv) | ((unsigned)f2bf((o0[1] * f0 + o1[1] * f1) * inv) << 16);
+    pk.y = (unsigned)f2bf((o0[2] * f0 + o1[2] * f1) * inv) | ((unsigned)f2bf((o0[3] * f0 + o1[3] * f1) * inv) << 16);
+    *reinterpret_cast<uint2*>(out) = pk;
   }
 }
 
@@ -456,13 +524,22 @@ hipError_t launch_attention(AttnArgs& a, int dtype, hipStream_t s) {
     return hipGetLastError();
   }
   if (split) {
+    // keys in two halves (a.part: the caller's scratch of attn_part_floats) when the query
+    // blocks alone would not give every CU two workgroups and d <= 384 -- decided on the
+    // whole image, so every band table computes the same sums
+    if (a.part && (a.c > 384 || (long long)a.L.n_img * (((long long)a.L.H * a.L.W + 63) / 64) >= 512))
+      a.part = nullptr;
+    const unsigned g = (unsigned)t * (a.part ? 2u : 1u);
     switch (a.c) {
-      case 128: hipLaunchKernelGGL(attn_split<32>, dim3(t), dim3(256), 0, s, a); break;
-      case 256: hipLaunchKernelGGL(attn_split<64>, dim3(t), dim3(256), 0, s, a); break;
-      case 384: hipLaunchKernelGGL(attn_split<96>, dim3(t), dim3(256), 0, s, a); break;
-      case 512: hipLaunchKernelGGL(attn_split<128>, dim3(t), dim3(256), 0, s, a); break;
+      case 128: hipLaunchKernelGGL(attn_split<32>, dim3(g), dim3(256), 0, s, a); break;
+      case 256: hipLaunchKernelGGL(attn_split<64>, dim3(g), dim3(256), 0, s, a); break;
+      case 384: hipLaunchKernelGGL(attn_split<96>, dim3(g), dim3(256), 0, s, a); break;
+      case 512: hipLaunchKernelGGL(attn_split<128>, dim3(g), dim3(256), 0, s, a); break;
       default: return hipErrorInvalidValue;
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.part) return e;
+    hipLaunchKernelGGL(attn_merge, dim3(t), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   switch (a.c) {

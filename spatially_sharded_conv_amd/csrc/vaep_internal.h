@@ -188,7 +188,11 @@ struct AttnArgs {
   float scale;
   int tiles_total;
   int tile_start[kMaxBands + 1];  // query tiles per band (per image)
+  float* part;      // bf16 path: scratch of attn_part_floats() for the key-split form, or
+                    // NULL; the launch clears it where the split does not pay
 };
+// Scratch floats of the key-split attention: two halves of unnormalised O and (max, sum).
+inline long long attn_part_floats(int n_img, int tokens, int c) { return 2LL * n_img * tokens * (c + 2); }
 hipError_t launch_attention(AttnArgs& a, int dtype, hipStream_t s);
 
 // ------------------------------------------------------------------ data movement
