@@ -565,7 +565,8 @@ struct Exec {
       pe.mode = mode;
       pe.pixels = m;
       pe.flops = 2.0 * (double)m * w.co * (double)k;
-      const double in_b = (double)Lin.n_img * Lin.H * Lin.W * w.ci * (xk == kXOp && w.rep == 1 ? eb() : 4.0);
+      const double in_b = (double)Lin.n_img * Lin.H * Lin.W * (w.ci * (xk == kXOp && w.rep == 1 ? eb() : 4.0) +
+                                                               (x2 ? w.kext * 2.0 : 0.0));
       const double out_elem = mode == kModeQKV ? (double)eb() : 4.0;
       pe.bytes = in_b + (double)w.co * k * eb() + (double)m * w.co * out_elem + (res ? (double)m * w.co * 4 : 0.0);
       rec_begin(pe);
