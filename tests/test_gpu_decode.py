@@ -199,6 +199,22 @@ def test_full_size_bands_bit_identical_and_kernels(gpu_lib):
     dec.close()
 
 
+def test_video_band_decode_is_bit_identical_to_full(gpu_lib):
+    # the video decoder's causal convs, RMSNorm, temporal upsample and per-frame attention
+    # (d = 384: two key halves per query block, merged) compute each element identically
+    # on any band table
+    cfg = preset(5).with_size(frames=3, latent_h=9, latent_w=12, band_starts=(0, 9))
+    dec, _ = make_decoder(cfg, affine="random")
+    z = make_latent(cfg)
+    ws = dec.workspace(1, 3, 9, 12, 9)
+    full, rc, _ = gpu_decode(dec, cfg, z, (0, 9), ws)
+    assert rc == 0
+    for starts in [(0, 4, 9), (0, 1, 2, 5, 9), tuple(range(10))]:
+        y, rc, _ = gpu_decode(dec, cfg, z, starts, ws)
+        assert rc == 0 and torch.equal(y, full), starts
+    dec.close()
+
+
 @pytest.mark.parametrize("shape", [(10, 12), (12, 20), (9, 16)])
 def test_band_decode_is_bit_identical_to_full(gpu_lib, shape):
     # convs and attention compute each element identically on any band table, and the
