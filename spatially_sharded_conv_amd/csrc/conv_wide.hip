@@ -732,6 +732,8 @@ hipError_t go_tile(const ConvArgs& a, WideTile t, hipStream_t s) {
   if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
   if (t.bm == 256)
     hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 256, 256, 8>), dim3((unsigned)wgs), dim3(512), 0, s, a);
+  else if (t.bn == 256 && SUB)   // the fp8 step's extra issue slots want two waves per SIMD
+    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128, 256, 8>), dim3((unsigned)wgs), dim3(512), 0, s, a);
   else if (t.bn == 256)
     hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128, 256, 4>), dim3((unsigned)wgs), dim3(256), 0, s, a);
   else if constexpr (!SUB)
@@ -752,8 +754,8 @@ hipError_t go_mode(const ConvArgs& a, WideTile t, hipStream_t s) {
 // Workgroup tile (output channels x pixels) of the wide kernel: 256 x 256 when a layer
 // still fills the 256 CUs with two workgroups each (sub-pixel convs count their four
 // phases); else, for plain convs, 128 x 512 with 8 waves when that does; else 128 x 256
-// with 4 waves.  Decided on the whole image, so every band table of an image runs the same
-// kernel.
+// (8 waves for sub-pixel convs, 4 for plain ones).  Decided on the whole image, so every
+// band table of an image runs the same kernel.
 WideTile wide_tile(const ConvArgs& a) {
   const int ph = a.sub ? 4 : 1;
   const long long px = (long long)a.in.n_img * a.in.H * a.in.W;
