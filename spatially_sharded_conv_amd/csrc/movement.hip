@@ -87,14 +87,39 @@ __global__ void pack_weight_kernel(const T* src, int co, int ci, int taps, T* ds
 // dy reads source row offset floor((py + dy - 1) / 2), which is -1, 0, 0 for py = 0 and
 // 0, 0, 1 for py = 1; folded row tap a of phase py sums the kernel rows whose offset is
 // a - 1 + py (columns likewise).  The fp32 sum is stored as bf16 hi and lo parts.
-// Largest |w| of n bf16 weights (one workgroup of 256) -> scale[1] (float bits).
-__global__ void __launch_bounds__(256) absmax_kernel(const bf16* src, long long n, int* scale) {
-  __shared__ float part[256];
+// Largest |w| of n bf16 weights -> scale[1] (float bits).  One workgroup of 1024 threads;
+// with vec (src 16-byte aligned, n a multiple of 8) each thread keeps eight 16-byte loads
+// in flight, else it reads one weight at a time.
+__global__ void __launch_bounds__(1024) absmax_kernel(const bf16* src, long long n, int vec, int* scale) {
+  constexpr int kT = 1024, kU = 8;
+  __shared__ float part[kT];
   float m = 0.f;
-  for (long long i = threadIdx.x; i < n; i += 256) m = fmaxf(m, fabsf((float)src[i]));
+  if (vec) {
+    const uint4* s4 = reinterpret_cast<const uint4*>(src);
+    const long long n8 = n / 8;
+    for (long long i0 = 0; i0 < n8; i0 += (long long)kT * kU) {
+      uint4 v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const long long i = i0 + (long long)u * kT + threadIdx.x;
+        v[u] = i < n8 ? s4[i] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const unsigned w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          m = fmaxf(m, fabsf(__uint_as_float(w[e] << 16)));
+          m = fmaxf(m, fabsf(__uint_as_float(w[e] & 0xffff0000u)));
+        }
+      }
+    }
+  } else {
+    for (long long i = threadIdx.x; i < n; i += kT) m = fmaxf(m, fabsf((float)src[i]));
+  }
   part[threadIdx.x] = m;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
+  for (int w = kT / 2; w > 0; w >>= 1) {
     if ((int)threadIdx.x < w) part[threadIdx.x] = fmaxf(part[threadIdx.x], part[threadIdx.x + w]);
     __syncthreads();
   }
@@ -333,7 +358,9 @@ hipError_t launch_fold_subpixel_weight(const void* src, int co, int ci, void* ds
                                        hipStream_t s, bool transposed) {
   if (ci % 64 != 0) return hipErrorInvalidValue;
   if (!transposed) {
-    hipLaunchKernelGGL(absmax_kernel, dim3(1), dim3(256), 0, s, (const bf16*)src, 9LL * co * ci, scale);
+    const long long n = 9LL * co * ci;
+    const int vec = (reinterpret_cast<uintptr_t>(src) % 16 == 0 && n % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL(absmax_kernel, dim3(1), dim3(1024), 0, s, (const bf16*)src, n, vec, scale);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
