@@ -186,15 +186,16 @@ __global__ void __launch_bounds__(256) flash_bf16(const AttnArgs a) {
   }
 }
 
-// bf16 path, split-channel form (tokens a multiple of 8).  A workgroup owns 64 queries;
+// bf16 path, split-channel form (tokens a multiple of 8).  A workgroup owns 32 QB queries;
 // wave w owns channels [w*DS, (w+1)*DS) of both products (DS = d/4), so no K or V
 // element is read by two waves and both go straight from global memory into registers
 // (V of a tile loads while its S is formed, K of the next tile while its softmax and
 // P V run).  Per 32-key tile:
 //   1. each wave forms its partial S^T[key][q] = K[key][slice] Q^T[slice][q]
 //      (v_mfma_f32_32x32x16_bf16) and stores it to LDS;
-//   2. wave w sums the four partials for queries 16w .. 16w+15, runs the online softmax in
-//      fp32 (exp2 domain) and stores P (bf16) and the rescale factors;
+//   2. wave w sums the four partials for queries 16w .. 16w+15 (waves 0 and 1 only when
+//      QB = 1), runs the online softmax in fp32 (exp2 domain) and stores P (bf16) and the
+//      rescale factors;
 //   3. each wave accumulates O^T[slice][q] += V^T[slice][key] P^T[key][q].
 // The running max moves only when a row's tile max exceeds it by more than 8 (factor 256
 // in P); otherwise P is formed against the old max (still exact: numerator and
@@ -204,13 +205,15 @@ __global__ void __launch_bounds__(256) flash_bf16(const AttnArgs a) {
 // half of the key tiles and writes its unnormalised O, running max and sum (fp32) to
 // a.part; attn_merge combines the halves.  Two workgroups then share each CU, one's
 // barrier and softmax phases overlapping the other's products.  At d = 512 the registers
-// of two workgroups per CU do not hold Q, K, V and O without spilling: one per CU.
-template <int DS>
-__global__ void __launch_bounds__(256, DS <= 96 ? 2 : 1) attn_split(const AttnArgs a) {
+// of two 64-query workgroups per CU do not hold Q, K, V and O without spilling; 32-query
+// workgroups (QB = 1, half the Q, S and O registers) share a CU two at a time instead.
+template <int DS, int QB>
+__global__ void __launch_bounds__(256, (DS <= 96 || QB == 1) ? 2 : 1) attn_split(const AttnArgs a) {
   constexpr int D = 4 * DS;
   constexpr int KS = DS / 16;   // 16-channel steps of the S product
   constexpr int CB = DS / 32;   // 32-channel blocks of O^T
   constexpr int BK = 32;        // keys per tile
+  constexpr int NQ = 32 * QB;   // queries per workgroup
   __shared__ __attribute__((aligned(16))) float sS[4][64][36];
   __shared__ __attribute__((aligned(16))) unsigned short sP[64][40];
   __shared__ float sAlpha[64];
@@ -226,12 +229,13 @@ __global__ void __launch_bounds__(256, DS <= 96 ? 2 : 1) attn_split(const AttnAr
   const int local = blk - a.tile_start[b];
   const int W = a.L.W;
   const int nq = a.L.rows[b] * W;
-  const int qt_img = (nq + 63) / 64;
+  const int qt_img = (nq + NQ - 1) / NQ;
   const int n = local / qt_img;
-  const int q0 = (local - n * qt_img) * 64;
+  const int q0 = (local - n * qt_img) * NQ;
   const int tokens = a.tokens;
   const long long tok0 = (long long)a.L.row0[b] * W;
   const int l32 = lane & 31, hi = lane >> 5;
+  const bool smw = QB == 2 || wave < 2;   // this wave runs the softmax of 16 queries
   const int c0 = wave * DS;
 
   const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -244,11 +248,11 @@ __global__ void __launch_bounds__(256, DS <= 96 ? 2 : 1) attn_split(const AttnAr
       const_cast<unsigned short*>(vbase), 0, tokens * D * 2, 0x00020000);
 
   // Q^T fragments (B operand of S^T): query q0 + 32*qb + lane%32, channels c0 + 16*ks + 8*hi
-  bf16x8_t qf[2][KS];
+  bf16x8_t qf[QB][KS];
   {
     const unsigned short* qbase = reinterpret_cast<const unsigned short*>(a.q) + (long long)n * tokens * D;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       int ql = q0 + 32 * qb + l32;
       if (ql > nq - 1) ql = nq - 1;
       const unsigned short* qr = qbase + (tok0 + ql) * D + c0 + 8 * hi;
@@ -281,11 +285,11 @@ __global__ void __launch_bounds__(256, DS <= 96 ? 2 : 1) attn_split(const AttnAr
     }                                                                                          \
   }
 
-  f32x16_t oacc[CB][2];
+  f32x16_t oacc[CB][QB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) oacc[cb][qb][v] = 0.f;
   // softmax rows of this lane: query 16*wave + lane/4, keys 8*(lane%4) .. +8 of a tile
@@ -301,20 +305,20 @@ __global__ void __launch_bounds__(256, DS <= 96 ? 2 : 1) attn_split(const AttnAr
 #define VAEP_TILE(KF, VF, k0)                                                                  \
   {                                                                                            \
     VAEP_LOAD_V(VF, k0);                                                                       \
-    f32x16_t sacc[2];                                                                          \
-    _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                                         \
+    f32x16_t sacc[QB];                                                                         \
+    _Pragma("unroll") for (int qb = 0; qb < QB; ++qb) {                                         \
       _Pragma("unroll") for (int v = 0; v < 16; ++v) sacc[qb][v] = 0.f;                        \
       _Pragma("unroll") for (int ks = 0; ks < KS; ++ks)                                        \
         sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(KF[ks], qf[qb][ks], sacc[qb], 0, 0, 0); \
     }                                                                                          \
     if ((k0) + BK < tokens) VAEP_LOAD_K(KF, (k0) + BK);                                        \
     /* partial S^T: lane holds query 32qb + lane%32, keys 8g + 4hi + 0..3 */                   \
-    _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                                           \
+    _Pragma("unroll") for (int qb = 0; qb < QB; ++qb)                                           \
       _Pragma("unroll") for (int g = 0; g < 4; ++g)                                            \
         *reinterpret_cast<f32x4_t*>(&sS[wave][32 * qb + l32][8 * g + 4 * hi]) =                \
             f32x4_t{sacc[qb][4 * g], sacc[qb][4 * g + 1], sacc[qb][4 * g + 2], sacc[qb][4 * g + 3]}; \
     __syncthreads();                                                                           \
-    {                                                                                          \
+    if (smw) {                                                                                 \
       float sv[8];                                                                             \
       _Pragma("unroll") for (int e = 0; e < 8; ++e) sv[e] = 0.f;                               \
       _Pragma("unroll") for (int w = 0; w < 4; ++w) {                                          \
@@ -353,12 +357,12 @@ __global__ void __launch_bounds__(256, DS <= 96 ? 2 : 1) attn_split(const AttnAr
     }                                                                                          \
     __syncthreads();                                                                           \
     if (sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3]) {                                           \
-      _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                                       \
+      _Pragma("unroll") for (int qb = 0; qb < QB; ++qb) {                                       \
         const float al = sAlpha[32 * qb + l32];                                                \
         _Pragma("unroll") for (int cb = 0; cb < CB; ++cb) oacc[cb][qb] *= al;                  \
       }                                                                                        \
     }                                                                                          \
-    _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                                           \
+    _Pragma("unroll") for (int qb = 0; qb < QB; ++qb)                                           \
       _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                       \
         const bf16x8_t pf = *reinterpret_cast<const bf16x8_t*>(&sP[32 * qb + l32][16 * kk + 8 * hi]); \
         _Pragma("unroll") for (int cb = 0; cb < CB; ++cb)                                      \
@@ -366,6 +370,7 @@ __global__ void __launch_bounds__(256, DS <= 96 ? 2 : 1) attn_split(const AttnAr
       }                                                                                        \
   }
 
+  if (!smw && lane == 0) sFlag[wave] = 0;   // ordered before its reads by the tile's first barrier
   VAEP_LOAD_K(kf, tbeg * BK);
   for (int t = tbeg; t < tend; ++t) VAEP_TILE(kf, vf, t * BK);
 #undef VAEP_TILE
@@ -376,12 +381,12 @@ __global__ void __launch_bounds__(256, DS <= 96 ? 2 : 1) attn_split(const AttnAr
     // this half's unnormalised O^T, and (m, l) per query, at the query's global token
     float* po = a.part + ((long long)(half * a.L.n_img + n) * tokens + tok0) * D;
     float* pml = a.part + (long long)2 * a.L.n_img * tokens * D + ((long long)(half * a.L.n_img + n) * tokens + tok0) * 2;
-    if ((lane & 3) == 0 && q0 + qs < nq) {
+    if (smw && (lane & 3) == 0 && q0 + qs < nq) {
       pml[(long long)(q0 + qs) * 2] = m_run;
       pml[(long long)(q0 + qs) * 2 + 1] = l_run;
     }
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       const int ql = q0 + 32 * qb + l32;
       if (ql >= nq) continue;
 #pragma unroll
@@ -393,11 +398,11 @@ __global__ void __launch_bounds__(256, DS <= 96 ? 2 : 1) attn_split(const AttnAr
     }
     return;
   }
-  if ((lane & 3) == 0) sL[qs] = l_run;
+  if (smw && (lane & 3) == 0) sL[qs] = l_run;
   __syncthreads();
   // O^T block (cb, qb): lane holds query 32qb + lane%32, channels c0 + 32cb + 8g + 4hi + 0..3
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const int ql = q0 + 32 * qb + l32;
     if (ql >= nq) continue;
     const float inv = 1.f / sL[32 * qb + l32];
@@ -506,10 +511,16 @@ __global__ void __launch_bounds__(256) attn_f32(const AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attention(AttnArgs& a, int dtype, hipStream_t s) {
-  // split-channel kernel: 64 queries per workgroup, needs tokens % 8 == 0 (16-byte V^T rows)
+  // split-channel kernel: 64 queries per workgroup, needs tokens % 8 == 0 (16-byte V^T
+  // rows).  At d = 512 a workgroup holds a whole CU's registers; when the image's 64-query
+  // blocks leave CUs idle, 32-query workgroups (two per CU) run instead -- decided on the
+  // whole image, so every band table computes the same sums.  With 64-query blocks that
+  // fill the CUs the 32-query form is slower: each workgroup streams all of K and V.
   const bool split = dtype != VAEP_DTYPE_F32 && a.tokens % 8 == 0 &&
                      (long long)a.tokens * a.c * 2 < (1LL << 31);
-  const int per = dtype == VAEP_DTYPE_F32 ? 4 : (split ? 64 : kQ);
+  const long long q64 = (long long)a.L.n_img * (((long long)a.L.H * a.L.W + 63) / 64);
+  const int qb = (split && a.c == 512 && q64 < 256) ? 1 : 2;
+  const int per = dtype == VAEP_DTYPE_F32 ? 4 : (split ? 32 * qb : kQ);
   int t = 0;
   for (int b = 0; b < a.L.nb; ++b) {
     a.tile_start[b] = t;
@@ -527,14 +538,18 @@ hipError_t launch_attention(AttnArgs& a, int dtype, hipStream_t s) {
     // keys in two halves (a.part: the caller's scratch of attn_part_floats) when the query
     // blocks alone would not give every CU two workgroups and d <= 384 -- decided on the
     // whole image, so every band table computes the same sums
-    if (a.part && (a.c > 384 || (long long)a.L.n_img * (((long long)a.L.H * a.L.W + 63) / 64) >= 512))
-      a.part = nullptr;
+    if (a.part && (a.c > 384 || q64 >= 512)) a.part = nullptr;
     const unsigned g = (unsigned)t * (a.part ? 2u : 1u);
     switch (a.c) {
-      case 128: hipLaunchKernelGGL(attn_split<32>, dim3(g), dim3(256), 0, s, a); break;
-      case 256: hipLaunchKernelGGL(attn_split<64>, dim3(g), dim3(256), 0, s, a); break;
-      case 384: hipLaunchKernelGGL(attn_split<96>, dim3(g), dim3(256), 0, s, a); break;
-      case 512: hipLaunchKernelGGL(attn_split<128>, dim3(g), dim3(256), 0, s, a); break;
+      case 128: hipLaunchKernelGGL((attn_split<32, 2>), dim3(g), dim3(256), 0, s, a); break;
+      case 256: hipLaunchKernelGGL((attn_split<64, 2>), dim3(g), dim3(256), 0, s, a); break;
+      case 384: hipLaunchKernelGGL((attn_split<96, 2>), dim3(g), dim3(256), 0, s, a); break;
+      case 512:
+        if (qb == 1)
+          hipLaunchKernelGGL((attn_split<128, 1>), dim3(g), dim3(256), 0, s, a);
+        else
+          hipLaunchKernelGGL((attn_split<128, 2>), dim3(g), dim3(256), 0, s, a);
+        break;
       default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();

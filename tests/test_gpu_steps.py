@@ -264,6 +264,44 @@ def test_attention_step(gpu_lib, case):
     assert_close(got, ref, *STEP_TOL[dtype], what=f"attention {case}")
 
 
+def test_attention_step_d512_full_grid(gpu_lib):
+    """d = 512 over 128 x 128 tokens on uneven bands: 256 blocks of 64 queries fill the CUs,
+    so the one-workgroup-per-CU form runs (the 200-token case above runs the 32-query form).
+    Sampled query rows of every band, first and last tokens included, against the float64
+    reference; the output does not depend on the band table."""
+    C, G, H, W = 512, 32, 128, 128
+    starts = (0, 31, 64, 96, 128)
+    x = seeded((1, C, H, W), 241, dtype="f32")
+    g = seeded((C,), 242, 0.25, offset=1.0, dtype="f32")
+    be = seeded((C,), 243, 0.1, dtype="f32")
+    ws = [seeded((C, C), 244 + i, 1 / math.sqrt(C), dtype="bf16") for i in range(4)]
+    bs = [seeded((C,), 250 + i, 0.1, dtype="bf16") for i in range(4)]
+    dev = [to_dev(t, "bf16") for t in ws + bs]
+    xd, gd, bed = x.cuda(), g.cuda(), be.cuda()
+    got = vaep.step_attention(xd, G, 1e-6, gd, bed, dev[0], dev[4], dev[1], dev[5], dev[2], dev[6],
+                              dev[3], dev[7], starts)
+    whole = vaep.step_attention(xd, G, 1e-6, gd, bed, dev[0], dev[4], dev[1], dev[5], dev[2], dev[6],
+                                dev[3], dev[7], (0, H))
+    assert torch.equal(got, whole)
+    # float64 reference of the sampled query rows (same rounding points as _attn_ref)
+    fin = Precision("bf16").finish
+    x5 = x[:, :, None]
+    _, m, v = ops.groupnorm_moments(x5, G)
+    h = fin(ops.groupnorm_apply(x5, m, v, g, be, 1e-6, act=False))
+    tok = h[0, :, 0].reshape(C, -1).T.double()
+    q = fin(tok @ ws[0].double().T + bs[0].double())
+    k = fin(tok @ ws[1].double().T + bs[1].double())
+    v_ = fin(tok @ ws[2].double().T + bs[2].double())
+    gen = torch.Generator().manual_seed(245)
+    rows = torch.cat([torch.tensor([0, H * W - 1] + [s * W for s in starts[1:-1]] + [s * W - 1 for s in starts[1:-1]]),
+                      torch.randint(0, H * W, (184,), generator=gen)])
+    o = fin(ops.attention_rows(q[rows], k, v_, 1 / math.sqrt(C)))
+    out = x[0].reshape(C, -1).T.double()[rows] + o.double() @ ws[3].double().T + bs[3].double()
+    ref = Precision("bf16").acc(out)
+    sel = got[0].reshape(C, -1).T[rows].cpu()
+    assert_close(sel, ref, *STEP_TOL["bf16"], what="attention d=512, 16384 tokens, sampled rows")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_temporal_upsample_step(gpu_lib, dtype):
     C = 64
