@@ -155,7 +155,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: every band of the decode runs on this device and there "
-              f"is no multi-GPU path in this build (asked for --gpus {args.gpus}, WORLD_SIZE {world}).",
+              f"is no multi-GPU path in this library (asked for --gpus {args.gpus}, WORLD_SIZE {world}).",
               file=sys.stderr)
         sys.exit(2)
 
