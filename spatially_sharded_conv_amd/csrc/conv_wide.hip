@@ -730,16 +730,17 @@ hipError_t go_tile(const ConvArgs& a, WideTile t, hipStream_t s) {
   const int ph = SUB ? 4 : 1;
   const long long wgs = (long long)a.tiles_total * (a.cout_pad / t.bm) * ph;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (t.bm == 256)
+  if (t.bm == 256) {
     hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 256, 256, 8>), dim3((unsigned)wgs), dim3(512), 0, s, a);
-  else if (t.bn == 256 && SUB)   // the fp8 step's extra issue slots want two waves per SIMD
+  } else if constexpr (SUB) {
+    // 128 x 256 tiles: sub-pixel convs only (plain convs of that size run on the 128 x 128
+    // kernel); 8 waves, whose second wave per SIMD hides the fp8 step's extra issue slots
+    if (t.bn != 256) return hipErrorInvalidValue;
     hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128, 256, 8>), dim3((unsigned)wgs), dim3(512), 0, s, a);
-  else if (t.bn == 256)
-    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128, 256, 4>), dim3((unsigned)wgs), dim3(256), 0, s, a);
-  else if constexpr (!SUB)
+  } else {
+    if (t.bn != 512) return hipErrorInvalidValue;
     hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128, 512, 8>), dim3((unsigned)wgs), dim3(512), 0, s, a);
-  else
-    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -754,8 +755,9 @@ hipError_t go_mode(const ConvArgs& a, WideTile t, hipStream_t s) {
 // Workgroup tile (output channels x pixels) of the wide kernel: 256 x 256 when a layer
 // still fills the 256 CUs with two workgroups each (sub-pixel convs count their four
 // phases); else, for plain convs, 128 x 512 with 8 waves when that does; else 128 x 256
-// (8 waves for sub-pixel convs, 4 for plain ones).  Decided on the whole image, so every
-// band table of an image runs the same kernel.
+// (the launch runs it for sub-pixel convs only; conv_wide_fits sends such plain convs to
+// the 128 x 128 kernel).  Decided on the whole image, so every band table of an image runs
+// the same kernel.
 WideTile wide_tile(const ConvArgs& a) {
   const int ph = a.sub ? 4 : 1;
   const long long px = (long long)a.in.n_img * a.in.H * a.in.W;
