@@ -186,7 +186,7 @@ __global__ void __launch_bounds__(256) flash_bf16(const AttnArgs a) {
   }
 }
 
-// bf16 path, split-channel form (tokens a multiple of 8).  A workgroup owns 32 QB queries;
+// bf16 path, split-channel form (tokens a multiple of 8).  A workgroup owns 32 * QB queries;
 // wave w owns channels [w*DS, (w+1)*DS) of both products (DS = d/4), so no K or V
 // element is read by two waves and both go straight from global memory into registers
 // (V of a tile loads while its S is formed, K of the next tile while its softmax and
@@ -206,7 +206,8 @@ __global__ void __launch_bounds__(256) flash_bf16(const AttnArgs a) {
 // a.part; attn_merge combines the halves.  Two workgroups then share each CU, one's
 // barrier and softmax phases overlapping the other's products.  At d = 512 the registers
 // of two 64-query workgroups per CU do not hold Q, K, V and O without spilling; 32-query
-// workgroups (QB = 1, half the Q, S and O registers) share a CU two at a time instead.
+// workgroups (QB = 1, half the Q, S and O registers) fit two per CU, and the launch runs
+// them where 64-query blocks would leave CUs idle.
 template <int DS, int QB>
 __global__ void __launch_bounds__(256, (DS <= 96 || QB == 1) ? 2 : 1) attn_split(const AttnArgs a) {
   constexpr int D = 4 * DS;
