@@ -708,9 +708,9 @@ bool shortcut_folds(const ResW& r, const BandLayout& Lh, bool split_out) {
   a.mode = kModeBand;
   if (!conv_wide_fits(a)) return false;
   // the second operand's rows one tile reads stay within a buffer resource (2 GiB)
-  const long long bn = wide_tile(a).bn;
+  const int bn = wide_tile(a).bn;
   for (int b = 0; b < Lh.nb; ++b)
-    if ((long long)a.kt * (Lh.rows[b] + 2) * Lh.W * r.c2x.kext * 2 + 2 * bn * r.c2x.kext * 2 >= (1LL << 31) - 4096)
+    if ((tile_read_slots(Lh, b, a.kt, bn, false) * Lh.W + 2LL * bn) * r.c2x.kext * 2 >= (1LL << 31) - 4096)
       return false;
   return true;
 }

@@ -583,11 +583,11 @@ hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s) {
   if (a.split8 && (a.mode != kModeBandSplit || a.cout % 64 != 0)) return hipErrorInvalidValue;
   if (a.x2 || a.cin2) return hipErrorInvalidValue;   // a folded second operand needs the wide kernel
   if (dtype != VAEP_DTYPE_F32) {
-    // buffer-resource addressing: the rows one tile can read (at most KT frames of a
-    // band) and the weights stay below 2 GiB, so the padding offset reads out of range
+    // buffer-resource addressing: the rows one tile can read and the weights stay below
+    // 2 GiB, so the padding offset reads out of range
     const long long xb = a.x_f32 ? 4 : 2;
     for (int b = 0; b < a.in.nb; ++b)
-      if ((long long)a.kt * (a.in.rows[b] + 2) * a.in.W * a.in.C * xb + 2LL * kConvTileM * a.in.C * xb >=
+      if ((tile_read_slots(a.in, b, a.kt, kConvTileM, ups) * a.in.W + 2LL * kConvTileM) * a.in.C * xb >=
           (1LL << 31) - 4096)
         return hipErrorInvalidValue;
     if ((long long)a.cout_pad * a.kt * a.ks * a.ks * a.cin * 2 >= (1LL << 31)) return hipErrorInvalidValue;

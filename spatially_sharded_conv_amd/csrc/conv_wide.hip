@@ -793,15 +793,13 @@ hipError_t launch_conv_wide(ConvArgs& a, hipStream_t s) {
   if (a.in.C != (a.x_split ? 2 * a.cin : a.cin)) return hipErrorInvalidValue;
   const WideTile wt = wide_tile(a);
   const int bn = wt.bn;
-  if (a.x2)
-    for (int b = 0; b < a.in.nb; ++b)
-      if ((long long)a.kt * (a.in.rows[b] + 2) * a.in.W * a.cin2 * 2 + 2LL * bn * a.cin2 * 2 >= (1LL << 31) - 4096)
-        return hipErrorInvalidValue;
-  // buffer-resource addressing: the rows one tile reads and the weights stay below 2 GiB
-  for (int b = 0; b < a.in.nb; ++b)
-    if ((long long)a.kt * (a.in.rows[b] + 2) * a.in.W * a.in.C * 2 + 2LL * bn * a.in.C * 2 >=
-        (1LL << 31) - 4096)
-      return hipErrorInvalidValue;
+  // buffer-resource addressing: the rows one tile reads (of the operand and of a second
+  // operand) and the weights stay below 2 GiB, the padding offset beyond them
+  for (int b = 0; b < a.in.nb; ++b) {
+    const long long slot_px = tile_read_slots(a.in, b, a.kt, bn, false) * a.in.W;
+    if (a.x2 && (slot_px + 2LL * bn) * a.cin2 * 2 >= (1LL << 31) - 4096) return hipErrorInvalidValue;
+    if ((slot_px + 2LL * bn) * a.in.C * 2 >= (1LL << 31) - 4096) return hipErrorInvalidValue;
+  }
   const long long kw = (long long)a.kt * (a.sub ? 4 * 2 : a.ks * a.ks) * a.cin + a.cin2;
   if ((long long)a.cout_pad * kw * 2 >= (1LL << 31)) return hipErrorInvalidValue;
   // tiles over the compute pixels (the source grid for sub-pixel convs)

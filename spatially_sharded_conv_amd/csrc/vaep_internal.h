@@ -38,6 +38,22 @@ inline long long layout_elems(const BandLayout& L) {
   return e;
 }
 
+// Slots (rows, halo slots included) of band b's buffer that one conv tile of `bn` compute
+// pixels can read: the conv kernels give every tile a buffer resource over the slots from
+// its first pixel's row - 1, kt - 1 images back, to its last pixel's row + 1 (with ups, the
+// source rows of a compute grid of twice the rows and width).  A tile's compute rows within
+// one image number at most c = ceil(bn / wc) + 1; when the tile also reaches into the next
+// image the range adds that image's first rows: at most (kt - 1)(rows + 2) + 2c + 4 slots
+// while an image holds at least bn compute pixels.  Capped at the whole buffer.
+inline long long tile_read_slots(const BandLayout& in, int b, int kt, int bn, bool ups) {
+  const long long R = in.rows[b], wc = (ups ? 2LL : 1LL) * in.W;
+  const long long plane = (ups ? 2 : 1) * R * wc;
+  const long long c = (bn + wc - 1) / wc + 1;
+  long long slots = plane >= bn ? (kt - 1) * (R + 2) + 2 * c + 4 : (kt + 1 + (bn + plane - 1) / plane) * (R + 2);
+  const long long all = (long long)in.n_img * (R + 2);
+  return slots < all ? slots : all;
+}
+
 // Fill a layout from band row counts; bands are stored back to back from element 0.
 BandLayout make_layout(int nb, const int* rows, int n_img, int frames, int W, int C);
 // The same bands after a nearest-2x upsample: rows and width double.

@@ -199,6 +199,24 @@ def test_full_size_bands_bit_identical_and_kernels(gpu_lib):
     dec.close()
 
 
+def test_2048_single_band_decode_equals_band_decode(gpu_lib):
+    """A 2048 x 2048 decode (256 x 256 latent, the 1024^2 model) as one band: its last
+    stages' band buffers exceed 2 GiB (up to 4.3 GB of fp32 stream), beyond a buffer
+    resource's range, which the conv kernels never span (each tile addresses its own rows).
+    It equals the four-band decode bit for bit."""
+    cfg = preset(3).with_size(latent_h=256, latent_w=256, band_starts=(0, 62, 128, 192, 256))
+    dec, _ = make_decoder(cfg)
+    z = make_latent(cfg)
+    y1, rc, _ = gpu_decode(dec, cfg, z, (0, 256))
+    assert rc == 0
+    y4, rc, info = gpu_decode(dec, cfg, z, cfg.band_starts)
+    assert rc == 0 and info.bands_used == 4
+    assert list(y1.shape) == [1, 3, 2048, 2048]
+    assert torch.isfinite(y1).all()
+    assert torch.equal(y1, y4)
+    dec.close()
+
+
 def test_video_band_decode_is_bit_identical_to_full(gpu_lib):
     # the video decoder's causal convs, RMSNorm, temporal upsample and per-frame attention
     # (d = 384: two key halves per query block, merged) compute each element identically

@@ -77,6 +77,34 @@ def test_conv3x3_step_wide_tiles(gpu_lib):
     assert_close(got, ref, *ACC_TOL, what="conv3x3 wide tiles")
 
 
+def test_conv_step_single_band_above_2gib(gpu_lib):
+    """One band whose buffer exceeds a buffer resource's 2 GiB range: 2048 x 2048 pixels of
+    256 bf16 channels (2.15 GB with the halo rows).  The conv kernels address only the rows
+    each tile reads, so the single band runs; it equals the two-band run bit for bit, and
+    sampled outputs (corners, edges, the band seam) match the float64 definition."""
+    cin, cout, H, W = 256, 128, 2048, 2048
+    gen = torch.Generator(device="cuda").manual_seed(261)
+    x = torch.randn((1, cin, H, W), generator=gen, device="cuda").to(torch.bfloat16)
+    w = seeded((cout, cin, 3, 3), 262, 1 / math.sqrt(cin * 9), dtype="bf16")
+    b = seeded((cout,), 263, 0.1, dtype="bf16")
+    wd, bd = to_dev(w, "bf16"), to_dev(b, "bf16")
+    one = vaep.step_conv(x, wd, bd, (0, H))
+    two = vaep.step_conv(x, wd, bd, (0, 1000, H))
+    assert torch.equal(one, two)
+    pts = [(0, 0), (0, W - 1), (H - 1, 0), (H - 1, W - 1), (999, 5), (1000, 7), (1000, W - 1), (517, 0)]
+    g2 = torch.Generator().manual_seed(264)
+    pts += [(int(h), int(c)) for h, c in zip(torch.randint(0, H, (24,), generator=g2),
+                                              torch.randint(0, W, (24,), generator=g2))]
+    xp = torch.nn.functional.pad(x[0].float(), (1, 1, 1, 1))       # zero padding at the image edges
+    wdb = w.double()
+    got, ref = [], []
+    for h, c in pts:
+        patch = xp[:, h:h + 3, c:c + 3].cpu().double()                # rows h-1..h+1, columns c-1..c+1
+        ref.append((wdb * patch).sum(dim=(1, 2, 3)) + b.double())
+        got.append(one[0, :, h, c].cpu().double())
+    assert_close(torch.stack(got), torch.stack(ref), *ACC_TOL, what="2048^2 single-band conv, sampled pixels")
+
+
 def test_upsample_conv_from_fp32_wide_tiles(gpu_lib):
     # sub-pixel upsample conv with 256-channel output tiles
     x = seeded((1, 64, 130, 260), 27, dtype="f32")
