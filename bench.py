@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=3, help="preset id (3 = the 1024^2 headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-latent", type=int, default=48,
+    ap.add_argument("--cpu-sample-latent", type=int, default=72,
                     help="latent side of the oracle's bounded sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="only run a device-to-device copy of MB MiB (reference dispatch for HBM counters)")
