@@ -34,7 +34,18 @@ def errors(got, ref):
     return d.abs().max().item(), (d.norm() / max(r.norm().item(), 1e-30)).item()
 
 
-def assert_close(got, ref, max_abs, rel_l2, what=""):
+# Measured parity figures of the session, printed in pytest's terminal summary
+# (tests/conftest.py) so that the margins to the bar are visible in the run's log.
+PARITY_LOG = []
+
+
+def record(what, max_abs, rel_l2, bar_abs=None, bar_rel=None):
+    PARITY_LOG.append((what, max_abs, rel_l2, bar_abs, bar_rel))
+
+
+def assert_close(got, ref, max_abs, rel_l2, what="", log=False):
     ma, rl = errors(got, ref)
+    if log:
+        record(what, ma, rl, max_abs, rel_l2)
     assert ma <= max_abs and rl <= rel_l2, f"{what}: max-abs {ma:.3e} (bar {max_abs}), rel-L2 {rl:.3e} (bar {rel_l2})"
     return ma, rl

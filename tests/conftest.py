@@ -21,3 +21,14 @@ def gpu_lib():
         pytest.fail("GPU test run without a visible GPU")
     from spatially_sharded_conv_amd import _lib
     return _lib.load()
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Parity figures the tests recorded (max-abs and rel-L2 against the bar), one line each."""
+    from tests._util import PARITY_LOG
+    if not PARITY_LOG:
+        return
+    terminalreporter.section("parity (measured / bar)")
+    for what, ma, rl, ba, br in PARITY_LOG:
+        bars = f" / {ba:g}, {br:g}" if ba is not None else ""
+        terminalreporter.write_line(f"{what}: max-abs {ma:.3e} rel-L2 {rl:.3e}{bars}")
