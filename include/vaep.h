@@ -82,18 +82,21 @@ typedef struct vaep_config {
   float eps;                                /* norm epsilon */
 } vaep_config;
 
-/* Shard axes (vaep_decode_sharded, vaep_select_axis, vaep_decode_info.axis). */
+/* Shard axes and strategies (vaep_decode_sharded, vaep_select_axis, vaep_decode_info.axis). */
 enum { VAEP_AXIS_AUTO = 0,     /* pick per request (vaep_select_axis) */
        VAEP_AXIS_HEIGHT = 1,   /* bands of latent rows */
        VAEP_AXIS_WIDTH = 2,    /* bands of latent columns */
-       VAEP_AXIS_DENSE = 3 };  /* result only: one dense band */
+       VAEP_AXIS_DENSE = 3,    /* result only: one dense band */
+       VAEP_AXIS_TILE = 4 };   /* the overlap-blending tile decode (vaep_decode_tiled) */
 
 /* Optional report filled by the decode entry points. */
 typedef struct vaep_decode_info {
   int32_t bands_used;        /* number of bands actually decoded */
-  int32_t fell_back;         /* 1 if the dense one-band path replaced a multi-shard request */
+  int32_t fell_back;         /* 1 if a fallback replaced the request: the dense one-band path
+                                (vaep_decode_bands) or the tile decode (vaep_decode_sharded) */
   int32_t n_launches;        /* kernels enqueued by the call */
-  int32_t axis;              /* VAEP_AXIS_HEIGHT / _WIDTH of the bands, or _DENSE */
+  int32_t axis;              /* VAEP_AXIS_HEIGHT / _WIDTH of the bands, _DENSE, or _TILE (then
+                                bands_used is the number of tiles) */
   uint64_t workspace_bytes;  /* bytes of the workspace the call used */
 } vaep_decode_info;
 
@@ -152,14 +155,20 @@ int vaep_decode_full(vaep_model* model, const void* latent, int batch, int frame
                      int latent_h, int latent_w, void* out, void* ws, size_t ws_bytes,
                      void* stream);
 
-/* Band decode.  row_starts: host array of n_bands+1 latent row indices with
- * row_starts[0] = 0 < row_starts[1] < ... < row_starts[n_bands] = latent_h; band i owns
- * latent rows [row_starts[i], row_starts[i+1]) and the matching output rows scaled by
- * 2^(n_stages-1).  Every layer runs on all bands; convs read one halo row from each
- * neighbour band (the 3x3 kernels' radius), so every band must own at least one row.
- * A table with more than VAEP_MAX_BANDS bands is decoded as one dense band and
- * VAEP_WARN_FELL_BACK is returned (the dense fallback of the pages).  Other arguments
- * as for vaep_decode_full; info (nullable) receives a report.
+/* Band decode -- the layer-wise decode of the feature page ("VAEP: VAE 并行解码",
+ * sections on height bands, conv halo exchange, the GroupNorm statistics merge and AGKV
+ * attention) with the operator semantics of the validation page ("Static Layer-Wise VAE
+ * Decode", "Semantics and Communication").  row_starts: host array of n_bands+1 latent
+ * row indices with row_starts[0] = 0 < row_starts[1] < ... < row_starts[n_bands] =
+ * latent_h; band i owns latent rows [row_starts[i], row_starts[i+1]) and the matching
+ * output rows scaled by 2^(n_stages-1) (uneven bands allowed: the feature page keeps
+ * uneven lengths throughout the decode).  Every layer runs on all bands; convs read one
+ * halo row from each neighbour band (the 3x3 kernels' radius), so every band must own
+ * at least one row.  A table with more than VAEP_MAX_BANDS bands is decoded as one dense
+ * band and VAEP_WARN_FELL_BACK is returned (the pages' warn-and-dense fallback for
+ * ineligible requests: feature page, usage and validation scope; validation page,
+ * eligibility).  Other arguments as for vaep_decode_full; info (nullable) receives a
+ * report.
  * Errors: INVALID_ARG (non-monotonic, zero-length or uncovered bands, NULL pointers),
  * WORKSPACE, HIP. */
 int vaep_decode_bands(vaep_model* model, const void* latent, int batch, int frames,
@@ -169,16 +178,17 @@ int vaep_decode_bands(vaep_model* model, const void* latent, int batch, int fram
 
 /* Axis policy of a sharded decode (the distributed-VAE strategy page, "Strategy
  * Selection Contract" and the Wan spatial-shard notes: `auto` takes the longer axis
- * that can cover every shard, width winning ties, and falls back when neither can).
- * A shard needs at least one latent row or column (the 3x3 kernels' radius at latent
- * resolution), so an axis covers n_shards when its length is >= n_shards.  Writes
- * VAEP_AXIS_HEIGHT, VAEP_AXIS_WIDTH or VAEP_AXIS_DENSE (n_shards = 1, or neither axis
- * covers) to *axis_out.  Host only: touches no device.  Deterministic and free of state.
+ * that can cover every shard, width winning ties, and uses the tile decode when neither
+ * can).  A shard needs at least one latent row or column (the 3x3 kernels' radius at
+ * latent resolution), so an axis covers n_shards when its length is >= n_shards.  Writes
+ * VAEP_AXIS_HEIGHT, VAEP_AXIS_WIDTH, VAEP_AXIS_TILE (neither axis covers) or
+ * VAEP_AXIS_DENSE (n_shards = 1) to *axis_out.  Host only: touches no device.
+ * Deterministic and free of state.
  * Errors: INVALID_ARG (NULL axis_out, sizes < 1). */
 int vaep_select_axis(int latent_h, int latent_w, int n_shards, int32_t* axis_out);
 
-/* Sharded decode along a chosen axis (strategy page: explicit height or width
- * sharding, or `auto`, decided per request).
+/* Sharded decode with a chosen strategy (strategy page, "Strategy Selection Contract":
+ * tile, auto, forced height or forced width, decided per request).
  * axis = VAEP_AXIS_HEIGHT: bands of latent rows, exactly vaep_decode_bands.
  * axis = VAEP_AXIS_WIDTH: bands of latent columns; every rule of the band decode holds
  *   with rows and columns exchanged (convs read one halo column from each neighbour
@@ -186,21 +196,33 @@ int vaep_select_axis(int latent_h, int latent_w, int n_shards, int32_t* axis_out
  *   attention runs each band's queries against the K/V of every band).  Internally the
  *   decode runs on the transposed image with transposed 3x3 kernels (built by
  *   vaep_model_create); latent and output keep their NC[T]HW layout.
- * axis = VAEP_AXIS_AUTO: vaep_select_axis picks the axis; starts must be NULL.
+ * axis = VAEP_AXIS_TILE: the tile decode of vaep_decode_tiled with latent tiles of 32
+ *   rows and columns every 24; starts must be NULL and n_shards is not used.
+ * axis = VAEP_AXIS_AUTO: vaep_select_axis picks the strategy; starts must be NULL.
  * starts: host array of n_shards+1 indices along the axis (0 = starts[0] < ... <
  *   starts[n_shards] = axis length), or NULL for even shards (sizes differ by at most
  *   one, larger shards first).
- * Fallback: an explicit axis with NULL starts that is shorter than n_shards, or more
- *   than VAEP_MAX_BANDS shards, decodes one dense band and returns VAEP_WARN_FELL_BACK;
- *   `auto` with neither axis covering decodes one dense band and returns VAEP_OK
- *   (info->axis = VAEP_AXIS_DENSE, info->fell_back = 1 when n_shards > 1).
- * Other arguments as for vaep_decode_bands; ws >= vaep_workspace_bytes(..., n_shards).
- * Errors: INVALID_ARG (unknown axis, starts with AUTO, bad table, NULL pointers),
+ * Fallback (the contract's "ineligible request" column): an explicit axis with NULL
+ *   starts that is shorter than n_shards, or more than VAEP_MAX_BANDS shards, uses the
+ *   tile decode and returns VAEP_WARN_FELL_BACK; `auto` with neither axis covering, or
+ *   with more than VAEP_MAX_BANDS shards, uses the tile decode and returns VAEP_OK.  In
+ *   both cases info->axis = VAEP_AXIS_TILE and info->fell_back = 1.
+ * Workspace: ws >= vaep_workspace_bytes(..., n_shards) for band decodes; a request that
+ *   runs the tile decode needs vaep_sharded_workspace_bytes(..., n_shards), which covers
+ *   every outcome (with less it returns VAEP_ERR_WORKSPACE before enqueuing anything).
+ * Other arguments as for vaep_decode_bands.
+ * Errors: INVALID_ARG (unknown axis, starts with AUTO or TILE, bad table, NULL pointers),
  * WORKSPACE, HIP. */
 int vaep_decode_sharded(vaep_model* model, const void* latent, int batch, int frames,
                         int latent_h, int latent_w, int axis, const int32_t* starts,
                         int n_shards, void* out, void* ws, size_t ws_bytes, void* stream,
                         vaep_decode_info* info);
+
+/* Workspace that serves every outcome of vaep_decode_sharded with at most n_shards
+ * shards: the larger of vaep_workspace_bytes(..., n_shards) and the tile decode's
+ * vaep_tiled_workspace_bytes at its tile geometry.  Errors as vaep_workspace_bytes. */
+int vaep_sharded_workspace_bytes(const vaep_model* model, int batch, int frames, int latent_h,
+                                 int latent_w, int n_shards, size_t* bytes_out);
 
 /* Tiled decode with overlap blending -- the comparison baseline the sharded decode
  * replaces (distributed-VAE strategy page, "Tile/Patch Implementation (Decode)"):

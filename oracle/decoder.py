@@ -252,12 +252,14 @@ def decode_bands(cfg, params: Dict[str, torch.Tensor], latent: torch.Tensor,
 def choose_axis(latent_h: int, latent_w: int, n_shards: int) -> str:
     """The ``auto`` strategy of the Wan spatial-shard decode, per request.
 
-    Model-specific notes on the strategy page: auto takes the longer axis
+    Strategy page, "Strategy Selection Contract" (the ``auto`` row: tile when
+    ineligible) and the Wan spatial-shard notes: auto takes the longer axis
     that can cover every shard, width winning ties; when neither axis can
-    cover the shards it falls back.  A shard needs at least one latent row
-    (the kernel radius at the latent level), so an axis covers ``n_shards``
-    when its length is at least ``n_shards``.  Returns "height", "width" or
-    "dense" (the fallback: one band).
+    cover the shards it uses the tile decode.  A shard needs at least one
+    latent row (the kernel radius at the latent level), so an axis covers
+    ``n_shards`` when its length is at least ``n_shards``.  One shard is the
+    plain dense decode (a reading: there is nothing to shard).  Returns
+    "height", "width", "tile" or "dense".
     """
     assert n_shards >= 1
     if n_shards == 1:
@@ -267,7 +269,12 @@ def choose_axis(latent_h: int, latent_w: int, n_shards: int) -> str:
         return "width"
     if cover_h:
         return "height"
-    return "dense"
+    return "tile"
+
+
+# Tile geometry of the tile strategy (a reading: the strategy page names the tile
+# attributes but not their values): latent tiles of 32 rows and columns every 24.
+AUTO_TILE, AUTO_TILE_STRIDE = 32, 24
 
 
 def even_starts(length: int, n_shards: int) -> List[int]:
@@ -281,10 +288,14 @@ def even_starts(length: int, n_shards: int) -> List[int]:
 
 def decode_auto(cfg, params: Dict[str, torch.Tensor], latent: torch.Tensor, n_shards: int,
                 prec: Precision = None):
-    """Decode with the axis ``choose_axis`` picks and even shards; returns (output, axis)."""
+    """Decode with the strategy ``choose_axis`` picks (even shards, or the tile decode);
+    returns (output, strategy)."""
+    from .tiled import decode_tiled
     h, w = latent.shape[-2:]
     axis = choose_axis(h, w, n_shards)
     if axis == "dense":
         return decode_full(cfg, params, latent, prec), axis
+    if axis == "tile":
+        return decode_tiled(cfg, params, latent, AUTO_TILE, AUTO_TILE_STRIDE, prec), axis
     starts = even_starts(h if axis == "height" else w, n_shards)
     return decode_bands(cfg, params, latent, starts, prec, axis), axis

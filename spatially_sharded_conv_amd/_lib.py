@@ -25,13 +25,14 @@ DTYPE_F32 = 1
 DTYPE_BF16 = 2
 MAX_STAGES = 6
 MAX_BANDS = 64
-AXIS_AUTO, AXIS_HEIGHT, AXIS_WIDTH, AXIS_DENSE = 0, 1, 2, 3
+AXIS_AUTO, AXIS_HEIGHT, AXIS_WIDTH, AXIS_DENSE, AXIS_TILE = 0, 1, 2, 3, 4
 
 # every symbol the public headers declare
 EXPORTS = [
     "vaep_last_error", "vaep_version", "vaep_config_preset", "vaep_param_count",
     "vaep_param_info", "vaep_model_create", "vaep_model_destroy", "vaep_workspace_bytes",
     "vaep_decode_full", "vaep_decode_bands", "vaep_select_axis", "vaep_decode_sharded",
+    "vaep_sharded_workspace_bytes",
     "vaep_tiled_workspace_bytes", "vaep_decode_tiled",
     "vaep_groupnorm_merge",
     "vaep_step_conv", "vaep_step_groupnorm", "vaep_step_rmsnorm", "vaep_step_attention",
@@ -104,6 +105,7 @@ def _proto(lib):
     f("vaep_decode_tiled", I, P, P, I, I, I, I, I, I, P, P, SZ, P)
     f("vaep_decode_sharded", I, P, P, I, I, I, I, I, C.POINTER(C.c_int32), I, P, P, SZ, P,
       C.POINTER(VaepDecodeInfo))
+    f("vaep_sharded_workspace_bytes", I, P, I, I, I, I, I, C.POINTER(SZ))
     f("vaep_groupnorm_merge", I, I, I, P, P, P, P, P, P)
     f("vaep_profile_begin", I, P, I)
     f("vaep_profile_end", I, P, C.POINTER(VaepProfileEntry), I, C.POINTER(C.c_int))

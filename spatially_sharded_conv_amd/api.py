@@ -135,7 +135,7 @@ class Decoder:
         return rc, info
 
     def decode_sharded(self, latent, axis: str, n_shards: int, out, ws, starts=None, stream=None):
-        """axis: 'height', 'width' or 'auto'; starts: shard boundaries along the axis or None."""
+        """axis: 'height', 'width', 'tile' or 'auto'; starts: shard boundaries along the axis or None."""
         b, t, h, w = self._dims(latent)
         _dev(latent, self.dtype, "latent")
         _dev(out, torch.float32, "out")
@@ -150,6 +150,13 @@ class Decoder:
                                                   C.byref(info)))
         return rc, info
 
+
+    def sharded_workspace(self, batch, frames, latent_h, latent_w, n_shards, device="cuda") -> torch.Tensor:
+        """Workspace for every outcome of decode_sharded, the tile fallback included."""
+        n = C.c_size_t()
+        L.check(L.load().vaep_sharded_workspace_bytes(self._h, batch, frames, latent_h, latent_w, n_shards,
+                                                      C.byref(n)))
+        return torch.empty(n.value, dtype=torch.uint8, device=device)
 
     def tiled_workspace(self, batch, frames, latent_h, latent_w, tile, stride, device="cuda") -> torch.Tensor:
         n = C.c_size_t()
@@ -166,12 +173,12 @@ class Decoder:
                                                   ws.numel(), _stream(stream)))
 
 
-AXES = {"auto": L.AXIS_AUTO, "height": L.AXIS_HEIGHT, "width": L.AXIS_WIDTH}
-AXIS_NAMES = {L.AXIS_HEIGHT: "height", L.AXIS_WIDTH: "width", L.AXIS_DENSE: "dense"}
+AXES = {"auto": L.AXIS_AUTO, "height": L.AXIS_HEIGHT, "width": L.AXIS_WIDTH, "tile": L.AXIS_TILE}
+AXIS_NAMES = {L.AXIS_HEIGHT: "height", L.AXIS_WIDTH: "width", L.AXIS_DENSE: "dense", L.AXIS_TILE: "tile"}
 
 
 def select_axis(latent_h: int, latent_w: int, n_shards: int) -> str:
-    """The library's per-request axis policy: 'height', 'width' or 'dense'."""
+    """The library's per-request axis policy: 'height', 'width', 'tile' or 'dense'."""
     a = C.c_int32()
     L.check(L.load().vaep_select_axis(latent_h, latent_w, n_shards, C.byref(a)), allow_warning=False)
     return AXIS_NAMES[a.value]

@@ -959,14 +959,19 @@ int tile_plan(const vaep_model* m, int batch, int frames, int h, int w, int tile
 }
 
 // The per-request axis policy: the longer axis that gives every shard at least one latent
-// row (the kernel radius at latent resolution), width on ties; otherwise one dense band.
+// row (the kernel radius at latent resolution), width on ties; the tile decode when neither
+// axis covers the shards; one dense band for a single shard.
 int select_axis(int h, int w, int n) {
   if (n <= 1) return VAEP_AXIS_DENSE;
   const bool cover_h = h >= n, cover_w = w >= n;
   if (cover_w && (w >= h || !cover_h)) return VAEP_AXIS_WIDTH;
   if (cover_h) return VAEP_AXIS_HEIGHT;
-  return VAEP_AXIS_DENSE;
+  return VAEP_AXIS_TILE;
 }
+
+// Tile geometry of the tile strategy: latent tiles of 32 rows and columns every 24 (the
+// strategy page names the tile attributes but not their values).
+constexpr int kShardTile = 32, kShardTileStride = 24;
 
 
 // ------------------------------------------------------------------ step helpers
@@ -1179,11 +1184,14 @@ int vaep_tiled_workspace_bytes(const vaep_model* model, int batch, int frames, i
   return VAEP_OK;
 }
 
-int vaep_decode_tiled(vaep_model* model, const void* latent, int batch, int frames, int latent_h, int latent_w,
-                      int tile, int stride, void* out, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_latent_dims(model, batch, frames, latent_h, latent_w);
-  if (rc) return rc;
-  if (!latent || !out) return fail(VAEP_ERR_INVALID_ARG, "latent and out must be device pointers");
+// The tile decode (split, decode every tile alone, blend, gather); arguments validated by
+// the caller.  *launches receives the kernels enqueued, *tiles the tile count.
+int tiled_decode(vaep_model* model, const void* latent, int batch, int frames, int latent_h, int latent_w,
+                 int tile, int stride, void* out, void* ws, size_t ws_bytes, void* stream, int* launches,
+                 int* tiles) {
+  int rc;
+  int n_launch = 0;
+  vaep_decode_info sub{};
   TilePlan tp;
   if ((rc = tile_plan(model, batch, frames, latent_h, latent_w, tile, stride, &tp))) return rc;
   if (!ws || ws_bytes < tp.total)
@@ -1213,8 +1221,9 @@ int vaep_decode_tiled(vaep_model* model, const void* latent, int batch, int fram
       }
     const std::vector<int> rows(1, tile);
     rc = run_decode(model, lat, batch * tp.nfull, frames, tile, false, rows, VAEP_AXIS_DENSE, VAEP_OK, slots, dec_ws,
-                    tp.dec_bytes, stream, nullptr);
+                    tp.dec_bytes, stream, &sub);
     if (rc) return rc;
+    n_launch += tp.nfull + sub.n_launches;
   }
   for (int gi = 0; gi < tp.nr; ++gi)
     for (int gj = 0; gj < tp.nc; ++gj) {
@@ -1226,8 +1235,9 @@ int vaep_decode_tiled(vaep_model* model, const void* latent, int batch, int fram
       if (e != hipSuccess) return hip_fail(e, "latent tile crop");
       const std::vector<int> rows(1, th);
       rc = run_decode(model, lat, batch, frames, tw, false, rows, VAEP_AXIS_DENSE, VAEP_OK,
-                      slots + (long long)k * tp.slot_elems, dec_ws, tp.dec_bytes, stream, nullptr);
+                      slots + (long long)k * tp.slot_elems, dec_ws, tp.dec_bytes, stream, &sub);
       if (rc) return rc;
+      n_launch += 1 + sub.n_launches;
     }
   // merge: raster order, upper neighbour over the overlap rows, then left over the columns
   auto out_len = [&](int g, int len) { return std::min(tile, len - g * stride) * tp.up; };
@@ -1247,12 +1257,24 @@ int vaep_decode_tiled(vaep_model* model, const void* latent, int batch, int fram
                          std::min(std::min(lw, tw), tp.blend), 1, st);
       }
       if (e != hipSuccess) return hip_fail(e, "tile blend");
+      n_launch += (gi > 0) + (gj > 0);
     }
   hipError_t e = launch_tiles_gather(slots, tp.slot_elems, tp.planes, latent_h * tp.up, latent_w * tp.up,
                                      stride * tp.up, tile * tp.up, tp.nc, tp.full_r, tp.full_c, latent_h, latent_w,
                                      stride, tp.up, (float*)out, st);
   if (e != hipSuccess) return hip_fail(e, "tile gather");
+  if (launches) *launches = n_launch + 1;
+  if (tiles) *tiles = tp.nr * tp.nc;
   return VAEP_OK;
+}
+
+int vaep_decode_tiled(vaep_model* model, const void* latent, int batch, int frames, int latent_h, int latent_w,
+                      int tile, int stride, void* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_latent_dims(model, batch, frames, latent_h, latent_w);
+  if (rc) return rc;
+  if (!latent || !out) return fail(VAEP_ERR_INVALID_ARG, "latent and out must be device pointers");
+  return tiled_decode(model, latent, batch, frames, latent_h, latent_w, tile, stride, out, ws, ws_bytes, stream,
+                      nullptr, nullptr);
 }
 
 int vaep_select_axis(int latent_h, int latent_w, int n_shards, int32_t* axis_out) {
@@ -1263,6 +1285,17 @@ int vaep_select_axis(int latent_h, int latent_w, int n_shards, int32_t* axis_out
   return VAEP_OK;
 }
 
+int vaep_sharded_workspace_bytes(const vaep_model* model, int batch, int frames, int latent_h, int latent_w,
+                                 int n_shards, size_t* bytes_out) {
+  size_t bands = 0, tiles = 0;
+  int rc = vaep_workspace_bytes(model, batch, frames, latent_h, latent_w, n_shards, &bands);
+  if (rc) return rc;
+  if ((rc = vaep_tiled_workspace_bytes(model, batch, frames, latent_h, latent_w, kShardTile, kShardTileStride, &tiles)))
+    return rc;
+  *bytes_out = std::max(bands, tiles);
+  return VAEP_OK;
+}
+
 int vaep_decode_sharded(vaep_model* model, const void* latent, int batch, int frames, int latent_h,
                         int latent_w, int axis, const int32_t* starts, int n_shards, void* out, void* ws,
                         size_t ws_bytes, void* stream, vaep_decode_info* info) {
@@ -1270,38 +1303,60 @@ int vaep_decode_sharded(vaep_model* model, const void* latent, int batch, int fr
   if (rc) return rc;
   if (!latent || !out) return fail(VAEP_ERR_INVALID_ARG, "latent and out must be device pointers");
   if (n_shards < 1) return fail(VAEP_ERR_INVALID_ARG, "n_shards must be >= 1");
-  if (axis != VAEP_AXIS_AUTO && axis != VAEP_AXIS_HEIGHT && axis != VAEP_AXIS_WIDTH)
-    return fail(VAEP_ERR_INVALID_ARG, "axis %d is not VAEP_AXIS_AUTO, _HEIGHT or _WIDTH", axis);
-  if (axis == VAEP_AXIS_AUTO && starts)
-    return fail(VAEP_ERR_INVALID_ARG, "VAEP_AXIS_AUTO picks the axis per request: starts must be NULL");
+  if (axis != VAEP_AXIS_AUTO && axis != VAEP_AXIS_HEIGHT && axis != VAEP_AXIS_WIDTH && axis != VAEP_AXIS_TILE)
+    return fail(VAEP_ERR_INVALID_ARG, "axis %d is not VAEP_AXIS_AUTO, _HEIGHT, _WIDTH or _TILE", axis);
+  if ((axis == VAEP_AXIS_AUTO || axis == VAEP_AXIS_TILE) && starts)
+    return fail(VAEP_ERR_INVALID_ARG, "VAEP_AXIS_AUTO and VAEP_AXIS_TILE take no shard table: starts must be NULL");
   int status = VAEP_OK;
   int chosen = axis;
   const char* why = nullptr;
   if (axis == VAEP_AXIS_AUTO) {
     chosen = select_axis(latent_h, latent_w, n_shards);
-    if (chosen != VAEP_AXIS_DENSE && n_shards > kMaxBands) chosen = VAEP_AXIS_DENSE;
+    if ((chosen == VAEP_AXIS_HEIGHT || chosen == VAEP_AXIS_WIDTH) && n_shards > kMaxBands) chosen = VAEP_AXIS_TILE;
   }
-  const int len = chosen == VAEP_AXIS_WIDTH ? latent_w : latent_h;
   std::vector<int> rows;
-  if (chosen != VAEP_AXIS_DENSE && starts) {
-    if ((rc = table_rows(starts, n_shards, len, chosen == VAEP_AXIS_WIDTH ? "column" : "row", rows))) return rc;
-  } else if (chosen != VAEP_AXIS_DENSE) {
-    if (len < n_shards) why = "the axis is shorter than the shard count";
-    else rows = even_rows(len, n_shards);
+  if (chosen == VAEP_AXIS_HEIGHT || chosen == VAEP_AXIS_WIDTH) {
+    const int len = chosen == VAEP_AXIS_WIDTH ? latent_w : latent_h;
+    if (starts) {
+      if ((rc = table_rows(starts, n_shards, len, chosen == VAEP_AXIS_WIDTH ? "column" : "row", rows))) return rc;
+    } else if (len < n_shards) {
+      why = "the axis is shorter than the shard count";
+    } else {
+      rows = even_rows(len, n_shards);
+    }
+    if (!why && n_shards > kMaxBands) why = "the shard count exceeds the band limit";
+    if (why) {            // an explicit axis that cannot be honoured: warn and use the tile decode
+      chosen = VAEP_AXIS_TILE;
+      status = VAEP_WARN_FELL_BACK;
+    }
   }
-  if (chosen != VAEP_AXIS_DENSE && !why && n_shards > kMaxBands) why = "the shard count exceeds the band limit";
-  if (why) {              // an explicit axis that cannot be honoured: warn and decode dense
-    chosen = VAEP_AXIS_DENSE;
-    status = VAEP_WARN_FELL_BACK;
+  if (chosen == VAEP_AXIS_TILE) {
+    TilePlan tp;
+    if ((rc = tile_plan(model, batch, frames, latent_h, latent_w, kShardTile, kShardTileStride, &tp))) return rc;
+    if (!ws || ws_bytes < tp.total)
+      return fail(VAEP_ERR_WORKSPACE, "the tile decode needs a workspace of %zu bytes (vaep_sharded_workspace_bytes), "
+                                      "%zu given", tp.total, ws ? ws_bytes : (size_t)0);
+    int launches = 0, tiles = 0;
+    if ((rc = tiled_decode(model, latent, batch, frames, latent_h, latent_w, kShardTile, kShardTileStride, out, ws,
+                           ws_bytes, stream, &launches, &tiles)))
+      return rc;
+    if (info) {
+      info->bands_used = tiles;
+      info->fell_back = axis != VAEP_AXIS_TILE;
+      info->n_launches = launches;
+      info->axis = VAEP_AXIS_TILE;
+      info->workspace_bytes = tp.total;
+    }
+  } else {
+    if (chosen == VAEP_AXIS_DENSE) rows.assign(1, latent_h);
+    const bool tr = chosen == VAEP_AXIS_WIDTH;
+    rc = run_decode(model, latent, batch, frames, tr ? latent_h : latent_w, tr, rows, chosen, status, out, ws,
+                    ws_bytes, stream, info);
+    if (rc) return rc;
+    if (info) info->fell_back = 0;
   }
-  if (chosen == VAEP_AXIS_DENSE) rows.assign(1, latent_h);
-  const bool tr = chosen == VAEP_AXIS_WIDTH;
-  rc = run_decode(model, latent, batch, frames, tr ? latent_h : latent_w, tr, rows, chosen, status, out, ws,
-                  ws_bytes, stream, info);
-  if (rc) return rc;
-  if (info) info->fell_back = chosen == VAEP_AXIS_DENSE && n_shards > 1;
   if (status == VAEP_WARN_FELL_BACK)
-    fail(VAEP_WARN_FELL_BACK, "%d shards along the %s: %s; decoded as one dense band", n_shards,
+    fail(VAEP_WARN_FELL_BACK, "%d shards along the %s: %s; decoded with the tile strategy", n_shards,
          axis == VAEP_AXIS_WIDTH ? "width" : "height", why);
   return status;
 }

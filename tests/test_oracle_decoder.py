@@ -10,12 +10,12 @@
 * output shapes of every preset;
 * the per-request ``auto`` axis policy (strategy page, Wan spatial-shard
   notes: the longer axis that covers every shard, width winning ties, else the
-  fallback).
+  tile decode).
 """
 import pytest
 import torch
 
-from oracle import choose_axis, decode_auto, decode_bands, decode_full, even_starts, Precision
+from oracle import choose_axis, decode_auto, decode_bands, decode_full, decode_tiled, even_starts, Precision
 from synth import make_latent, make_params, preset
 
 
@@ -156,7 +156,7 @@ def test_width_bands_are_not_row_bands():
     (2, 3, 3, "width"),
     (2, 5, 3, "width"),
     (5, 2, 3, "height"),
-    (2, 2, 3, "dense"),        # neither axis covers the shards
+    (2, 2, 3, "tile"),         # neither axis covers the shards: the tile decode
     (8, 8, 1, "dense"),        # one shard is the dense decode
     (8, 8, 8, "width"),
     (8, 7, 8, "height"),
@@ -184,3 +184,14 @@ def test_decode_auto_cfg1():
     zt = z.transpose(-1, -2).contiguous()   # 5 x 8
     y, axis = decode_auto(CFG1, p, zt, 3)
     assert axis == "width" and _rel(y, decode_full(CFG1, p, zt)) <= 1e-6
+
+
+def test_decode_auto_uses_tiles_when_no_axis_covers():
+    # strategy page: "If neither axis can cover the group, auto mode uses tile decode"
+    cfg = CFG1.with_size(latent_h=40, latent_w=3, band_starts=(0, 40))
+    p = make_params(cfg, affine="random")
+    z = make_latent(cfg)
+    y, axis = decode_auto(cfg, p, z, 41)
+    assert axis == "tile"
+    assert torch.equal(y, decode_tiled(cfg, p, z, 32, 24))
+    assert _rel(y, decode_full(cfg, p, z)) > 1e-3          # tiles are not the full decode
