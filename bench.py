@@ -10,13 +10,23 @@ Prints ONE JSON line.  `value` is decoded Mpixel/s from a plain timed region
 of K decodes brackets every kernel launch with HIP events on the decode stream
 (vaep_profile_begin/_end) to give each kernel's average duration, from which
 the roofline fractions are computed with algorithmic flops / bytes per launch.
-The CPU baseline times the oracle on a bounded sample of the same decoder.
-`shard_axes` times the same latent decoded on column bands of the same sizes
-(vaep_decode_sharded, width axis) and with the per-request `auto` axis policy;
-`tiled_baseline` times the overlap-blending tile decode (vaep_decode_tiled) and
-reports its distance from the band decode and its row-seam diagnostic.
+Each timed decode is also bracketed by its own pair of events, which gives
+the median per-decode time beside the mean.  The CPU baseline times the
+oracle's decode of the same workload (the 1024^2 preset itself) on the host
+cores.  `shard_axes` times the same latent decoded on column bands of the same
+sizes (vaep_decode_sharded, width axis) and with the per-request `auto` axis
+policy; `tiled_baseline` times the overlap-blending tile decode
+(vaep_decode_tiled) and reports its distance from the band decode and its
+row-seam diagnostic.  `other_configs` times the batch-4 1024^2 preset and the
+video preset in the same run (per-decode time, Mpixel/s, conv and norm
+fractions).
 
-usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+`--only-bands` runs nothing but the band decodes of the chosen preset (no
+width, auto, tiled or other-preset decodes, no CPU baseline): the form used
+under rocprofv3, so that per-kernel averages describe the band decode alone.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--only-bands]
+                       [--no-cpu-baseline] [--no-other-configs]
 """
 import argparse
 import json
@@ -39,8 +49,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=3, help="preset id (3 = the 1024^2 headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-latent", type=int, default=72,
-                    help="latent side of the oracle's bounded sample")
+    ap.add_argument("--no-other-configs", action="store_true")
+    ap.add_argument("--only-bands", action="store_true",
+                    help="band decodes of --config only (for profiler runs)")
+    ap.add_argument("--cpu-sample-latent", type=int, default=0,
+                    help="latent side of a smaller oracle sample (0: the preset's own latent)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="only run a device-to-device copy of MB MiB (reference dispatch for HBM counters)")
     return ap.parse_args()
@@ -133,21 +146,119 @@ def measured_traffic():
         return None
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cfg_id, side):
-    """The oracle as it stands, on a bounded sample: the same decoder on a side x side latent."""
+    """The oracle as it stands, timed on the host cores: one full decode of the preset's own
+    latent (side 0), or of a side x side latent of the same decoder."""
     import torch
     from oracle import Precision, decode_full
     from synth import make_latent, make_params, preset
-    cfg = preset(cfg_id).with_size(latent_h=side, latent_w=side, band_starts=(0, side))
+    cfg = preset(cfg_id)
+    if side:
+        cfg = cfg.with_size(latent_h=side, latent_w=side, band_starts=(0, side))
     params = make_params(cfg)
     z = make_latent(cfg)
     t0 = time.perf_counter()
     y = decode_full(cfg, params, z, Precision("f32"))
     dt = time.perf_counter() - t0
     px = y.shape[0] * y.shape[-1] * y.shape[-2] * (y.shape[2] if y.dim() == 5 else 1)
+    what = "the workload itself" if not side else f"a seeded {side}x{side} latent of the same decoder"
     return {"value": px / dt / 1e6, "unit": "Mpixel/s", "cores": torch.get_num_threads(), "kind": "oracle",
-            "sample": f"one full decode of the same decoder and weights on a seeded {side}x{side} latent "
-                      f"({y.shape[-2]}x{y.shape[-1]} output, {px} px) in {dt:.1f} s, fp64 arithmetic"}
+            "sample": f"one full decode by the oracle of {what} ({cfg.name}, latent "
+                      f"{cfg.z_channels}x{cfg.latent_h}x{cfg.latent_w}, output {list(y.shape)}, {px} px) "
+                      f"in {dt:.1f} s, float32 storage and float64 arithmetic",
+            "seconds": round(dt, 2), "hardware_concurrency": os.cpu_count(),
+            "torch_threads": torch.get_num_threads(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "cpu_model": _cpu_model()}
+
+
+def build_decoder(cfg_id):
+    import torch
+    import spatially_sharded_conv_amd as vaep
+    from synth import make_latent, make_params, preset
+    cfg = preset(cfg_id)
+    params = make_params(cfg)
+    lc = vaep.make_config(cfg.family, cfg.dtype, cfg.z_channels, cfg.stage_channels,
+                          cfg.resnets_per_stage, cfg.norm_groups, cfg.temporal_up_stages, cfg.eps)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dev = [params[n].to(tdt).cuda() for n, _ in vaep.param_info(lc)]
+    dec = vaep.Decoder(lc, dev)
+    del dev, params
+    latent = make_latent(cfg).to(tdt).cuda()
+    out = torch.empty(cfg.output_shape(), dtype=torch.float32, device="cuda")
+    ws = dec.workspace(cfg.batch, cfg.frames, cfg.latent_h, cfg.latent_w, len(cfg.band_starts) - 1)
+    return cfg, dec, latent, out, ws
+
+
+def timed_decodes(run, steps, warmup, stream):
+    """W untimed calls, then K timed calls between stream synchronisations; each call also
+    bracketed by its own events.  Returns (mean ms over the region, median ms per call, last result)."""
+    import torch
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    res = None
+    for k in range(steps):
+        res = run()
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(steps))
+    mean = ev[0].elapsed_time(ev[steps]) / steps
+    med = per[steps // 2] if steps % 2 else 0.5 * (per[steps // 2 - 1] + per[steps // 2])
+    return mean, med, res
+
+
+def profiled_decodes(dec, run, steps, launches, stream):
+    """K band decodes with every kernel launch bracketed by HIP events on the decode stream."""
+    import torch
+    import spatially_sharded_conv_amd as vaep
+    vaep.profile_begin(dec, max_launches=steps * (launches + 8))
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        run()
+    b.record(stream)
+    torch.cuda.synchronize()
+    recs = vaep.profile_end(dec)
+    return recs, a.elapsed_time(b) / steps
+
+
+def other_config(cfg_id, steps, warmup, stream):
+    """Per-decode time, throughput and the conv / norm fractions of another preset's band decode."""
+    cfg, dec, latent, out, ws = build_decoder(cfg_id)
+    starts = cfg.band_starts
+    pixels = out.numel() // 3
+    run = lambda: dec.decode_bands(latent, starts, out, ws, stream)
+    mean, med, (rc, info) = timed_decodes(run, steps, warmup, stream)
+    recs, _ = profiled_decodes(dec, run, steps, info.n_launches, stream)
+    cls = summarise(recs, steps)
+    agg = aggregates(recs, steps)
+    nk = "groupnorm" if "groupnorm" in cls else "rmsnorm"
+    norm = cls.get(nk, {"gbs": 0.0, "ms_per_step": 0.0})
+    dec.close()
+    return {"workload": f"{cfg.name}: band decode of a seeded {cfg.z_channels}x{cfg.latent_h}x{cfg.latent_w} latent "
+                        f"(batch {cfg.batch}{', frames ' + str(cfg.frames) if cfg.is_video else ''}) on "
+                        f"{len(starts) - 1} latent row bands {[b - a for a, b in zip(starts, starts[1:])]}, "
+                        f"output {list(out.shape)}",
+            "ms_per_step": round(mean, 4), "ms_per_step_median": round(med, 4),
+            "mpixel_s": round(pixels / (mean * 1e-3) / 1e6, 3),
+            "conv_mfma_util": agg["conv_mfma_util"],
+            "norm": {"kernel": nk, "gbs": round(norm["gbs"], 1), "frac": round(norm["gbs"] / PEAK_HBM_GBS, 4),
+                     "ms_per_step": round(norm["ms_per_step"], 4)},
+            "breakdown_ms": {k: round(v["ms_per_step"], 4) for k, v in sorted(cls.items())}}
 
 
 def main():
@@ -160,9 +271,6 @@ def main():
         sys.exit(2)
 
     import torch
-    import spatially_sharded_conv_amd as vaep
-    from synth import make_latent, make_params, preset
-
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         n = args.calibrate_copy << 20
@@ -173,50 +281,19 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
         return
-    cfg = preset(args.config)
-    params = make_params(cfg)
-    lc = vaep.make_config(cfg.family, cfg.dtype, cfg.z_channels, cfg.stage_channels,
-                          cfg.resnets_per_stage, cfg.norm_groups, cfg.temporal_up_stages, cfg.eps)
-    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-    dev = [params[n].to(tdt).cuda() for n, _ in vaep.param_info(lc)]
-    dec = vaep.Decoder(lc, dev)
-    del dev
-    latent = make_latent(cfg).to(tdt).cuda()
+    cfg, dec, latent, out, ws = build_decoder(args.config)
     starts = cfg.band_starts
     nb = len(starts) - 1
-    out = torch.empty(cfg.output_shape(), dtype=torch.float32, device="cuda")
-    ws = dec.workspace(cfg.batch, cfg.frames, cfg.latent_h, cfg.latent_w, nb)
     stream = torch.cuda.current_stream()
     pixels = out.numel() // 3
 
-    for _ in range(args.warmup):
-        dec.decode_bands(latent, starts, out, ws, stream)
-    torch.cuda.synchronize()
-
-    # plain timed region
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for _ in range(args.steps):
-        rc, info = dec.decode_bands(latent, starts, out, ws, stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_end) / args.steps
+    # plain timed region (value), with per-decode events for the median
+    run = lambda: dec.decode_bands(latent, starts, out, ws, stream)
+    ms, ms_med, (rc, info) = timed_decodes(run, args.steps, args.warmup, stream)
     value = pixels / (ms * 1e-3) / 1e6
 
     # event-bracketed region: per-launch kernel durations on the decode stream
-    vaep.profile_begin(dec, max_launches=args.steps * (info.n_launches + 8))
-    torch.cuda.synchronize()
-    p_start = torch.cuda.Event(enable_timing=True)
-    p_end = torch.cuda.Event(enable_timing=True)
-    p_start.record(stream)
-    for _ in range(args.steps):
-        dec.decode_bands(latent, starts, out, ws, stream)
-    p_end.record(stream)
-    torch.cuda.synchronize()
-    recs = vaep.profile_end(dec)
-    ms_prof = p_start.elapsed_time(p_end) / args.steps
+    recs, ms_prof = profiled_decodes(dec, run, args.steps, info.n_launches, stream)
     cls = summarise(recs, args.steps)
     conv = cls.get("conv_wide_3x3", {"tflops": 0.0, "flops": 0.0, "launches": 1, "avg_launch_ms": 0.0})
     gn = cls.get("groupnorm") or cls.get("rmsnorm") or {"gbs": 0.0}
@@ -234,48 +311,31 @@ def main():
         "avg_launch_ms": round(conv["avg_launch_ms"], 4),
         "flops_per_launch": conv["flops"] / max(1, conv["launches"]),
     }
-    # the same workload sharded along the width (the row bands' sizes laid across the
-    # columns when they fit) and with the per-request axis policy
-    axes = {}
-    sizes = [b - a for a, b in zip(starts, starts[1:])]
-    col = [0]
-    for v in sizes:
-        col.append(col[-1] + v)
-    for name, st in (("width", tuple(col) if col[-1] == cfg.latent_w else None), ("auto", None)):
-        for _ in range(args.warmup):
-            dec.decode_sharded(latent, name, nb, out, ws, st, stream)
-        torch.cuda.synchronize()
-        a_start = torch.cuda.Event(enable_timing=True)
-        a_end = torch.cuda.Event(enable_timing=True)
-        a_start.record(stream)
-        for _ in range(args.steps):
-            _, ainfo = dec.decode_sharded(latent, name, nb, out, ws, st, stream)
-        a_end.record(stream)
-        torch.cuda.synchronize()
-        a_ms = a_start.elapsed_time(a_end) / args.steps
-        axes[name] = {"axis": {1: "height", 2: "width", 3: "dense"}[ainfo.axis],
-                      "bands": list(st) if st else ainfo.bands_used,
-                      "ms_per_step": round(a_ms, 4), "mpixel_s": round(pixels / (a_ms * 1e-3) / 1e6, 3)}
-    # the overlap-blending tile decode the sharded decode replaces (latent tiles of 32 with
-    # stride 24: 256-pixel tiles every 192 output pixels at 8x upsampling), same latent
-    tiled = None
-    if not cfg.is_video:
+    axes, tiled = {}, None
+    if not args.only_bands:
+        # the same workload sharded along the width (the row bands' sizes laid across the
+        # columns when they fit) and with the per-request axis policy
+        sizes = [b - a for a, b in zip(starts, starts[1:])]
+        col = [0]
+        for v in sizes:
+            col.append(col[-1] + v)
+        for name, st in (("width", tuple(col) if col[-1] == cfg.latent_w else None), ("auto", None)):
+            a_ms, a_med, (_, ainfo) = timed_decodes(
+                lambda: dec.decode_sharded(latent, name, nb, out, ws, st, stream), args.steps, args.warmup, stream)
+            axes[name] = {"axis": {1: "height", 2: "width", 3: "dense", 4: "tile"}.get(ainfo.axis, ainfo.axis),
+                          "bands": list(st) if st else ainfo.bands_used,
+                          "ms_per_step": round(a_ms, 4), "mpixel_s": round(pixels / (a_ms * 1e-3) / 1e6, 3)}
+    if not args.only_bands and not cfg.is_video:
+        # the overlap-blending tile decode the sharded decode replaces (latent tiles of 32 with
+        # stride 24: 256-pixel tiles every 192 output pixels at 8x upsampling), same latent
         tile, tstride = 32, 24
         band_out = torch.empty_like(out)
         dec.decode_bands(latent, starts, band_out, ws, stream)
         tws = dec.tiled_workspace(cfg.batch, cfg.frames, cfg.latent_h, cfg.latent_w, tile, tstride)
         tout = torch.empty_like(out)
-        for _ in range(args.warmup):
-            dec.decode_tiled(latent, tile, tstride, tout, tws, stream)
-        torch.cuda.synchronize()
-        t_a = torch.cuda.Event(enable_timing=True)
-        t_b = torch.cuda.Event(enable_timing=True)
-        t_a.record(stream)
-        for _ in range(args.steps):
-            dec.decode_tiled(latent, tile, tstride, tout, tws, stream)
-        t_b.record(stream)
-        torch.cuda.synchronize()
-        t_ms = t_a.elapsed_time(t_b) / args.steps
+        t_ms, t_med, _ = timed_decodes(lambda: dec.decode_tiled(latent, tile, tstride, tout, tws, stream),
+                                       args.steps, args.warmup, stream)
+
         # seam diagnostic (validation page): mean absolute jump between adjacent rows of the
         # per-pixel RGB mean, 0-255 units; at the tiles' row boundaries and over all rows
         def row_jumps(y):
@@ -292,6 +352,15 @@ def main():
                  "row_jump_at_tile_rows": round(jt[bnd].mean().item(), 4),
                  "row_jump_at_those_rows_band_decode": round(jb[bnd].mean().item(), 4),
                  "row_jump_all_rows": round(jt.mean().item(), 4)}
+    dec.close()
+    del ws, out, latent
+    torch.cuda.empty_cache()
+    others = {}
+    if not args.only_bands and not args.no_other_configs:
+        for cid in (4, 5):
+            if cid != args.config:
+                others[f"config{cid}"] = other_config(cid, max(5, min(args.steps, 8)), max(1, args.warmup), stream)
+                torch.cuda.empty_cache()
     norm_key = "groupnorm" if "groupnorm" in cls else "rmsnorm"
     line = {
         "metric": METRIC,
@@ -301,6 +370,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(ms_med, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -310,7 +380,7 @@ def main():
             "workload": f"{cfg.name}: band decode of a seeded {cfg.z_channels}x{cfg.latent_h}x{cfg.latent_w} "
                         f"latent (batch {cfg.batch}{', frames ' + str(cfg.frames) if cfg.is_video else ''}) "
                         f"on {nb} latent row bands {[b - a for a, b in zip(starts, starts[1:])]}, "
-                        f"output {list(out.shape)}",
+                        f"output {list(cfg.output_shape())}",
             "batch": cfg.batch, "bands": list(starts), "random_init": True,
             "storage": "bf16 weights/latent/matrix operands, fp32 conv outputs and statistics",
         },
@@ -328,11 +398,11 @@ def main():
         "shard_axes": axes,
         "tiled_baseline": tiled,
         **aggregates(recs, args.steps),
+        "other_configs": others,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample_latent if not cfg.is_video else 8)
-    dec.close()
+    if not args.no_cpu_baseline and not args.only_bands:
+        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample_latent)
     print(json.dumps(line), flush=True)
 
 
