@@ -176,6 +176,21 @@ int vaep_decode_bands(vaep_model* model, const void* latent, int batch, int fram
                       void* out, void* ws, size_t ws_bytes, void* stream,
                       vaep_decode_info* info);
 
+/* Band decode that allocates nothing, for callers that cannot call hipMalloc or hold a
+ * workspace of their own (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, kernels, results and errors as
+ * vaep_decode_bands, without ws / ws_bytes: the workspace is a static device array of
+ * vaep_noalloc_scratch_bytes() bytes (64 MiB) that every GPU the library runs on holds
+ * until the process ends.  A decode whose workspace (vaep_workspace_bytes) exceeds it is
+ * rejected with VAEP_ERR_WORKSPACE before anything is enqueued.  The array is shared by
+ * every call on a GPU: calls that overlap on one GPU (other streams, other threads) race,
+ * so serialise them.  The first call on a device looks up the array's device address
+ * (hipGetSymbolAddress) and keeps it; no call allocates or frees device memory. */
+size_t vaep_noalloc_scratch_bytes(void);
+int vaep_decode_bands_noalloc(vaep_model* model, const void* latent, int batch, int frames,
+                              int latent_h, int latent_w, const int32_t* row_starts,
+                              int n_bands, void* out, void* stream, vaep_decode_info* info);
+
 /* Axis policy of a sharded decode (the distributed-VAE strategy page, "Strategy
  * Selection Contract" and the Wan spatial-shard notes: `auto` takes the longer axis
  * that can cover every shard, width winning ties, and uses the tile decode when neither

@@ -32,7 +32,7 @@ EXPORTS = [
     "vaep_last_error", "vaep_version", "vaep_config_preset", "vaep_param_count",
     "vaep_param_info", "vaep_model_create", "vaep_model_destroy", "vaep_workspace_bytes",
     "vaep_decode_full", "vaep_decode_bands", "vaep_select_axis", "vaep_decode_sharded",
-    "vaep_sharded_workspace_bytes",
+    "vaep_sharded_workspace_bytes", "vaep_noalloc_scratch_bytes", "vaep_decode_bands_noalloc",
     "vaep_tiled_workspace_bytes", "vaep_decode_tiled",
     "vaep_groupnorm_merge",
     "vaep_step_conv", "vaep_step_groupnorm", "vaep_step_rmsnorm", "vaep_step_attention",
@@ -101,6 +101,9 @@ def _proto(lib):
     f("vaep_decode_bands", I, P, P, I, I, I, I, C.POINTER(C.c_int32), I, P, P, SZ, P,
       C.POINTER(VaepDecodeInfo))
     f("vaep_select_axis", I, I, I, I, C.POINTER(C.c_int32))
+    f("vaep_noalloc_scratch_bytes", SZ)
+    f("vaep_decode_bands_noalloc", I, P, P, I, I, I, I, C.POINTER(C.c_int32), I, P, P,
+      C.POINTER(VaepDecodeInfo))
     f("vaep_tiled_workspace_bytes", I, P, I, I, I, I, I, I, C.POINTER(SZ))
     f("vaep_decode_tiled", I, P, P, I, I, I, I, I, I, P, P, SZ, P)
     f("vaep_decode_sharded", I, P, P, I, I, I, I, I, C.POINTER(C.c_int32), I, P, P, SZ, P,

@@ -134,6 +134,17 @@ class Decoder:
                                                 _stream(stream), C.byref(info)))
         return rc, info
 
+    def decode_bands_noalloc(self, latent, row_starts, out, stream=None):
+        """decode_bands with the library's static scratch as workspace (allocates nothing)."""
+        b, t, h, w = self._dims(latent)
+        _dev(latent, self.dtype, "latent")
+        _dev(out, torch.float32, "out")
+        info = L.VaepDecodeInfo()
+        rc = L.check(L.load().vaep_decode_bands_noalloc(self._h, _p(latent), b, t, h, w, _starts(row_starts),
+                                                        len(row_starts) - 1, _p(out), _stream(stream),
+                                                        C.byref(info)))
+        return rc, info
+
     def decode_sharded(self, latent, axis: str, n_shards: int, out, ws, starts=None, stream=None):
         """axis: 'height', 'width', 'tile' or 'auto'; starts: shard boundaries along the axis or None."""
         b, t, h, w = self._dims(latent)

@@ -1015,6 +1015,10 @@ int norm_channels_ok(int dtype, int c) {
 
 }  // namespace
 
+namespace vaep {
+int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+}  // namespace vaep
+
 extern "C" {
 
 const char* vaep_last_error(void) { return g_err.c_str(); }

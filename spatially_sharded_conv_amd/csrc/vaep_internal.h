@@ -258,4 +258,7 @@ hipError_t launch_tiles_gather(const float* slots, long long slot_elems, long lo
 
 inline size_t dtype_bytes(int dtype) { return dtype == VAEP_DTYPE_F32 ? 4 : 2; }
 
+// Set the thread's vaep_last_error() text and return `code`.
+int set_error(int code, const char* msg);
+
 }  // namespace vaep
