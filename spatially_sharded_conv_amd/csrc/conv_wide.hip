@@ -75,15 +75,6 @@ __device__ __forceinline__ void dma16(bool first, u32x4_t r, unsigned lds, unsig
                     "{m0}"(__builtin_amdgcn_readfirstlane(lds))
                  : "memory");
 }
-// L2 prefetch: 4 bytes per lane (one per 128-byte line) into a scratch LDS word per lane;
-// the data is never read.  soff may just have been written by a readfirstlane.
-__device__ __forceinline__ void prefetch4(u32x4_t r, unsigned lds, unsigned voff, unsigned soff) {
-  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff)),
-                  "{m0}"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory");
-}
-
 __device__ __forceinline__ unsigned lds_addr(const unsigned short* p) {
   return (unsigned)reinterpret_cast<unsigned long long>((const lds_u16*)p);
 }
@@ -226,15 +217,14 @@ struct LoadOrder {
   }
 };
 
-template <int KT, int KS, bool SUB, int PARTS, int MODE, int BM, int BN, int NW>
+// X2: the conv reads a second operand (a.x2, a folded 1x1 shortcut) after its taps.
+template <int KT, int KS, bool SUB, int PARTS, int MODE, int BM, int BN, int NW, bool X2>
 __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
+  static_assert(!X2 || (!SUB && MODE == kModeBand), "a second operand folds into plain band convs only");
   // NW waves: 2 along the output channels x NW/2 along the pixels.  With 8 waves two
   // share each SIMD, so one wave's loads, LDS reads and barrier waits hide behind the
   // other's MFMAs.
   constexpr int S = (BM == 128 && BN == 256) ? 3 : 2;   // LDS stages
-  // L2 prefetch of the step PFD ahead needs 256 bytes of LDS beyond the stages (its landing
-  // words); the 128 x 512 tile fills the 160 KiB with its two stages and goes without.
-  constexpr bool PF = S * (BM + BN) * 64 * 2 + 256 <= 160 * 1024;
   constexpr int TAPS = SUB ? 4 : KT * KS * KS;
   static_assert(SUB ? PARTS == 2 : PARTS == 1, "sub-pixel convs run a bf16 and an fp8 part");
   constexpr int WP = PARTS;                   // weight parts per tap in the packed rows
@@ -246,14 +236,9 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   typedef LoadOrder<NA, NB> LO;
   static_assert(LO::NL >= 4 && LO::count(0) >= 1 && MI * NJ >= 3, "loads per quarter step");
   constexpr int PH = SUB ? 4 : 1;
-  // S operand stages: A (BM x 64) then B (BN x 64) per stage, then the prefetch landing
-  // words (never read); the epilogue reuses the space
+  // S operand stages: A (BM x 64) then B (BN x 64) per stage; the epilogue reuses the space
   constexpr int kStageElems = S * (BM + BN) * 64;
-  __shared__ __attribute__((aligned(1024))) unsigned short smem[kStageElems + (PF ? 128 : 0)];
-  const unsigned short* sPF = smem + kStageElems;
-  constexpr int PFD = 2;                       // prefetch target: PFD steps past the step issued
-  constexpr int PFN = PF ? 2 : 0;              // prefetch loads per issued step
-  constexpr int NG = LO::NL + PFN;             // loads per thread per issued step
+  __shared__ __attribute__((aligned(1024))) unsigned short smem[kStageElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -281,8 +266,9 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   // pixel itself -- a 1x1 conv folded into this one (a resnet's shortcut): its weights
   // follow the taps' in every packed row
   const int nsteps1 = TAPS * PARTS * csteps;
-  const int nsteps = nsteps1 + (a.cin2 >> 6);
-  const int kw = TAPS * WP * C + a.cin2;               // packed weight row length (elements)
+  const int cin2 = X2 ? a.cin2 : 0;
+  const int nsteps = nsteps1 + (cin2 >> 6);
+  const int kw = TAPS * WP * C + cin2;                 // packed weight row length (elements)
 
   // Input rows the tile can read: from its first pixel's row - 1 (KT - 1 frames back) to
   // its last pixel's row + 1; halo slots cover the rows beyond the band.
@@ -351,33 +337,6 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
     pmask[j] = ok ? m : 0;
   }
   unsigned bvo[NB];
-  // prefetch roles: weight row (wave*64 + lane) % BM, tile pixel wave*64 + lane
-  const unsigned pf_avo = (unsigned)((long long)(co0 + (wave * 64 + lane) % BM) * kw * 2);
-  const int pf_px = (wave * 64 + lane) % BN;
-  unsigned pf_base;
-  int pf_mask;
-  {
-    const long long p = (long long)tile * BN + pf_px;
-    const bool ok = p < m_band;
-    const long long q = ok ? p : 0;
-    const int n = (int)(q / plane);
-    const int rem = (int)(q - (long long)n * plane);
-    const int r = rem / W;
-    const int c = rem - r * W;
-    const long long slot = (long long)n * (rows_in + 2) + r + 1;
-    pf_base = (unsigned)(((slot - first_slot) * W + c) * XC * 2);
-    const int g = g0 + r;
-    int m = 2 | 16;
-    m |= (g - 1 >= 0) ? 1 : 0;
-    m |= (g + 1 < H) ? 4 : 0;
-    m |= (c - 1 >= 0) ? 8 : 0;
-    m |= (c + 1 < W) ? 32 : 0;
-    const int t = n % a.in.frames;
-#pragma unroll
-    for (int dt = 0; dt < KT; ++dt) m |= (t + dt - (KT - 1) >= 0) ? (64 << dt) : 0;
-    pf_mask = ok ? m : 0;
-  }
-
   // acc[i][j][v]: channel co0 + wco + 32i + 8(v/4) + 4(lane/32) + v%4, pixel
   // tile*BN + wpx + 32j + lane%32 (source grid for sub-pixel convs).
   // fp8 step scales (E8M0 in every byte): A's removes the weights' and the operand's
@@ -452,8 +411,6 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
     need = (1 << (sy + 1)) | (8 << (sx + 1)) | (64 << dt);                                     \
     delta = (int)((((long long)(dt - (KT - 1)) * (rows_in + 2) + sy) * W + sx) * XC * 2);      \
   }
-  // prefetch cursor: step issued + PFD (held at the last step of the taps)
-  int ptap = 0, ppart = 0, pc = 0, pstep = 0;
 #define VAEP_ADVANCE(tp, pt, cc)                                                               \
   if (++tp == TAPS) {                                                                          \
     tp = 0;                                                                                    \
@@ -462,22 +419,16 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
       cc += 64;                                                                                \
     }                                                                                          \
   }
-#pragma unroll
-  for (int i = 0; i < PFD; ++i)
-    if (pstep + 1 < nsteps1) {
-      ++pstep;
-      VAEP_ADVANCE(ptap, ppart, pc);
-    }
 #define VAEP_SA(st) (smem + (st) * (BM * 64))
 #define VAEP_SB(st) (smem + S * (BM * 64) + (st) * (BN * 64))
 // The loads of one step go out in four parts, one before each group of MFMAs of the
 // current step, so that the wave never waits on a full load queue with the matrix cores
 // idle.  One load of a step: quarter q (0..3), index t within the quarter (LoadOrder).
-// Quarter 0's first load also forms the tap's offsets; quarter 3's last load adds the
-// prefetch and advances the step counters.
+// Quarter 0's first load also forms the tap's offsets; quarter 3's last load advances the
+// step counters.
 #define VAEP_ISSUE_ONE(st, q, t)                                                               \
   {                                                                                            \
-    const bool ext_ = !SUB && issued >= nsteps1;   /* a step of the second operand */         \
+    const bool ext_ = X2 && issued >= nsteps1;     /* a step of the second operand */         \
     if ((q) == 0 && (t) == 0) {                                                                \
       if (ext_) {                                                                              \
         _Pragma("unroll") for (int j = 0; j < NB; ++j) bvo[j] = pmask[j] ? pbase2[j] : kPadOffset; \
@@ -499,18 +450,8 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
       dma16(LO::first((q), (t)), ext_ ? x2rs : xrs, lds_addr(VAEP_SB(st)) + wrow + j * kRowStep, bvo[j], bso); \
     }                                                                                          \
     if ((q) == 3 && (t) == LO::count(3) - 1) {                                                 \
-      if constexpr (PF) {                                                                      \
-        VAEP_TAP_GEO(ptap, need, delta);                                                       \
-        const unsigned pbv = ((pf_mask & need) == need) ? (unsigned)((int)pf_base + delta) : kPadOffset; \
-        prefetch4(wrs, lds_addr(sPF), pf_avo, ((ptap * WP + wpart(PARTS, ppart)) * C + pc) * 2); \
-        prefetch4(xrs, lds_addr(sPF), pbv, (xpart(ppart) * C + pc) * 2);                       \
-      }                                                                                        \
       ++issued;                                                                                \
       VAEP_ADVANCE(itap, ipart, ic);                                                           \
-      if (pstep + 1 < nsteps1) {   /* the prefetch covers the taps' steps */                  \
-        ++pstep;                                                                               \
-        VAEP_ADVANCE(ptap, ppart, pc);                                                         \
-      }                                                                                        \
     }                                                                                          \
   }
 #define VAEP_ISSUE_PART(st, q)                                                                 \
@@ -535,14 +476,15 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   // Step s computes from stage s % S and first issues step s + S - 1 into stage
   // (s + S - 1) % S, which every wave finished reading before the barrier.  Loads complete
   // in issue order; this thread's loads of step s have landed once at most the loads
-  // issued after them (the prefetches of that step, if any, and the next step's group
-  // when S is 3) are outstanding.  The barrier then publishes every thread's chunks.
+  // issued after them (the next step's group when S is 3) are outstanding.  The barrier
+  // then publishes every thread's chunks.  (An L2 prefetch of later steps' lines was
+  // measured here: it slowed the 256 x 256 convs by 10 %.)
 #define VAEP_STEP_K(cs, ns, si, F8)                                                              \
   {                                                                                            \
     if (S == 3 && (si) + 2 <= nsteps)                                                          \
-      __builtin_amdgcn_s_waitcnt(((NG + PFN) & 15) | (((NG + PFN) >> 4) << 14) | (7 << 4) | (15 << 8)); \
+      __builtin_amdgcn_s_waitcnt((LO::NL & 15) | ((LO::NL >> 4) << 14) | (7 << 4) | (15 << 8)); \
     else                                                                                       \
-      __builtin_amdgcn_s_waitcnt(PFN | (7 << 4) | (15 << 8));                                  \
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));                                        \
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                            \
     const bool more = issued < nsteps;                                                         \
     const unsigned short* A = VAEP_SA(cs);                                                     \
@@ -651,7 +593,7 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
 #undef VAEP_ADVANCE
 #undef VAEP_ISSUE_PART
 #undef VAEP_ISSUE_ONE
-  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // prefetches still in flight
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // every operand load has landed
 #undef VAEP_ISSUE
 #undef VAEP_SET_TAP
 
@@ -725,29 +667,32 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   if (gn) gn_stats(std::false_type{});
 }
 
-template <int KT, int KS, bool SUB, int PARTS, int MODE>
+template <int KT, int KS, bool SUB, int PARTS, int MODE, bool X2>
 hipError_t go_tile(const ConvArgs& a, WideTile t, hipStream_t s) {
   const int ph = SUB ? 4 : 1;
   const long long wgs = (long long)a.tiles_total * (a.cout_pad / t.bm) * ph;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
   if (t.bm == 256) {
-    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 256, 256, 8>), dim3((unsigned)wgs), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 256, 256, 8, X2>), dim3((unsigned)wgs), dim3(512), 0, s, a);
   } else if constexpr (SUB) {
     // 128 x 256 tiles: sub-pixel convs only (plain convs of that size run on the 128 x 128
     // kernel); 8 waves, whose second wave per SIMD hides the fp8 step's extra issue slots
     if (t.bn != 256) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128, 256, 8>), dim3((unsigned)wgs), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128, 256, 8, X2>), dim3((unsigned)wgs), dim3(512), 0, s, a);
   } else {
     if (t.bn != 512) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128, 512, 8>), dim3((unsigned)wgs), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128, 512, 8, X2>), dim3((unsigned)wgs), dim3(512), 0, s, a);
   }
   return hipGetLastError();
 }
 
 template <int KT, int KS, bool SUB, int PARTS>
 hipError_t go_mode(const ConvArgs& a, WideTile t, hipStream_t s) {
-  if (a.mode == kModeBandSplit) return go_tile<KT, KS, SUB, PARTS, kModeBandSplit>(a, t, s);
-  return go_tile<KT, KS, SUB, PARTS, kModeBand>(a, t, s);
+  if (a.mode == kModeBandSplit) return go_tile<KT, KS, SUB, PARTS, kModeBandSplit, false>(a, t, s);
+  if constexpr (!SUB && KS == 3)
+    if (a.x2) return go_tile<KT, KS, SUB, PARTS, kModeBand, true>(a, t, s);
+  if (a.x2) return hipErrorInvalidValue;
+  return go_tile<KT, KS, SUB, PARTS, kModeBand, false>(a, t, s);
 }
 
 }  // namespace
