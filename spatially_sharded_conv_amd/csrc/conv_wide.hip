@@ -478,7 +478,10 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   // in issue order; this thread's loads of step s have landed once at most the loads
   // issued after them (the next step's group when S is 3) are outstanding.  The barrier
   // then publishes every thread's chunks.  (An L2 prefetch of later steps' lines was
-  // measured here: it slowed the 256 x 256 convs by 10 %.)
+  // measured here: it slowed the 256 x 256 convs by 10 %.)  The last S - 1 steps issue
+  // loads for steps past the end too, into stages no step reads, so the issue slots need
+  // no branch: their offsets run past the operand rows, and a buffer load past a
+  // resource's end returns zeros; the wait after the loop drains them.
 #define VAEP_STEP_K(cs, ns, si, F8)                                                              \
   {                                                                                            \
     if (S == 3 && (si) + 2 <= nsteps)                                                          \
@@ -486,7 +489,6 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
     else                                                                                       \
       __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));                                        \
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                            \
-    const bool more = issued < nsteps;                                                         \
     const unsigned short* A = VAEP_SA(cs);                                                     \
     const unsigned short* B = VAEP_SB(cs);                                                     \
     if (F8) {                                                                                  \
@@ -511,10 +513,8 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
         }                                                                                      \
         /* the group's MFMAs (64 cycles each) run while quarters 2g, 2g+1 issue */            \
         __builtin_amdgcn_sched_barrier(0);                                                     \
-        if (more) {                                                                            \
-          VAEP_ISSUE_PART(ns, 2 * grp);                                                        \
-          VAEP_ISSUE_PART(ns, 2 * grp + 1);                                                    \
-        }                                                                                      \
+        VAEP_ISSUE_PART(ns, 2 * grp);                                                          \
+        VAEP_ISSUE_PART(ns, 2 * grp + 1);                                                      \
         __builtin_amdgcn_sched_barrier(0);                                                     \
       }                                                                                        \
     } else {                                                                                   \
@@ -541,7 +541,7 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
             const int idx = i * NJ + j;                                                        \
             if (idx % per == per - 1 && idx / per < LO::count(kk)) {                           \
               __builtin_amdgcn_sched_barrier(0);                                               \
-              if (more) VAEP_ISSUE_ONE(ns, kk, idx / per);                                     \
+              VAEP_ISSUE_ONE(ns, kk, idx / per);                                               \
               __builtin_amdgcn_sched_barrier(0);                                               \
             }                                                                                  \
           }                                                                                    \
