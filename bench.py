@@ -102,7 +102,10 @@ def summarise(recs, steps):
             # tiles and fp32 band output (one template instance of conv_wide); other wide
             # launches (sub-pixel upsample, split output), the 128x128-tile kernel and the
             # narrow conv_out are reported apart
-            if r["kernel"] == L.KERNEL_CONV_WIDE256 and r["ks"] == 3 and r["ups"] == 0 and r["mode"] == 0:
+            if r["kernel"] == L.KERNEL_CONV_HALO:
+                # halo-tile kernel: 128 x (4 x 128) tiles for 128-channel outputs, 256 x (4 x 64) else
+                add("conv_halo_128" if r["cout"] <= 128 else "conv_halo_256", r)
+            elif r["kernel"] == L.KERNEL_CONV_WIDE256 and r["ks"] == 3 and r["ups"] == 0 and r["mode"] == 0:
                 add("conv_wide_3x3", r)
             elif r["kernel"] == L.KERNEL_CONV_WIDE128X512:
                 add("conv_wide_512px", r)

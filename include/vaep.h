@@ -272,10 +272,11 @@ enum { VAEP_STEP_CONV = 1, VAEP_STEP_GROUPNORM = 2, VAEP_STEP_RMSNORM = 3,
        VAEP_STEP_ATTENTION = 4, VAEP_STEP_MOVE = 5 };
 /* Convolution kernel that ran a conv step: 128x128 tiles two per CU, the wide kernel
  * with 256 x 256, 128 x 256 or 128 x 512 (channels x pixels) tiles, the narrow-output
- * kernel, the fp32 kernel. */
+ * kernel, the fp32 kernel, the halo-tile kernel (2-D pixel tiles, the pixel operand
+ * staged once per channel block). */
 enum { VAEP_KERNEL_OTHER = 0, VAEP_KERNEL_CONV_TILE128 = 1, VAEP_KERNEL_CONV_WIDE256 = 2,
        VAEP_KERNEL_CONV_WIDE128 = 3, VAEP_KERNEL_CONV_NARROW = 4, VAEP_KERNEL_CONV_F32 = 5,
-       VAEP_KERNEL_CONV_WIDE128X512 = 6 };
+       VAEP_KERNEL_CONV_WIDE128X512 = 6, VAEP_KERNEL_CONV_HALO = 7 };
 typedef struct vaep_profile_entry {
   int32_t step;        /* VAEP_STEP_* */
   int32_t n_kernels;   /* kernels inside the bracket */

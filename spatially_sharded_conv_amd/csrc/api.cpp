@@ -468,7 +468,7 @@ struct Exec {
   // epilogue), and their chunk width; the next norm of exactly that buffer uses them.
   const void* gn_src = nullptr;
   int gn_src_chunk = 0;
-  static constexpr int kMinGnChunk = kConvTileM;   // narrowest conv pixel tile
+  static constexpr int kMinGnChunk = 64;   // narrowest conv pixel tile width (halo kernel, 4 x 64)
   int base_rows = 0;   // rows of the band table's own resolution (latent rows of a decode)
 
   size_t eb() const { return dtype_bytes(dtype); }   // operand (normalised activation) element

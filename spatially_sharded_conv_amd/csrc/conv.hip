@@ -572,6 +572,7 @@ hipError_t go(const ConvArgs& a, hipStream_t s) {
 hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s) {
   const bool ups = a.ups != 0;
   a.gn_chunk = 0;
+  if (dtype != VAEP_DTYPE_F32 && conv_halo_fits(a)) return launch_conv_halo(a, s);
   if (dtype != VAEP_DTYPE_F32 && conv_wide_fits(a)) return launch_conv_wide(a, s);
   if (dtype != VAEP_DTYPE_F32 && conv_narrow_fits(a)) {
     a.gn_part = nullptr;

@@ -133,6 +133,10 @@ WideTile wide_tile(const ConvArgs& a);
 // always run there.
 bool conv_wide_fits(const ConvArgs& a);
 hipError_t launch_conv_wide(ConvArgs& a, hipStream_t s);
+// Plain 3x3 convs on the halo-tile kernel (conv_halo.hip): 4-row pixel tiles aligned to
+// global rows, the pixel operand staged once per 32-channel block.
+bool conv_halo_fits(const ConvArgs& a);
+hipError_t launch_conv_halo(ConvArgs& a, hipStream_t s);
 // The final conv (kModeFinal) with at most 16 output channels: pixels on the MFMA rows.
 bool conv_narrow_fits(const ConvArgs& a);
 hipError_t launch_conv_narrow(ConvArgs& a, hipStream_t s);

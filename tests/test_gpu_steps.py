@@ -77,6 +77,28 @@ def test_conv3x3_step_wide_tiles(gpu_lib):
     assert_close(got, ref, *ACC_TOL, what="conv3x3 wide tiles")
 
 
+@pytest.mark.parametrize("case", [
+    # (B, cin, cout, H, W, starts): 128 x (4 x 128) tiles; 256 x (4 x 64) tiles
+    (1, 128, 128, 1030, 256, (0, 5, 6, 261, 517, 1030)),
+    (1, 64, 256, 516, 256, (0, 1, 130, 131, 387, 516)),
+])
+def test_conv3x3_halo_tiles(gpu_lib, case):
+    """The halo-tile kernel (pixel operand staged once per 32-channel block, 4-row tiles
+    aligned to global rows and clipped at band edges): residual, uneven and one-row bands,
+    bit-identical on every band table."""
+    B, cin, cout, H, W, starts = case
+    x = seeded((B, cin, H, W), 41, dtype="bf16")
+    w = seeded((cout, cin, 3, 3), 42, 1 / math.sqrt(cin * 9), dtype="bf16")
+    b = seeded((cout,), 43, 0.1, dtype="bf16")
+    r = seeded((B, cout, H, W), 44, dtype="f32")
+    ref = _conv_ref(x, w, b, False, r, "bf16")
+    xd, wd, bd, rd = to_dev(x, "bf16"), to_dev(w, "bf16"), to_dev(b, "bf16"), r.cuda()
+    got = vaep.step_conv(xd, wd, bd, starts, residual=rd)
+    assert_close(got, ref, *ACC_TOL, what=f"conv3x3 halo tiles {case}")
+    one = vaep.step_conv(xd, wd, bd, (0, H), residual=rd)
+    assert torch.equal(got, one)
+
+
 def test_conv_step_single_band_above_2gib(gpu_lib):
     """One band whose buffer exceeds a buffer resource's 2 GiB range: 2048 x 2048 pixels of
     256 bf16 channels (2.15 GB with the halo rows).  The conv kernels address only the rows
