@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libvaep.so")
 OBJ = os.path.join(HERE, "_build")
-SOURCES = ["conv.hip", "conv_wide.hip", "conv_halo.hip", "conv_narrow.hip", "norm.hip", "attn.hip", "movement.hip", "static_scratch.hip",
+SOURCES = ["conv.hip", "conv_wide.hip", "conv_halo.hip", "conv_narrow.hip", "norm.hip", "attn.hip", "attn_lds.hip", "movement.hip", "static_scratch.hip",
            "api.cpp"]
 
 

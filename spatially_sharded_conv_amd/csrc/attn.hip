@@ -201,13 +201,11 @@ __global__ void __launch_bounds__(256) flash_bf16(const AttnArgs a) {
 // in P); otherwise P is formed against the old max (still exact: numerator and
 // denominator use the same max), so the O rescale runs only on the rare tiles that move
 // a max.
-// Split keys (a.part set, d <= 384): workgroup 2i + s takes query block i against the s-th
-// half of the key tiles and writes its unnormalised O, running max and sum (fp32) to
-// a.part; attn_merge combines the halves.  Two workgroups then share each CU, one's
-// barrier and softmax phases overlapping the other's products.  At d = 512 the registers
-// of two 64-query workgroups per CU do not hold Q, K, V and O without spilling; 32-query
-// workgroups (QB = 1, half the Q, S and O registers) fit two per CU, and the launch runs
-// them where 64-query blocks would leave CUs idle.
+// Split keys (a.part set): workgroup 2i + s takes query block i against the s-th half of
+// the key tiles and writes its unnormalised O, running max and sum (fp32) to a.part;
+// attn_merge combines the halves.  Two workgroups then share each CU, one's barrier and
+// softmax phases overlapping the other's products.  Runs d = 128 and 256 (QB = 2); d = 384
+// and 512 run the LDS-staged kernel, which holds whole query rows per wave.
 template <int DS, int QB>
 __global__ void __launch_bounds__(256, (DS <= 96 || QB == 1) ? 2 : 1) attn_split(const AttnArgs a) {
   constexpr int D = 4 * DS;
@@ -512,47 +510,50 @@ __global__ void __launch_bounds__(256) attn_f32(const AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attention(AttnArgs& a, int dtype, hipStream_t s) {
-  // split-channel kernel: 64 queries per workgroup, needs tokens % 8 == 0 (16-byte V^T
-  // rows).  At d = 512 a workgroup holds a whole CU's registers; when the image's 64-query
-  // blocks leave CUs idle, 32-query workgroups (two per CU) run instead -- decided on the
-  // whole image, so every band table computes the same sums.  With 64-query blocks that
-  // fill the CUs the 32-query form is slower: each workgroup streams all of K and V.
+  // bf16 with tokens % 8 == 0 (16-byte V^T rows): the LDS-staged kernel (attn_lds.hip) at
+  // d = 384 and 512, the split-channel kernel at d = 128 and 256; flash_bf16 otherwise.
   const bool split = dtype != VAEP_DTYPE_F32 && a.tokens % 8 == 0 &&
                      (long long)a.tokens * a.c * 2 < (1LL << 31);
-  const long long q64 = (long long)a.L.n_img * (((long long)a.L.H * a.L.W + 63) / 64);
-  const int qb = (split && a.c == 512 && q64 < 256) ? 1 : 2;
-  const int per = dtype == VAEP_DTYPE_F32 ? 4 : (split ? 32 * qb : kQ);
-  int t = 0;
-  for (int b = 0; b < a.L.nb; ++b) {
-    a.tile_start[b] = t;
-    t += a.L.n_img * ((a.L.rows[b] * a.L.W + per - 1) / per);
+  auto block_starts = [&a](int per) {
+    int t = 0;
+    for (int b = 0; b < a.L.nb; ++b) {
+      a.tile_start[b] = t;
+      t += a.L.n_img * ((a.L.rows[b] * a.L.W + per - 1) / per);
+    }
+    a.tile_start[a.L.nb] = t;
+    a.tiles_total = t;
+    return t;
+  };
+  if (split && (a.c == 384 || a.c == 512)) {
+    // 128 queries per workgroup.  Keys split in two (a.part: the caller's scratch of
+    // attn_part_floats) when the whole image's 128-query blocks fill at most half of the
+    // CUs (256) -- decided on the whole image, so every band table computes the same sums.
+    const long long q128 = (long long)a.L.n_img * (((long long)a.L.H * a.L.W + 127) / 128);
+    if (q128 > 128) a.part = nullptr;
+    const int t = block_starts(128);
+    if (t == 0) return hipSuccess;
+    hipError_t e = launch_attn_lds(a, (unsigned)t * (a.part ? 2u : 1u), s);
+    if (e != hipSuccess || !a.part) return e;
+    hipLaunchKernelGGL(attn_merge, dim3(block_starts(64)), dim3(256), 0, s, a);
+    return hipGetLastError();
   }
-  a.tile_start[a.L.nb] = t;
-  a.tiles_total = t;
+  const int t = block_starts(dtype == VAEP_DTYPE_F32 ? 4 : kQ);
   if (t == 0) return hipSuccess;
   if (dtype == VAEP_DTYPE_F32) {
     if (a.c > 1024) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_f32, dim3(t), dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  if (split) {
-    // keys in two halves (a.part: the caller's scratch of attn_part_floats) when the query
-    // blocks alone would not give every CU two workgroups and d <= 384 -- decided on the
-    // whole image, so every band table computes the same sums
-    if (a.part && (a.c > 384 || q64 >= 512)) a.part = nullptr;
+  if (split && (a.c == 128 || a.c == 256)) {
+    // keys in two halves when the 64-query blocks alone would not give every CU two
+    // workgroups -- decided on the whole image
+    const long long q64 = (long long)a.L.n_img * (((long long)a.L.H * a.L.W + 63) / 64);
+    if (q64 >= 512) a.part = nullptr;
     const unsigned g = (unsigned)t * (a.part ? 2u : 1u);
-    switch (a.c) {
-      case 128: hipLaunchKernelGGL((attn_split<32, 2>), dim3(g), dim3(256), 0, s, a); break;
-      case 256: hipLaunchKernelGGL((attn_split<64, 2>), dim3(g), dim3(256), 0, s, a); break;
-      case 384: hipLaunchKernelGGL((attn_split<96, 2>), dim3(g), dim3(256), 0, s, a); break;
-      case 512:
-        if (qb == 1)
-          hipLaunchKernelGGL((attn_split<128, 1>), dim3(g), dim3(256), 0, s, a);
-        else
-          hipLaunchKernelGGL((attn_split<128, 2>), dim3(g), dim3(256), 0, s, a);
-        break;
-      default: return hipErrorInvalidValue;
-    }
+    if (a.c == 128)
+      hipLaunchKernelGGL((attn_split<32, 2>), dim3(g), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_split<64, 2>), dim3(g), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.part) return e;
     hipLaunchKernelGGL(attn_merge, dim3(t), dim3(256), 0, s, a);

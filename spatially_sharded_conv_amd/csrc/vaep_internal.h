@@ -214,6 +214,9 @@ struct AttnArgs {
 // Scratch floats of the key-split attention: two halves of unnormalised O and (max, sum).
 inline long long attn_part_floats(int n_img, int tokens, int c) { return 2LL * n_img * tokens * (c + 2); }
 hipError_t launch_attention(AttnArgs& a, int dtype, hipStream_t s);
+// The LDS-staged bf16 kernel for d = 384 and 512 (128 queries per workgroup, tile_start
+// counted in such blocks; grid doubled when a.part splits the keys).  Tokens % 8 == 0.
+hipError_t launch_attn_lds(const AttnArgs& a, unsigned grid, hipStream_t s);
 
 // ------------------------------------------------------------------ data movement
 // NC[T]HW tensor -> band layout (halo rows filled from neighbours, zeros at image

@@ -294,6 +294,7 @@ def _attn_ref(x, groups, g, be, wq, bq, wk, bk, wv, bv, wo, bo, dtype):
 @pytest.mark.parametrize("case", [
     ("bf16", 512, 32, (1, 8, 25), (0, 3, 8)),          # 200 tokens: ragged key and query tiles
     ("bf16", 384, 0, (2, 6, 10), (0, 1, 6)),           # per-frame span, RMSNorm pre-norm
+    ("bf16", 384, 0, (2, 8, 13), (0, 3, 8)),           # 104 tokens a frame: a ragged last key tile
     ("bf16", 256, 32, (1, 16, 32), (0, 5, 16)),         # 512 tokens, 64-channel wave slices
     ("bf16", 128, 32, (1, 12, 20), (0, 12)),            # 240 tokens, 32-channel wave slices
     ("f32", 64, 8, (1, 8, 8), (0, 3, 8)),
@@ -350,6 +351,40 @@ def test_attention_step_d512_full_grid(gpu_lib):
     ref = Precision("bf16").acc(out)
     sel = got[0].reshape(C, -1).T[rows].cpu()
     assert_close(sel, ref, *STEP_TOL["bf16"], what="attention d=512, 16384 tokens, sampled rows")
+
+
+def test_attention_step_d384_video_whole_key_range(gpu_lib):
+    """d = 384 per-frame attention over 3 frames of 64 x 96 tokens: 144 blocks of 128
+    queries, enough that the keys are not split in halves.  Sampled query rows of every frame
+    and band against the float64 reference; the output does not depend on the band table."""
+    C, T, H, W = 384, 3, 64, 96
+    starts = (0, 21, 40, 64)
+    x = seeded((1, C, T, H, W), 261, dtype="f32")
+    g = seeded((C,), 262, 0.25, offset=1.0, dtype="f32")
+    be = seeded((C,), 263, 0.1, dtype="f32")
+    ws = [seeded((C, C), 264 + i, 1 / math.sqrt(C), dtype="bf16") for i in range(4)]
+    bs = [seeded((C,), 270 + i, 0.1, dtype="bf16") for i in range(4)]
+    dev = [to_dev(t, "bf16") for t in ws + bs]
+    xd, gd, bed = x.cuda(), g.cuda(), be.cuda()
+    args = (dev[0], dev[4], dev[1], dev[5], dev[2], dev[6], dev[3], dev[7])
+    got = vaep.step_attention(xd, 0, 1e-6, gd, bed, *args, starts)
+    whole = vaep.step_attention(xd, 0, 1e-6, gd, bed, *args, (0, H))
+    assert torch.equal(got, whole)
+    fin = Precision("bf16").finish
+    h = fin(ops.rmsnorm(x, g, 1e-6, act=False))
+    gen = torch.Generator().manual_seed(275)
+    for t in range(T):
+        tok = h[0, :, t].reshape(C, -1).T.double()
+        q = fin(tok @ ws[0].double().T + bs[0].double())
+        k = fin(tok @ ws[1].double().T + bs[1].double())
+        v_ = fin(tok @ ws[2].double().T + bs[2].double())
+        rows = torch.cat([torch.tensor([0, H * W - 1] + [s * W for s in starts[1:-1]] + [s * W - 1 for s in starts[1:-1]]),
+                          torch.randint(0, H * W, (60,), generator=gen)])
+        o = fin(ops.attention_rows(q[rows], k, v_, 1 / math.sqrt(C)))
+        out = x[0, :, t].reshape(C, -1).T.double()[rows] + o.double() @ ws[3].double().T + bs[3].double()
+        ref = Precision("bf16").acc(out)
+        sel = got[0, :, t].reshape(C, -1).T[rows].cpu()
+        assert_close(sel, ref, *STEP_TOL["bf16"], what=f"attention d=384, frame {t}, sampled rows")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
