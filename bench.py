@@ -17,7 +17,9 @@ cores.  `shard_axes` times the same latent decoded on column bands of the same
 sizes (vaep_decode_sharded, width axis) and with the per-request `auto` axis
 policy; `tiled_baseline` times the overlap-blending tile decode
 (vaep_decode_tiled) and reports its distance from the band decode and its
-row-seam diagnostic.  `other_configs` times the batch-4 1024^2 preset and the
+row-seam diagnostic.  `norm_fold` times the decode with the GroupNorm apply folded into
+the latent-resolution resnet convs' operand load (vaep_model_set_norm_fold) beside
+the separate apply pass.  `other_configs` times the batch-4 1024^2 preset and the
 video preset in the same run (per-decode time, Mpixel/s, conv and norm
 fractions).
 
@@ -314,7 +316,21 @@ def main():
         "avg_launch_ms": round(conv["avg_launch_ms"], 4),
         "flops_per_launch": conv["flops"] / max(1, conv["launches"]),
     }
-    axes, tiled = {}, None
+    axes, tiled, fold = {}, None, None
+    if not args.only_bands and cfg.norm_groups > 0:
+        # the GroupNorm apply folded into the operand load of the latent-resolution resnet
+        # convs (vaep_model_set_norm_fold) beside the separate apply pass timed above
+        dec.set_norm_fold(True)
+        f_ms, f_med, (_, finfo) = timed_decodes(run, args.steps, args.warmup, stream)
+        frecs, _ = profiled_decodes(dec, run, args.steps, finfo.n_launches, stream)
+        dec.set_norm_fold(False)
+        fcls = summarise(frecs, args.steps)
+        pick = lambda c, k: round(c.get(k, {}).get("ms_per_step", 0.0), 4)
+        fold = {"ms_per_step": round(f_ms, 4), "ms_per_step_median": round(f_med, 4),
+                "mpixel_s": round(pixels / (f_ms * 1e-3) / 1e6, 3),
+                "speedup_vs_separate_apply": round(ms / f_ms, 4),
+                "groupnorm_ms": pick(fcls, "groupnorm"), "conv_tile128_ms": pick(fcls, "conv_tile128"),
+                "separate_apply": {"groupnorm_ms": pick(cls, "groupnorm"), "conv_tile128_ms": pick(cls, "conv_tile128")}}
     if not args.only_bands:
         # the same workload sharded along the width (the row bands' sizes laid across the
         # columns when they fit) and with the per-request axis policy
@@ -399,6 +415,7 @@ def main():
                       for k, v in sorted(cls.items())},
         "profiled_ms_per_step": round(ms_prof, 4),
         "shard_axes": axes,
+        "norm_fold": fold,
         "tiled_baseline": tiled,
         **aggregates(recs, args.steps),
         "other_configs": others,

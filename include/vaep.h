@@ -137,6 +137,17 @@ int vaep_model_create(const vaep_config* cfg, const void* const* params, int n_p
  * stream that uses it.  NULL is accepted (no-op). */
 int vaep_model_destroy(vaep_model* model);
 
+/* Fold the GroupNorm apply (scale, shift, SiLU) of the resnet convs into the conv's
+ * operand load where the convolution kernel that runs the conv supports it (3x3 convs on
+ * the 128 x 128-pixel-tile kernel: at most 512 input channels, every band's pixel count a
+ * multiple of 128), instead of a separate pass that writes the normalised operand.  The
+ * GroupNorm statistics and their merge are unchanged (ChituDiffusion "VAEP" feature page,
+ * GroupNorm section; "Static Layer-Wise VAE Decode", GroupNorm row: merged statistics,
+ * then the local normalisation); the folded apply computes the same operand bits, so the
+ * decoded output is the same.  on: 0 (default) or 1.  Affects later decodes of `model`;
+ * the workspace size does not depend on it.  Errors: INVALID_ARG (NULL model). */
+int vaep_model_set_norm_fold(vaep_model* model, int on);
+
 /* Workspace needed to decode a latent of `batch` x [frames x] latent_h x latent_w
  * with up to `n_bands` bands (frames = 1 for KL2D).  The same size serves
  * vaep_decode_full, every band table with at most n_bands bands, and

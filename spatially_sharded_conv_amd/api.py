@@ -88,6 +88,11 @@ class Decoder:
         L.check(lib.vaep_model_create(C.byref(cfg), arr, len(params), _stream(stream), C.byref(h)))
         self._h = h
 
+    def set_norm_fold(self, on: bool):
+        """Fold the resnet GroupNorm apply into the conv operand load where the kernel supports
+        it (vaep_model_set_norm_fold); the decoded output is the same."""
+        L.check(L.load().vaep_model_set_norm_fold(self._h, 1 if on else 0))
+
     def close(self):
         if getattr(self, "_h", None):
             L.check(L.load().vaep_model_destroy(self._h))

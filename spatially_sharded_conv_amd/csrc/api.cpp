@@ -236,6 +236,7 @@ struct Profiler {
 
 struct vaep_model {
   vaep_config cfg;
+  int fold_norm = 0;   // vaep_model_set_norm_fold
   void* mem = nullptr;
   size_t mem_bytes = 0;
   Profiler prof;
@@ -416,7 +417,7 @@ struct Builder {
 };
 
 // ------------------------------------------------------------------ executor
-enum XIn : int { kXOp = 0, kXF32 = 1, kXSplit = 2 };
+enum XIn : int { kXOp = 0, kXF32 = 1, kXSplit = 2, kXNorm = 3 };
 
 struct Exec {
   const vaep_model* m = nullptr;
@@ -430,8 +431,9 @@ struct Exec {
   void* kb = nullptr;
   void* vb = nullptr;
   float* scratch = nullptr;
+  float* ncoef = nullptr;   // (scale, shift) of a GroupNorm apply folded into the next conv
   // sizes (dry pass)
-  size_t act_bytes = 0, qkv_bytes = 0, scratch_bytes = 0;
+  size_t act_bytes = 0, qkv_bytes = 0, scratch_bytes = 0, ncoef_bytes = 0;
   int launches = 0;
   Profiler* prof = nullptr;
   bool recording = false;
@@ -475,7 +477,8 @@ struct Exec {
   void need_act(const BandLayout& L, size_t elem) { act_bytes = std::max(act_bytes, (size_t)layout_elems(L) * elem); }
 
   size_t total() const {
-    return 4 * align_up(act_bytes, 256) + 3 * align_up(qkv_bytes, 256) + align_up(scratch_bytes, 256);
+    return 4 * align_up(act_bytes, 256) + 3 * align_up(qkv_bytes, 256) + align_up(scratch_bytes, 256) +
+           align_up(ncoef_bytes, 256);
   }
   void assign(char* base) {
     ws = base;
@@ -491,6 +494,8 @@ struct Exec {
     vb = base + o;
     o += align_up(qkv_bytes, 256);
     scratch = (float*)(base + o);
+    o += align_up(scratch_bytes, 256);
+    ncoef = (float*)(base + o);
   }
 
   // xk: what the input buffer holds (kXOp: a normalised activation in the operand dtype;
@@ -508,7 +513,7 @@ struct Exec {
     if (w.kext > 0) need_act(reshaped(Lin, w.kext, Lin.n_img, Lin.frames), 2);
     if (mode == kModeBand || mode == kModeTimeInterleave) need_act(Lout, 4);
     if (mode == kModeBandSplit) need_act(Lout, 2);
-    need_act(Lin, xk == kXOp ? eb() : (xk == kXF32 ? 4 : 2));
+    need_act(Lin, xk == kXOp ? eb() : ((xk == kXF32 || xk == kXNorm) ? 4 : 2));
     gn_next = gn_next && groups > 0 && dtype == VAEP_DTYPE_BF16 &&
               (mode == kModeBand || mode == kModeBandSplit);
     if (gn_next) {
@@ -541,6 +546,8 @@ struct Exec {
     a.mode = mode;
     a.x_f32 = xk == kXF32 ? 1 : 0;
     a.x_split = xk == kXSplit ? 1 : 0;
+    a.x_norm = xk == kXNorm ? ncoef : nullptr;
+    a.x_norm_act = xk == kXNorm ? 1 : 0;
     a.sub = sub ? 1 : 0;
     a.sub_scale = sub ? w.sub_scale : nullptr;
     a.split8 = split8 && mode == kModeBandSplit ? 1 : 0;
@@ -583,10 +590,31 @@ struct Exec {
     return VAEP_OK;
   }
 
+  // Whether the GroupNorm + SiLU feeding conv w (Lin -> Lout, band mode) folds into the conv's
+  // operand load: the model asks for it and the conv runs on the kernel that supports it.
+  bool can_fold(const ConvW& w, const BandLayout& Lin, const BandLayout& Lout) const {
+    if (!m || !m->fold_norm || groups <= 0 || dtype != VAEP_DTYPE_BF16 || w.kext > 0 || w.rep != 1) return false;
+    ConvArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.in = Lin;
+    a.out = Lout;
+    a.cin = w.ci_pad;
+    a.cout = w.co;
+    a.cout_pad = w.co_pad;
+    a.kt = w.kt;
+    a.ks = w.ks;
+    a.mode = kModeBand;
+    return Lin.C == w.ci_pad && conv_norm_fold_ok(a);
+  }
+
   // x_split: x holds bf16 hi / lo halves of the fp32 input (L describes the logical tensor)
+  // stats_only: statistics and merge only, the apply's (scale, shift) into ncoef for the next
+  // conv, which folds the apply into its operand load (kXNorm)
   int norm(const NormW& w, const void* x, const BandLayout& L, void* y, int act, float* merged_out = nullptr,
-           bool x_split = false) {
+           bool x_split = false, bool stats_only = false) {
     need_act(L, 4);
+    // reserved for every GroupNorm, folded or not: the workspace does not depend on the fold
+    if (groups > 0) ncoef_bytes = std::max(ncoef_bytes, (size_t)L.n_img * L.C * 2 * sizeof(float));
     // statistics tiles never straddle a row any band table of this decode can cut at
     const int slab_rows = base_rows > 0 ? L.H / base_rows : 1;
     if (groups > 0)
@@ -610,21 +638,23 @@ struct Exec {
     a.partials = reinterpret_cast<double*>(scratch);
     a.merged_out = merged_out;
     a.slab_rows = slab_rows;
+    a.stats_only = stats_only ? 1 : 0;
+    a.coef_out = stats_only ? ncoef : nullptr;
+    const int nk = groups > 0 ? (pre ? 2 : 3) - (stats_only ? 1 : 0) : 1;
     {
-      vaep_profile_entry pe = entry(groups > 0 ? VAEP_STEP_GROUPNORM : VAEP_STEP_RMSNORM,
-                                    groups > 0 ? (pre ? 2 : 3) : 1);
+      vaep_profile_entry pe = entry(groups > 0 ? VAEP_STEP_GROUPNORM : VAEP_STEP_RMSNORM, nk);
       const double elems = (double)L.n_img * L.H * L.W * L.C;
       pe.cin = pe.cout = L.C;
       pe.pixels = (long long)L.n_img * L.H * L.W;
       // GroupNorm: statistics read (unless the producing conv formed them) + apply read
       // (fp32) + apply write; RMSNorm: one read + write
-      pe.bytes = elems * ((groups > 0 && !pre ? 8.0 : 4.0) + (double)eb());
+      pe.bytes = stats_only ? (pre ? 0.0 : elems * 4.0) : elems * ((groups > 0 && !pre ? 8.0 : 4.0) + (double)eb());
       rec_begin(pe);
     }
     hipError_t e = groups > 0 ? launch_groupnorm(a, dtype, st) : launch_rmsnorm(a, dtype, st);
     rec_end();
     if (e != hipSuccess) return hip_fail(e, "norm launch");
-    launches += groups > 0 ? (pre ? 2 : 3) : 1;
+    launches += nk;
     return VAEP_OK;
   }
 
@@ -722,8 +752,30 @@ int resnet(Exec& E, const ResW& r, int& cur, BandLayout& L, bool split_out = fal
   const BandLayout Lh = reshaped(L, r.c1.co, L.n_img, L.frames);
   const BandLayout Ly = split_out ? reshaped(L, 2 * r.c1.co, L.n_img, L.frames) : Lh;
   int rc;
-  if ((rc = E.norm(r.n1, E.act[cur], Lx, E.act[o[0]], 1, nullptr, r.split_in))) return rc;
-  if ((rc = E.conv(r.c1, E.act[o[0]], Lx, kXOp, E.act[o[1]], Lh, kModeBand, nullptr, 0, 1, true))) return rc;
+  // GroupNorm + SiLU -> conv1: the apply folded into conv1's operand load where the model
+  // asks for it and conv1 runs on the kernel that supports it, else a separate pass
+  if (!r.split_in && E.can_fold(r.c1, Lx, Lh)) {
+    if ((rc = E.norm(r.n1, E.act[cur], Lx, nullptr, 1, nullptr, false, true))) return rc;
+    if ((rc = E.conv(r.c1, E.act[cur], Lx, kXNorm, E.act[o[1]], Lh, kModeBand, nullptr, 0, 1, true))) return rc;
+  } else {
+    if ((rc = E.norm(r.n1, E.act[cur], Lx, E.act[o[0]], 1, nullptr, r.split_in))) return rc;
+    if ((rc = E.conv(r.c1, E.act[o[0]], Lx, kXOp, E.act[o[1]], Lh, kModeBand, nullptr, 0, 1, true))) return rc;
+  }
+  if (!shortcut_folds(r, Lh, split_out) && !split_out && E.can_fold(r.c2, Lh, Ly)) {
+    // conv2 reads conv1's raw output and writes the free operand buffer; the merge first,
+    // while conv1's statistics records are the latest in the scratch
+    if ((rc = E.norm(r.n2, E.act[o[1]], Lh, nullptr, 1, nullptr, false, true))) return rc;
+    const void* res = E.act[cur];
+    if (r.has_sc) {
+      if ((rc = E.conv(r.sc, E.act[cur], L, r.split_in ? kXOp : kXF32, E.act[o[2]], Lh, kModeBand, nullptr, 0)))
+        return rc;
+      res = E.act[o[2]];
+    }
+    if ((rc = E.conv(r.c2, E.act[o[1]], Lh, kXNorm, E.act[o[0]], Ly, kModeBand, res, 0, 1, true))) return rc;
+    cur = o[0];
+    L = Ly;
+    return VAEP_OK;
+  }
   if ((rc = E.norm(r.n2, E.act[o[1]], Lh, E.act[o[0]], 1))) return rc;
   if (shortcut_folds(r, Lh, split_out)) {
     // conv2 + shortcut in one conv: K runs over conv2's taps, then the block input's
@@ -1136,6 +1188,12 @@ int vaep_model_destroy(vaep_model* model) {
   return VAEP_OK;
 }
 
+int vaep_model_set_norm_fold(vaep_model* model, int on) {
+  if (!model) return fail(VAEP_ERR_INVALID_ARG, "model is NULL");
+  model->fold_norm = on ? 1 : 0;
+  return VAEP_OK;
+}
+
 int vaep_workspace_bytes(const vaep_model* model, int batch, int frames, int latent_h, int latent_w,
                          int n_bands, size_t* bytes_out) {
   int rc = check_latent_dims(model, batch, frames, latent_h, latent_w);
@@ -1537,6 +1595,7 @@ int vaep_step_groupnorm(int dtype, const void* x, int batch, int frames, int c, 
   a.partials = reinterpret_cast<double*>(scratch);
   a.merged_out = merged;
   a.slab_rows = 1;
+  a.want_band_moments = band_moments ? 1 : 0;
   e = launch_groupnorm(a, dtype, st);
   if (e == hipSuccess && band_moments)
     e = hipMemcpyAsync(band_moments, a.band_moments, sizeof(float) * 3 * nb * L.n_img * groups,

@@ -152,12 +152,13 @@ __global__ void __launch_bounds__(256, 1) attn_lds(const AttnArgs a) {
     const unsigned char* VB = KB + KT;
 
     // S^T: the products in VGPR form (inline asm; the builtin form would put S^T in the
-    // accumulation registers, which O^T fills), in two chains (even and odd channel steps)
-    // so that a product never waits on the one just issued.  Products accumulating in place
-    // need no wait states; 24 after the last one cover the VALU readers of both chains.  K fragments
+    // accumulation registers, which O^T fills), one chain accumulating in place (no wait
+    // states between its products); 24 after the last one cover its VALU readers.  (Two
+    // chains, even and odd channel steps, changed the decode beyond what the summation
+    // order explains, so the single chain stays.)  K fragments
     // come through a ring of RD, read RD - 1 products ahead (LDS latency under load is
     // several products long), fenced so the scheduler keeps that depth.
-    f32x16_t sacc, sacc1;
+    f32x16_t sacc;
     bf16x8_t kf[RD];
 #pragma unroll
     for (int i = 0; i < RD - 1; ++i)
@@ -173,21 +174,14 @@ __global__ void __launch_bounds__(256, 1) attn_lds(const AttnArgs a) {
       if (ks == 0)
         asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
                      : "=&v"(sacc) : "v"(kf[0]), "v"(qf[0]));
-      else if (ks == 1)
-        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
-                     : "=&v"(sacc1) : "v"(kf[1]), "v"(qf[1]));
-      else if (ks + 1 < KS && (ks & 1) == 0)
-        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                     : "+v"(sacc) : "v"(kf[ks % RD]), "v"(qf[ks]));
       else if (ks + 1 < KS)
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                     : "+v"(sacc1) : "v"(kf[ks % RD]), "v"(qf[ks]));
+                     : "+v"(sacc) : "v"(kf[ks % RD]), "v"(qf[ks]));
       else
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-                     : "+v"(sacc1) : "v"(kf[ks % RD]), "v"(qf[ks]));
+                     : "+v"(sacc) : "v"(kf[ks % RD]), "v"(qf[ks]));
       __builtin_amdgcn_sched_barrier(0);
     }
-    sacc += sacc1;
 
     // lane: query q0 + lane % 32; sacc[v] is key k0 + 16 (v >> 3) + 8 h + (v & 7)
     float sv[16];

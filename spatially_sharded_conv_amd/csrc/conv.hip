@@ -19,6 +19,9 @@
 #include "vaep_internal.h"
 #include "conv_gn_stats.h"
 #include "split8.h"
+#include "norm_act.h"
+
+#include <type_traits>
 
 namespace vaep {
 
@@ -178,7 +181,7 @@ __device__ __forceinline__ int xcd_remap(int lin, int total) {
     }                                                                         \
   }
 
-template <int KT, int KS, bool UPS, int MODE, bool XF32, int BK>
+template <int KT, int KS, bool UPS, int MODE, bool XF32, int BK, bool XN = false>
 __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
   constexpr int BM = kConvTileN;   // output channels per workgroup
   constexpr int BN = kConvTileM;   // pixels per workgroup
@@ -189,6 +192,9 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
   constexpr int NP = BN / RP;      // passes per tile
   __shared__ __attribute__((aligned(16))) unsigned short sW[2][BM * LDK];
   __shared__ __attribute__((aligned(16))) unsigned short sX[2][BN * LDK];
+  // XN (folded GroupNorm apply): the tile's image's (scale, shift) per input channel
+  __shared__ __attribute__((aligned(16))) float sN[XN ? 2 * 512 : 4];
+  static_assert(!(XN && XF32), "the folded apply reads the raw fp32 input in one pass");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -224,7 +230,7 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
     pr[j] = rem / wc;
     pc[j] = rem - pr[j] * wc;
   });
-  constexpr int XB = XF32 ? 4 : 2;   // bytes per input element
+  constexpr int XB = (XF32 || XN) ? 4 : 2;   // bytes per input element
   // weights: [cout_pad][taps][cin] bf16; thread rows co0 + rs + RP*j, chunk q8
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(a.w, (unsigned)((long long)a.cout_pad * ktot * 2));
   unsigned wvo[NP];
@@ -299,7 +305,22 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
   const int frag = (lane & 31) * LDK + (lane >> 5) * 8;
   const int srow = rs * LDK + q8;
 
-  u32x4_t wa[NP], xa[NP], wb[NP], xb[NP];
+  // XN stages hold the raw fp32 chunk (8 channels); the apply runs when it goes to LDS,
+  // with the stage's first channel and padding chunks (bit j) recorded at its load
+  struct F8 {
+    f32x4_t lo, hi;
+  };
+  using XR = typename std::conditional<XN, F8, u32x4_t>::type;
+  u32x4_t wa[NP], wb[NP];
+  XR xa[NP], xb[NP];
+  unsigned pma = 0, pmb = 0;
+  int csa = 0, csb = 0;
+  if constexpr (XN) {
+    const int n_t = (int)(((long long)tile * BN) / plane);   // every band's plane is a multiple of BN
+    const float* src = a.x_norm + (long long)n_t * cin * 2;
+    for (int i = tid; i < 2 * cin; i += 256) sN[i] = src[i];
+    __syncthreads();
+  }
   unsigned xo[NP];   // byte offset of this thread's chunk at the current tap, or kPadOffset
   VAEP_FOR_J({ xo[j] = kPadOffset; });
   int tap = 0, c0 = 0, loaded = 0;
@@ -308,7 +329,7 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
 // Loads: per step, weights at wvo[j] + (tap*cin + c0)*2 and inputs at xo[j] + c0*XB, both
 // with the step part as a scalar offset.  Padding taps read past the end of the band
 // buffer and get zeros; loads past the last step repeat the last step.
-#define VAEP_CONV_LOAD(W, X)                                                                    \
+#define VAEP_CONV_LOAD(W, X, PM, CS)                                                            \
   {                                                                                             \
     if (c0 == 0) {                                                                              \
       const int dt = tap / (KS * KS), dy = (tap / KS) % KS, dx = tap % KS;                      \
@@ -320,9 +341,19 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
     }                                                                                           \
     const int ws = (tap * cin + c0) * 2;                                                        \
     const int xs = c0 * XB;                                                                     \
+    if constexpr (XN) {                                                                         \
+      PM = 0u;                                                                                  \
+      CS = c0;                                                                                  \
+    }                                                                                           \
     VAEP_FOR_J({                                                                                \
       W[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wvo[j], ws, 0)); \
-      X[j] = load8<XF32>(xrs, xo[j], xs, lo);                                                   \
+      if constexpr (XN) {                                                                       \
+        X[j].lo = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)xo[j], xs, 0)); \
+        X[j].hi = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)xo[j] + 16, xs, 0)); \
+        if (xo[j] == kPadOffset) PM |= 1u << j;                                                 \
+      } else {                                                                                  \
+        X[j] = load8<XF32>(xrs, xo[j], xs, lo);                                                 \
+      }                                                                                         \
     });                                                                                         \
     if (++loaded < nsteps) {                                                                    \
       c0 += BK;                                                                                 \
@@ -335,12 +366,34 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
       }                                                                                         \
     }                                                                                           \
   }
-#define VAEP_CONV_STASH(W, X, buf)                                                              \
+#define VAEP_CONV_STASH(W, X, buf, PM, CS)                                                      \
   {                                                                                             \
-    VAEP_FOR_J({                                                                                \
-      *reinterpret_cast<u32x4_t*>(&sW[buf][srow + RP * j * LDK]) = W[j];                        \
-      *reinterpret_cast<u32x4_t*>(&sX[buf][srow + RP * j * LDK]) = X[j];                        \
-    });                                                                                         \
+    if constexpr (XN) {                                                                         \
+      const f32x4_t* nt = reinterpret_cast<const f32x4_t*>(&sN[2 * ((CS) + q8)]);               \
+      const f32x4_t n0 = nt[0], n1 = nt[1], n2 = nt[2], n3 = nt[3];                             \
+      const bool act = a.x_norm_act != 0;                                                       \
+      VAEP_FOR_J({                                                                              \
+        *reinterpret_cast<u32x4_t*>(&sW[buf][srow + RP * j * LDK]) = W[j];                      \
+        u32x4_t u = u32x4_t{0u, 0u, 0u, 0u};                                                    \
+        if (!(((PM) >> j) & 1u)) {                                                              \
+          const F8 v = X[j];                                                                    \
+          u.x = (unsigned)f2bf(gn_affine_act(v.lo.x, n0.x, n0.y, act)) |                        \
+                ((unsigned)f2bf(gn_affine_act(v.lo.y, n0.z, n0.w, act)) << 16);                 \
+          u.y = (unsigned)f2bf(gn_affine_act(v.lo.z, n1.x, n1.y, act)) |                        \
+                ((unsigned)f2bf(gn_affine_act(v.lo.w, n1.z, n1.w, act)) << 16);                 \
+          u.z = (unsigned)f2bf(gn_affine_act(v.hi.x, n2.x, n2.y, act)) |                        \
+                ((unsigned)f2bf(gn_affine_act(v.hi.y, n2.z, n2.w, act)) << 16);                 \
+          u.w = (unsigned)f2bf(gn_affine_act(v.hi.z, n3.x, n3.y, act)) |                        \
+                ((unsigned)f2bf(gn_affine_act(v.hi.w, n3.z, n3.w, act)) << 16);                 \
+        }                                                                                       \
+        *reinterpret_cast<u32x4_t*>(&sX[buf][srow + RP * j * LDK]) = u;                         \
+      });                                                                                       \
+    } else {                                                                                    \
+      VAEP_FOR_J({                                                                              \
+        *reinterpret_cast<u32x4_t*>(&sW[buf][srow + RP * j * LDK]) = W[j];                      \
+        *reinterpret_cast<u32x4_t*>(&sX[buf][srow + RP * j * LDK]) = X[j];                      \
+      });                                                                                       \
+    }                                                                                           \
   }
 #define VAEP_MFMA_K(buf, kk)                                                                    \
   {                                                                                             \
@@ -366,19 +419,19 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
   // Two register stages (a, b) and two LDS buffers: the loads of step s+2 are issued
   // before the MFMAs of step s and land in LDS at the end of step s+1.
   // (stashes past the last step write a buffer no step reads)
-  VAEP_CONV_LOAD(wa, xa);
-  VAEP_CONV_LOAD(wb, xb);
-  VAEP_CONV_STASH(wa, xa, 0);
+  VAEP_CONV_LOAD(wa, xa, pma, csa);
+  VAEP_CONV_LOAD(wb, xb, pmb, csb);
+  VAEP_CONV_STASH(wa, xa, 0, pma, csa);
   __syncthreads();
   for (int s = 0; s < nsteps; s += 2) {
-    VAEP_CONV_LOAD(wa, xa);
+    VAEP_CONV_LOAD(wa, xa, pma, csa);
     VAEP_CONV_COMPUTE(0);
-    VAEP_CONV_STASH(wb, xb, 1);
+    VAEP_CONV_STASH(wb, xb, 1, pmb, csb);
     __syncthreads();
     if (s + 1 == nsteps) break;
-    VAEP_CONV_LOAD(wb, xb);
+    VAEP_CONV_LOAD(wb, xb, pmb, csb);
     VAEP_CONV_COMPUTE(1);
-    VAEP_CONV_STASH(wa, xa, 0);
+    VAEP_CONV_STASH(wa, xa, 0, pma, csa);
     __syncthreads();
   }
 #undef VAEP_CONV_LOAD
@@ -556,6 +609,13 @@ hipError_t go(const ConvArgs& a, hipStream_t s) {
   const int ny = a.cout_pad / kConvTileN;
   dim3 grid(a.tiles_total, ny);
   const bool k64 = a.cin % 64 == 0;
+  if (a.x_norm) {
+    if constexpr (KT == 1 && KS == 3 && !UPS && MODE == kModeBand) {
+      hipLaunchKernelGGL((conv_mfma_bf16<KT, KS, UPS, MODE, false, 64, true>), grid, dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   if (a.x_f32 && k64)
     hipLaunchKernelGGL((conv_mfma_bf16<KT, KS, UPS, MODE, true, 64>), grid, dim3(256), 0, s, a);
   else if (a.x_f32)
@@ -569,12 +629,25 @@ hipError_t go(const ConvArgs& a, hipStream_t s) {
 
 }  // namespace
 
+bool conv_norm_fold_ok(const ConvArgs& a) {
+  if (a.kt != 1 || a.ks != 3 || a.ups || a.mode != kModeBand || a.x_f32 || a.x_split || a.sub || a.x2 || a.cin2)
+    return false;
+  if (a.cin % 64 != 0 || a.cin > 512 || a.in.C != a.cin) return false;
+  ConvArgs u = a;   // the same conv unfolded runs on the tile128 kernel too
+  u.x_norm = nullptr;
+  if (conv_halo_fits(u) || conv_wide_fits(u) || conv_narrow_fits(u)) return false;
+  for (int b = 0; b < a.in.nb; ++b)   // pixel tiles never straddle two images
+    if (((long long)a.in.rows[b] * a.in.W) % kConvTileM != 0) return false;
+  return true;
+}
+
 hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s) {
   const bool ups = a.ups != 0;
   a.gn_chunk = 0;
-  if (dtype != VAEP_DTYPE_F32 && conv_halo_fits(a)) return launch_conv_halo(a, s);
-  if (dtype != VAEP_DTYPE_F32 && conv_wide_fits(a)) return launch_conv_wide(a, s);
-  if (dtype != VAEP_DTYPE_F32 && conv_narrow_fits(a)) {
+  if (a.x_norm && (dtype != VAEP_DTYPE_BF16 || !conv_norm_fold_ok(a))) return hipErrorInvalidValue;
+  if (!a.x_norm && dtype != VAEP_DTYPE_F32 && conv_halo_fits(a)) return launch_conv_halo(a, s);
+  if (!a.x_norm && dtype != VAEP_DTYPE_F32 && conv_wide_fits(a)) return launch_conv_wide(a, s);
+  if (!a.x_norm && dtype != VAEP_DTYPE_F32 && conv_narrow_fits(a)) {
     a.gn_part = nullptr;
     return launch_conv_narrow(a, s);
   }
@@ -586,7 +659,7 @@ hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s) {
   if (dtype != VAEP_DTYPE_F32) {
     // buffer-resource addressing: the rows one tile can read and the weights stay below
     // 2 GiB, so the padding offset reads out of range
-    const long long xb = a.x_f32 ? 4 : 2;
+    const long long xb = (a.x_f32 || a.x_norm) ? 4 : 2;
     for (int b = 0; b < a.in.nb; ++b)
       if ((tile_read_slots(a.in, b, a.kt, kConvTileM, ups) * a.in.W + 2LL * kConvTileM) * a.in.C * xb >=
           (1LL << 31) - 4096)

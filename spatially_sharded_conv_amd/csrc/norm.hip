@@ -20,6 +20,7 @@
 // into the neighbours' halo slots.  Channel RMSNorm is local to a pixel and needs no
 // merge.
 #include "vaep_internal.h"
+#include "norm_act.h"
 
 namespace vaep {
 namespace {
@@ -101,12 +102,6 @@ __device__ __forceinline__ int band_of_block(const int* start, int nb, int blk) 
   while (b + 1 < nb && blk >= start[b + 1]) ++b;
   return b;
 }
-
-// SiLU(v) = v / (1 + e^-v), with the hardware reciprocal (1 ulp) instead of an IEEE
-// division: the result is rounded to the bf16 operand format (or feeds an fp32 conv
-// operand) and the division's ten-instruction sequence made the norm passes VALU-bound.
-// v -> -inf: e^-v = inf, rcp(inf) = 0, result -0 as with the division.
-__device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.f + __expf(-v)); }
 
 // Pass 1: central moments of one tile (a pixel chunk of one slab of one image):
 // partials[tile][g] = (mean, M2) of group g.  Each thread streams its channel slot over
@@ -241,15 +236,44 @@ __device__ void merge_tiles(const NormArgs& a, int n, int g, int t0, int t1, dou
   };
   // the tiles cover whole slabs: the element count is exact
   const double total = (double)((t1 - t0) / a.chunks) * (double)slab_pix * cpg;
+  // Each thread takes tiles t0 + tid, t0 + tid + kThreads, ... in that order; the loads of a
+  // batch of kBatch tiles are issued together (one memory latency per batch, not per tile),
+  // the sums still run tile by tile.
+  constexpr int kBatch = 16;
   double s = 0.0;
-  for (int t = t0 + tid; t < t1; t += kThreads) s += (tile_n(t) / total) * P[((long long)t * G + g) * 2];
+  for (int t_b = t0 + tid; t_b < t1; t_b += kBatch * kThreads) {
+    double mt[kBatch];
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) {
+      const int t = t_b + r * kThreads;
+      mt[r] = t < t1 ? P[((long long)t * G + g) * 2] : 0.0;
+    }
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) {
+      const int t = t_b + r * kThreads;
+      if (t < t1) s += (tile_n(t) / total) * mt[r];
+    }
+  }
   const double m = block_sum(s, sh);
   s = 0.0;
-  for (int t = t0 + tid; t < t1; t += kThreads) {
-    const double nt = tile_n(t);
-    const double* pr = P + ((long long)t * G + g) * 2;
-    const double d = pr[0] - m;
-    s += (nt / total) * (pr[1] / nt + d * d);
+  for (int t_b = t0 + tid; t_b < t1; t_b += kBatch * kThreads) {
+    double mt[kBatch], vt[kBatch];
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) {
+      const int t = t_b + r * kThreads;
+      const double* pr = P + ((long long)(t < t1 ? t : t0) * G + g) * 2;
+      mt[r] = pr[0];
+      vt[r] = pr[1];
+    }
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) {
+      const int t = t_b + r * kThreads;
+      if (t < t1) {
+        const double nt = tile_n(t);
+        const double d = mt[r] - m;
+        s += (nt / total) * (vt[r] / nt + d * d);
+      }
+    }
   }
   const double v = block_sum(s, sh);
   *cnt = total;
@@ -258,7 +282,7 @@ __device__ void merge_tiles(const NormArgs& a, int n, int g, int t0, int t1, dou
 }
 
 // Pass 2: one workgroup per (image n, group g, k): k < nb reports band k's moments (its
-// own tiles merged); k = nb merges all tiles of the image into the statistics the apply
+// own tiles merged; only when a.want_band_moments); k = nb merges all tiles of the image into the statistics the apply
 // uses, rounded to fp32 once, and writes the per-channel scale/shift of the apply.  Each
 // result is a fixed function of the tiles, whatever workgroup computes it.
 __global__ void __launch_bounds__(kThreads) gn_merge(const NormArgs a, float* coef) {
@@ -266,8 +290,9 @@ __global__ void __launch_bounds__(kThreads) gn_merge(const NormArgs a, float* co
   __shared__ float fin[2];
   const BandLayout& L = a.L;
   const int G = a.groups, C = L.C, cpg = C / G;
-  const int k = blockIdx.x % (L.nb + 1);
-  const int ng = blockIdx.x / (L.nb + 1);
+  const int kparts = a.want_band_moments ? L.nb + 1 : 1;
+  const int k = a.want_band_moments ? blockIdx.x % kparts : L.nb;
+  const int ng = blockIdx.x / kparts;
   const int n = ng / G, g = ng - (ng / G) * G;
   const int tid = threadIdx.x;
   const int s_idx = n * G + g, ns = L.n_img * G;
@@ -343,8 +368,7 @@ __global__ void __launch_bounds__(kThreads) gn_apply(const NormArgs a, const flo
     loadx4<XS, NT>(a.x, xrow + p * C, C, slot * V, x);
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      const float y = x[e] * sc[e] + sh[e];
-      x[e] = a.act ? silu(y) : y;
+      x[e] = gn_affine_act(x[e], sc[e], sh[e], a.act);
     }
     Out<TO>::store4(Y + ybase + p * C, x);
     if (p < L.W && b > 0) Out<TO>::store4(Y + row_up + p * C, x);
@@ -580,7 +604,7 @@ hipError_t launch_groupnorm(NormArgs& a, int dtype, hipStream_t s) {
   if (blocks_ll > 0x7fffffffLL) return hipErrorInvalidValue;
   const int blocks = (int)blocks_ll;
   // Scratch carve-up inside a.partials (sized by gn_partials_floats).
-  float* coef = reinterpret_cast<float*>(a.partials + (size_t)blocks * a.groups * 2);
+  float* coef = a.coef_out ? a.coef_out : reinterpret_cast<float*>(a.partials + (size_t)blocks * a.groups * 2);
   a.band_moments = coef + 2LL * L.n_img * L.C;
   a.stats = a.band_moments + 3LL * L.nb * L.n_img * a.groups;
   if (blocks == 0) return hipSuccess;
@@ -596,7 +620,10 @@ hipError_t launch_groupnorm(NormArgs& a, int dtype, hipStream_t s) {
     else
       hipLaunchKernelGGL((gn_stats<false, false>), dim3(blocks), dim3(kThreads), 0, s, a);
   }
-  hipLaunchKernelGGL(gn_merge, dim3(L.n_img * a.groups * (L.nb + 1)), dim3(kThreads), 0, s, a, coef);
+  // band moments (k < nb workgroups) only when the caller reads them
+  const int kparts = a.want_band_moments ? L.nb + 1 : 1;
+  hipLaunchKernelGGL(gn_merge, dim3(L.n_img * a.groups * kparts), dim3(kThreads), 0, s, a, coef);
+  if (a.stats_only) return hipGetLastError();
   a.apply_pix = apply_pixels(L);
   long long nblk = 0;   // apply workgroups: runs of apply_pix pixels per (band, image)
   for (int b = 0; b < L.nb; ++b) {

@@ -100,6 +100,11 @@ struct ConvArgs {
   int cin2;             // geometry with cin2 channels, read at the output pixel itself (a 1x1
                         // conv folded in: K grows by cin2, its weights follow the taps' in
                         // every packed row); NULL / 0 for none
+  const float* x_norm;  // bf16 path, tile128 kernel, kModeBand 3x3 convs: the input is the raw
+  int x_norm_act;       // fp32 output of the previous conv and a GroupNorm apply is folded into
+                        // the operand load -- x * scale_c + shift_c (SiLU when x_norm_act) with
+                        // x_norm = [n_img][cin][2] (scale, shift) per image and channel, taps
+                        // outside the image reading zero; NULL for none
   int final_frames;     // kModeFinal: frames per sample of the output tensor
   int out_transposed;   // kModeFinal: the bands cut the output's columns -- band-layout row g,
                         // column c is output pixel (row c, column g) of an in.W x in.H image
@@ -132,6 +137,10 @@ WideTile wide_tile(const ConvArgs& a);
 // channels, output channels a multiple of 128, band-layout epilogues.  Sub-pixel convs
 // always run there.
 bool conv_wide_fits(const ConvArgs& a);
+// Whether launch_conv runs the conv described by `a` on the tile128 kernel with a folded
+// GroupNorm apply (a.x_norm set): the shape it would run there anyway unfolded, 3x3, band
+// mode, 64-channel K steps, cin <= 512, every band's pixels a multiple of the 128-pixel tile.
+bool conv_norm_fold_ok(const ConvArgs& a);
 hipError_t launch_conv_wide(ConvArgs& a, hipStream_t s);
 // Plain 3x3 convs on the halo-tile kernel (conv_halo.hip): 4-row pixel tiles aligned to
 // global rows, the pixel operand staged once per 32-channel block.
@@ -170,6 +179,11 @@ struct NormArgs {
   int act;               // SiLU after the affine
   double* partials;      // [blocks][groups][2] fp64 (mean, M2) of each stats block, then scratch
   float* band_moments;   // [3][nb][n_img*groups] count, mean, var (device scratch)
+  int want_band_moments; // GroupNorm: also fill band_moments (each band's own tiles merged)
+  float* coef_out;       // GroupNorm: the apply's per-(image, channel) (scale, shift) go here
+                         // ([n_img][C][2]) instead of into the scratch (NULL: scratch)
+  int stats_only;         // GroupNorm: stop after the merge (the apply is folded into the
+                         // next conv, which reads coef_out)
   float* stats;          // [2][n_img*groups] merged mean, rstd
   float* merged_out;     // optional [2][n_img*groups] merged mean, var
   // GroupNorm statistics tiles.  The image is cut into slabs of `slab_rows` rows (the

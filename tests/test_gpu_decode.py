@@ -226,6 +226,40 @@ def test_full_size_bands_bit_identical_and_kernels(gpu_lib):
     dec.close()
 
 
+def test_norm_fold_gives_the_same_decode(gpu_lib):
+    """With the GroupNorm apply folded into the operand load of the latent-resolution resnet
+    convs (vaep_model_set_norm_fold), the decode is bit-identical to the one with separate
+    apply passes: the fold computes the same operand bits (same scale/shift, SiLU and
+    rounding, zero padding), and the halo rows it reads are the producing conv's raw rows.
+    Also on a band table whose odd bands keep the convs unfolded, and with batch 2."""
+    # (preset, band table, whether fewer apply passes run): at 64 latent columns a 7-row band
+    # is not a whole number of 128-pixel tiles, so the latent-resolution convs stay unfolded
+    # there (the next stage's 14-row band folds)
+    cases = ((preset(3), None, True), (preset(3), (0, 31, 64, 96, 128), True),
+             (preset(2).with_size(batch=2), None, True), (preset(2).with_size(batch=2), (0, 7, 20, 33, 64), None))
+    for cfg, starts, folds in cases:
+        dec, _ = make_decoder(cfg)
+        z = make_latent(cfg)
+        b = z.shape[0]
+        ws = dec.workspace(b, 1, cfg.latent_h, cfg.latent_w, 4)
+        starts = starts or cfg.band_starts
+        dec.set_norm_fold(False)
+        vaep.profile_begin(dec)
+        y0, rc, _ = gpu_decode(dec, cfg, z, starts, ws)
+        r0 = vaep.profile_end(dec)
+        assert rc == 0
+        dec.set_norm_fold(True)
+        vaep.profile_begin(dec)
+        y1, rc, _ = gpu_decode(dec, cfg, z, starts, ws)
+        r1 = vaep.profile_end(dec)
+        assert rc == 0
+        assert torch.equal(y0, y1), (cfg.name, starts)
+        gn0 = sum(r["n_kernels"] for r in r0 if r["step"] == L.STEP_GROUPNORM)
+        gn1 = sum(r["n_kernels"] for r in r1 if r["step"] == L.STEP_GROUPNORM)
+        assert folds is None or (gn1 < gn0) == folds, (cfg.name, starts, gn0, gn1)   # applies folded away
+        dec.close()
+
+
 def test_2048_single_band_decode_equals_band_decode(gpu_lib):
     """A 2048 x 2048 decode (256 x 256 latent, the 1024^2 model) as one band: its last
     stages' band buffers exceed 2 GiB (up to 4.3 GB of fp32 stream), beyond a buffer
