@@ -100,10 +100,10 @@ def summarise(recs, steps):
 
     for r in recs:
         if r["step"] == L.STEP_CONV:
-            # the roofline kernel: the wide kernel's plain 3x3 (x3) form with 256-channel
-            # tiles and fp32 band output (one template instance of conv_wide); other wide
-            # launches (sub-pixel upsample, split output), the 128x128-tile kernel and the
-            # narrow conv_out are reported apart
+            # the roofline kernel: the halo-tile kernel's 128-channel form (the 1024^2 stage's
+            # 3x3 convs); its 256-channel form, the wide kernel's launches (plain 3x3 at 256^2,
+            # sub-pixel upsample, split output, folded shortcut), the 128x128-tile kernel and
+            # the narrow conv_out are reported apart
             if r["kernel"] == L.KERNEL_CONV_HALO:
                 # halo-tile kernel: 128 x (4 x 128) tiles for 128-channel outputs, 256 x (4 x 64) else
                 add("conv_halo_128" if r["cout"] <= 128 else "conv_halo_256", r)
@@ -139,12 +139,12 @@ def measured_traffic():
     """HBM bytes per launch of the roofline kernel from the committed rocprofv3 counter summary,
     if the kernel source is still the one the counters were taken on (else None)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "conv_wide_3x3_1024_hbm_traffic.md")
-    src = os.path.join(ROOT, "spatially_sharded_conv_amd", "csrc", "conv_wide.hip")
+    path = os.path.join(ROOT, "profiles", "conv_halo_128_1024_hbm_traffic.md")
+    src = os.path.join(ROOT, "spatially_sharded_conv_amd", "csrc", "conv_halo.hip")
     try:
         fields = dict(l.split(": ", 1) for l in open(path).read().splitlines() if ": " in l and " " not in l.split(": ", 1)[0])
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if fields.get("conv_wide_source_sha256", "").strip() != sha:
+        if fields.get("conv_halo_source_sha256", "").strip() != sha:
             return None
         return float(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -300,12 +300,13 @@ def main():
     # event-bracketed region: per-launch kernel durations on the decode stream
     recs, ms_prof = profiled_decodes(dec, run, args.steps, info.n_launches, stream)
     cls = summarise(recs, args.steps)
-    conv = cls.get("conv_wide_3x3", {"tflops": 0.0, "flops": 0.0, "launches": 1, "avg_launch_ms": 0.0})
+    conv = cls.get("conv_halo_128", {"tflops": 0.0, "flops": 0.0, "bytes": 0.0, "launches": 1, "avg_launch_ms": 0.0})
     gn = cls.get("groupnorm") or cls.get("rmsnorm") or {"gbs": 0.0}
 
     roofline = {
-        "kernel": "conv_wide<1, 3, false, 1, 0, 256, 256, 8> (implicit-GEMM 3x3 halo conv, 256x256 tiles, 8 waves, "
-                  "LDS-DMA operands, v_mfma_f32_32x32x16_bf16)",
+        "kernel": "conv_halo<128, 128> (3x3 band conv of the 1024^2 stage: 128 output channels x 4 rows x 128 "
+                  "pixels per workgroup, halo pixel tile and weights staged in LDS by buffer-to-LDS loads once per "
+                  "32-channel block, 8 waves, v_mfma_f32_32x32x16_bf16, fp32 output with GroupNorm records)",
         "bound": "mfma",
         "achieved": round(conv["tflops"], 2),
         "peak": PEAK_BF16_TFLOPS,
@@ -315,6 +316,7 @@ def main():
         "launches_per_step": conv["launches"] // args.steps,
         "avg_launch_ms": round(conv["avg_launch_ms"], 4),
         "flops_per_launch": conv["flops"] / max(1, conv["launches"]),
+        "algorithmic_bytes_per_launch": conv.get("bytes", 0.0) / max(1, conv["launches"]),
     }
     axes, tiled, fold = {}, None, None
     if not args.only_bands and cfg.norm_groups > 0:

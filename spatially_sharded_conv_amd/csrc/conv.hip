@@ -450,9 +450,10 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
       const int rem0 = (int)(p0 - (long long)n0 * plane);
       const int cg = a.cout / a.gn_groups;
       const long long rec = gnstats::tile_record(a.out, band, n0, rem0 / wc, (rem0 % wc) / BN, wc / BN);
+      const long long tiles = (long long)a.out.H * (wc / BN);
       gnstats::tile_stats<2, 2, 4, 2, BM, false>(acc, wave, lane, cg, BN,
-                                                 a.gn_part + (rec * a.gn_groups + co0 / cg) * 2,
-                                                 reinterpret_cast<float*>(&sW[0][0]));
+                                                 gnstats::record(a.gn_part, rec, co0 / cg, a.gn_groups, tiles),
+                                                 2 * tiles, reinterpret_cast<float*>(&sW[0][0]));
     }
   }
 #pragma unroll

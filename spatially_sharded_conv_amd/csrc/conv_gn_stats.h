@@ -8,8 +8,8 @@
 // tile is the conv workgroup's pixel tile -- BN consecutive pixels of one image row (the
 // launch requires the row width to be a multiple of BN) -- so the tiling is a function of
 // the image alone and band decodes stay bit-identical to the full decode.  Tile index:
-// (image * rows + row) * (W / BN) + column / BN, the layout gn_merge reads with one-row
-// slabs and BN-pixel chunks.
+// (image * rows + row) * (W / BN) + column / BN, the tiling gn_merge reads with one-row
+// slabs and BN-pixel chunks; records are stored group-major (see record()).
 #pragma once
 
 #include "vaep_internal.h"
@@ -47,7 +47,8 @@ __device__ __forceinline__ float half_sum(float v) {
 // out WPX along the pixels and NWAVES/WPX along the channels (wave w: channel half w/WPX).
 // lds: at least NWAVES*MI*8 + BM floats + BM/4 doubles of workgroup scratch no other thread
 // uses meanwhile.  cg: channels per group (multiple of 4, divides BM).  part: the tile's
-// record, [G][2] doubles (mean, M2), already offset to the workgroup's first group.
+// record of the workgroup's first group, (mean, M2) doubles; the next group's record is
+// `gstride` doubles further (the group-major layout of record()).
 // Contains LDS barriers (lds_barrier); every thread of the workgroup must call it, and
 // the caller must have passed an lds_barrier since the last use of `lds` for anything else.
 // SPLITV: the output is stored as bf16 hi / lo parts, which the norm reads back as
@@ -63,7 +64,7 @@ __device__ __forceinline__ float seen(float v) {
 }
 template <int MI, int NJ, int NWAVES, int WPX, int BM, bool SPLITV>
 __device__ __forceinline__ void tile_stats(const f32x16_t (&val)[MI][NJ], int wave, int lane, int cg,
-                                           int tile_pixels, double* part, float* lds) {
+                                           int tile_pixels, double* part, long long gstride, float* lds) {
   constexpr int NQ = MI * 8;                  // 4-channel quads per wave (both half-waves)
   float* qs = lds;                            // [NWAVES][NQ] quad sums
   float* gmean = lds + NWAVES * NQ;           // [BM / 4] group means (fp32), indexed by group
@@ -93,8 +94,8 @@ __device__ __forceinline__ void tile_stats(const f32x16_t (&val)[MI][NJ], int wa
         // sum (x - m_f)^2 = M2 + n (m - m_f)^2 with m_f the fp32 mean used by the lanes
         const double d = gm64[gi] - (double)gmean[gi];
         double m2 = s - cnt * d * d;
-        part[2 * gi] = gm64[gi];
-        part[2 * gi + 1] = m2 > 0.0 ? m2 : 0.0;
+        part[gi * gstride] = gm64[gi];
+        part[gi * gstride + 1] = m2 > 0.0 ? m2 : 0.0;
       }
     }
     if (!second) lds_barrier();   // the group means are read by every lane next
@@ -132,6 +133,14 @@ __device__ __forceinline__ void tile_stats(const f32x16_t (&val)[MI][NJ], int wa
       if ((lane & 31) == 0) qs[wave * NQ + (i * 4 + g) * 2 + h] = s;
     }
   reduce_groups(true);
+}
+
+// Records are stored [image][group][tile of the image][2] doubles (mean, M2), `tiles` per
+// image and group, so that the merge reads each group's records contiguously.  rec: the
+// tile's index image * tiles + tile; g: the group.
+__device__ __forceinline__ double* record(double* gn_part, long long rec, int g, int groups, long long tiles) {
+  const long long n = rec / tiles;
+  return gn_part + ((n * groups + g) * tiles + (rec - n * tiles)) * 2;
 }
 
 // Record of the tile holding pixel p0 (first pixel of the workgroup tile) of band b in the

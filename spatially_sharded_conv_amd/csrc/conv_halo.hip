@@ -287,12 +287,13 @@ __global__ void __launch_bounds__(512, 1) conv_halo(const ConvArgs a) {
 
   // Epilogue 2: GroupNorm statistics of the output row (when a GroupNorm reads it next):
   // per group, mean and M2 = sum (x - mean)^2 over the TW pixels of this row and tile and
-  // the group's channels, two-pass; record (image * H + row) * (W / TW) + column / TW.
+  // the group's channels, two-pass; record (image * H + row) * (W / TW) + column / TW in
+  // the group-major layout of gnstats::record.
   if (a.gn_part && row_ok) {
     const int cg = a.cout / a.gn_groups;               // 4, 8 or 16 (the launch checks)
     const double cnt = (double)TW * cg;
     const long long rec = ((long long)n * H + gw) * ctiles + c0 / TW;
-    double* part = a.gn_part + rec * a.gn_groups * 2;
+    const long long tiles = (long long)H * ctiles;
     // quad sums: channels co0 + wco + 32 i + 8 g + 4 h + 0..3 over the wave's pixels
     float qs[MI][4];
 #pragma unroll
@@ -366,8 +367,9 @@ __global__ void __launch_bounds__(512, 1) conv_halo(const ConvArgs a) {
           const double mx = (double)gs[i][g] / cnt;
           const double d = mx - (double)mean[i][g];
           const double m2 = (double)gm2[i][g] - cnt * d * d;
-          part[2 * grp] = mx;
-          part[2 * grp + 1] = m2 > 0.0 ? m2 : 0.0;
+          double* pr = gnstats::record(a.gn_part, rec, grp, a.gn_groups, tiles);
+          pr[0] = mx;
+          pr[1] = m2 > 0.0 ? m2 : 0.0;
         }
       }
   }

@@ -579,8 +579,10 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
     const long long rec = gnstats::tile_record(a.out, band, n0, SUB ? 2 * r0 + py : r0,
                                                (SUB ? px * (W / BN) : 0) + c0 / BN, chunks);
     const int cg = a.cout / a.gn_groups;
+    const long long tiles = (long long)a.out.H * chunks;
     gnstats::tile_stats<MI, NJ, NW, WPX, BM, decltype(splitv)::value>(
-        acc, wave, lane, cg, BN, a.gn_part + (rec * a.gn_groups + co0 / cg) * 2, reinterpret_cast<float*>(smem));
+        acc, wave, lane, cg, BN, gnstats::record(a.gn_part, rec, co0 / cg, a.gn_groups, tiles), 2 * tiles,
+        reinterpret_cast<float*>(smem));
   };
   if (MODE == kModeBandSplit && gn) gn_stats(std::true_type{});
   if (MODE == kModeBandSplit) {

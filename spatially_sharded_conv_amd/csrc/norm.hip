@@ -197,7 +197,8 @@ __global__ void __launch_bounds__(kThreads) gn_stats(const NormArgs a) {
       const double dm = mean - (double)shift[c];
       m2 += a2 - 2.0 * dm * a1 + cnt * dm * dm;
     }
-    double* out = a.partials + ((long long)blk * G + tid) * 2;
+    // group-major records: [image][group][tile of the image]
+    double* out = a.partials + (((long long)n * G + tid) * per_img + (blk - n * per_img)) * 2;
     out[0] = mean;
     out[1] = m2 > 0.0 ? m2 : 0.0;
   }
@@ -227,7 +228,8 @@ __device__ void merge_tiles(const NormArgs& a, int n, int g, int t0, int t1, dou
   const int tid = threadIdx.x;
   const int G = a.groups, cpg = a.L.C / G;
   const long long slab_pix = (long long)a.slab_rows * a.L.W;
-  const double* P = a.partials + ((long long)n * a.slabs * a.chunks) * G * 2;
+  // group g's records of image n, contiguous (group-major layout)
+  const double* P = a.partials + ((long long)n * G + g) * ((long long)a.slabs * a.chunks) * 2;
   auto tile_n = [&](int t) {
     const int chunk = t % a.chunks;
     long long tp = slab_pix - (long long)chunk * a.chunk_pix;
@@ -239,14 +241,14 @@ __device__ void merge_tiles(const NormArgs& a, int n, int g, int t0, int t1, dou
   // Each thread takes tiles t0 + tid, t0 + tid + kThreads, ... in that order; the loads of a
   // batch of kBatch tiles are issued together (one memory latency per batch, not per tile),
   // the sums still run tile by tile.
-  constexpr int kBatch = 16;
+  constexpr int kBatch = 8;
   double s = 0.0;
   for (int t_b = t0 + tid; t_b < t1; t_b += kBatch * kThreads) {
     double mt[kBatch];
 #pragma unroll
     for (int r = 0; r < kBatch; ++r) {
       const int t = t_b + r * kThreads;
-      mt[r] = t < t1 ? P[((long long)t * G + g) * 2] : 0.0;
+      mt[r] = t < t1 ? P[(long long)t * 2] : 0.0;
     }
 #pragma unroll
     for (int r = 0; r < kBatch; ++r) {
@@ -261,7 +263,7 @@ __device__ void merge_tiles(const NormArgs& a, int n, int g, int t0, int t1, dou
 #pragma unroll
     for (int r = 0; r < kBatch; ++r) {
       const int t = t_b + r * kThreads;
-      const double* pr = P + ((long long)(t < t1 ? t : t0) * G + g) * 2;
+      const double* pr = P + (long long)(t < t1 ? t : t0) * 2;
       mt[r] = pr[0];
       vt[r] = pr[1];
     }

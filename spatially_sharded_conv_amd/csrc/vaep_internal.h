@@ -112,8 +112,8 @@ struct ConvArgs {
   int tile_start[kMaxBands + 1];  // prefix of M tiles per band
   int kernel_used;      // set by the launch: VAEP_KERNEL_*
   // GroupNorm statistics of the output for the norm that consumes it (kModeBand /
-  // kModeBandSplit).  The caller sets gn_part (fp64 tile records, [tiles][gn_groups][2]
-  // mean and M2) and gn_groups; the launch keeps gn_part only if the kernel it picks forms
+  // kModeBandSplit).  The caller sets gn_part (fp64 tile records, [n_img][gn_groups][tiles
+  // of one image][2] mean and M2) and gn_groups; the launch keeps gn_part only if the kernel it picks forms
   // the records in its epilogue (pixel tiles of whole rows), sets gn_chunk to the tile
   // width in pixels, and else clears gn_part and gn_chunk.  Tile index:
   // (image * out.H + row) * (out.W / gn_chunk) + column / gn_chunk.
@@ -177,7 +177,8 @@ struct NormArgs {
   const float* gamma;
   const float* beta;
   int act;               // SiLU after the affine
-  double* partials;      // [blocks][groups][2] fp64 (mean, M2) of each stats block, then scratch
+  double* partials;      // [n_img][groups][blocks of one image][2] fp64 (mean, M2) of each
+                         // stats block, then scratch
   float* band_moments;   // [3][nb][n_img*groups] count, mean, var (device scratch)
   int want_band_moments; // GroupNorm: also fill band_moments (each band's own tiles merged)
   float* coef_out;       // GroupNorm: the apply's per-(image, channel) (scale, shift) go here
