@@ -27,8 +27,14 @@
  *     stream has finished.  No entry point synchronises the stream, except
  *     vaep_model_create (see there).
  *   - Return value: VAEP_OK (0) on success, a positive warning code on success with a
- *     warning, or a negative error code.  On error nothing has been enqueued and
- *     output buffers are untouched; vaep_last_error() describes the failure.
+ *     warning, or a negative error code; vaep_last_error() describes the failure.
+ *     Argument, shape, band-table and workspace errors (INVALID_ARG, UNSUPPORTED,
+ *     WORKSPACE, NOT_READY) are found before anything is enqueued: nothing has run and
+ *     output buffers are untouched.  VAEP_ERR_HIP reports a HIP call that failed while
+ *     work was being enqueued (a kernel launch the runtime or a kernel's own launch
+ *     checks refused, such as a band buffer whose rows exceed a buffer resource's
+ *     range); earlier layers of that call may already be enqueued and the output is
+ *     then undefined.
  *   - No C++ exception crosses this boundary.
  */
 #ifndef VAEP_H
