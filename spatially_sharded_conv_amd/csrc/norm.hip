@@ -562,9 +562,15 @@ static int chunk_pixels(const BandLayout& L) {
   const long long pix = tb / (4LL * L.C);
   return (int)(pix < 1 ? 1 : pix);
 }
-// Apply run length: enough workgroups to fill the GPU on small layers.
+// Apply run length: enough workgroups to fill the GPU on small layers.  Tensors below the
+// streaming threshold (cache-resident, latency-bound) get runs of four pixels per thread
+// lane, so that each thread's loop is four loads long.
 static int apply_pixels(const BandLayout& L) {
   const long long pix = (long long)L.n_img * L.H * L.W;
+  if (pix * L.C * 4 < kStreamBytes) {
+    const int lanes = kThreads / (L.C / V);   // pixel lanes of a workgroup
+    return 4 * (lanes < 1 ? 1 : lanes);
+  }
   long long run = pix / 2048;
   if (run < 32) run = 32;
   if (run > 256) run = 256;
