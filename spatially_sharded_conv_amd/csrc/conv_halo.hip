@@ -199,11 +199,31 @@ __global__ void __launch_bounds__(512, 1) conv_halo(const ConvArgs a) {
   // block's halo tile into the other halo stage (read last in the previous block), so the
   // loads go out between groups of matrix products.  Every load issued during a step has
   // landed by the next step's barrier.
+  // Fragments of sub-step u = 2 dx + kk (tap dx, 16-channel half kk) of a step; the reads
+  // of sub-step u + 1 go out before the products of u (two fragment sets), so LDS latency
+  // hides behind matrix work within the wave.
+  auto read_frags = [&](const unsigned char* AB, const unsigned char* HB, int dy, int u, bf16x8_t(&af)[MI],
+                        bf16x8_t(&bfr)[NJ]) {
+    const int dx = u >> 1, c = 2 * (u & 1) + h;
+    const int dq = (dy - 1) * HW + (dx - 1);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int r = wco + 32 * i + (lane & 31);
+      af[i] = *reinterpret_cast<const bf16x8_t*>(AB + (dx * BM + r) * 64 + ((c ^ ((r >> 2) & 3)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int q = pq[j] + dq;
+      bfr[j] = *reinterpret_cast<const bf16x8_t*>(HB + q * 64 + ((c ^ ((q >> 2) & 3)) << 4));
+    }
+  };
   for (int s = 0; s < nsteps; ++s) {
     const int cb = s / 3, dy = s - 3 * cb;
     asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const unsigned char* HB = smem + (cb & 1) * HST;
     const unsigned char* AB = smem + 2 * HST + (s & 1) * AST;
+    bf16x8_t af[2][MI], bfr[2][NJ];
+    read_frags(AB, HB, dy, 0, af[0], bfr[0]);
 #pragma unroll
     for (int dx = 0; dx < 3; ++dx) {
       __builtin_amdgcn_sched_barrier(0);
@@ -215,26 +235,29 @@ __global__ void __launch_bounds__(512, 1) conv_halo(const ConvArgs a) {
           if (k * 3 / HROUNDS == dy && k % 3 == dx) VAEP_HALO_ISSUE((cb + 1) & 1, cb + 1, k);
       }
       __builtin_amdgcn_sched_barrier(0);
-      const int dq = (dy - 1) * HW + (dx - 1);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const int c = 2 * kk + h;
-        bf16x8_t af[MI], bfr[NJ];
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-          const int r = wco + 32 * i + (lane & 31);
-          af[i] = *reinterpret_cast<const bf16x8_t*>(AB + (dx * BM + r) * 64 + ((c ^ ((r >> 2) & 3)) << 4));
-        }
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int q = pq[j] + dq;
-          bfr[j] = *reinterpret_cast<const bf16x8_t*>(HB + q * 64 + ((c ^ ((q >> 2) & 3)) << 4));
-        }
+        const int u = 2 * dx + kk, cur = u & 1;
+        if (u + 1 < 6) read_frags(AB, HB, dy, u + 1, af[cur ^ 1], bfr[cur ^ 1]);
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+      }
+      // issue order: each read of the next sub-step between two products of this one
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        if (2 * dx + kk + 1 < 6) {
+#pragma unroll
+          for (int t = 0; t < MI + NJ; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ - (MI + NJ), 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ, 0);
+        }
       }
     }
   }
