@@ -154,6 +154,18 @@ int vaep_model_destroy(vaep_model* model);
  * the workspace size does not depend on it.  Errors: INVALID_ARG (NULL model). */
 int vaep_model_set_norm_fold(vaep_model* model, int on);
 
+/* Debug mode for the halo exchange.  Before each layer writes a band buffer (conv, norm
+ * and attention outputs), every halo slot of that buffer -- the row above and below each
+ * band, per image -- is filled with 0xFF bytes, which is NaN in every float format the
+ * buffers hold.  A layer's halo rows must come from its neighbours' boundary rows
+ * (ChituDiffusion "VAEP" feature page, convolution section: the halo rows exchanged before
+ * each conv; "Static Layer-Wise VAE Decode", operator table, "Spatial convolution" row), and
+ * slots past the image edge must never be read (they stand for zero padding); a slot read
+ * before its push, or an edge slot read at all, turns outputs into NaN.  A decode that is
+ * correct gives the same bits with or without it.  Costs one fill kernel per such layer.
+ * on: 0 (default) or 1.  Affects later decodes of `model`.  Errors: INVALID_ARG (NULL model). */
+int vaep_model_set_halo_poison(vaep_model* model, int on);
+
 /* Workspace needed to decode a latent of `batch` x [frames x] latent_h x latent_w
  * with up to `n_bands` bands (frames = 1 for KL2D).  The same size serves
  * vaep_decode_full, every band table with at most n_bands bands, and

@@ -31,6 +31,7 @@ AXIS_AUTO, AXIS_HEIGHT, AXIS_WIDTH, AXIS_DENSE, AXIS_TILE = 0, 1, 2, 3, 4
 EXPORTS = [
     "vaep_last_error", "vaep_version", "vaep_config_preset", "vaep_param_count",
     "vaep_param_info", "vaep_model_create", "vaep_model_destroy", "vaep_model_set_norm_fold",
+    "vaep_model_set_halo_poison",
     "vaep_workspace_bytes",
     "vaep_decode_full", "vaep_decode_bands", "vaep_select_axis", "vaep_decode_sharded",
     "vaep_sharded_workspace_bytes", "vaep_noalloc_scratch_bytes", "vaep_decode_bands_noalloc",
@@ -98,6 +99,7 @@ def _proto(lib):
     f("vaep_model_create", I, C.POINTER(VaepConfig), C.POINTER(P), I, P, C.POINTER(P))
     f("vaep_model_destroy", I, P)
     f("vaep_model_set_norm_fold", I, P, I)
+    f("vaep_model_set_halo_poison", I, P, I)
     f("vaep_workspace_bytes", I, P, I, I, I, I, I, C.POINTER(SZ))
     f("vaep_decode_full", I, P, P, I, I, I, I, P, P, SZ, P)
     f("vaep_decode_bands", I, P, P, I, I, I, I, C.POINTER(C.c_int32), I, P, P, SZ, P,

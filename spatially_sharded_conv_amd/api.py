@@ -93,6 +93,11 @@ class Decoder:
         it (vaep_model_set_norm_fold); the decoded output is the same."""
         L.check(L.load().vaep_model_set_norm_fold(self._h, 1 if on else 0))
 
+    def set_halo_poison(self, on: bool):
+        """Debug mode: every halo slot of a band buffer is filled with NaN before the layer
+        that writes the buffer runs (vaep_model_set_halo_poison)."""
+        L.check(L.load().vaep_model_set_halo_poison(self._h, 1 if on else 0))
+
     def close(self):
         if getattr(self, "_h", None):
             L.check(L.load().vaep_model_destroy(self._h))

@@ -237,6 +237,7 @@ struct Profiler {
 struct vaep_model {
   vaep_config cfg;
   int fold_norm = 0;   // vaep_model_set_norm_fold
+  int poison_halos = 0;   // vaep_model_set_halo_poison
   void* mem = nullptr;
   size_t mem_bytes = 0;
   Profiler prof;
@@ -475,6 +476,16 @@ struct Exec {
 
   size_t eb() const { return dtype_bytes(dtype); }   // operand (normalised activation) element
   void need_act(const BandLayout& L, size_t elem) { act_bytes = std::max(act_bytes, (size_t)layout_elems(L) * elem); }
+  // Debug mode: the halo slots of a band buffer a layer is about to write are filled with NaN
+  // first, so a slot read before the neighbour's push (or an image-edge slot read at all)
+  // poisons the result.
+  int poison(void* y, const BandLayout& L, int elem_bytes) {
+    if (dry || !m || !m->poison_halos) return VAEP_OK;
+    hipError_t e = launch_poison_halos(y, L, elem_bytes, st);
+    if (e != hipSuccess) return hip_fail(e, "halo poison");
+    ++launches;
+    return VAEP_OK;
+  }
 
   size_t total() const {
     return 4 * align_up(act_bytes, 256) + 3 * align_up(qkv_bytes, 256) + align_up(scratch_bytes, 256) +
@@ -560,6 +571,10 @@ struct Exec {
     a.gn_groups = gn_next ? groups : 0;
     if (Lin.C != (xk == kXSplit ? 2 : 1) * w.ci_pad)
       return fail(VAEP_ERR_INVALID_ARG, "internal: conv input has %d channels, weight %d", Lin.C, w.ci_pad);
+    if (mode == kModeBand || mode == kModeTimeInterleave || mode == kModeBandSplit) {
+      const int rc = poison(y, Lout, mode == kModeBandSplit ? 2 : 4);
+      if (rc) return rc;
+    }
     {
       vaep_profile_entry pe = entry(VAEP_STEP_CONV, 1);
       const long long m = (long long)Lin.n_img * Lin.H * Lin.W * (ups ? 4 : 1);
@@ -641,6 +656,10 @@ struct Exec {
     a.stats_only = stats_only ? 1 : 0;
     a.coef_out = stats_only ? ncoef : nullptr;
     const int nk = groups > 0 ? (pre ? 2 : 3) - (stats_only ? 1 : 0) : 1;
+    if (!stats_only) {
+      const int rc = poison(y, L, (int)eb());
+      if (rc) return rc;
+    }
     {
       vaep_profile_entry pe = entry(groups > 0 ? VAEP_STEP_GROUPNORM : VAEP_STEP_RMSNORM, nk);
       const double elems = (double)L.n_img * L.H * L.W * L.C;
@@ -685,6 +704,7 @@ struct Exec {
     rc = conv(w.qkv, a_buf, L, kXOp, nullptr, L, kModeQKV, nullptr, 0);
     if (rc) return rc;
     need_act(L, eb());
+    if ((rc = poison(o_buf, L, (int)eb()))) return rc;
     if (!dry) {
       AttnArgs aa;
       std::memset(&aa, 0, sizeof(aa));
@@ -1191,6 +1211,12 @@ int vaep_model_destroy(vaep_model* model) {
 int vaep_model_set_norm_fold(vaep_model* model, int on) {
   if (!model) return fail(VAEP_ERR_INVALID_ARG, "model is NULL");
   model->fold_norm = on ? 1 : 0;
+  return VAEP_OK;
+}
+
+int vaep_model_set_halo_poison(vaep_model* model, int on) {
+  if (!model) return fail(VAEP_ERR_INVALID_ARG, "model is NULL");
+  model->poison_halos = on ? 1 : 0;
   return VAEP_OK;
 }
 

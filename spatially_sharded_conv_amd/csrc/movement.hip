@@ -63,6 +63,21 @@ __global__ void copy_frame0_kernel(const T* src, const BandLayout Ls, T* dst, co
     d[i] = s[i];
 }
 
+// Debug fill of every halo slot (the row above and below each band, per image) with 0xFF
+// bytes: NaN as fp32, bf16 and either fp8 format.  Slot blockIdx.y = (band, image, side);
+// the row holds row_words 32-bit words.
+__global__ void poison_halo_kernel(unsigned* buf, const BandLayout L, int elem_bytes) {
+  const int k = blockIdx.y;
+  const int side = k & 1, bn = k >> 1;
+  const int b = bn / L.n_img, n = bn - b * L.n_img;
+  const long long row_elems = (long long)L.W * L.C;
+  const long long slot = (long long)n * (L.rows[b] + 2) + (side ? L.rows[b] + 1 : 0);
+  const long long first = (L.off[b] + slot * row_elems) * elem_bytes / 4;
+  const long long words = row_elems * elem_bytes / 4;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (long long)gridDim.x * blockDim.x)
+    buf[first + i] = 0xffffffffu;
+}
+
 template <typename T>
 __global__ void pack_weight_kernel(const T* src, int co, int ci, int taps, T* dst, int co_pad,
                                    int ci_pad, int rep, int tr) {
@@ -337,6 +352,18 @@ hipError_t launch_copy_frame0(const void* src, const BandLayout& Ls, void* dst, 
     hipLaunchKernelGGL(copy_frame0_kernel<float>, grid, dim3(256), 0, s, (const float*)src, Ls, (float*)dst, Ld);
   else
     hipLaunchKernelGGL(copy_frame0_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)src, Ls, (bf16*)dst, Ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_poison_halos(void* buf, const BandLayout& L, int elem_bytes, hipStream_t s) {
+  const long long slots = 2LL * L.nb * L.n_img;
+  if (slots == 0 || L.W == 0 || L.C == 0) return hipSuccess;
+  if (slots > 65535 || (elem_bytes != 2 && elem_bytes != 4) || ((long long)L.W * L.C * elem_bytes) % 4 != 0 ||
+      (reinterpret_cast<unsigned long long>(buf) & 3) != 0)
+    return hipErrorInvalidValue;
+  const long long words = (long long)L.W * L.C * elem_bytes / 4;
+  dim3 grid((unsigned)std::min<long long>((words + 255) / 256, 64), (unsigned)slots);
+  hipLaunchKernelGGL(poison_halo_kernel, grid, dim3(256), 0, s, reinterpret_cast<unsigned*>(buf), L, elem_bytes);
   return hipGetLastError();
 }
 

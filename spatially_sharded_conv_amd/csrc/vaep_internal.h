@@ -245,6 +245,9 @@ hipError_t launch_unpack(const void* src, const BandLayout& L, void* dst, int c_
                          hipStream_t s);
 // Copy frame 0 of every sample of `src` (frames T) to frame 0 of `dst` (frames 2T-1),
 // halo rows included.
+// Debug: fill every halo slot of a band buffer (elements of elem_bytes = 2 or 4) with 0xFF
+// bytes (NaN in every float format the buffers hold).
+hipError_t launch_poison_halos(void* buf, const BandLayout& L, int elem_bytes, hipStream_t s);
 hipError_t launch_copy_frame0(const void* src, const BandLayout& Ls, void* dst,
                               const BandLayout& Ld, int dtype, hipStream_t s);
 // Conv weight [co][ci][taps] (dtype) -> [co_pad][taps][rep * ci_pad] (dtype), zero padded;

@@ -98,6 +98,12 @@ def test_model_create_rejects_bad_param_counts_without_gpu_work():
     assert not h.value
 
 
+def test_model_switches_reject_a_null_model():
+    lib = L.load()
+    assert lib.vaep_model_set_norm_fold(None, 1) == L.VAEP_ERR_INVALID_ARG
+    assert lib.vaep_model_set_halo_poison(None, 1) == L.VAEP_ERR_INVALID_ARG
+
+
 def test_groupnorm_merge_argument_checks():
     lib = L.load()
     assert lib.vaep_groupnorm_merge(0, 4, None, None, None, None, None, None) == L.VAEP_ERR_INVALID_ARG

@@ -260,6 +260,50 @@ def test_norm_fold_gives_the_same_decode(gpu_lib):
         dec.close()
 
 
+def test_halo_poison_gives_the_same_decode(gpu_lib):
+    """With every halo slot of a band buffer filled with NaN before the layer that writes
+    it (vaep_model_set_halo_poison), a decode gives the same bits as without: each halo row
+    a layer reads came from its neighbour's push in that decode, and no slot past the image
+    edge is read.  One-band, uneven and one-row band tables; width bands; the full-size
+    1024^2, batch-4 and video presets; the folded GroupNorm apply."""
+    def width_decode(dec, cfg, latent, starts):
+        lat = to_dev(latent, cfg.dtype)
+        out = torch.empty(cfg.output_shape(latent.shape[0], 1, *latent.shape[-2:]), dtype=torch.float32,
+                          device="cuda")
+        ws = dec.workspace(latent.shape[0], 1, *latent.shape[-2:], len(starts) - 1)
+        rc, info = dec.decode_sharded(lat, "width", len(starts) - 1, out, ws, starts)
+        torch.cuda.synchronize()
+        return out, rc, info
+
+    cases = [(preset(1), (0, 8), "height", False), (preset(1), (0, 3, 8), "height", False),
+             (preset(1), tuple(range(9)), "height", False), (preset(1), (0, 3, 8), "width", False),
+             (preset(2).with_size(batch=2), (0, 7, 20, 33, 64), "width", False),
+             (preset(3), None, "height", False), (preset(3), (0, 1, 2, 64, 127, 128), "height", False),
+             (preset(3), None, "height", True), (preset(4), None, "height", False),
+             (preset(5), None, "height", False), (preset(5), (0, 1, 29, 30, 60), "height", False)]
+    for cfg, starts, axis, fold in cases:
+        dec, _ = make_decoder(cfg)
+        z = make_latent(cfg)
+        starts = starts or cfg.band_starts
+        dec.set_norm_fold(fold)
+        outs = []
+        for poison in (False, True):
+            dec.set_halo_poison(poison)
+            if axis == "height":
+                y, rc, info = gpu_decode(dec, cfg, z, starts)
+            else:
+                y, rc, info = width_decode(dec, cfg, z, starts)
+            assert rc == 0 and info.bands_used == len(starts) - 1
+            outs.append((y, info.n_launches))
+        (y0, n0), (y1, n1) = outs
+        what = (cfg.name, starts, axis, fold)
+        assert n1 > n0, what                      # the fills ran
+        assert not torch.isnan(y1).any().item(), what
+        assert torch.equal(y0, y1), what
+        dec.close()
+        del outs, y0, y1
+
+
 def test_2048_single_band_decode_equals_band_decode(gpu_lib):
     """A 2048 x 2048 decode (256 x 256 latent, the 1024^2 model) as one band: its last
     stages' band buffers exceed 2 GiB (up to 4.3 GB of fp32 stream), beyond a buffer
