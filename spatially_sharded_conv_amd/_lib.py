@@ -9,7 +9,9 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libvaep.so")
+# VAEP_LIB selects another build of the same library (the host-sanitized one of
+# build_sanitized.py); there is no other implementation to fall back to.
+LIB_PATH = os.environ.get("VAEP_LIB") or os.path.join(HERE, "libvaep.so")
 
 VAEP_OK = 0
 VAEP_WARN_FELL_BACK = 1
