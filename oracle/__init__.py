@@ -15,7 +15,8 @@ What it computes follows the pages on the method:
 * The distributed-VAE strategy page -- "Strategy Selection Contract" and the
   Wan spatial-shard notes (height or width sharding, the ``auto`` axis
   policy), and the tile/patch decode (split / exec / merge with overlap
-  blending), the comparison baseline in ``tiled.py``.
+  blending), the comparison baseline in ``tiled.py``, and the tile/patch encode
+  (``encoder.py``: the encoder of the 2-D presets on overlapping image tiles).
 
 Both pages state that the layer-wise decode keeps full-image semantics, so the
 oracle's primary output is the plain full-image decoder forward
@@ -31,13 +32,15 @@ Parity status of every function is listed in ``oracle/PINS.md``.
 """
 from .ops import (conv_padded, conv_full, conv_band, groupnorm_moments, merge_moments,
                   groupnorm_apply, rmsnorm, silu, attention_rows, upsample_nearest2x,
-                  temporal_upsample_interleave)
+                  temporal_upsample_interleave, downsample_conv)
 from .decoder import decode_full, decode_bands, decode_auto, choose_axis, even_starts, Precision
 from .tiled import blend_h, blend_v, decode_tiled, row_seam, tile_origins
+from .encoder import encode_full, encode_tiled
 
 __all__ = [
     "conv_padded", "conv_full", "conv_band", "groupnorm_moments", "merge_moments",
     "groupnorm_apply", "rmsnorm", "silu", "attention_rows", "upsample_nearest2x",
     "temporal_upsample_interleave", "decode_full", "decode_bands", "decode_auto", "choose_axis",
     "even_starts", "Precision", "blend_h", "blend_v", "decode_tiled", "row_seam", "tile_origins",
+    "downsample_conv", "encode_full", "encode_tiled",
 ]

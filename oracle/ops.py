@@ -220,6 +220,30 @@ def attention_rows(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: flo
     return out
 
 
+def downsample_conv(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor], finish) -> torch.Tensor:
+    """Stride-2 3x3 convolution of the encoder's down stages (2-D, T = 1).
+
+    The input is zero-padded by one row at the bottom and one column at the right
+    (none at the top or left), and
+    ``y[n,o,0,h,w] = bias[o] + sum_{i,dy,dx} W[o,i,0,dy,dx] * xp[n,i,0,2h+dy,2w+dx]``
+    for h < H/2, w < W/2 (H and W even), accumulated in float64, then ``finish``.
+    """
+    n_img, ci, t, hh, ww = x.shape
+    co, ci2, kt, kh, kw = w.shape
+    assert ci == ci2 and t == 1 and kt == 1 and kh == 3 and kw == 3 and hh % 2 == 0 and ww % 2 == 0
+    ho, wo = hh // 2, ww // 2
+    xp = torch.nn.functional.pad(x.to(F64), (0, 1, 0, 1))
+    y = torch.zeros((n_img, co, 1, ho, wo), dtype=F64)
+    if b is not None:
+        y += b.to(F64).view(1, co, 1, 1, 1)
+    for dy in range(3):
+        for dx in range(3):
+            xs = xp[:, :, :, dy:dy + 2 * ho:2, dx:dx + 2 * wo:2]            # [N, Ci, 1, Ho, Wo]
+            wt = w[:, :, 0, dy, dx].to(F64)                                # [Co, Ci]
+            y += torch.matmul(wt, xs.reshape(n_img, ci, -1)).view(n_img, co, 1, ho, wo)
+    return finish(y)
+
+
 def upsample_nearest2x(x: torch.Tensor) -> torch.Tensor:
     """u[..., y, x] = v[..., floor(y/2), floor(x/2)] on H and W."""
     return x.repeat_interleave(2, dim=3).repeat_interleave(2, dim=4)

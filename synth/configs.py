@@ -14,6 +14,14 @@ up block but the last, and GroupNorm -> SiLU -> conv_out to RGB.  The Wan
 variant swaps GroupNorm for channel RMSNorm, 2D convs for causal 3x3x3 convs,
 runs the mid attention per frame, and adds a causal temporal upsample in the
 first ``temporal_up_stages`` up stages.
+
+The 2-D presets also describe the encoder of the tiled encode (``encoder_param_specs``):
+the decoder's mirror -- conv_in from RGB to the narrowest width, down stages over
+``block_out_channels`` with one resnet fewer than the decoder's up stages (the
+common AutoencoderKL layout: two per down block, three per up block) and a 3x3
+stride-2 convolution after every stage but the last, the same mid block, then
+GroupNorm -> SiLU -> conv_out to 2 x z channels (mean and log-variance) and a 1x1
+``quant_conv`` over them.
 """
 from __future__ import annotations
 
@@ -80,6 +88,26 @@ class DecoderConfig:
             return (b, self.z_channels, t, h, w)
         return (b, self.z_channels, h, w)
 
+    @property
+    def encoder_resnets(self) -> int:
+        """Resnets per encoder down stage (2-D presets): one fewer than per decoder up stage."""
+        return max(1, self.resnets_per_stage - 1)
+
+    def image_shape(self, batch=None, latent_h=None, latent_w=None):
+        """The image an encoder reads: (B, 3, H, W) at the decoder's output resolution."""
+        b = self.batch if batch is None else batch
+        h = self.latent_h if latent_h is None else latent_h
+        w = self.latent_w if latent_w is None else latent_w
+        ups = self.n_stages - 1
+        return (b, 3, h << ups, w << ups)
+
+    def moments_shape(self, batch=None, latent_h=None, latent_w=None):
+        """The encoder's output: (B, 2 z, H / 2^(n_stages-1), W / 2^(n_stages-1)), mean | log-variance."""
+        b = self.batch if batch is None else batch
+        h = self.latent_h if latent_h is None else latent_h
+        w = self.latent_w if latent_w is None else latent_w
+        return (b, 2 * self.z_channels, h, w)
+
     def with_size(self, **kw) -> "DecoderConfig":
         d = dict(self.__dict__)
         d.update(kw)
@@ -139,28 +167,37 @@ def _norm(name, c, video):
     return [ParamSpec(name + ".weight", (c,), "gamma"), ParamSpec(name + ".bias", (c,), "beta")]
 
 
+def _resnet_specs(out, prefix, ci, co, v):
+    k3 = (3, 3, 3) if v else (3, 3)
+    k1 = (1, 1, 1) if v else (1, 1)
+    out.extend(_norm(prefix + ".norm1", ci, v))
+    out.extend(_conv(prefix + ".conv1", co, ci, k3))
+    out.extend(_norm(prefix + ".norm2", co, v))
+    out.extend(_conv(prefix + ".conv2", co, co, k3))
+    if ci != co:
+        out.extend(_conv(prefix + ".shortcut", co, ci, k1))
+
+
+def _mid_specs(out, c, v):
+    _resnet_specs(out, "mid.res0", c, c, v)
+    out.extend(_norm("mid.attn.norm", c, v))
+    for p in ("q", "k", "v", "out"):
+        out.extend(_lin("mid.attn." + p, c, c))
+    _resnet_specs(out, "mid.res1", c, c, v)
+
+
 def param_specs(cfg: DecoderConfig) -> List[ParamSpec]:
     """Canonical, ordered parameter list of the decoder described by ``cfg``."""
     v = cfg.is_video
     k3 = (3, 3, 3) if v else (3, 3)
-    k1 = (1, 1, 1) if v else (1, 1)
     out: List[ParamSpec] = []
 
     def resnet(prefix, ci, co):
-        out.extend(_norm(prefix + ".norm1", ci, v))
-        out.extend(_conv(prefix + ".conv1", co, ci, k3))
-        out.extend(_norm(prefix + ".norm2", co, v))
-        out.extend(_conv(prefix + ".conv2", co, co, k3))
-        if ci != co:
-            out.extend(_conv(prefix + ".shortcut", co, ci, k1))
+        _resnet_specs(out, prefix, ci, co, v)
 
     c = cfg.top_channels
     out.extend(_conv("conv_in", c, cfg.z_channels, k3))
-    resnet("mid.res0", c, c)
-    out.extend(_norm("mid.attn.norm", c, v))
-    for p in ("q", "k", "v", "out"):
-        out.extend(_lin("mid.attn." + p, c, c))
-    resnet("mid.res1", c, c)
+    _mid_specs(out, c, v)
     prev = c
     for i, co in enumerate(cfg.stage_channels):
         for j in range(cfg.resnets_per_stage):
@@ -172,4 +209,25 @@ def param_specs(cfg: DecoderConfig) -> List[ParamSpec]:
             out.extend(_conv(f"up{i}.upsample", co, co, (3, 3)))
     out.extend(_norm("norm_out", prev, v))
     out.extend(_conv("conv_out", 3, prev, k3))
+    return out
+
+
+def encoder_param_specs(cfg: DecoderConfig) -> List[ParamSpec]:
+    """Canonical, ordered parameter list of the encoder of a 2-D preset (see the module text)."""
+    if cfg.is_video:
+        raise ValueError("the tiled encode is built for the 2-D (AutoencoderKL) presets only")
+    block_out = tuple(reversed(cfg.stage_channels))
+    out: List[ParamSpec] = []
+    out.extend(_conv("conv_in", block_out[0], 3, (3, 3)))
+    prev = block_out[0]
+    for i, co in enumerate(block_out):
+        for j in range(cfg.encoder_resnets):
+            _resnet_specs(out, f"down{i}.res{j}", prev, co, False)
+            prev = co
+        if i < len(block_out) - 1:
+            out.extend(_conv(f"down{i}.downsample", co, co, (3, 3)))
+    _mid_specs(out, prev, False)
+    out.extend(_norm("norm_out", prev, False))
+    out.extend(_conv("conv_out", 2 * cfg.z_channels, prev, (3, 3)))
+    out.extend(_conv("quant_conv", 2 * cfg.z_channels, 2 * cfg.z_channels, (1, 1)))
     return out

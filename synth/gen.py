@@ -23,7 +23,7 @@ from typing import Dict
 import numpy as np
 import torch
 
-from .configs import DecoderConfig, param_specs
+from .configs import DecoderConfig, encoder_param_specs, param_specs
 
 _GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
@@ -78,8 +78,29 @@ def make_latent(cfg: DecoderConfig, batch=None, frames=None, latent_h=None, late
 def make_params(cfg: DecoderConfig, affine: str = "default", seed_base=None) -> Dict[str, torch.Tensor]:
     """Ordered dict name -> fp32 tensor for every parameter of ``cfg``'s decoder."""
     base = 0x5EED0000 + 1000 * cfg.id if seed_base is None else seed_base
+    return _draw(param_specs(cfg), base, affine, cfg.dtype)
+
+
+def make_encoder_params(cfg: DecoderConfig, affine: str = "default", seed_base=None) -> Dict[str, torch.Tensor]:
+    """Ordered dict name -> fp32 tensor for every parameter of ``cfg``'s encoder (2-D presets);
+    parameter j uses seed ``0x5EEE0000 + 1000*cfg + j``."""
+    base = 0x5EEE0000 + 1000 * cfg.id if seed_base is None else seed_base
+    return _draw(encoder_param_specs(cfg), base, affine, cfg.dtype)
+
+
+def make_image(cfg: DecoderConfig, batch=None, latent_h=None, latent_w=None, seed_base=None) -> torch.Tensor:
+    """Image (B, 3, H, W) for the encoder, uniform in [-1, 1) (the value range of a
+    normalised RGB image); sample b uses seed ``1000*cfg + 500 + b``."""
+    shape = cfg.image_shape(batch, latent_h, latent_w)
+    base = 1000 * cfg.id + 500 if seed_base is None else seed_base
+    per = int(np.prod(shape[1:]))
+    parts = [2.0 * uniform_draws(base + b, per) - 1.0 for b in range(shape[0])]
+    return _finish(np.concatenate(parts), shape, cfg.dtype)
+
+
+def _draw(specs, base: int, affine: str, dtype: str) -> Dict[str, torch.Tensor]:
     out: Dict[str, torch.Tensor] = {}
-    for j, p in enumerate(param_specs(cfg)):
+    for j, p in enumerate(specs):
         n = int(np.prod(p.shape))
         if p.kind == "weight":
             a = normal_draws(base + j, n) / np.sqrt(p.fan_in)
@@ -93,5 +114,5 @@ def make_params(cfg: DecoderConfig, affine: str = "default", seed_base=None) -> 
             a = np.ones(n)
         else:
             a = np.zeros(n)
-        out[p.name] = _finish(a, p.shape, cfg.dtype)
+        out[p.name] = _finish(a, p.shape, dtype)
     return out
