@@ -288,6 +288,61 @@ int vaep_decode_tiled(vaep_model* model, const void* latent, int batch, int fram
                       int latent_w, int tile, int stride, void* out, void* ws, size_t ws_bytes,
                       void* stream);
 
+/* Tiled encode with overlap blending (distributed-VAE strategy page, "Tile/Patch Encode
+ * Implementation": split the image into overlapping tiles, encode every tile on its own
+ * -- the encoder, then quant_conv -- and merge the encoded tiles in latent space as the
+ * tile decode merges decoded ones).  The page takes a video encoder as its example; this
+ * library builds the encoder of the 2-D family (VAEP_FAMILY_KL2D configs), a reading:
+ * the decoder's mirror -- conv_in from RGB to the narrowest width, down stages over the
+ * reversed stage widths with resnets_per_stage - 1 resnets each (at least one) and, in
+ * every stage but the last, a 3x3 stride-2 convolution over the input zero-padded by one
+ * row at the bottom and one column at the right, the mid block (resnet, single-head
+ * attention, resnet), GroupNorm -> SiLU -> conv_out to 2 z channels (mean | log-variance),
+ * and a 1x1 quant_conv over those.  Same storage policy as the decoder: bf16 weights and
+ * matrix-core operands, fp32 conv outputs, statistics and output. */
+typedef struct vaep_encoder vaep_encoder;   /* opaque; owned by the library */
+
+/* Number of encoder parameters of `cfg`, or a negative error (INVALID_ARG for a bad
+ * config, UNSUPPORTED for a video config).  Canonical order, names and shapes as
+ * vaep_param_info (weights [Co, Ci, kh, kw], linear weights [Co, Ci], biases [Co]). */
+int vaep_encoder_param_count(const vaep_config* cfg);
+int vaep_encoder_param_info(const vaep_config* cfg, int j, char* name, int name_cap, int64_t shape[5],
+                            int* ndim);
+
+/* Build an encoder (params as for vaep_model_create: device pointers in canonical order,
+ * the config's dtype; copied and repacked, so the caller may free them once this returns;
+ * synchronises `stream`).  Errors: INVALID_ARG, UNSUPPORTED (video config), HIP,
+ * NOT_READY. */
+int vaep_encoder_create(const vaep_config* cfg, const void* const* params, int n_params, void* stream,
+                        vaep_encoder** out);
+/* Release an encoder (the caller has finished every stream that uses it).  NULL is a no-op. */
+int vaep_encoder_destroy(vaep_encoder* enc);
+
+/* Workspace of vaep_encode_tiled for these arguments.  Errors as vaep_encode_tiled's
+ * argument checks. */
+int vaep_encode_tiled_workspace_bytes(const vaep_encoder* enc, int batch, int height, int width, int tile,
+                                      int stride, size_t* bytes_out);
+
+/* Encode `batch` images.
+ * image: device, contiguous (batch, 3, height, width) in the config's dtype; height and
+ *        width positive multiples of 2^(n_stages-1).
+ * tile, stride: in latent pixels (image pixels / 2^(n_stages-1)); image tiles of
+ *        tile * 2^(n_stages-1) pixels start every stride * 2^(n_stages-1) pixels (clipped at
+ *        the edge); each is encoded as a whole image (its own GroupNorm statistics and
+ *        attention tokens); the merge cross-fades each encoded tile's first tile - stride
+ *        rows from its upper neighbour and then its first columns from its left neighbour
+ *        (the linear blend of vaep_decode_tiled), keeps stride rows and columns of every
+ *        tile and crops to the latent size.  One tile covering the image (tile >= both
+ *        latent sides) is the whole-image encode.
+ * out:   device, contiguous fp32 (batch, 2 z, height / 2^(n_stages-1), width / 2^(n_stages-1)).
+ * ws:    device workspace of at least vaep_encode_tiled_workspace_bytes(...) bytes.
+ * info (nullable): bands_used = number of tiles, axis = VAEP_AXIS_TILE, n_launches,
+ *        workspace_bytes.
+ * Errors: INVALID_ARG (NULL pointers, image sizes, 1 <= stride <= tile violated),
+ * WORKSPACE (nothing enqueued), HIP (earlier work may remain enqueued). */
+int vaep_encode_tiled(vaep_encoder* enc, const void* image, int batch, int height, int width, int tile,
+                      int stride, void* out, void* ws, size_t ws_bytes, void* stream, vaep_decode_info* info);
+
 /* Launch timing.  While profiling is on for a model, every kernel launch of its decodes
  * is bracketed by two HIP events on the caller's stream and the library records the
  * step's kind, shape and algorithmic work (each tensor counted once; convolution flops

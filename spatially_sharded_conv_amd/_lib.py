@@ -38,6 +38,8 @@ EXPORTS = [
     "vaep_decode_full", "vaep_decode_bands", "vaep_select_axis", "vaep_decode_sharded",
     "vaep_sharded_workspace_bytes", "vaep_noalloc_scratch_bytes", "vaep_decode_bands_noalloc",
     "vaep_tiled_workspace_bytes", "vaep_decode_tiled",
+    "vaep_encoder_param_count", "vaep_encoder_param_info", "vaep_encoder_create", "vaep_encoder_destroy",
+    "vaep_encode_tiled_workspace_bytes", "vaep_encode_tiled",
     "vaep_groupnorm_merge",
     "vaep_step_conv", "vaep_step_groupnorm", "vaep_step_rmsnorm", "vaep_step_attention",
     "vaep_step_temporal_upsample", "vaep_profile_begin", "vaep_profile_end",
@@ -112,6 +114,13 @@ def _proto(lib):
       C.POINTER(VaepDecodeInfo))
     f("vaep_tiled_workspace_bytes", I, P, I, I, I, I, I, I, C.POINTER(SZ))
     f("vaep_decode_tiled", I, P, P, I, I, I, I, I, I, P, P, SZ, P)
+    f("vaep_encoder_param_count", I, C.POINTER(VaepConfig))
+    f("vaep_encoder_param_info", I, C.POINTER(VaepConfig), I, C.c_char_p, I, C.POINTER(C.c_int64),
+      C.POINTER(C.c_int))
+    f("vaep_encoder_create", I, C.POINTER(VaepConfig), C.POINTER(P), I, P, C.POINTER(P))
+    f("vaep_encoder_destroy", I, P)
+    f("vaep_encode_tiled_workspace_bytes", I, P, I, I, I, I, I, C.POINTER(SZ))
+    f("vaep_encode_tiled", I, P, P, I, I, I, I, I, P, P, SZ, P, C.POINTER(VaepDecodeInfo))
     f("vaep_decode_sharded", I, P, P, I, I, I, I, I, C.POINTER(C.c_int32), I, P, P, SZ, P,
       C.POINTER(VaepDecodeInfo))
     f("vaep_sharded_workspace_bytes", I, P, I, I, I, I, I, C.POINTER(SZ))

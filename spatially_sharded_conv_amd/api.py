@@ -194,6 +194,66 @@ class Decoder:
                                                   ws.numel(), _stream(stream)))
 
 
+def encoder_param_info(cfg: L.VaepConfig) -> List[Tuple[str, Tuple[int, ...]]]:
+    """Canonical (name, shape) list of the encoder of a 2-D config (vaep_encoder_param_info)."""
+    lib = L.load()
+    n = L.check(lib.vaep_encoder_param_count(C.byref(cfg)))
+    out = []
+    for j in range(n):
+        name = C.create_string_buffer(128)
+        shape = (C.c_int64 * 5)()
+        nd = C.c_int()
+        L.check(lib.vaep_encoder_param_info(C.byref(cfg), j, name, 128, shape, C.byref(nd)))
+        out.append((name.value.decode(), tuple(shape[i] for i in range(nd.value))))
+    return out
+
+
+class Encoder:
+    """A vaep_encoder (the tiled encode of a 2-D config): weights repacked into library-owned
+    device memory."""
+
+    def __init__(self, cfg: L.VaepConfig, params: Sequence[torch.Tensor], stream=None):
+        self.cfg = cfg
+        self.dtype = TORCH_DTYPE[cfg.dtype]
+        lib = L.load()
+        for t in params:
+            _dev(t, self.dtype, "parameter")
+        arr = (C.c_void_p * len(params))(*[t.data_ptr() for t in params])
+        h = C.c_void_p()
+        L.check(lib.vaep_encoder_create(C.byref(cfg), arr, len(params), _stream(stream), C.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            L.check(L.load().vaep_encoder_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace(self, batch, height, width, tile, stride, device="cuda") -> torch.Tensor:
+        n = C.c_size_t()
+        L.check(L.load().vaep_encode_tiled_workspace_bytes(self._h, batch, height, width, tile, stride,
+                                                           C.byref(n)))
+        return torch.empty(n.value, dtype=torch.uint8, device=device)
+
+    def encode_tiled(self, image, tile: int, stride: int, out, ws, stream=None):
+        """image (B, 3, H, W) in the config's dtype -> out (B, 2 z, H / up, W / up) fp32; returns
+        (status, info)."""
+        if image.dim() != 4 or image.shape[1] != 3:
+            raise ValueError("image must be (batch, 3, height, width)")
+        b, _, h, w = image.shape
+        _dev(image, self.dtype, "image")
+        _dev(out, torch.float32, "out")
+        info = L.VaepDecodeInfo()
+        rc = L.check(L.load().vaep_encode_tiled(self._h, _p(image), b, h, w, tile, stride, _p(out), _p(ws),
+                                                ws.numel(), _stream(stream), C.byref(info)))
+        return rc, info
+
+
 AXES = {"auto": L.AXIS_AUTO, "height": L.AXIS_HEIGHT, "width": L.AXIS_WIDTH, "tile": L.AXIS_TILE}
 AXIS_NAMES = {L.AXIS_HEIGHT: "height", L.AXIS_WIDTH: "width", L.AXIS_DENSE: "dense", L.AXIS_TILE: "tile"}
 

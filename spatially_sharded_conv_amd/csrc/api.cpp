@@ -149,6 +149,54 @@ std::vector<ParamDesc> param_list(const vaep_config& c) {
   return P;
 }
 
+// Resnets per encoder down stage: one fewer than per decoder up stage (at least one).
+int encoder_resnets(const vaep_config& c) { return c.resnets_per_stage > 1 ? c.resnets_per_stage - 1 : 1; }
+
+// Canonical parameter list of the encoder of a 2-D config: conv_in (RGB -> the narrowest
+// width), down stages over the reversed decoder widths (resnets, then a stride-2 3x3 conv
+// in every stage but the last), the mid block, norm_out, conv_out (2 z channels: mean and
+// log-variance) and a 1x1 quant_conv.
+std::vector<ParamDesc> encoder_param_list(const vaep_config& c) {
+  std::vector<ParamDesc> P;
+  auto conv = [&](const std::string& n, int co, int ci, int k) {
+    P.push_back({n + ".weight", {co, ci, k, k}});
+    P.push_back({n + ".bias", {co}});
+  };
+  auto norm = [&](const std::string& n, int ch) {
+    P.push_back({n + ".weight", {ch}});
+    P.push_back({n + ".bias", {ch}});
+  };
+  auto resnet = [&](const std::string& p, int ci, int co) {
+    norm(p + ".norm1", ci);
+    conv(p + ".conv1", co, ci, 3);
+    norm(p + ".norm2", co);
+    conv(p + ".conv2", co, co, 3);
+    if (ci != co) conv(p + ".shortcut", co, ci, 1);
+  };
+  const int ns = c.n_stages;
+  conv("conv_in", c.stage_channels[ns - 1], 3, 3);
+  int prev = c.stage_channels[ns - 1];
+  for (int i = 0; i < ns; ++i) {
+    const int co = c.stage_channels[ns - 1 - i];
+    for (int j = 0; j < encoder_resnets(c); ++j) {
+      resnet("down" + std::to_string(i) + ".res" + std::to_string(j), prev, co);
+      prev = co;
+    }
+    if (i < ns - 1) conv("down" + std::to_string(i) + ".downsample", co, co, 3);
+  }
+  resnet("mid.res0", prev, prev);
+  norm("mid.attn.norm", prev);
+  for (const char* s : {"q", "k", "v", "out"}) {
+    P.push_back({std::string("mid.attn.") + s + ".weight", {prev, prev}});
+    P.push_back({std::string("mid.attn.") + s + ".bias", {prev}});
+  }
+  resnet("mid.res1", prev, prev);
+  norm("norm_out", prev);
+  conv("conv_out", 2 * c.z_channels, prev, 3);
+  conv("quant_conv", 2 * c.z_channels, 2 * c.z_channels, 1);
+  return P;
+}
+
 int check_config(const vaep_config* c) {
   if (!c) return fail(VAEP_ERR_INVALID_ARG, "config is NULL");
   if (c->family != VAEP_FAMILY_KL2D && c->family != VAEP_FAMILY_WAN3D)
@@ -247,6 +295,25 @@ struct vaep_model {
   std::vector<StageW> stages;
   NormW norm_out;
   ConvW conv_out;
+};
+
+// Encoder of a 2-D config (the tiled encode): the decoder's mirror.
+struct EncStageW {
+  std::vector<ResW> res;
+  bool down = false;   // a stride-2 3x3 conv ends the stage
+  ConvW down_conv;
+};
+
+struct vaep_encoder {
+  vaep_config cfg;
+  void* mem = nullptr;
+  size_t mem_bytes = 0;
+  ConvW conv_in;
+  std::vector<EncStageW> stages;
+  ResW mid0, mid1;
+  AttnW attn;
+  NormW norm_out;
+  ConvW conv_out, quant;
 };
 
 namespace {
@@ -415,6 +482,29 @@ struct Builder {
     m.norm_out = norm("norm_out", prev);
     m.conv_out = conv("conv_out", 3, prev, kt, 3);
   }
+  void build_encoder(vaep_encoder& e) {
+    const int ns = c.n_stages;
+    int prev = c.stage_channels[ns - 1];
+    e.conv_in = conv("conv_in", prev, 3, 1, 3);
+    e.stages.clear();
+    for (int i = 0; i < ns; ++i) {
+      EncStageW s;
+      const int co = c.stage_channels[ns - 1 - i];
+      for (int j = 0; j < encoder_resnets(c); ++j) {
+        s.res.push_back(resnet("down" + std::to_string(i) + ".res" + std::to_string(j), prev, co));
+        prev = co;
+      }
+      s.down = i < ns - 1;
+      if (s.down) s.down_conv = conv("down" + std::to_string(i) + ".downsample", co, co, 1, 3);
+      e.stages.push_back(s);
+    }
+    e.mid0 = resnet("mid.res0", prev, prev);
+    e.attn = attention(prev);
+    e.mid1 = resnet("mid.res1", prev, prev);
+    e.norm_out = norm("norm_out", prev);
+    e.conv_out = conv("conv_out", 2 * c.z_channels, prev, 1, 3);
+    e.quant = conv("quant_conv", 2 * c.z_channels, 2 * c.z_channels, 1, 1);
+  }
 };
 
 // ------------------------------------------------------------------ executor
@@ -518,9 +608,10 @@ struct Exec {
   // reader is a sub-pixel upsample conv) instead of bf16 hi / lo halves.
   // x2: the second operand of a conv with a folded 1x1 part (w.kext > 0): bf16, w.kext
   // channels per pixel in Lin's band geometry.
+  // down: a stride-2 conv (Lout has half Lin's rows and width).
   int conv(const ConvW& w, const void* x, const BandLayout& Lin, int xk, void* y,
            const BandLayout& Lout, int mode, const void* res, int ups, int final_frames = 1,
-           bool gn_next = false, bool split8 = false, const void* x2 = nullptr) {
+           bool gn_next = false, bool split8 = false, const void* x2 = nullptr, int down = 0) {
     if (w.kext > 0) need_act(reshaped(Lin, w.kext, Lin.n_img, Lin.frames), 2);
     if (mode == kModeBand || mode == kModeTimeInterleave) need_act(Lout, 4);
     if (mode == kModeBandSplit) need_act(Lout, 2);
@@ -554,6 +645,7 @@ struct Exec {
     a.kt = w.kt;
     a.ks = w.ks;
     a.ups = ups;
+    a.down = down;
     a.mode = mode;
     a.x_f32 = xk == kXF32 ? 1 : 0;
     a.x_split = xk == kXSplit ? 1 : 0;
@@ -577,7 +669,7 @@ struct Exec {
     }
     {
       vaep_profile_entry pe = entry(VAEP_STEP_CONV, 1);
-      const long long m = (long long)Lin.n_img * Lin.H * Lin.W * (ups ? 4 : 1);
+      const long long m = (long long)Lin.n_img * Lin.H * Lin.W * (ups ? 4 : 1) / (down ? 4 : 1);
       const long long k = (long long)w.kt * w.ks * w.ks * w.ci + w.kext_ci;
       pe.kt = w.kt;
       pe.ks = w.ks;
@@ -982,6 +1074,147 @@ int table_rows(const int32_t* starts, int n, int len, const char* what, std::vec
       return fail(VAEP_ERR_INVALID_ARG, "%s band %d is empty or reversed (%d..%d)", what, i, starts[i], starts[i + 1]);
     rows.push_back(starts[i + 1] - starts[i]);
   }
+  return VAEP_OK;
+}
+
+// The same bands after a stride-2 conv: rows and width halve (every band's row count even).
+BandLayout halved(const BandLayout& L, int C) {
+  int rows[kMaxBands];
+  for (int i = 0; i < L.nb; ++i) rows[i] = L.rows[i] / 2;
+  return make_layout(L.nb, rows, L.n_img, L.frames, L.W / 2, C);
+}
+
+// Encoder forward of `batch` images of H x W (multiples of 2^(n_stages-1)) as one band:
+// image (NCHW, the config's dtype) -> moments (NCHW fp32, 2 z channels).
+int walk_encoder(Exec& E, const vaep_encoder& e, const void* image, int B, int H, int W, void* out) {
+  const vaep_config& c = e.cfg;
+  E.groups = c.norm_groups;
+  E.eps = c.eps;
+  E.base_rows = H >> (c.n_stages - 1);   // GroupNorm statistics tiles of whole latent-row slabs
+  const int rows[1] = {H};
+  BandLayout L = make_layout(1, rows, B, 1, W, e.conv_in.ci_pad);
+  int rc;
+  E.need_act(L, E.eb());
+  if (!E.dry) {
+    hipError_t err = launch_pack(image, 3, E.act[0], L, E.dtype, E.st, false);
+    if (err != hipSuccess) return hip_fail(err, "image pack");
+    ++E.launches;
+  }
+  BandLayout L1 = reshaped(L, e.conv_in.co, B, 1);
+  if ((rc = E.conv(e.conv_in, E.act[0], L, kXOp, E.act[1], L1, kModeBand, nullptr, 0, 1, true))) return rc;
+  int cur = 1;
+  L = L1;
+  for (const EncStageW& st : e.stages) {
+    for (const ResW& r : st.res)
+      if ((rc = resnet(E, r, cur, L))) return rc;
+    if (st.down) {
+      int o[3];
+      others(cur, o);
+      const BandLayout Ld = halved(L, st.down_conv.co);
+      if ((rc = E.conv(st.down_conv, E.act[cur], L, kXF32, E.act[o[0]], Ld, kModeBand, nullptr, 0, 1, false, false,
+                       nullptr, 1)))
+        return rc;
+      cur = o[0];
+      L = Ld;
+    }
+  }
+  if ((rc = resnet(E, e.mid0, cur, L))) return rc;
+  {
+    int o[3];
+    others(cur, o);
+    if ((rc = E.attention(e.attn, E.act[cur], L, E.act[o[0]], E.act[o[1]], E.act[o[2]]))) return rc;
+    cur = o[2];
+  }
+  if ((rc = resnet(E, e.mid1, cur, L))) return rc;
+  int o[3];
+  others(cur, o);
+  if ((rc = E.norm(e.norm_out, E.act[cur], L, E.act[o[0]], 1))) return rc;
+  const BandLayout Lz = reshaped(L, e.conv_out.co, B, 1);
+  if ((rc = E.conv(e.conv_out, E.act[o[0]], L, kXOp, E.act[o[1]], Lz, kModeBand, nullptr, 0))) return rc;
+  if ((rc = E.conv(e.quant, E.act[o[1]], Lz, kXF32, E.act[o[2]], Lz, kModeBand, nullptr, 0))) return rc;
+  if (!E.dry) {
+    hipError_t err = launch_unpack(E.act[o[2]], Lz, out, e.quant.co, VAEP_DTYPE_F32, E.st);
+    if (err != hipSuccess) return hip_fail(err, "moments gather");
+    ++E.launches;
+  }
+  return VAEP_OK;
+}
+
+// Workspace of one whole-image encode of `batch` images of H x W.
+int encode_plan_bytes(const vaep_encoder* e, int batch, int H, int W, size_t* bytes) {
+  Exec E;
+  E.dtype = e->cfg.dtype;
+  E.dry = true;
+  int rc = walk_encoder(E, *e, nullptr, batch, H, W, nullptr);
+  if (rc) return rc;
+  *bytes = E.total();
+  return VAEP_OK;
+}
+
+// Dry pass (sizing), workspace check and the encode of `batch` images of H x W.
+int run_encode(const vaep_encoder* e, const void* image, int batch, int H, int W, void* out, void* ws,
+               size_t ws_bytes, void* stream, int* launches) {
+  Exec E;
+  E.dtype = e->cfg.dtype;
+  E.st = (hipStream_t)stream;
+  E.dry = true;
+  int rc;
+  if ((rc = walk_encoder(E, *e, image, batch, H, W, out))) return rc;
+  const size_t need = E.total();
+  if (!ws || ws_bytes < need)
+    return fail(VAEP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  E.assign((char*)ws);
+  E.dry = false;
+  if ((rc = walk_encoder(E, *e, image, batch, H, W, out))) return rc;
+  if (launches) *launches += E.launches;
+  return VAEP_OK;
+}
+
+// Tiled encode: tiles of tile x tile latent pixels (tile * up image pixels) every stride.
+struct EncTilePlan {
+  int up = 1, lh = 0, lw = 0;
+  int nr = 0, nc = 0, nfull = 0, full_r = 0, full_c = 0;
+  long long planes = 0;      // moment planes: batch * 2 z
+  long long slot_elems = 0;  // fp32 elements of one tile slot (largest tile)
+  size_t enc_bytes = 0, img_bytes = 0, store_bytes = 0, total = 0;
+};
+
+int enc_tile_plan(const vaep_encoder* e, int batch, int H, int W, int tile, int stride, EncTilePlan* tp) {
+  if (tile < 1 || stride < 1 || stride > tile)
+    return fail(VAEP_ERR_INVALID_ARG, "tile %d and stride %d must satisfy 1 <= stride <= tile", tile, stride);
+  tp->up = 1 << (e->cfg.n_stages - 1);
+  tp->lh = H / tp->up;
+  tp->lw = W / tp->up;
+  tp->nr = (tp->lh + stride - 1) / stride;
+  tp->nc = (tp->lw + stride - 1) / stride;
+  tp->planes = (long long)batch * 2 * e->cfg.z_channels;
+  const int th = std::min(tile, tp->lh), tw = std::min(tile, tp->lw);
+  tp->slot_elems = tp->planes * th * tw;
+  int full_r = 0, full_c = 0;
+  for (int i = 0; i < tp->lh; i += stride) full_r += i + tile <= tp->lh ? 1 : 0;
+  for (int j = 0; j < tp->lw; j += stride) full_c += j + tile <= tp->lw ? 1 : 0;
+  tp->full_r = full_r;
+  tp->full_c = full_c;
+  tp->nfull = full_r * full_c;
+  size_t one = 0, many = 0;
+  int rc = encode_plan_bytes(e, batch, th * tp->up, tw * tp->up, &one);
+  if (rc) return rc;
+  if (tp->nfull > 0 && (rc = encode_plan_bytes(e, batch * tp->nfull, tile * tp->up, tile * tp->up, &many))) return rc;
+  tp->enc_bytes = align_up(std::max(one, many), 256);
+  tp->img_bytes = align_up((size_t)std::max(tp->nfull, 1) * batch * 3 * (size_t)(th * tp->up) * (tw * tp->up) *
+                               dtype_bytes(e->cfg.dtype),
+                           256);
+  tp->store_bytes = (size_t)tp->nr * tp->nc * tp->slot_elems * sizeof(float);
+  tp->total = tp->enc_bytes + tp->img_bytes + tp->store_bytes;
+  return VAEP_OK;
+}
+
+int check_image_dims(const vaep_encoder* e, int batch, int H, int W) {
+  if (!e) return fail(VAEP_ERR_INVALID_ARG, "encoder is NULL");
+  const int up = 1 << (e->cfg.n_stages - 1);
+  if (batch < 1 || H < up || W < up || H % up != 0 || W % up != 0)
+    return fail(VAEP_ERR_INVALID_ARG, "image %dx%d (batch %d) must be positive multiples of %d", H, W, batch, up);
+  if ((long long)H * W > (1LL << 26)) return fail(VAEP_ERR_INVALID_ARG, "image %dx%d too large", H, W);
   return VAEP_OK;
 }
 
@@ -1791,6 +2024,174 @@ int vaep_step_temporal_upsample(int dtype, const void* x, int batch, int frames,
   e = launch_copy_frame0(xin, Lx, yo, Lt, VAEP_DTYPE_F32, st);
   if (e == hipSuccess) e = launch_unpack(yo, Lt, y, c, VAEP_DTYPE_F32, st);
   if (e != hipSuccess) return hip_fail(e, "step temporal upsample");
+  return VAEP_OK;
+}
+
+// ------------------------------------------------------------------ tiled encode
+
+int vaep_encoder_param_count(const vaep_config* cfg) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (is_video(*cfg)) return fail(VAEP_ERR_UNSUPPORTED, "the encoder is built for the 2-D family only");
+  return (int)encoder_param_list(*cfg).size();
+}
+
+int vaep_encoder_param_info(const vaep_config* cfg, int j, char* name, int name_cap, int64_t shape[5], int* ndim) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (is_video(*cfg)) return fail(VAEP_ERR_UNSUPPORTED, "the encoder is built for the 2-D family only");
+  const auto P = encoder_param_list(*cfg);
+  if (j < 0 || j >= (int)P.size()) return fail(VAEP_ERR_INVALID_ARG, "parameter index %d outside 0..%d", j, (int)P.size() - 1);
+  if (name && name_cap > 0) {
+    std::strncpy(name, P[j].name.c_str(), name_cap - 1);
+    name[name_cap - 1] = 0;
+  }
+  if (shape)
+    for (size_t i = 0; i < P[j].shape.size() && i < 5; ++i) shape[i] = P[j].shape[i];
+  if (ndim) *ndim = (int)P[j].shape.size();
+  return VAEP_OK;
+}
+
+int vaep_encoder_create(const vaep_config* cfg, const void* const* params, int n_params, void* stream,
+                        vaep_encoder** out) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (is_video(*cfg)) return fail(VAEP_ERR_UNSUPPORTED, "the encoder is built for the 2-D family only");
+  if (!out) return fail(VAEP_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  const auto P = encoder_param_list(*cfg);
+  if (!params) return fail(VAEP_ERR_INVALID_ARG, "params is NULL");
+  if (n_params != (int)P.size()) return fail(VAEP_ERR_INVALID_ARG, "expected %d parameters, got %d", (int)P.size(), n_params);
+  for (int j = 0; j < n_params; ++j)
+    if (!params[j]) return fail(VAEP_ERR_INVALID_ARG, "parameter %d (%s) is NULL", j, P[j].name.c_str());
+  if ((rc = check_device())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  vaep_encoder* e = new (std::nothrow) vaep_encoder();
+  if (!e) return fail(VAEP_ERR_INVALID_ARG, "out of host memory");
+  e->cfg = *cfg;
+  Builder sz{*cfg, params, {}, {}, st, true, cfg->dtype};
+  for (size_t j = 0; j < P.size(); ++j) sz.index[P[j].name] = (int)j;
+  sz.build_encoder(*e);
+  e->mem_bytes = sz.carve.used;
+  hipError_t err = hipMalloc(&e->mem, e->mem_bytes);
+  if (err != hipSuccess) {
+    delete e;
+    return hip_fail(err, "hipMalloc(encoder)");
+  }
+  err = hipMemsetAsync(e->mem, 0, e->mem_bytes, st);
+  Builder b{*cfg, params, sz.index, {}, st, false, cfg->dtype};
+  b.carve.base = (char*)e->mem;
+  b.build_encoder(*e);
+  if (err == hipSuccess) err = b.err;
+  if (err == hipSuccess) err = hipStreamSynchronize(st);
+  if (err != hipSuccess) {
+    (void)hipFree(e->mem);
+    delete e;
+    return hip_fail(err, "encoder build");
+  }
+  *out = e;
+  return VAEP_OK;
+}
+
+int vaep_encoder_destroy(vaep_encoder* enc) {
+  if (!enc) return VAEP_OK;
+  hipError_t e = enc->mem ? hipFree(enc->mem) : hipSuccess;
+  delete enc;
+  return e == hipSuccess ? VAEP_OK : hip_fail(e, "hipFree(encoder)");
+}
+
+int vaep_encode_tiled_workspace_bytes(const vaep_encoder* enc, int batch, int height, int width, int tile,
+                                      int stride, size_t* bytes_out) {
+  int rc = check_image_dims(enc, batch, height, width);
+  if (rc) return rc;
+  if (!bytes_out) return fail(VAEP_ERR_INVALID_ARG, "bytes_out is NULL");
+  EncTilePlan tp;
+  if ((rc = enc_tile_plan(enc, batch, height, width, tile, stride, &tp))) return rc;
+  *bytes_out = tp.total;
+  return VAEP_OK;
+}
+
+int vaep_encode_tiled(vaep_encoder* enc, const void* image, int batch, int height, int width, int tile, int stride,
+                      void* out, void* ws, size_t ws_bytes, void* stream, vaep_decode_info* info) {
+  int rc = check_image_dims(enc, batch, height, width);
+  if (rc) return rc;
+  if (!image || !out) return fail(VAEP_ERR_INVALID_ARG, "image and out must be device pointers");
+  EncTilePlan tp;
+  if ((rc = enc_tile_plan(enc, batch, height, width, tile, stride, &tp))) return rc;
+  if (!ws || ws_bytes < tp.total)
+    return fail(VAEP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", tp.total, ws ? ws_bytes : (size_t)0);
+  hipStream_t st = (hipStream_t)stream;
+  char* base = (char*)ws;
+  void* enc_ws = base;
+  void* img = base + tp.enc_bytes;
+  float* slots = (float*)(base + tp.enc_bytes + tp.img_bytes);
+  const int up = tp.up, dt = enc->cfg.dtype;
+  const long long img_planes = (long long)batch * 3;
+  int n_launch = 0;
+  std::vector<int> slot_of(tp.nr * tp.nc);
+  for (int gi = 0; gi < tp.nr; ++gi)
+    for (int gj = 0; gj < tp.nc; ++gj) slot_of[gi * tp.nc + gj] = tile_slot(gi, gj, tp.nc, tp.full_r, tp.full_c);
+  // split / exec: every tile encoded on its own; the full-size tiles together as one batch
+  // of images whose moments land in consecutive slots, the clipped edge tiles one by one
+  const int ts = tile * up;
+  const size_t img_tile = (size_t)img_planes * ts * ts * dtype_bytes(dt);
+  if (tp.nfull > 0) {
+    for (int gi = 0; gi < tp.nr; ++gi)
+      for (int gj = 0; gj < tp.nc; ++gj) {
+        const int k = slot_of[gi * tp.nc + gj];
+        if (k >= tp.nfull) continue;
+        hipError_t e = launch_crop(image, img_planes, height, width, gi * stride * up, gj * stride * up, ts, ts,
+                                   (char*)img + k * img_tile, dt, st);
+        if (e != hipSuccess) return hip_fail(e, "image tile crop");
+        ++n_launch;
+      }
+    if ((rc = run_encode(enc, img, batch * tp.nfull, ts, ts, slots, enc_ws, tp.enc_bytes, stream, &n_launch)))
+      return rc;
+  }
+  for (int gi = 0; gi < tp.nr; ++gi)
+    for (int gj = 0; gj < tp.nc; ++gj) {
+      const int k = slot_of[gi * tp.nc + gj];
+      if (k < tp.nfull) continue;
+      const int i = gi * stride, j = gj * stride;
+      const int th = std::min(tile, tp.lh - i) * up, tw = std::min(tile, tp.lw - j) * up;
+      hipError_t e = launch_crop(image, img_planes, height, width, i * up, j * up, th, tw, img, dt, st);
+      if (e != hipSuccess) return hip_fail(e, "image tile crop");
+      ++n_launch;
+      if ((rc = run_encode(enc, img, batch, th, tw, slots + (long long)k * tp.slot_elems, enc_ws, tp.enc_bytes,
+                           stream, &n_launch)))
+        return rc;
+    }
+  // merge in latent space: raster order, upper neighbour over the overlap rows, then left
+  auto len = [&](int g, int n) { return std::min(tile, n - g * stride); };
+  const int blend = tile - stride;
+  for (int gi = 0; gi < tp.nr; ++gi)
+    for (int gj = 0; gj < tp.nc; ++gj) {
+      float* t = slots + (long long)slot_of[gi * tp.nc + gj] * tp.slot_elems;
+      const int th = len(gi, tp.lh), tw = len(gj, tp.lw);
+      hipError_t e = hipSuccess;
+      if (gi > 0) {
+        const int uh = len(gi - 1, tp.lh);
+        e = launch_blend(slots + (long long)slot_of[(gi - 1) * tp.nc + gj] * tp.slot_elems, t, tp.planes, th, tw, uh,
+                         std::min(std::min(uh, th), blend), 0, st);
+      }
+      if (e == hipSuccess && gj > 0) {
+        const int lw = len(gj - 1, tp.lw);
+        e = launch_blend(slots + (long long)slot_of[gi * tp.nc + gj - 1] * tp.slot_elems, t, tp.planes, th, tw, lw,
+                         std::min(std::min(lw, tw), blend), 1, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "tile blend");
+      n_launch += (gi > 0) + (gj > 0);
+    }
+  hipError_t e = launch_tiles_gather(slots, tp.slot_elems, tp.planes, tp.lh, tp.lw, stride, tile, tp.nc, tp.full_r,
+                                     tp.full_c, tp.lh, tp.lw, stride, 1, (float*)out, st);
+  if (e != hipSuccess) return hip_fail(e, "tile gather");
+  if (info) {
+    info->bands_used = tp.nr * tp.nc;
+    info->fell_back = 0;
+    info->n_launches = n_launch + 1;
+    info->axis = VAEP_AXIS_TILE;
+    info->workspace_bytes = tp.total;
+  }
   return VAEP_OK;
 }
 

@@ -35,7 +35,7 @@ namespace {
 // band b; *ok is false when the tap reads padding (outside the image or before frame 0).
 __device__ __forceinline__ long long tap_source(const BandLayout& in, int b, int n, int r, int c,
                                                 int dt, int dy, int dx, int kt, int ks, bool ups,
-                                                bool* ok) {
+                                                bool* ok, bool down = false) {
   bool valid = true;
   int sn = n;
   if (kt > 1) {
@@ -46,7 +46,13 @@ __device__ __forceinline__ long long tap_source(const BandLayout& in, int b, int
   }
   const int h = ks >> 1;
   int sr, sc;
-  if (ups) {
+  if (down) {
+    // stride 2, no padding above or left of the image, one zero row / column below / right
+    sr = 2 * r + dy;
+    sc = 2 * c + dx;
+    const int gr = in.row0[b] + sr;
+    valid = valid && gr < in.H && sc < in.W;
+  } else if (ups) {
     const int ur = r + dy - h, uc = c + dx - h;          // coordinates in the upsampled band
     const int gr = 2 * in.row0[b] + ur;
     valid = valid && gr >= 0 && gr < 2 * in.H && uc >= 0 && uc < 2 * in.W;
@@ -181,8 +187,9 @@ __device__ __forceinline__ int xcd_remap(int lin, int total) {
     }                                                                         \
   }
 
-template <int KT, int KS, bool UPS, int MODE, bool XF32, int BK, bool XN = false>
+template <int KT, int KS, bool UPS, int MODE, bool XF32, int BK, bool XN = false, bool DS = false>
 __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
+  static_assert(!(DS && (UPS || KS != 3 || KT != 1 || XN)), "stride 2 for plain 3x3 2-D convs");
   constexpr int BM = kConvTileN;   // output channels per workgroup
   constexpr int BN = kConvTileM;   // pixels per workgroup
   // BK: K per pipeline step (64, or 32 when Cin is not a multiple of 64), one tap
@@ -206,8 +213,8 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
   const int co0 = (lin / gridDim.x) * BM;
 
   const int rows_in = a.in.rows[band];
-  const int rows_c = UPS ? 2 * rows_in : rows_in;
-  const int wc = UPS ? 2 * a.in.W : a.in.W;
+  const int rows_c = UPS ? 2 * rows_in : (DS ? rows_in / 2 : rows_in);
+  const int wc = UPS ? 2 * a.in.W : (DS ? a.in.W / 2 : a.in.W);
   const int plane = rows_c * wc;
   const long long m_band = (long long)a.in.n_img * plane;
   const int cin = a.cin;
@@ -246,8 +253,8 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
     if (p1 >= m_band) p1 = m_band - 1;
     const int n0 = (int)(p0 / plane), r0 = (int)((p0 - (long long)n0 * plane) / wc);
     const int n1 = (int)(p1 / plane), r1 = (int)((p1 - (long long)n1 * plane) / wc);
-    const int top = UPS ? ((r0 - 1) >> 1) : r0 - 1;     // lowest source row (-1 = halo)
-    const int bot = UPS ? ((r1 + 1) >> 1) : r1 + 1;     // highest source row
+    const int top = UPS ? ((r0 - 1) >> 1) : (DS ? 2 * r0 : r0 - 1);     // lowest source row (-1 = halo)
+    const int bot = UPS ? ((r1 + 1) >> 1) : (DS ? 2 * r1 + 2 : r1 + 1);  // highest source row
     first_slot = (long long)(n0 - (KT - 1)) * (rows_in + 2) + top + 1;
     if (first_slot < 0) first_slot = 0;
     last_slot = (long long)n1 * (rows_in + 2) + bot + 1;
@@ -335,7 +342,7 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
       const int dt = tap / (KS * KS), dy = (tap / KS) % KS, dx = tap % KS;                      \
       VAEP_FOR_J({                                                                              \
         bool ok;                                                                                \
-        const long long o = tap_source(a.in, band, pn[j], pr[j], pc[j], dt, dy, dx, KT, KS, UPS, &ok); \
+        const long long o = tap_source(a.in, band, pn[j], pr[j], pc[j], dt, dy, dx, KT, KS, UPS, &ok, DS); \
         xo[j] = (ok && pv[j]) ? (unsigned)((o - x_base + q8) * XB) : kPadOffset;                \
       });                                                                                       \
     }                                                                                           \
@@ -547,9 +554,9 @@ __global__ void __launch_bounds__(128) conv_f32(const ConvArgs a) {
   const int tile = mt - a.tile_start[band];
   const int co = blockIdx.y;
   const int rows_in = a.in.rows[band];
-  const bool ups = a.ups != 0;
-  const int rows_c = ups ? 2 * rows_in : rows_in;
-  const int wc = ups ? 2 * a.in.W : a.in.W;
+  const bool ups = a.ups != 0, down = a.down != 0;
+  const int rows_c = ups ? 2 * rows_in : (down ? rows_in / 2 : rows_in);
+  const int wc = ups ? 2 * a.in.W : (down ? a.in.W / 2 : a.in.W);
   const int plane = rows_c * wc;
   const long long p = (long long)tile * kConvTileM + threadIdx.x;
   if (p >= (long long)a.in.n_img * plane || co >= a.cout) return;
@@ -564,7 +571,7 @@ __global__ void __launch_bounds__(128) conv_f32(const ConvArgs a) {
   for (int tap = 0; tap < taps; ++tap) {
     const int dt = tap / (a.ks * a.ks), dy = (tap / a.ks) % a.ks, dx = tap % a.ks;
     bool ok;
-    const long long off = tap_source(a.in, band, n, r, c, dt, dy, dx, a.kt, a.ks, ups, &ok);
+    const long long off = tap_source(a.in, band, n, r, c, dt, dy, dx, a.kt, a.ks, ups, &ok, down);
     if (!ok) continue;
     const float* wr = wg + (long long)co * ktot + (long long)tap * a.cin;
     for (int ci = 0; ci < a.cin; ++ci) acc = fmaf(wr[ci], xg[off + ci], acc);
@@ -605,7 +612,7 @@ __global__ void __launch_bounds__(128) conv_f32(const ConvArgs a) {
   }
 }
 
-template <int KT, int KS, bool UPS, int MODE>
+template <int KT, int KS, bool UPS, int MODE, bool DS = false>
 hipError_t go(const ConvArgs& a, hipStream_t s) {
   const int ny = a.cout_pad / kConvTileN;
   dim3 grid(a.tiles_total, ny);
@@ -618,20 +625,21 @@ hipError_t go(const ConvArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   }
   if (a.x_f32 && k64)
-    hipLaunchKernelGGL((conv_mfma_bf16<KT, KS, UPS, MODE, true, 64>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((conv_mfma_bf16<KT, KS, UPS, MODE, true, 64, false, DS>), grid, dim3(256), 0, s, a);
   else if (a.x_f32)
-    hipLaunchKernelGGL((conv_mfma_bf16<KT, KS, UPS, MODE, true, 32>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((conv_mfma_bf16<KT, KS, UPS, MODE, true, 32, false, DS>), grid, dim3(256), 0, s, a);
   else if (k64)
-    hipLaunchKernelGGL((conv_mfma_bf16<KT, KS, UPS, MODE, false, 64>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((conv_mfma_bf16<KT, KS, UPS, MODE, false, 64, false, DS>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((conv_mfma_bf16<KT, KS, UPS, MODE, false, 32>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((conv_mfma_bf16<KT, KS, UPS, MODE, false, 32, false, DS>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool conv_norm_fold_ok(const ConvArgs& a) {
-  if (a.kt != 1 || a.ks != 3 || a.ups || a.mode != kModeBand || a.x_f32 || a.x_split || a.sub || a.x2 || a.cin2)
+  if (a.kt != 1 || a.ks != 3 || a.ups || a.down || a.mode != kModeBand || a.x_f32 || a.x_split || a.sub || a.x2 ||
+      a.cin2)
     return false;
   if (a.cin % 64 != 0 || a.cin > 512 || a.in.C != a.cin) return false;
   ConvArgs u = a;   // the same conv unfolded runs on the tile128 kernel too
@@ -643,8 +651,17 @@ bool conv_norm_fold_ok(const ConvArgs& a) {
 }
 
 hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s) {
-  const bool ups = a.ups != 0;
+  const bool ups = a.ups != 0, down = a.down != 0;
   a.gn_chunk = 0;
+  if (down) {
+    // stride 2: plain 3x3 2-D band convs, even band rows and width, on the tile kernels
+    if (ups || a.kt != 1 || a.ks != 3 || a.mode != kModeBand || a.x_split || a.sub || a.x2 || a.cin2 || a.x_norm ||
+        a.in.W % 2 != 0 || a.out.W != a.in.W / 2 || a.out.nb != a.in.nb)
+      return hipErrorInvalidValue;
+    for (int b = 0; b < a.in.nb; ++b)
+      if (a.in.rows[b] % 2 != 0 || a.out.rows[b] != a.in.rows[b] / 2) return hipErrorInvalidValue;
+    a.gn_part = nullptr;   // the next norm forms its own statistics
+  }
   if (a.x_norm && (dtype != VAEP_DTYPE_BF16 || !conv_norm_fold_ok(a))) return hipErrorInvalidValue;
   if (!a.x_norm && dtype != VAEP_DTYPE_F32 && conv_halo_fits(a)) return launch_conv_halo(a, s);
   if (!a.x_norm && dtype != VAEP_DTYPE_F32 && conv_wide_fits(a)) return launch_conv_wide(a, s);
@@ -662,7 +679,7 @@ hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s) {
     // 2 GiB, so the padding offset reads out of range
     const long long xb = (a.x_f32 || a.x_norm) ? 4 : 2;
     for (int b = 0; b < a.in.nb; ++b)
-      if ((tile_read_slots(a.in, b, a.kt, kConvTileM, ups) * a.in.W + 2LL * kConvTileM) * a.in.C * xb >=
+      if ((tile_read_slots(a.in, b, a.kt, kConvTileM, ups, down) * a.in.W + 2LL * kConvTileM) * a.in.C * xb >=
           (1LL << 31) - 4096)
         return hipErrorInvalidValue;
     if ((long long)a.cout_pad * a.kt * a.ks * a.ks * a.cin * 2 >= (1LL << 31)) return hipErrorInvalidValue;
@@ -670,7 +687,8 @@ hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s) {
   int t = 0;
   for (int b = 0; b < a.in.nb; ++b) {
     a.tile_start[b] = t;
-    const long long m = (long long)a.in.n_img * (ups ? 2 : 1) * a.in.rows[b] * (ups ? 2 : 1) * a.in.W;
+    const long long m = down ? (long long)a.in.n_img * (a.in.rows[b] / 2) * (a.in.W / 2)
+                             : (long long)a.in.n_img * (ups ? 2 : 1) * a.in.rows[b] * (ups ? 2 : 1) * a.in.W;
     t += (int)((m + kConvTileM - 1) / kConvTileM);
   }
   a.tile_start[a.in.nb] = t;
@@ -692,6 +710,7 @@ hipError_t launch_conv(ConvArgs& a, int dtype, hipStream_t s) {
     return hipGetLastError();
   }
   const int kt = a.kt, ks = a.ks, m = a.mode;
+  if (down) return go<1, 3, false, kModeBand, true>(a, s);
   if (kt == 1 && ks == 3 && !ups && m == kModeBand) return go<1, 3, false, kModeBand>(a, s);
   if (kt == 1 && ks == 3 && !ups && m == kModeBandSplit) return go<1, 3, false, kModeBandSplit>(a, s);
   if (kt == 3 && ks == 3 && !ups && m == kModeBandSplit) return go<3, 3, false, kModeBandSplit>(a, s);

@@ -425,7 +425,7 @@ int halo_bm(const ConvArgs& a) {
 // fill the GPU.  Decided on the layer's shape alone: every band table of a layer uses the
 // same kernel.
 bool conv_halo_fits(const ConvArgs& a) {
-  if (a.kt != 1 || a.ks != 3 || a.ups || a.sub || a.x_split || a.x_f32 || a.x2 || a.cin2) return false;
+  if (a.kt != 1 || a.ks != 3 || a.ups || a.down || a.sub || a.x_split || a.x_f32 || a.x2 || a.cin2) return false;
   if (a.mode != kModeBand || a.split8) return false;
   if (a.cin % 32 != 0 || a.in.C != a.cin || a.cout != a.cout_pad) return false;
   const int bm = halo_bm(a);

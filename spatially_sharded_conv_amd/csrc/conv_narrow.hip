@@ -146,7 +146,7 @@ __global__ void __launch_bounds__(256) conv_narrow(const ConvArgs a) {
 
 bool conv_narrow_fits(const ConvArgs& a) {
   return a.mode == kModeFinal && a.cout <= 16 && a.cout_pad >= 16 && (a.in.C == 96 || a.in.C == 128) && !a.x_f32 &&
-         !a.x_split && !a.ups && a.ks == 3 && (a.kt == 1 || a.kt == 3);
+         !a.x_split && !a.ups && !a.down && a.ks == 3 && (a.kt == 1 || a.kt == 3);
 }
 
 hipError_t launch_conv_narrow(ConvArgs& a, hipStream_t s) {

@@ -681,7 +681,7 @@ WideTile wide_tile(const ConvArgs& a) {
 
 bool conv_wide_fits(const ConvArgs& a) {
   if (a.sub) return true;
-  if (a.x_f32 || a.x_split || a.ups) return false;
+  if (a.x_f32 || a.x_split || a.ups || a.down) return false;
   if (a.mode != kModeBand && a.mode != kModeBandSplit) return false;
   if (a.cin % 64 != 0 || a.cout_pad % 128 != 0) return false;
   const bool geo = (a.kt == 1 && (a.ks == 3 || a.ks == 1)) || (a.kt == 3 && a.ks == 3);

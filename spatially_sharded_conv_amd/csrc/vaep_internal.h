@@ -45,11 +45,15 @@ inline long long layout_elems(const BandLayout& L) {
 // one image number at most c = ceil(bn / wc) + 1; when the tile also reaches into the next
 // image the range adds that image's first rows: at most (kt - 1)(rows + 2) + 2c + 4 slots
 // while an image holds at least bn compute pixels.  Capped at the whole buffer.
-inline long long tile_read_slots(const BandLayout& in, int b, int kt, int bn, bool ups) {
-  const long long R = in.rows[b], wc = (ups ? 2LL : 1LL) * in.W;
-  const long long plane = (ups ? 2 : 1) * R * wc;
+// With down (a stride-2 conv: compute grid of half the rows and width) c compute rows read
+// 2c + 1 source rows.
+inline long long tile_read_slots(const BandLayout& in, int b, int kt, int bn, bool ups, bool down = false) {
+  const long long R = in.rows[b], wc = ups ? 2LL * in.W : (down ? in.W / 2 : in.W);
+  const long long plane = (ups ? 2 * R : (down ? R / 2 : R)) * wc;
+  if (wc < 1 || plane < 1) return (long long)in.n_img * (R + 2);
   const long long c = (bn + wc - 1) / wc + 1;
-  long long slots = plane >= bn ? (kt - 1) * (R + 2) + 2 * c + 4 : (kt + 1 + (bn + plane - 1) / plane) * (R + 2);
+  const long long src = down ? 2 * c + 1 : c;
+  long long slots = plane >= bn ? (kt - 1) * (R + 2) + 2 * src + 4 : (kt + 1 + (bn + plane - 1) / plane) * (R + 2);
   const long long all = (long long)in.n_img * (R + 2);
   return slots < all ? slots : all;
 }
@@ -87,6 +91,8 @@ struct ConvArgs {
   int cout_pad;         // rows of the packed weight
   int kt, ks;           // temporal taps (1 or 3, causal), spatial kernel (1 or 3)
   int ups;              // nearest-2x fused into the load
+  int down;             // stride 2 (3x3, input zero-padded by one row / column at the bottom /
+                        // right only): output rows and width are half the input's
   int mode;
   int x_f32;            // bf16 path: operand source stored as fp32 (rounded on load)
   int x_split;          // bf16 path: operand source stored as bf16 [hi | lo] parts, channel

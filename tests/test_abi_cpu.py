@@ -104,6 +104,29 @@ def test_model_switches_reject_a_null_model():
     assert lib.vaep_model_set_halo_poison(None, 1) == L.VAEP_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("i", [1, 2, 3, 4])
+def test_encoder_param_list_matches_generator(i):
+    from synth import encoder_param_specs, preset
+    cfg = preset(i)
+    lc = api.make_config(cfg.family, cfg.dtype, cfg.z_channels, cfg.stage_channels, cfg.resnets_per_stage,
+                         cfg.norm_groups, cfg.temporal_up_stages, cfg.eps)
+    assert api.encoder_param_info(lc) == [(s.name, tuple(s.shape)) for s in encoder_param_specs(cfg)]
+
+
+def test_encoder_argument_checks_without_gpu_work():
+    lib = L.load()
+    c = L.VaepConfig()
+    assert lib.vaep_config_preset(5, C.byref(c)) == 0
+    assert lib.vaep_encoder_param_count(C.byref(c)) == L.VAEP_ERR_UNSUPPORTED   # video config
+    assert lib.vaep_config_preset(2, C.byref(c)) == 0
+    h = C.c_void_p()
+    assert lib.vaep_encoder_create(C.byref(c), None, 0, None, C.byref(h)) == L.VAEP_ERR_INVALID_ARG
+    n = C.c_size_t()
+    assert lib.vaep_encode_tiled_workspace_bytes(None, 1, 64, 64, 4, 4, C.byref(n)) == L.VAEP_ERR_INVALID_ARG
+    assert lib.vaep_encode_tiled(None, None, 1, 64, 64, 4, 4, None, None, 0, None, None) == L.VAEP_ERR_INVALID_ARG
+    assert lib.vaep_encoder_destroy(None) == 0
+
+
 def test_groupnorm_merge_argument_checks():
     lib = L.load()
     assert lib.vaep_groupnorm_merge(0, 4, None, None, None, None, None, None) == L.VAEP_ERR_INVALID_ARG
