@@ -21,7 +21,9 @@ row-seam diagnostic.  `norm_fold` times the decode with the GroupNorm apply fold
 the latent-resolution resnet convs' operand load (vaep_model_set_norm_fold) beside
 the separate apply pass.  `other_configs` times the batch-4 1024^2 preset and the
 video preset in the same run (per-decode time, Mpixel/s, conv and norm
-fractions).
+fractions).  `tiled_encode` times the tiled encode of the same preset's image size
+(vaep_encode_tiled: the 2-D encoder on 32-latent tiles every 24, and as one
+whole-image tile) with seeded encoder weights and image.
 
 `--only-bands` runs nothing but the band decodes of the chosen preset (no
 width, auto, tiled or other-preset decodes, no CPU baseline): the form used
@@ -241,6 +243,41 @@ def profiled_decodes(dec, run, steps, launches, stream):
     return recs, a.elapsed_time(b) / steps
 
 
+def tiled_encode(cfg_id, steps, warmup, stream):
+    """Time the tiled encode of preset cfg_id's image size: overlapping 32-latent tiles every 24
+    and one whole-image tile; report image Mpixel/s and the distance between the two."""
+    import torch
+    import spatially_sharded_conv_amd as vaep
+    from synth import make_encoder_params, make_image, preset
+    cfg = preset(cfg_id)
+    params = make_encoder_params(cfg)
+    lc = vaep.make_config(cfg.family, cfg.dtype, cfg.z_channels, cfg.stage_channels,
+                          cfg.resnets_per_stage, cfg.norm_groups, cfg.temporal_up_stages, cfg.eps)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    enc = vaep.Encoder(lc, [params[n].to(tdt).cuda() for n, _ in vaep.encoder_param_info(lc)])
+    img = make_image(cfg).to(tdt).cuda()
+    b, _, h, w = img.shape
+    pixels = b * h * w
+    res = {"image": list(img.shape)}
+    outs = {}
+    for name, tile, stride in (("tiles_32_every_24", 32, 24), ("whole_image", max(cfg.latent_h, cfg.latent_w),
+                                                                  max(cfg.latent_h, cfg.latent_w))):
+        out = torch.empty(cfg.moments_shape(), dtype=torch.float32, device="cuda")
+        ws = enc.workspace(b, h, w, tile, stride)
+        ms, med, (rc, info) = timed_decodes(lambda: enc.encode_tiled(img, tile, stride, out, ws, stream), steps,
+                                            warmup, stream)
+        res[name] = {"tiles": info.bands_used, "ms_per_step": round(ms, 4), "ms_median": round(med, 4),
+                     "mpixel_s": round(pixels / (ms * 1e-3) / 1e6, 3)}
+        outs[name] = out
+        del ws
+    d = outs["tiles_32_every_24"].double() - outs["whole_image"].double()
+    res["rel_l2_tiles_vs_whole_image"] = round((d.norm() / outs["whole_image"].double().norm()).item(), 5)
+    enc.close()
+    del outs, img
+    torch.cuda.empty_cache()
+    return res
+
+
 def other_config(cfg_id, steps, warmup, stream):
     """Per-decode time, throughput and the conv / norm fractions of another preset's band decode."""
     cfg, dec, latent, out, ws = build_decoder(cfg_id)
@@ -376,6 +413,9 @@ def main():
     dec.close()
     del ws, out, latent
     torch.cuda.empty_cache()
+    encode = None
+    if not args.only_bands and not cfg.is_video:
+        encode = tiled_encode(args.config, max(3, min(args.steps, 8)), max(1, args.warmup), stream)
     others = {}
     if not args.only_bands and not args.no_other_configs:
         for cid in (4, 5):
@@ -419,6 +459,7 @@ def main():
         "shard_axes": axes,
         "norm_fold": fold,
         "tiled_baseline": tiled,
+        "tiled_encode": encode,
         **aggregates(recs, args.steps),
         "other_configs": others,
         "cpu_baseline": None,
