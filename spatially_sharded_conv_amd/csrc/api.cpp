@@ -1077,6 +1077,30 @@ int table_rows(const int32_t* starts, int n, int len, const char* what, std::vec
   return VAEP_OK;
 }
 
+// Clipped edge tiles of a tile grid grouped by their size (latent rows x columns), in
+// raster order of first appearance: each group runs as one batch of images.
+struct EdgeGroup {
+  int th = 0, tw = 0;
+  std::vector<int> tiles;   // gi * nc + gj
+};
+std::vector<EdgeGroup> edge_groups(int nr, int nc, int full_r, int full_c, int tile, int stride, int h, int w) {
+  std::vector<EdgeGroup> g;
+  for (int gi = 0; gi < nr; ++gi)
+    for (int gj = 0; gj < nc; ++gj) {
+      if (gi < full_r && gj < full_c) continue;
+      const int th = std::min(tile, h - gi * stride), tw = std::min(tile, w - gj * stride);
+      size_t k = 0;
+      while (k < g.size() && (g[k].th != th || g[k].tw != tw)) ++k;
+      if (k == g.size()) {
+        g.push_back(EdgeGroup());
+        g[k].th = th;
+        g[k].tw = tw;
+      }
+      g[k].tiles.push_back(gi * nc + gj);
+    }
+  return g;
+}
+
 // The same bands after a stride-2 conv: rows and width halve (every band's row count even).
 BandLayout halved(const BandLayout& L, int C) {
   int rows[kMaxBands];
@@ -1176,7 +1200,8 @@ struct EncTilePlan {
   int nr = 0, nc = 0, nfull = 0, full_r = 0, full_c = 0;
   long long planes = 0;      // moment planes: batch * 2 z
   long long slot_elems = 0;  // fp32 elements of one tile slot (largest tile)
-  size_t enc_bytes = 0, img_bytes = 0, store_bytes = 0, total = 0;
+  std::vector<EdgeGroup> edges;
+  size_t enc_bytes = 0, img_bytes = 0, stage_bytes = 0, store_bytes = 0, total = 0;
 };
 
 int enc_tile_plan(const vaep_encoder* e, int batch, int H, int W, int tile, int stride, EncTilePlan* tp) {
@@ -1196,16 +1221,29 @@ int enc_tile_plan(const vaep_encoder* e, int batch, int H, int W, int tile, int 
   tp->full_r = full_r;
   tp->full_c = full_c;
   tp->nfull = full_r * full_c;
-  size_t one = 0, many = 0;
-  int rc = encode_plan_bytes(e, batch, th * tp->up, tw * tp->up, &one);
-  if (rc) return rc;
-  if (tp->nfull > 0 && (rc = encode_plan_bytes(e, batch * tp->nfull, tile * tp->up, tile * tp->up, &many))) return rc;
-  tp->enc_bytes = align_up(std::max(one, many), 256);
-  tp->img_bytes = align_up((size_t)std::max(tp->nfull, 1) * batch * 3 * (size_t)(th * tp->up) * (tw * tp->up) *
-                               dtype_bytes(e->cfg.dtype),
-                           256);
+  // the full tiles, then each edge group, run as one batch each in the same workspace; the
+  // edge groups' moments pass through a staging area on their way to the slots
+  tp->edges = edge_groups(tp->nr, tp->nc, full_r, full_c, tile, stride, tp->lh, tp->lw);
+  const size_t img_px = (size_t)batch * 3 * dtype_bytes(e->cfg.dtype) * tp->up * tp->up;
+  size_t enc = 0, img = 0, stage = 0;
+  int rc;
+  if (tp->nfull > 0) {
+    if ((rc = encode_plan_bytes(e, batch * tp->nfull, tile * tp->up, tile * tp->up, &enc))) return rc;
+    img = (size_t)tp->nfull * tile * tile * img_px;
+  }
+  for (const EdgeGroup& g : tp->edges) {
+    const int n = (int)g.tiles.size();
+    size_t b = 0;
+    if ((rc = encode_plan_bytes(e, batch * n, g.th * tp->up, g.tw * tp->up, &b))) return rc;
+    enc = std::max(enc, b);
+    img = std::max(img, (size_t)n * g.th * g.tw * img_px);
+    stage = std::max(stage, (size_t)n * (size_t)tp->planes * g.th * g.tw * sizeof(float));
+  }
+  tp->enc_bytes = align_up(enc, 256);
+  tp->img_bytes = align_up(img, 256);
+  tp->stage_bytes = align_up(stage, 256);
   tp->store_bytes = (size_t)tp->nr * tp->nc * tp->slot_elems * sizeof(float);
-  tp->total = tp->enc_bytes + tp->img_bytes + tp->store_bytes;
+  tp->total = tp->enc_bytes + tp->img_bytes + tp->stage_bytes + tp->store_bytes;
   return VAEP_OK;
 }
 
@@ -1227,7 +1265,8 @@ struct TilePlan {
   int blend = 0;               // overlap in output rows / columns
   long long planes = 0;        // output planes: batch * 3 * output frames
   long long slot_elems = 0;    // fp32 elements of one tile slot (largest tile)
-  size_t dec_bytes = 0, lat_bytes = 0, store_bytes = 0, total = 0;
+  std::vector<EdgeGroup> edges;
+  size_t dec_bytes = 0, lat_bytes = 0, stage_bytes = 0, store_bytes = 0, total = 0;
 };
 
 int tile_plan(const vaep_model* m, int batch, int frames, int h, int w, int tile, int stride, TilePlan* tp) {
@@ -1251,15 +1290,29 @@ int tile_plan(const vaep_model* m, int batch, int frames, int h, int w, int tile
   tp->full_r = full_r;
   tp->full_c = full_c;
   tp->nfull = full_r * full_c;
-  const int nb = std::max(tp->nfull, 1);
-  size_t one = 0, many = 0;
-  int rc = plan_bytes(m, batch, frames, th, tw, 1, false, &one);
-  if (rc) return rc;
-  if (tp->nfull > 0 && (rc = plan_bytes(m, batch * tp->nfull, frames, tile, tile, 1, false, &many))) return rc;
-  tp->dec_bytes = align_up(std::max(one, many), 256);
-  tp->lat_bytes = align_up((size_t)nb * batch * m->cfg.z_channels * frames * th * tw * dtype_bytes(m->cfg.dtype), 256);
+  // every batch (the full tiles, then each edge group) decodes in the same workspace; the
+  // edge groups' outputs pass through a staging area on their way to the slots
+  tp->edges = edge_groups(tp->nr, tp->nc, full_r, full_c, tile, stride, h, w);
+  const size_t lat_px = (size_t)batch * m->cfg.z_channels * frames * dtype_bytes(m->cfg.dtype);
+  size_t dec = 0, lat = 0, stage = 0;
+  int rc;
+  if (tp->nfull > 0) {
+    if ((rc = plan_bytes(m, batch * tp->nfull, frames, tile, tile, 1, false, &dec))) return rc;
+    lat = (size_t)tp->nfull * tile * tile * lat_px;
+  }
+  for (const EdgeGroup& g : tp->edges) {
+    const int n = (int)g.tiles.size();
+    size_t b = 0;
+    if ((rc = plan_bytes(m, batch * n, frames, g.th, g.tw, 1, false, &b))) return rc;
+    dec = std::max(dec, b);
+    lat = std::max(lat, (size_t)n * g.th * g.tw * lat_px);
+    stage = std::max(stage, (size_t)n * (size_t)tp->planes * g.th * tp->up * g.tw * tp->up * sizeof(float));
+  }
+  tp->dec_bytes = align_up(dec, 256);
+  tp->lat_bytes = align_up(lat, 256);
+  tp->stage_bytes = align_up(stage, 256);
   tp->store_bytes = (size_t)tp->nr * tp->nc * tp->slot_elems * sizeof(float);
-  tp->total = tp->dec_bytes + tp->lat_bytes + tp->store_bytes;
+  tp->total = tp->dec_bytes + tp->lat_bytes + tp->stage_bytes + tp->store_bytes;
   return VAEP_OK;
 }
 
@@ -1521,7 +1574,8 @@ int tiled_decode(vaep_model* model, const void* latent, int batch, int frames, i
   char* base = (char*)ws;
   void* dec_ws = base;
   void* lat = base + tp.dec_bytes;
-  float* slots = (float*)(base + tp.dec_bytes + tp.lat_bytes);
+  float* stage = (float*)(base + tp.dec_bytes + tp.lat_bytes);
+  float* slots = (float*)(base + tp.dec_bytes + tp.lat_bytes + tp.stage_bytes);
   const int cz = model->cfg.z_channels;
   const long long lat_planes = (long long)batch * cz * frames;
   // split / exec: every tile decoded on its own (its own statistics and attention), the
@@ -1546,20 +1600,30 @@ int tiled_decode(vaep_model* model, const void* latent, int batch, int frames, i
     if (rc) return rc;
     n_launch += tp.nfull + sub.n_launches;
   }
-  for (int gi = 0; gi < tp.nr; ++gi)
-    for (int gj = 0; gj < tp.nc; ++gj) {
-      const int k = slot_of[gi * tp.nc + gj];
-      if (k < tp.nfull) continue;
-      const int i = gi * stride, j = gj * stride;
-      const int th = std::min(tile, latent_h - i), tw = std::min(tile, latent_w - j);
-      hipError_t e = launch_crop(latent, lat_planes, latent_h, latent_w, i, j, th, tw, lat, model->cfg.dtype, st);
+  // the clipped edge tiles, one batch per size: decoded into the staging area, then each
+  // tile's output copied to its slot
+  for (const EdgeGroup& g : tp.edges) {
+    const int n = (int)g.tiles.size();
+    const size_t lat_g = (size_t)lat_planes * g.th * g.tw * dtype_bytes(model->cfg.dtype);
+    for (int q = 0; q < n; ++q) {
+      const int gi = g.tiles[q] / tp.nc, gj = g.tiles[q] % tp.nc;
+      hipError_t e = launch_crop(latent, lat_planes, latent_h, latent_w, gi * stride, gj * stride, g.th, g.tw,
+                                 (char*)lat + q * lat_g, model->cfg.dtype, st);
       if (e != hipSuccess) return hip_fail(e, "latent tile crop");
-      const std::vector<int> rows(1, th);
-      rc = run_decode(model, lat, batch, frames, tw, false, rows, VAEP_AXIS_DENSE, VAEP_OK,
-                      slots + (long long)k * tp.slot_elems, dec_ws, tp.dec_bytes, stream, &sub);
-      if (rc) return rc;
-      n_launch += 1 + sub.n_launches;
     }
+    const std::vector<int> rows(1, g.th);
+    rc = run_decode(model, lat, batch * n, frames, g.tw, false, rows, VAEP_AXIS_DENSE, VAEP_OK, stage, dec_ws,
+                    tp.dec_bytes, stream, &sub);
+    if (rc) return rc;
+    n_launch += n + sub.n_launches;
+    const size_t out_g = (size_t)tp.planes * g.th * tp.up * g.tw * tp.up;
+    for (int q = 0; q < n; ++q) {
+      hipError_t e = hipMemcpyAsync(slots + (long long)slot_of[g.tiles[q]] * tp.slot_elems, stage + q * out_g,
+                                    out_g * sizeof(float), hipMemcpyDeviceToDevice, st);
+      if (e != hipSuccess) return hip_fail(e, "tile output copy");
+      ++n_launch;
+    }
+  }
   // merge: raster order, upper neighbour over the overlap rows, then left over the columns
   auto out_len = [&](int g, int len) { return std::min(tile, len - g * stride) * tp.up; };
   for (int gi = 0; gi < tp.nr; ++gi)
@@ -2124,7 +2188,8 @@ int vaep_encode_tiled(vaep_encoder* enc, const void* image, int batch, int heigh
   char* base = (char*)ws;
   void* enc_ws = base;
   void* img = base + tp.enc_bytes;
-  float* slots = (float*)(base + tp.enc_bytes + tp.img_bytes);
+  float* stage = (float*)(base + tp.enc_bytes + tp.img_bytes);
+  float* slots = (float*)(base + tp.enc_bytes + tp.img_bytes + tp.stage_bytes);
   const int up = tp.up, dt = enc->cfg.dtype;
   const long long img_planes = (long long)batch * 3;
   int n_launch = 0;
@@ -2148,19 +2213,26 @@ int vaep_encode_tiled(vaep_encoder* enc, const void* image, int batch, int heigh
     if ((rc = run_encode(enc, img, batch * tp.nfull, ts, ts, slots, enc_ws, tp.enc_bytes, stream, &n_launch)))
       return rc;
   }
-  for (int gi = 0; gi < tp.nr; ++gi)
-    for (int gj = 0; gj < tp.nc; ++gj) {
-      const int k = slot_of[gi * tp.nc + gj];
-      if (k < tp.nfull) continue;
-      const int i = gi * stride, j = gj * stride;
-      const int th = std::min(tile, tp.lh - i) * up, tw = std::min(tile, tp.lw - j) * up;
-      hipError_t e = launch_crop(image, img_planes, height, width, i * up, j * up, th, tw, img, dt, st);
+  for (const EdgeGroup& g : tp.edges) {
+    const int n = (int)g.tiles.size();
+    const int th = g.th * up, tw = g.tw * up;
+    const size_t img_g = (size_t)img_planes * th * tw * dtype_bytes(dt);
+    for (int q = 0; q < n; ++q) {
+      const int gi = g.tiles[q] / tp.nc, gj = g.tiles[q] % tp.nc;
+      hipError_t e = launch_crop(image, img_planes, height, width, gi * stride * up, gj * stride * up, th, tw,
+                                 (char*)img + q * img_g, dt, st);
       if (e != hipSuccess) return hip_fail(e, "image tile crop");
       ++n_launch;
-      if ((rc = run_encode(enc, img, batch, th, tw, slots + (long long)k * tp.slot_elems, enc_ws, tp.enc_bytes,
-                           stream, &n_launch)))
-        return rc;
     }
+    if ((rc = run_encode(enc, img, batch * n, th, tw, stage, enc_ws, tp.enc_bytes, stream, &n_launch))) return rc;
+    const size_t out_g = (size_t)tp.planes * g.th * g.tw;
+    for (int q = 0; q < n; ++q) {
+      hipError_t e = hipMemcpyAsync(slots + (long long)slot_of[g.tiles[q]] * tp.slot_elems, stage + q * out_g,
+                                    out_g * sizeof(float), hipMemcpyDeviceToDevice, st);
+      if (e != hipSuccess) return hip_fail(e, "tile moments copy");
+      ++n_launch;
+    }
+  }
   // merge in latent space: raster order, upper neighbour over the overlap rows, then left
   auto len = [&](int g, int n) { return std::min(tile, n - g * stride); };
   const int blend = tile - stride;
