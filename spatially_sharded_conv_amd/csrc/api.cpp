@@ -1283,7 +1283,7 @@ int tile_plan(const vaep_model* m, int batch, int frames, int h, int w, int tile
   const int th = std::min(tile, h), tw = std::min(tile, w);
   tp->slot_elems = tp->planes * (long long)th * tp->up * tw * tp->up;
   // tiles lying wholly inside the image share one size and decode as one batch; the
-  // clipped edge tiles decode one at a time
+  // clipped edge tiles decode as one batch per tile size
   int full_r = 0, full_c = 0;
   for (int i = 0; i < h; i += stride) full_r += i + tile <= h ? 1 : 0;
   for (int j = 0; j < w; j += stride) full_c += j + tile <= w ? 1 : 0;
@@ -2197,7 +2197,7 @@ int vaep_encode_tiled(vaep_encoder* enc, const void* image, int batch, int heigh
   for (int gi = 0; gi < tp.nr; ++gi)
     for (int gj = 0; gj < tp.nc; ++gj) slot_of[gi * tp.nc + gj] = tile_slot(gi, gj, tp.nc, tp.full_r, tp.full_c);
   // split / exec: every tile encoded on its own; the full-size tiles together as one batch
-  // of images whose moments land in consecutive slots, the clipped edge tiles one by one
+  // of images whose moments land in consecutive slots, the clipped edge tiles one batch per size
   const int ts = tile * up;
   const size_t img_tile = (size_t)img_planes * ts * ts * dtype_bytes(dt);
   if (tp.nfull > 0) {
