@@ -61,8 +61,10 @@ def _check(cfg, tables, batch=1):
 
 
 def test_encode_tiny_fp32():
+    """Covering tile; overlapping tiles; stride 1 (64 tiles, edge tiles of eight sizes down
+    to one latent pixel, i.e. 2 x 2-pixel images through the whole encoder)."""
     cfg = preset(1)
-    _check(cfg, [(8, 8), (4, 3), (3, 2)])
+    _check(cfg, [(8, 8), (4, 3), (3, 2), (3, 1)])
 
 
 def test_encode_reduced_bf16():
