@@ -8,7 +8,8 @@
   tile's unblended block against the oracle's encode of that 256 x 256 tile;
 * argument errors leave the output untouched.
 """
-import numpy as np
+import ctypes as C
+
 import pytest
 import torch
 
@@ -127,13 +128,8 @@ def test_encode_errors_leave_output_untouched():
         (P(img), 1, 32, 32, 4, 4, P(out), P(ws), ws.numel() // 2, L.VAEP_ERR_WORKSPACE),
     ]
     for im, b, h, w, tile, stride, o, wsp, nbytes, code in cases:
-        rc = lib.vaep_encode_tiled(enc._h, im, b, h, w, tile, stride, o, wsp, nbytes, None, C_ref(info))
+        rc = lib.vaep_encode_tiled(enc._h, im, b, h, w, tile, stride, o, wsp, nbytes, None, C.byref(info))
         assert rc == code, (h, w, tile, stride, nbytes, rc, L.last_error())
     torch.cuda.synchronize()
     assert (out == 7.0).all().item()
     enc.close()
-
-
-def C_ref(x):
-    import ctypes
-    return ctypes.byref(x)
