@@ -265,7 +265,7 @@ def test_halo_poison_gives_the_same_decode(gpu_lib):
     it (vaep_model_set_halo_poison), a decode gives the same bits as without: each halo row
     a layer reads came from its neighbour's push in that decode, and no slot past the image
     edge is read.  One-band, uneven and one-row band tables; width bands; the full-size
-    1024^2, batch-4 and video presets; the folded GroupNorm apply."""
+    1024^2, batch-4 and video presets; the folded GroupNorm apply; the tile decode."""
     def width_decode(dec, cfg, latent, starts):
         lat = to_dev(latent, cfg.dtype)
         out = torch.empty(cfg.output_shape(latent.shape[0], 1, *latent.shape[-2:]), dtype=torch.float32,
@@ -302,6 +302,21 @@ def test_halo_poison_gives_the_same_decode(gpu_lib):
         assert torch.equal(y0, y1), what
         dec.close()
         del outs, y0, y1
+    # the tile decode (full tiles in one batch, clipped edge tiles batched per size) on the
+    # same switch
+    cfg = preset(2).with_size(latent_h=20, latent_w=14)
+    dec, _ = make_decoder(cfg)
+    z = to_dev(make_latent(cfg), cfg.dtype)
+    ws = dec.tiled_workspace(1, 1, 20, 14, 8, 6)
+    ys = []
+    for poison in (False, True):
+        dec.set_halo_poison(poison)
+        y = torch.empty(cfg.output_shape(), dtype=torch.float32, device="cuda")
+        assert dec.decode_tiled(z, 8, 6, y, ws) == 0
+        torch.cuda.synchronize()
+        ys.append(y)
+    assert not torch.isnan(ys[1]).any().item() and torch.equal(ys[0], ys[1])
+    dec.close()
 
 
 def test_2048_single_band_decode_equals_band_decode(gpu_lib):
