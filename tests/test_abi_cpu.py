@@ -33,6 +33,24 @@ def test_library_exports_every_declared_symbol():
     assert declared == set(L.EXPORTS)
 
 
+@pytest.mark.parametrize("header", ["vaep.h", "vaep_steps.h"])
+@pytest.mark.parametrize("lang", ["c", "c++"])
+def test_public_header_compiles_alone(header, lang, tmp_path):
+    """Each public header is self-contained plain C (no torch or HIP types leak into the
+    boundary): it compiles alone as strict C99 and as C++17 with warnings as errors."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip("no host compiler")
+    src = tmp_path / "use.c"
+    src.write_text(f'#include "{header}"\nint main(void) {{ return 0; }}\n')
+    std = ["-std=c99", "-pedantic"] if lang == "c" else ["-x", "c++", "-std=c++17"]
+    r = subprocess.run([cc, *std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                        "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def test_version_and_presets_match_synth():
     assert "gfx950" in api.version()
     for i in range(1, 6):
