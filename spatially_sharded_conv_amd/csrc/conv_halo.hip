@@ -41,6 +41,14 @@ using dma::u32x4_t;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float nt_f32x4_t;
+
+// Whole-line output store with the nontemporal hint: the kernel never re-reads its output,
+// and lines written whole need no merging in L2 (measured: the 1024^2 decode's 128-channel
+// layers 2 % faster than with plain stores).
+__device__ __forceinline__ void store_line16(float* p, float4 v) {
+  __builtin_nontemporal_store(nt_f32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_f32x4_t*>(p));
+}
 
 constexpr int kTH = 4;   // tile rows (one per pixel-wave)
 
@@ -299,9 +307,9 @@ __global__ void __launch_bounds__(512, 1) conv_halo(const ConvArgs a) {
           const float4 v = *reinterpret_cast<const float4*>(wl + px * 36 + c4);
           const long long col = c0 + 32 * j + px;
           if (cb32 + c4 < a.cout) {
-            *reinterpret_cast<float4*>(y + own_row + col * O.C + cb32 + c4) = v;
-            if (up_row >= 0) *reinterpret_cast<float4*>(y + up_row + col * O.C + cb32 + c4) = v;
-            if (dn_row >= 0) *reinterpret_cast<float4*>(y + dn_row + col * O.C + cb32 + c4) = v;
+            store_line16(y + own_row + col * O.C + cb32 + c4, v);
+            if (up_row >= 0) store_line16(y + up_row + col * O.C + cb32 + c4, v);
+            if (dn_row >= 0) store_line16(y + dn_row + col * O.C + cb32 + c4, v);
           }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

@@ -69,13 +69,14 @@ __device__ __forceinline__ unsigned short f2bf(float v) {
 }
 __device__ __forceinline__ float bf2f(unsigned short u) { return __uint_as_float(((unsigned)u) << 16); }
 
-// Split-output epilogue (acc holds the final values).  Lanes l and l+32 hold alternate
-// 4-channel groups of one pixel; v_permlane32_swap pairs them up so that each lane owns 8
-// consecutive channels and stores their hi and lo parts as one 16-byte store each.
+// Split-output epilogue in the fp8 encoding of split8.h (acc holds the final values): bf16
+// hi parts, then per 64-channel block the fp8 bytes of x_lo and x.  Lanes l and l+32 hold
+// alternate 4-channel groups of one pixel; v_permlane32_swap pairs them up so that each
+// lane owns 8 consecutive channels.
 template <bool SUB, int MI, int NJ, int BN>
-__device__ __forceinline__ void split_epilogue(const ConvArgs& a, const f32x16_t (&acc)[MI][NJ], int band,
-                                               int tile, int plane, long long m_band, int W, int py, int px,
-                                               int co0, int wco, int wpx, int lane) {
+__device__ __forceinline__ void split8_epilogue(const ConvArgs& a, const f32x16_t (&acc)[MI][NJ], int band,
+                                                int tile, int plane, long long m_band, int W, int py, int px,
+                                                int co0, int wco, int wpx, int lane) {
   const int hi = lane >> 5;
   const int half = a.cout;
 #pragma unroll
@@ -112,25 +113,95 @@ __device__ __forceinline__ void split_epilogue(const ConvArgs& a, const f32x16_t
         const int co = co0 + wco + 32 * i + 8 * (2 * m + hi);
         if (!pv || co >= a.cout) continue;
         unsigned short* y = reinterpret_cast<unsigned short*>(a.y);
-        if (a.split8) {
-          // bf16 hi parts, then the fp8 bytes of x_lo and x (split8.h)
-          unsigned hw[4];
+        unsigned hw[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) hw[e] = (unsigned)f2bf(v[2 * e]) | ((unsigned)f2bf(v[2 * e + 1]) << 16);
-          uint2 lo, xs;
-          split8::operand_bytes4(v, &lo.x, &xs.x);
-          split8::operand_bytes4(v + 4, &lo.y, &xs.y);
-          const long long f = split8::lo_byte(half, co);
-          auto put8 = [&](long long q) {
-            *reinterpret_cast<uint4*>(y + q + co) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-            *reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(y + q) + f) = lo;
-            *reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(y + q) + f + 64) = xs;
-          };
-          put8(o);
-          if (hu >= 0) put8(hu);
-          if (hd >= 0) put8(hd);
-          continue;
-        }
+        for (int e = 0; e < 4; ++e) hw[e] = (unsigned)f2bf(v[2 * e]) | ((unsigned)f2bf(v[2 * e + 1]) << 16);
+        uint2 lo, xs;
+        split8::operand_bytes4(v, &lo.x, &xs.x);
+        split8::operand_bytes4(v + 4, &lo.y, &xs.y);
+        const long long f = split8::lo_byte(half, co);
+        auto put8 = [&](long long q) {
+          *reinterpret_cast<uint4*>(y + q + co) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+          *reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(y + q) + f) = lo;
+          *reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(y + q) + f + 64) = xs;
+        };
+        put8(o);
+        if (hu >= 0) put8(hu);
+        if (hd >= 0) put8(hd);
+      }
+    }
+  }
+}
+
+// 16-byte global store with the nontemporal hint, for epilogues that write whole 128-byte
+// lines: the kernel never re-reads its output, and whole lines need no merging in L2.
+typedef __attribute__((ext_vector_type(4))) unsigned nt_u32x4_t;
+typedef __attribute__((ext_vector_type(4))) float nt_f32x4_t;
+__device__ __forceinline__ void store_line16(void* p, uint4 v) {
+  __builtin_nontemporal_store(nt_u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_u32x4_t*>(p));
+}
+__device__ __forceinline__ void store_line16(void* p, float4 v) {
+  __builtin_nontemporal_store(nt_f32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_f32x4_t*>(p));
+}
+
+// Output slots of compute pixel p of the tile's band (own slot; halo slots in the bands
+// above / below for a band's first / last row, -1 where there is none); own = -1 past the
+// band's pixels.
+template <bool SUB>
+__device__ __forceinline__ void out_slots(const ConvArgs& a, int band, long long p, long long m_band, int plane,
+                                          int W, int py, int px, long long& own, long long& hu, long long& hd) {
+  own = hu = hd = -1;
+  if (p >= m_band) return;
+  const int n = (int)(p / plane);
+  const int rem = (int)(p - (long long)n * plane);
+  int r = rem / W;
+  int c = rem - r * W;
+  if (SUB) {
+    r = 2 * r + py;
+    c = 2 * c + px;
+  }
+  own = band_offset(a.out, band, n, r, c);
+  if (r == 0 && band > 0) hu = band_offset(a.out, band - 1, n, a.out.rows[band - 1], c);
+  if (r == a.out.rows[band] - 1 && band + 1 < a.out.nb) hd = band_offset(a.out, band + 1, n, -1, c);
+}
+
+// Split-output epilogue in whole lines (bf16 hi and lo planes, no fp8 bytes).  Per pixel
+// block and pair of 32-channel blocks the wave passes its accumulators through its own LDS
+// rows (68 floats per pixel); eight lanes then own one pixel's 64 channels, 8 each, and
+// write its 128-byte hi line and 128-byte lo line.  wl: this wave's 32 x 68 floats, free.
+template <bool SUB, int MI, int NJ, int BN>
+__device__ __forceinline__ void split_epilogue_lines(const ConvArgs& a, const f32x16_t (&acc)[MI][NJ], int band,
+                                                     int tile, int plane, long long m_band, int W, int py, int px,
+                                                     int co0, int wco, int wpx, int lane, float* wl) {
+  static_assert(MI % 2 == 0, "pairs of channel blocks");
+  const int h = lane >> 5;
+  const int half = a.cout;
+  const int c8 = (lane & 7) * 8;
+  unsigned short* y = reinterpret_cast<unsigned short*>(a.y);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    long long own[4], hu[4], hd[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      out_slots<SUB>(a, band, (long long)tile * BN + wpx + 32 * j + 8 * rr + (lane >> 3), m_band, plane, W, py, px,
+                     own[rr], hu[rr], hd[rr]);
+#pragma unroll
+    for (int ip = 0; ip < MI / 2; ++ip) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(wl + (lane & 31) * 68 + 32 * t + 8 * g + 4 * h) =
+              make_float4(acc[2 * ip + t][j][4 * g], acc[2 * ip + t][j][4 * g + 1], acc[2 * ip + t][j][4 * g + 2],
+                          acc[2 * ip + t][j][4 * g + 3]);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int co = co0 + wco + 64 * ip + c8;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float* src = wl + (8 * rr + (lane >> 3)) * 68 + c8;
+        const float4 v0 = *reinterpret_cast<const float4*>(src);
+        const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+        const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
         unsigned hw[4], lw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -139,14 +210,20 @@ __device__ __forceinline__ void split_epilogue(const ConvArgs& a, const f32x16_t
           hw[e] = (unsigned)h0 | ((unsigned)h1 << 16);
           lw[e] = (unsigned)l0 | ((unsigned)l1 << 16);
         }
-        auto put = [&](long long q) {
-          *reinterpret_cast<uint4*>(y + q + co) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-          *reinterpret_cast<uint4*>(y + q + half + co) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        };
-        put(o);
-        if (hu >= 0) put(hu);
-        if (hd >= 0) put(hd);
+        if (own[rr] < 0 || co >= a.cout) continue;
+        const uint4 hv = make_uint4(hw[0], hw[1], hw[2], hw[3]), lv = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        store_line16(y + own[rr] + co, hv);
+        store_line16(y + own[rr] + half + co, lv);
+        if (hu[rr] >= 0) {
+          store_line16(y + hu[rr] + co, hv);
+          store_line16(y + hu[rr] + half + co, lv);
+        }
+        if (hd[rr] >= 0) {
+          store_line16(y + hd[rr] + co, hv);
+          store_line16(y + hd[rr] + half + co, lv);
+        }
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
   }
 }
@@ -205,6 +282,7 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   // S operand stages: A (BM x 64) then B (BN x 64) per stage; the epilogue reuses the space
   constexpr int kStageElems = S * (BM + BN) * 64;
   __shared__ __attribute__((aligned(1024))) unsigned short smem[kStageElems];
+  static_assert(NW * 32 * 68 * 4 <= kStageElems * 2, "epilogue transpose rows");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -585,50 +663,47 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
         reinterpret_cast<float*>(smem));
   };
   if (MODE == kModeBandSplit && gn) gn_stats(std::true_type{});
+  // The operand stages are free (the LDS barrier below, after the last products, or inside
+  // the statistics); each wave transposes through its own 32 x 68 floats.
+  gnstats::lds_barrier();
+  float* wl = reinterpret_cast<float*>(smem) + wave * (32 * 68);
   if (MODE == kModeBandSplit) {
-    split_epilogue<SUB, MI, NJ, BN>(a, acc, band, tile, plane, m_band, W, py, px, co0, wco, wpx, lane);
+    if (a.split8)
+      split8_epilogue<SUB, MI, NJ, BN>(a, acc, band, tile, plane, m_band, W, py, px, co0, wco, wpx, lane);
+    else
+      split_epilogue_lines<SUB, MI, NJ, BN>(a, acc, band, tile, plane, m_band, W, py, px, co0, wco, wpx, lane, wl);
     return;
   }
-  // Each pixel's own slot and its halo slots in the neighbours (boundary rows; a one-row
-  // band has both) are formed once per pixel block: formed per store, the band fields are
-  // re-read from the kernel arguments with a scalar-load wait before every store.
+  // Plain fp32 output: each 32-channel x 32-pixel block passes through this wave's LDS rows,
+  // then eight lanes write one pixel's 32 channels (a whole 128-byte line) to its own slot
+  // and, for a band's first or last row, to the neighbour's halo slot.
   {
-    const BandLayout& L = a.out;
-    const long long off_b = L.off[band];
-    const int rows_b = L.rows[band];
-    const bool has_u = band > 0, has_d = band + 1 < L.nb;
-    const long long off_u = has_u ? L.off[band - 1] : 0, off_d = has_d ? L.off[band + 1] : 0;
-    const int rows_u = has_u ? L.rows[band - 1] : 0;
-    const int OW = L.W;
-    const long long OC = L.C;
     float* y = reinterpret_cast<float*>(a.y);
+    const int c4 = (lane & 7) * 4;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const long long p = (long long)tile * BN + wpx + 32 * j + (lane & 31);
-      if (p >= m_band) continue;
-      const int n = (int)(p / plane);
-      const int rem = (int)(p - (long long)n * plane);
-      int r = rem / W;
-      int c = rem - r * W;
-      if (SUB) {
-        r = 2 * r + py;
-        c = 2 * c + px;
-      }
-      const long long own = off_b + (((long long)n * (rows_b + 2) + r + 1) * OW + c) * OC;
-      const long long hu = (has_u && r == 0) ? off_u + (((long long)n * (rows_u + 2) + rows_u + 1) * OW + c) * OC : -1;
-      const long long hd = (has_d && r == rows_b - 1) ? off_d + ((long long)n * (L.rows[band + 1] + 2) * OW + c) * OC : -1;
+      long long own[4], hu[4], hd[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        out_slots<SUB>(a, band, (long long)tile * BN + wpx + 32 * j + 8 * rr + (lane >> 3), m_band, plane, W, py,
+                       px, own[rr], hu[rr], hd[rr]);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int co = co0 + wco + 32 * i + 8 * g + 4 * (lane >> 5);
-          if (co >= a.cout) continue;
-          const float4 v = make_float4(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                       acc[i][j][4 * g + 3]);
-          *reinterpret_cast<float4*>(y + own + co) = v;
-          if (hu >= 0) *reinterpret_cast<float4*>(y + hu + co) = v;
-          if (hd >= 0) *reinterpret_cast<float4*>(y + hd + co) = v;
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(wl + (lane & 31) * 68 + 8 * g + 4 * (lane >> 5)) =
+              make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int co = co0 + wco + 32 * i + c4;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float4 v = *reinterpret_cast<const float4*>(wl + (8 * rr + (lane >> 3)) * 68 + c4);
+          if (own[rr] < 0 || co >= a.cout) continue;
+          store_line16(y + own[rr] + co, v);
+          if (hu[rr] >= 0) store_line16(y + hu[rr] + co, v);
+          if (hd[rr] >= 0) store_line16(y + hd[rr] + co, v);
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
     }
   }
