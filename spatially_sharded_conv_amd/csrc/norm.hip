@@ -19,6 +19,8 @@
 // the apply pass streams the rows again and writes the result plus the boundary rows
 // into the neighbours' halo slots.  Channel RMSNorm is local to a pixel and needs no
 // merge.
+#include <type_traits>
+
 #include "vaep_internal.h"
 #include "norm_act.h"
 
@@ -241,43 +243,64 @@ __device__ void merge_tiles(const NormArgs& a, int n, int g, int t0, int t1, dou
   // Each thread takes tiles t0 + tid, t0 + tid + kThreads, ... in that order; the loads of a
   // batch of kBatch tiles are issued together (one memory latency per batch, not per tile),
   // the sums still run tile by tile.
+  //
+  // When the chunks divide the slab (the records of every conv epilogue) all tiles hold the
+  // same count nt, so nt / total is one double formed once instead of per tile; when nt is
+  // a power of two, M2_t / nt is exactly M2_t * (1 / nt).  Either way every term is the
+  // same double as the per-tile form, and the merge result does not change.
   constexpr int kBatch = 8;
-  double s = 0.0;
-  for (int t_b = t0 + tid; t_b < t1; t_b += kBatch * kThreads) {
-    double mt[kBatch];
+  const bool uniform = slab_pix % a.chunk_pix == 0;
+  const long long nt_i = (long long)a.chunk_pix * cpg;
+  const double nt_u = (double)nt_i, w_u = nt_u / total, inv_u = 1.0 / nt_u;
+  const bool pow2 = (nt_i & (nt_i - 1)) == 0;
+  auto pass1 = [&](auto U) {
+    constexpr bool kU = decltype(U)::value;
+    double s = 0.0;
+    for (int t_b = t0 + tid; t_b < t1; t_b += kBatch * kThreads) {
+      double mt[kBatch];
 #pragma unroll
-    for (int r = 0; r < kBatch; ++r) {
-      const int t = t_b + r * kThreads;
-      mt[r] = t < t1 ? P[(long long)t * 2] : 0.0;
-    }
+      for (int r = 0; r < kBatch; ++r) {
+        const int t = t_b + r * kThreads;
+        mt[r] = t < t1 ? P[(long long)t * 2] : 0.0;
+      }
 #pragma unroll
-    for (int r = 0; r < kBatch; ++r) {
-      const int t = t_b + r * kThreads;
-      if (t < t1) s += (tile_n(t) / total) * mt[r];
-    }
-  }
-  const double m = block_sum(s, sh);
-  s = 0.0;
-  for (int t_b = t0 + tid; t_b < t1; t_b += kBatch * kThreads) {
-    double mt[kBatch], vt[kBatch];
-#pragma unroll
-    for (int r = 0; r < kBatch; ++r) {
-      const int t = t_b + r * kThreads;
-      const double* pr = P + (long long)(t < t1 ? t : t0) * 2;
-      mt[r] = pr[0];
-      vt[r] = pr[1];
-    }
-#pragma unroll
-    for (int r = 0; r < kBatch; ++r) {
-      const int t = t_b + r * kThreads;
-      if (t < t1) {
-        const double nt = tile_n(t);
-        const double d = mt[r] - m;
-        s += (nt / total) * (vt[r] / nt + d * d);
+      for (int r = 0; r < kBatch; ++r) {
+        const int t = t_b + r * kThreads;
+        if (t < t1) s += (kU ? w_u : tile_n(t) / total) * mt[r];
       }
     }
-  }
-  const double v = block_sum(s, sh);
+    return s;
+  };
+  const double m = block_sum(uniform ? pass1(std::true_type{}) : pass1(std::false_type{}), sh);
+  auto pass2 = [&](auto U, auto P2) {
+    constexpr bool kU = decltype(U)::value, kP2 = decltype(P2)::value;
+    double s = 0.0;
+    for (int t_b = t0 + tid; t_b < t1; t_b += kBatch * kThreads) {
+      double mt[kBatch], vt[kBatch];
+#pragma unroll
+      for (int r = 0; r < kBatch; ++r) {
+        const int t = t_b + r * kThreads;
+        const double* pr = P + (long long)(t < t1 ? t : t0) * 2;
+        mt[r] = pr[0];
+        vt[r] = pr[1];
+      }
+#pragma unroll
+      for (int r = 0; r < kBatch; ++r) {
+        const int t = t_b + r * kThreads;
+        if (t < t1) {
+          const double nt = kU ? nt_u : tile_n(t);
+          const double d = mt[r] - m;
+          const double var_t = kP2 ? vt[r] * inv_u : vt[r] / nt;
+          s += (kU ? w_u : nt / total) * (var_t + d * d);
+        }
+      }
+    }
+    return s;
+  };
+  const double s2 = !uniform ? pass2(std::false_type{}, std::false_type{})
+                    : pow2   ? pass2(std::true_type{}, std::true_type{})
+                             : pass2(std::true_type{}, std::false_type{});
+  const double v = block_sum(s2, sh);
   *cnt = total;
   *mean = m;
   *var = v;
