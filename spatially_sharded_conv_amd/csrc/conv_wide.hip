@@ -69,70 +69,6 @@ __device__ __forceinline__ unsigned short f2bf(float v) {
 }
 __device__ __forceinline__ float bf2f(unsigned short u) { return __uint_as_float(((unsigned)u) << 16); }
 
-// Split-output epilogue in the fp8 encoding of split8.h (acc holds the final values): bf16
-// hi parts, then per 64-channel block the fp8 bytes of x_lo and x.  Lanes l and l+32 hold
-// alternate 4-channel groups of one pixel; v_permlane32_swap pairs them up so that each
-// lane owns 8 consecutive channels.
-template <bool SUB, int MI, int NJ, int BN>
-__device__ __forceinline__ void split8_epilogue(const ConvArgs& a, const f32x16_t (&acc)[MI][NJ], int band,
-                                                int tile, int plane, long long m_band, int W, int py, int px,
-                                                int co0, int wco, int wpx, int lane) {
-  const int hi = lane >> 5;
-  const int half = a.cout;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const long long p = (long long)tile * BN + wpx + 32 * j + (lane & 31);
-    const bool pv = p < m_band;
-    long long o = 0, hu = -1, hd = -1;   // own slot; halo slots in the bands above / below
-    if (pv) {
-      const int n = (int)(p / plane);
-      const int rem = (int)(p - (long long)n * plane);
-      int r = rem / W;
-      int c = rem - r * W;
-      if (SUB) {
-        r = 2 * r + py;
-        c = 2 * c + px;
-      }
-      o = band_offset(a.out, band, n, r, c);
-      // a one-row band pushes its row into both neighbours' halos
-      if (r == 0 && band > 0) hu = band_offset(a.out, band - 1, n, a.out.rows[band - 1], c);
-      if (r == a.out.rows[band] - 1 && band + 1 < a.out.nb) hd = band_offset(a.out, band + 1, n, -1, c);
-    }
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][j][8 * m + e]),
-                                                           __float_as_uint(acc[i][j][8 * m + 4 + e]), false, false);
-          v[e] = __uint_as_float(r2[0]);
-          v[4 + e] = __uint_as_float(r2[1]);
-        }
-        const int co = co0 + wco + 32 * i + 8 * (2 * m + hi);
-        if (!pv || co >= a.cout) continue;
-        unsigned short* y = reinterpret_cast<unsigned short*>(a.y);
-        unsigned hw[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hw[e] = (unsigned)f2bf(v[2 * e]) | ((unsigned)f2bf(v[2 * e + 1]) << 16);
-        uint2 lo, xs;
-        split8::operand_bytes4(v, &lo.x, &xs.x);
-        split8::operand_bytes4(v + 4, &lo.y, &xs.y);
-        const long long f = split8::lo_byte(half, co);
-        auto put8 = [&](long long q) {
-          *reinterpret_cast<uint4*>(y + q + co) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-          *reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(y + q) + f) = lo;
-          *reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(y + q) + f + 64) = xs;
-        };
-        put8(o);
-        if (hu >= 0) put8(hu);
-        if (hd >= 0) put8(hd);
-      }
-    }
-  }
-}
-
 // 16-byte global store with the nontemporal hint, for epilogues that write whole 128-byte
 // lines: the kernel never re-reads its output, and whole lines need no merging in L2.
 typedef __attribute__((ext_vector_type(4))) unsigned nt_u32x4_t;
@@ -222,6 +158,77 @@ __device__ __forceinline__ void split_epilogue_lines(const ConvArgs& a, const f3
           store_line16(y + hd[rr] + co, hv);
           store_line16(y + hd[rr] + half + co, lv);
         }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+  }
+}
+
+// Split-output epilogue in whole lines for the fp8 encoding of split8.h.  After the same
+// LDS transpose as split_epilogue_lines, lane k (of the eight on a pixel) owns channels
+// 8k .. 8k+7 of a 64-channel block: it stores their bf16 hi parts (eight lanes, one
+// 128-byte line).  The block's fp8 bytes are a second 128-byte line, 64 bytes of x_lo then
+// 64 of x; lanes 2m and 2m+1 swap halves (one DPP move) so that lane 2m stores the x_lo
+// bytes of channels 16m .. 16m+15 and lane 2m+1 their x bytes, 16 contiguous bytes each.
+template <bool SUB, int MI, int NJ, int BN>
+__device__ __forceinline__ void split8_epilogue_lines(const ConvArgs& a, const f32x16_t (&acc)[MI][NJ], int band,
+                                                      int tile, int plane, long long m_band, int W, int py,
+                                                      int px, int co0, int wco, int wpx, int lane, float* wl) {
+  static_assert(MI % 2 == 0, "pairs of channel blocks");
+  const int h = lane >> 5;
+  const int half = a.cout;
+  const int k8 = lane & 7;
+  const bool odd = k8 & 1;
+  unsigned short* y = reinterpret_cast<unsigned short*>(a.y);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    long long own[4], hu[4], hd[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      out_slots<SUB>(a, band, (long long)tile * BN + wpx + 32 * j + 8 * rr + (lane >> 3), m_band, plane, W, py, px,
+                     own[rr], hu[rr], hd[rr]);
+#pragma unroll
+    for (int ip = 0; ip < MI / 2; ++ip) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(wl + (lane & 31) * 68 + 32 * t + 8 * g + 4 * h) =
+              make_float4(acc[2 * ip + t][j][4 * g], acc[2 * ip + t][j][4 * g + 1], acc[2 * ip + t][j][4 * g + 2],
+                          acc[2 * ip + t][j][4 * g + 3]);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int cblk = co0 + wco + 64 * ip;   // first channel of the 64-channel block
+      const int co = cblk + 8 * k8;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float* src = wl + (8 * rr + (lane >> 3)) * 68 + 8 * k8;
+        const float4 v0 = *reinterpret_cast<const float4*>(src);
+        const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+        const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        uint4 hv;
+        hv.x = (unsigned)f2bf(v[0]) | ((unsigned)f2bf(v[1]) << 16);
+        hv.y = (unsigned)f2bf(v[2]) | ((unsigned)f2bf(v[3]) << 16);
+        hv.z = (unsigned)f2bf(v[4]) | ((unsigned)f2bf(v[5]) << 16);
+        hv.w = (unsigned)f2bf(v[6]) | ((unsigned)f2bf(v[7]) << 16);
+        uint2 lo, xs;
+        split8::operand_bytes4(v, &lo.x, &xs.x);
+        split8::operand_bytes4(v + 4, &lo.y, &xs.y);
+        // even lanes send their x bytes and keep their x_lo bytes; odd lanes the reverse
+        const uint2 send = odd ? lo : xs;
+        uint2 recv;
+        recv.x = (unsigned)__builtin_amdgcn_update_dpp(0, (int)send.x, 0xB1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+        recv.y = (unsigned)__builtin_amdgcn_update_dpp(0, (int)send.y, 0xB1, 0xf, 0xf, false);
+        const uint4 fv = odd ? make_uint4(recv.x, recv.y, xs.x, xs.y) : make_uint4(lo.x, lo.y, recv.x, recv.y);
+        if (own[rr] < 0 || co >= a.cout) continue;
+        // this lane's 16 fp8 bytes: x_lo (even) or x (odd) of channels cblk + 16 (k8 / 2) ..
+        const long long fb = split8::lo_byte(half, cblk) + 16 * (k8 >> 1) + (odd ? 64 : 0);
+        auto put = [&](long long q) {
+          store_line16(y + q + co, hv);
+          store_line16(reinterpret_cast<unsigned char*>(y + q) + fb, fv);
+        };
+        put(own[rr]);
+        if (hu[rr] >= 0) put(hu[rr]);
+        if (hd[rr] >= 0) put(hd[rr]);
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
@@ -669,7 +676,7 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   float* wl = reinterpret_cast<float*>(smem) + wave * (32 * 68);
   if (MODE == kModeBandSplit) {
     if (a.split8)
-      split8_epilogue<SUB, MI, NJ, BN>(a, acc, band, tile, plane, m_band, W, py, px, co0, wco, wpx, lane);
+      split8_epilogue_lines<SUB, MI, NJ, BN>(a, acc, band, tile, plane, m_band, W, py, px, co0, wco, wpx, lane, wl);
     else
       split_epilogue_lines<SUB, MI, NJ, BN>(a, acc, band, tile, plane, m_band, W, py, px, co0, wco, wpx, lane, wl);
     return;
