@@ -18,6 +18,7 @@
 // previous tile feeds the MFMAs).
 #include "vaep_internal.h"
 #include "conv_gn_stats.h"
+#include "conv_epilogue.h"
 #include "split8.h"
 #include "norm_act.h"
 
@@ -462,6 +463,20 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_bf16(const ConvArgs a) {
                                                  gnstats::record(a.gn_part, rec, co0 / cg, a.gn_groups, tiles),
                                                  2 * tiles, reinterpret_cast<float*>(&sW[0][0]));
     }
+  }
+  // Band outputs leave in whole lines through the weight stages (free once every wave has
+  // passed the LDS barrier after its last products or the statistics), 32 x 68 floats per
+  // wave; with 32-channel steps the stages are too small and the stores below run instead.
+  if constexpr ((MODE == kModeBand || MODE == kModeBandSplit) && sizeof(sW) >= 4 * 32 * 68 * sizeof(float)) {
+    gnstats::lds_barrier();
+    float* wl = reinterpret_cast<float*>(&sW[0][0]) + wave * (32 * 68);
+    if (MODE == kModeBandSplit && a.split8)
+      epi::split8_epilogue_lines<false, 2, 2, BN>(a, acc, band, tile, plane, m_band, wc, 0, 0, co0, wco, wpx, lane, wl);
+    else if (MODE == kModeBandSplit)
+      epi::split_epilogue_lines<false, 2, 2, BN>(a, acc, band, tile, plane, m_band, wc, 0, 0, co0, wco, wpx, lane, wl);
+    else
+      epi::band_epilogue_lines<false, 2, 2, BN>(a, acc, band, tile, plane, m_band, wc, 0, 0, co0, wco, wpx, lane, wl);
+    return;
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
