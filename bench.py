@@ -103,12 +103,15 @@ def summarise(recs, steps):
     for r in recs:
         if r["step"] == L.STEP_CONV:
             # the roofline kernel: the halo-tile kernel's 128-channel form (the 1024^2 stage's
-            # 3x3 convs); its 256-channel form, the wide kernel's launches (plain 3x3 at 256^2,
-            # sub-pixel upsample, split output, folded shortcut), the 128x128-tile kernel and
-            # the narrow conv_out are reported apart
+            # plain 3x3 convs); its 256-channel form, its launches with a folded shortcut, the
+            # wide kernel's launches (plain 3x3 at 256^2, sub-pixel upsample, split output), the
+            # 128x128-tile kernel and the narrow conv_out are reported apart
             if r["kernel"] == L.KERNEL_CONV_HALO:
                 # halo-tile kernel: 128 x (4 x 128) tiles for 128-channel outputs, 256 x (4 x 64) else
                 add("conv_halo_128" if r["cout"] <= 128 else "conv_halo_256", r)
+            elif r["kernel"] == L.KERNEL_CONV_HALO_X2:
+                # the same kernel with a resnet's 1x1 shortcut folded in as extra K steps
+                add("conv_halo_shortcut", r)
             elif r["kernel"] == L.KERNEL_CONV_WIDE256 and r["ks"] == 3 and r["ups"] == 0 and r["mode"] == 0:
                 add("conv_wide_3x3", r)
             elif r["kernel"] == L.KERNEL_CONV_WIDE128X512:

@@ -357,10 +357,11 @@ enum { VAEP_STEP_CONV = 1, VAEP_STEP_GROUPNORM = 2, VAEP_STEP_RMSNORM = 3,
 /* Convolution kernel that ran a conv step: 128x128 tiles two per CU, the wide kernel
  * with 256 x 256, 128 x 256 or 128 x 512 (channels x pixels) tiles, the narrow-output
  * kernel, the fp32 kernel, the halo-tile kernel (2-D pixel tiles, the pixel operand
- * staged once per channel block). */
+ * staged once per channel block), and the halo-tile kernel with a folded 1x1 second
+ * operand (a resnet's shortcut run as extra K steps of its conv2). */
 enum { VAEP_KERNEL_OTHER = 0, VAEP_KERNEL_CONV_TILE128 = 1, VAEP_KERNEL_CONV_WIDE256 = 2,
        VAEP_KERNEL_CONV_WIDE128 = 3, VAEP_KERNEL_CONV_NARROW = 4, VAEP_KERNEL_CONV_F32 = 5,
-       VAEP_KERNEL_CONV_WIDE128X512 = 6, VAEP_KERNEL_CONV_HALO = 7 };
+       VAEP_KERNEL_CONV_WIDE128X512 = 6, VAEP_KERNEL_CONV_HALO = 7, VAEP_KERNEL_CONV_HALO_X2 = 8 };
 typedef struct vaep_profile_entry {
   int32_t step;        /* VAEP_STEP_* */
   int32_t n_kernels;   /* kernels inside the bracket */

@@ -47,7 +47,7 @@ EXPORTS = [
 
 STEP_CONV, STEP_GROUPNORM, STEP_RMSNORM, STEP_ATTENTION, STEP_MOVE = 1, 2, 3, 4, 5
 (KERNEL_OTHER, KERNEL_CONV_TILE128, KERNEL_CONV_WIDE256, KERNEL_CONV_WIDE128, KERNEL_CONV_NARROW,
- KERNEL_CONV_F32, KERNEL_CONV_WIDE128X512, KERNEL_CONV_HALO) = 0, 1, 2, 3, 4, 5, 6, 7
+ KERNEL_CONV_F32, KERNEL_CONV_WIDE128X512, KERNEL_CONV_HALO, KERNEL_CONV_HALO_X2) = 0, 1, 2, 3, 4, 5, 6, 7, 8
 
 
 class VaepConfig(C.Structure):

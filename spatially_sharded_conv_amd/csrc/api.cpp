@@ -848,6 +848,13 @@ bool shortcut_folds(const ResW& r, const BandLayout& Lh, bool split_out) {
   a.kt = r.c2x.kt;
   a.ks = r.c2x.ks;
   a.mode = kModeBand;
+  // the halo kernel takes the second operand in 32-channel steps (its launch checks the
+  // buffer-resource sizes)
+  a.x2 = r.c2x.w;   // any non-null pointer: only the fit is asked here
+  a.cin2 = r.c2x.kext;
+  if (conv_halo_fits(a)) return true;
+  a.x2 = nullptr;
+  a.cin2 = 0;
   if (!conv_wide_fits(a)) return false;
   // the second operand's rows one tile reads stay within a buffer resource (2 GiB)
   const int bn = wide_tile(a).bn;

@@ -24,6 +24,12 @@
 //
 // The K order of every output element is (channel block, kernel row, kernel column, 16
 // channels), independent of the tile shape and the band table.
+//
+// X2: a second operand read at the pixel itself (a resnet's 1x1 shortcut folded into its
+// conv2, a.x2 with a.cin2 channels in the input's band geometry; its weights follow the
+// nine taps in every packed weight row) adds one K step per 32 of its channels after the
+// taps.  Such a step stages the operand's 4 x TW tile in the centre of a halo stage and its
+// weights in the centre-tap slot of a weight stage, and runs the centre tap's products.
 #include "vaep_internal.h"
 #include "conv_dma.h"
 #include "conv_gn_stats.h"
@@ -65,7 +71,7 @@ __device__ __host__ __forceinline__ int tile_rows(const BandLayout& L, int b) {
 // Sum over the 32 lanes of each half-wave (DPP row butterflies and v_permlane16_swap).
 __device__ __forceinline__ float half_sum(float v) { return gnstats::half_sum(v); }
 
-template <int BM, int TW>
+template <int BM, int TW, bool X2>
 __global__ void __launch_bounds__(512, 1) conv_halo(const ConvArgs a) {
   constexpr int NW = 8;
   constexpr int MI = BM / 64;                   // 32-channel blocks per wave
@@ -119,8 +125,14 @@ __global__ void __launch_bounds__(512, 1) conv_halo(const ConvArgs a) {
   const long long slot0 = (long long)n * (rbn + 2) + s_first;
   const u32x4_t xrs = make_rsrc(reinterpret_cast<const unsigned short*>(a.x) + L.off[band] + slot0 * row_elems,
                                 (unsigned)((long long)(s_last - s_first + 1) * row_elems * 2));
-  const int kw = 9 * C;                                    // packed weight row (elements)
+  const int cin2 = X2 ? a.cin2 : 0;
+  const int kw = 9 * C + cin2;                             // packed weight row (elements)
   const u32x4_t wrs = make_rsrc(a.w, (unsigned)((long long)a.cout_pad * kw * 2));
+  // second operand: the same slots of its band buffer, cin2 channels per pixel
+  const u32x4_t x2rs =
+      X2 ? make_rsrc(reinterpret_cast<const unsigned short*>(a.x2) + L.off[band] / XC * cin2 + slot0 * W * cin2,
+                     (unsigned)((long long)(s_last - s_first + 1) * W * cin2 * 2))
+         : u32x4_t{0u, 0u, 0u, 0u};
 
   // Halo loads of this thread: round k loads chunk (k * NW + wave) * 64 + lane of the tile.
   unsigned hoff[HROUNDS];
@@ -135,6 +147,22 @@ __global__ void __launch_bounds__(512, 1) conv_halo(const ConvArgs a) {
     const int logical = slot ^ ((q >> 2) & 3);
     hoff[k] = in ? (unsigned)((((long long)(sl - s_first) * W + col) * XC + logical * 8) * 2) : kPadOffset;
   }
+  // Second-operand loads: the same chunks of the halo stage, filled only at the tile's own
+  // pixels (halo rows 1 .. 4, columns 1 .. TW) of rows inside the band; only the wave-loads
+  // [X2L0, X2L1) hold such chunks.
+  constexpr int X2L0 = HW * 4 / 64, X2L1 = (5 * HW * 4 + 63) / 64;
+  unsigned hoff2[X2 ? HROUNDS : 1];
+#pragma unroll
+  for (int k = 0; k < (X2 ? HROUNDS : 1); ++k) {
+    const int hc = (k * NW + wave) * 64 + lane;
+    const int q = hc >> 2, slot = hc & 3;
+    const int hr = q / HW, hx = q - hr * HW;
+    const int gr = g0 - 1 + hr, col = c0 - 1 + hx;
+    const int sl = gr - rb0 + 1;
+    const bool in = X2 && hc < HCH && hr >= 1 && hr <= kTH && hx >= 1 && hx <= TW && gr >= rb0 && gr < rb0 + rbn;
+    const int logical = slot ^ ((q >> 2) & 3);
+    hoff2[k] = in ? (unsigned)((((long long)(sl - s_first) * W + col) * cin2 + logical * 8) * 2) : kPadOffset;
+  }
   // Weight loads: chunk u * 512 + tid of a step = tap t3 (of the kernel row), row, slot.
   unsigned aoff[AL];
 #pragma unroll
@@ -146,11 +174,26 @@ __global__ void __launch_bounds__(512, 1) conv_halo(const ConvArgs a) {
     aoff[u] = (unsigned)((((long long)(co0 + row) * kw + t3 * C) + logical * 8) * 2);
   }
   const int ncb = C >> 5;
-  const int nsteps = 3 * ncb;
+  const int nsteps = 3 * ncb;                              // the taps' steps
+  const int ncb2 = cin2 >> 5;                              // second-operand steps after them
 #define VAEP_HALO_ISSUE(st, cb, k)                                                             \
   {                                                                                            \
     if ((k) * NW + wave < HWL)                                                                 \
       dma16((k) == 0, xrs, lds_addr(smem + (st) * HST) + ((k) * NW + wave) * 1024, hoff[k], (cb) * 64); \
+  }
+// second-operand block e (32 channels) into halo stage st: the wave-loads holding the
+// tile's own pixels
+#define VAEP_X2_ISSUE(st, e, k)                                                                \
+  {                                                                                            \
+    if ((k) * NW + wave >= X2L0 && (k) * NW + wave < X2L1)                                     \
+      dma16(true, x2rs, lds_addr(smem + (st) * HST) + ((k) * NW + wave) * 1024, hoff2[k], (e) * 64); \
+  }
+// weights of second-operand block e into the centre-tap slot of weight stage st
+#define VAEP_A2_ISSUE(st, e)                                                                   \
+  {                                                                                            \
+    _Pragma("unroll") for (int u = AL / 3; u < 2 * AL / 3; ++u)                                \
+      dma16(u == AL / 3, wrs, lds_addr(smem + 2 * HST + (st) * AST) + (u * NW + wave) * 1024,   \
+            aoff[u], (8 * C + (e) * 32) * 2);                                                  \
   }
 // weight loads of tap t3 (0..2) of step s: loads u with u * 512 / (4 BM) == t3
 #define VAEP_A_ISSUE(st, s, t3)                                                                \
@@ -236,11 +279,17 @@ __global__ void __launch_bounds__(512, 1) conv_halo(const ConvArgs a) {
     for (int dx = 0; dx < 3; ++dx) {
       __builtin_amdgcn_sched_barrier(0);
       if (s + 1 < nsteps) VAEP_A_ISSUE((s + 1) & 1, s + 1, dx);
+      if (X2 && s + 1 == nsteps && ncb2 > 0 && dx == 1) VAEP_A2_ISSUE((s + 1) & 1, 0);
       if (cb + 1 < ncb) {
         // halo round k goes out in step dy = k * 3 / HROUNDS of the block, tap k % 3
 #pragma unroll
         for (int k = 0; k < HROUNDS; ++k)
           if (k * 3 / HROUNDS == dy && k % 3 == dx) VAEP_HALO_ISSUE((cb + 1) & 1, cb + 1, k);
+      } else if (X2 && ncb2 > 0) {
+        // the last block stages the first second-operand tile instead
+#pragma unroll
+        for (int k = 0; k < HROUNDS; ++k)
+          if (k * 3 / HROUNDS == dy && k % 3 == dx) VAEP_X2_ISSUE((cb + 1) & 1, 0, k);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -269,8 +318,37 @@ __global__ void __launch_bounds__(512, 1) conv_halo(const ConvArgs a) {
       }
     }
   }
+  // Second-operand steps: block e sits in halo stage (ncb + e) & 1 and weight stage
+  // (nsteps + e) & 1; each step stages block e + 1 into the other stages.
+  if constexpr (X2) {
+    for (int e = 0; e < ncb2; ++e) {
+      const int s = nsteps + e;
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      const unsigned char* HB = smem + ((ncb + e) & 1) * HST;
+      const unsigned char* AB = smem + 2 * HST + (s & 1) * AST;
+      bf16x8_t af[2][MI], bfr[2][NJ];
+      read_frags(AB, HB, 1, 2, af[0], bfr[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (e + 1 < ncb2) {
+        VAEP_A2_ISSUE((s + 1) & 1, e + 1);
+#pragma unroll
+        for (int k = 0; k < HROUNDS; ++k) VAEP_X2_ISSUE((ncb + e + 1) & 1, e + 1, k);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(AB, HB, 1, 3, af[1], bfr[1]);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bfr[kk][j], acc[i][j], 0, 0, 0);
+    }
+  }
 #undef VAEP_HALO_ISSUE
 #undef VAEP_A_ISSUE
+#undef VAEP_X2_ISSUE
+#undef VAEP_A2_ISSUE
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // every operand load has landed
 
   // Epilogue 1: fp32 band output.  Each 32-channel x 32-pixel block passes through this
@@ -410,7 +488,10 @@ template <int BM, int TW>
 hipError_t go(const ConvArgs& a, hipStream_t s) {
   const long long wgs = (long long)a.tiles_total * (a.cout_pad / BM);
   if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((conv_halo<BM, TW>), dim3((unsigned)wgs), dim3(512), 0, s, a);
+  if (a.x2)
+    hipLaunchKernelGGL((conv_halo<BM, TW, true>), dim3((unsigned)wgs), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((conv_halo<BM, TW, false>), dim3((unsigned)wgs), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
@@ -433,7 +514,9 @@ int halo_bm(const ConvArgs& a) {
 // fill the GPU.  Decided on the layer's shape alone: every band table of a layer uses the
 // same kernel.
 bool conv_halo_fits(const ConvArgs& a) {
-  if (a.kt != 1 || a.ks != 3 || a.ups || a.down || a.sub || a.x_split || a.x_f32 || a.x2 || a.cin2) return false;
+  if (a.kt != 1 || a.ks != 3 || a.ups || a.down || a.sub || a.x_split || a.x_f32) return false;
+  // a folded 1x1 second operand in 32-channel steps
+  if ((a.x2 != nullptr) != (a.cin2 > 0) || a.cin2 % 32 != 0) return false;
   if (a.mode != kModeBand || a.split8) return false;
   if (a.cin % 32 != 0 || a.in.C != a.cin || a.cout != a.cout_pad) return false;
   const int bm = halo_bm(a);
@@ -450,7 +533,8 @@ hipError_t launch_conv_halo(ConvArgs& a, hipStream_t s) {
   const int tw = bm == 128 ? 128 : 64;
   // buffer-resource addressing: six rows of the input, and the weights, below 2 GiB
   if ((long long)(kTH + 2) * a.in.W * a.in.C * 2 >= (1LL << 31) - 4096) return hipErrorInvalidValue;
-  if ((long long)a.cout_pad * 9 * a.cin * 2 >= (1LL << 31)) return hipErrorInvalidValue;
+  if ((long long)a.cout_pad * (9 * a.cin + a.cin2) * 2 >= (1LL << 31)) return hipErrorInvalidValue;
+  if ((long long)(kTH + 2) * a.in.W * a.cin2 * 2 >= (1LL << 31) - 4096) return hipErrorInvalidValue;
   if (a.out.W != a.in.W || a.out.C < a.cout || a.out.nb != a.in.nb) return hipErrorInvalidValue;
   int t = 0;
   for (int b = 0; b < a.in.nb; ++b) {
@@ -459,7 +543,7 @@ hipError_t launch_conv_halo(ConvArgs& a, hipStream_t s) {
   }
   a.tile_start[a.in.nb] = t;
   a.tiles_total = t;
-  a.kernel_used = VAEP_KERNEL_CONV_HALO;
+  a.kernel_used = a.x2 ? VAEP_KERNEL_CONV_HALO_X2 : VAEP_KERNEL_CONV_HALO;
   // GroupNorm records of the output: one-row slabs, chunks of the tile width; every group
   // inside one wave's channels
   a.gn_chunk = 0;

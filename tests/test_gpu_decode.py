@@ -206,9 +206,10 @@ def test_repeat_and_alternating_calls(gpu_lib):
 
 def test_full_size_bands_bit_identical_and_kernels(gpu_lib):
     # The 1024^2 decode runs every conv kernel family (128x128 tiles, wide tiles for the
-    # sub-pixel upsamples, split outputs and folded shortcuts, halo tiles with GroupNorm
-    # moments in the epilogue for the plain 3x3 convs, narrow conv_out); its band decode
-    # must equal the full decode bit for bit.
+    # sub-pixel upsamples and split outputs, halo tiles with GroupNorm moments in the
+    # epilogue for the plain 3x3 convs and, with the 1x1 shortcut folded in as extra K
+    # steps, for the resnets that change the channel count, narrow conv_out); its band
+    # decode must equal the full decode bit for bit.
     cfg = preset(3)
     dec, _ = make_decoder(cfg)
     z = make_latent(cfg)
@@ -220,7 +221,8 @@ def test_full_size_bands_bit_identical_and_kernels(gpu_lib):
     recs = vaep.profile_end(dec)
     assert rc == 0
     used = {r["kernel"] for r in recs if r["step"] == L.STEP_CONV}
-    for k in (L.KERNEL_CONV_TILE128, L.KERNEL_CONV_WIDE256, L.KERNEL_CONV_HALO, L.KERNEL_CONV_NARROW):
+    for k in (L.KERNEL_CONV_TILE128, L.KERNEL_CONV_WIDE256, L.KERNEL_CONV_HALO, L.KERNEL_CONV_HALO_X2,
+              L.KERNEL_CONV_NARROW):
         assert k in used, (k, used)
     assert torch.equal(y_band, y_full)
     dec.close()
