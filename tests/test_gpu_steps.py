@@ -50,6 +50,9 @@ def _conv_ref(x, w, b, causal, res, dtype, upsample=False, x_exact=False):
     (2, 64, 96, 13, 37, (0, 1, 6, 13), True),
     (1, 32, 128, 16, 16, (0, 16), False),
     (1, 128, 256, 9, 70, (0, 4, 5, 9), True),
+    # 96 input channels (not a multiple of 64): the tile kernel's 32-channel K steps,
+    # three per tap, ragged bands and a one-row band
+    (2, 96, 128, 11, 29, (0, 3, 4, 11), True),
 ])
 def test_conv3x3_step(gpu_lib, dtype, case):
     B, cin, cout, H, W, starts, with_res = case
@@ -212,7 +215,7 @@ def test_upsample_conv_step(gpu_lib, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("cin", [32, 64])
+@pytest.mark.parametrize("cin", [32, 64, 96])
 def test_causal_conv3d_step(gpu_lib, dtype, cin):
     x = seeded((1, cin, 4, 9, 11), 41, dtype=dtype)
     w = seeded((64, cin, 3, 3, 3), 42, 1 / math.sqrt(cin * 27), dtype=dtype)
