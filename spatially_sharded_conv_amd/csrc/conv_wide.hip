@@ -98,7 +98,8 @@ struct LoadOrder {
 };
 
 // X2: the conv reads a second operand (a.x2, a folded 1x1 shortcut) after its taps.
-template <int KT, int KS, bool SUB, int PARTS, int MODE, int BM, int BN, int NW, bool X2>
+// H32: C = 32 mod 64, each tap's last 64-channel step half empty (not the sub-pixel form).
+template <int KT, int KS, bool SUB, int PARTS, int MODE, int BM, int BN, int NW, bool X2, bool H32 = false>
 __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   static_assert(!X2 || (!SUB && MODE == kModeBand), "a second operand folds into plain band convs only");
   // NW waves: 2 along the output channels x NW/2 along the pixels.  With 8 waves two
@@ -142,7 +143,10 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   const long long m_band = (long long)a.in.n_img * plane;
   const int C = a.cin;                                 // input channels
   const int XC = a.in.C;                               // channel stride of the input buffer
-  const int csteps = C >> 6;
+  // 64-channel steps per tap; with C = 32 mod 64 (H32) the last step of a tap is half empty:
+  // its pixel chunks past C read zeros (the padding offset), so whatever weights meet them add 0
+  static_assert(!H32 || !SUB, "half-empty channel steps: not the sub-pixel form");
+  const int csteps = H32 ? (C + 63) >> 6 : C >> 6;
   // K: the taps of the operand, then (a.x2) the channels of a second operand read at the
   // pixel itself -- a 1x1 conv folded into this one (a resnet's shortcut): its weights
   // follow the taps' in every packed row
@@ -317,6 +321,10 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
         VAEP_TAP_GEO(itap, need, delta);                                                       \
         _Pragma("unroll") for (int j = 0; j < NB; ++j)                                         \
           bvo[j] = ((pmask[j] & need) == need) ? (unsigned)((int)pbase[j] + delta) : kPadOffset; \
+        /* a half-empty last channel step: this lane's 8 channels past C read zeros */         \
+        if (H32 && ic + 64 > C && ic + ck * 8 >= C) {                                          \
+          _Pragma("unroll") for (int j = 0; j < NB; ++j) bvo[j] = kPadOffset;                  \
+        }                                                                                      \
       }                                                                                        \
     }                                                                                          \
     const int lg_ = LO::at((q), (t));                                                          \
@@ -515,27 +523,36 @@ __global__ void __launch_bounds__(NW * 64, 1) conv_wide(const ConvArgs a) {
   if (gn) gn_stats(std::false_type{});
 }
 
-template <int KT, int KS, bool SUB, int PARTS, int MODE, bool X2>
+template <int KT, int KS, bool SUB, int PARTS, int MODE, bool X2, bool H32 = false>
 hipError_t go_tile(const ConvArgs& a, WideTile t, hipStream_t s) {
   const int ph = SUB ? 4 : 1;
   const long long wgs = (long long)a.tiles_total * (a.cout_pad / t.bm) * ph;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
   if (t.bm == 256) {
-    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 256, 256, 8, X2>), dim3((unsigned)wgs), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 256, 256, 8, X2, H32>), dim3((unsigned)wgs), dim3(512), 0, s, a);
   } else if constexpr (SUB) {
     // 128 x 256 tiles: sub-pixel convs only (plain convs of that size run on the 128 x 128
     // kernel); 8 waves, whose second wave per SIMD hides the fp8 step's extra issue slots
     if (t.bn != 256) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128, 256, 8, X2>), dim3((unsigned)wgs), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128, 256, 8, X2, H32>), dim3((unsigned)wgs), dim3(512), 0, s, a);
   } else {
     if (t.bn != 512) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128, 512, 8, X2>), dim3((unsigned)wgs), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((conv_wide<KT, KS, SUB, PARTS, MODE, 128, 512, 8, X2, H32>), dim3((unsigned)wgs), dim3(512), 0, s, a);
   }
   return hipGetLastError();
 }
 
 template <int KT, int KS, bool SUB, int PARTS>
 hipError_t go_mode(const ConvArgs& a, WideTile t, hipStream_t s) {
+  if constexpr (!SUB) {
+    if (a.cin % 64 == 32) {   // half-empty last channel step per tap
+      if (a.mode == kModeBandSplit) return go_tile<KT, KS, SUB, PARTS, kModeBandSplit, false, true>(a, t, s);
+      if constexpr (KS == 3)
+        if (a.x2) return go_tile<KT, KS, SUB, PARTS, kModeBand, true, true>(a, t, s);
+      if (a.x2) return hipErrorInvalidValue;
+      return go_tile<KT, KS, SUB, PARTS, kModeBand, false, true>(a, t, s);
+    }
+  }
   if (a.mode == kModeBandSplit) return go_tile<KT, KS, SUB, PARTS, kModeBandSplit, false>(a, t, s);
   if constexpr (!SUB && KS == 3)
     if (a.x2) return go_tile<KT, KS, SUB, PARTS, kModeBand, true>(a, t, s);
@@ -563,7 +580,7 @@ bool conv_wide_fits(const ConvArgs& a) {
   if (a.sub) return true;
   if (a.x_f32 || a.x_split || a.ups || a.down) return false;
   if (a.mode != kModeBand && a.mode != kModeBandSplit) return false;
-  if (a.cin % 64 != 0 || a.cout_pad % 128 != 0) return false;
+  if (a.cin % 32 != 0 || (a.sub && a.cin % 64 != 0) || a.cout_pad % 128 != 0) return false;
   const bool geo = (a.kt == 1 && (a.ks == 3 || a.ks == 1)) || (a.kt == 3 && a.ks == 3);
   // With 128 x 256 tiles the 1-workgroup-per-CU kernel cannot hide its fp32 epilogue
   // behind another workgroup's K loop; those layers stay on the 2-per-CU kernel.
@@ -573,7 +590,7 @@ bool conv_wide_fits(const ConvArgs& a) {
 
 hipError_t launch_conv_wide(ConvArgs& a, hipStream_t s) {
   a.gn_chunk = 0;
-  if (a.cin % 64 != 0 || a.cout_pad % 128 != 0) return hipErrorInvalidValue;
+  if (a.cin % 32 != 0 || a.cout_pad % 128 != 0) return hipErrorInvalidValue;
   // split operands feed the sub-pixel form only, whose fp8 part needs 64-channel blocks and
   // its scale; the fp8 split output likewise needs 64-channel blocks
   if (a.sub != a.x_split || (a.sub && (a.kt != 1 || a.ks != 3 || a.cin % 64 != 0 || !a.sub_scale)))

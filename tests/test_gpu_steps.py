@@ -67,17 +67,19 @@ def test_conv3x3_step(gpu_lib, dtype, case):
     assert_close(got, ref, *ACC_TOL, what=f"conv3x3 {case}")
 
 
-def test_conv3x3_step_wide_tiles(gpu_lib):
+@pytest.mark.parametrize("cin", [64, 96])
+def test_conv3x3_step_wide_tiles(gpu_lib, cin):
     # enough 256-pixel tiles for the 256-channel output tiles of the wide kernel (ragged
-    # rows, a one-row band, residual)
-    B, cin, cout, H, W, starts = 1, 64, 256, 130, 1030, (0, 40, 41, 130)
+    # rows, a one-row band, residual); 96 input channels: each tap's second 64-channel
+    # step half empty
+    B, cout, H, W, starts = 1, 256, 130, 1030, (0, 40, 41, 130)
     x = seeded((B, cin, H, W), 15, dtype="bf16")
     w = seeded((cout, cin, 3, 3), 16, 1 / math.sqrt(cin * 9), dtype="bf16")
     b = seeded((cout,), 17, 0.1, dtype="bf16")
     r = seeded((B, cout, H, W), 18, dtype="f32")
     ref = _conv_ref(x, w, b, False, r, "bf16")
     got = vaep.step_conv(to_dev(x, "bf16"), to_dev(w, "bf16"), to_dev(b, "bf16"), starts, residual=r.cuda())
-    assert_close(got, ref, *ACC_TOL, what="conv3x3 wide tiles")
+    assert_close(got, ref, *ACC_TOL, what=f"conv3x3 wide tiles, cin {cin}")
 
 
 @pytest.mark.parametrize("case", [
@@ -227,16 +229,18 @@ def test_causal_conv3d_step(gpu_lib, dtype, cin):
     assert_close(got, ref, *ACC_TOL, what="causal conv3d")
 
 
-def test_causal_conv3d_step_wide_tiles(gpu_lib):
-    # causal 3x3x3 conv on 256-channel output tiles of the wide kernel
-    x = seeded((1, 64, 4, 130, 260), 45, dtype="bf16")
-    w = seeded((256, 64, 3, 3, 3), 46, 1 / math.sqrt(64 * 27), dtype="bf16")
+@pytest.mark.parametrize("cin", [64, 96])
+def test_causal_conv3d_step_wide_tiles(gpu_lib, cin):
+    # causal 3x3x3 conv on 256-channel output tiles of the wide kernel (96 input channels:
+    # half-empty second channel step per tap)
+    x = seeded((1, cin, 4, 130, 260), 45, dtype="bf16")
+    w = seeded((256, cin, 3, 3, 3), 46, 1 / math.sqrt(cin * 27), dtype="bf16")
     b = seeded((256,), 47, 0.1, dtype="bf16")
     r = seeded((1, 256, 4, 130, 260), 48, dtype="f32")
     ref = _conv_ref(x, w, b, True, r, "bf16")
     got = vaep.step_conv(to_dev(x, "bf16"), to_dev(w, "bf16"), to_dev(b, "bf16"), (0, 61, 62, 130), causal=True,
                          residual=r.cuda())
-    assert_close(got, ref, *ACC_TOL, what="causal conv3d, wide tiles")
+    assert_close(got, ref, *ACC_TOL, what=f"causal conv3d, wide tiles, cin {cin}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
